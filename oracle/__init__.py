@@ -1,0 +1,279 @@
+"""CPU oracle for the QLoRA NF4 hot path -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The product library never imports it
+and shares no code with it.
+
+This module is a thin ctypes layer over ``qlora_oracle.c`` (plain C, fp64
+GEMM loops, fp32 quantiser written step by step from the pages).  Citations
+of the passages each step follows are in the C source.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from dataclasses import dataclass
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "qlora_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+CFLAGS = ["-O2", "-std=c11", "-fno-fast-math", "-ffp-contract=off", "-fopenmp",
+          "-fPIC", "-shared"]
+
+OK, EINVAL, ENONFINITE = 0, 1, 2
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (no HIP, no SIMD intrinsics, no BLAS)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.run(["gcc", *CFLAGS, "-o", tmp, _SRC, "-lm"], check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        L = ctypes.CDLL(_LIB)
+        L.orc_codebook.argtypes = [_P]
+        L.orc_nf4_code.argtypes = [ctypes.c_float]
+        L.orc_nf4_code.restype = ctypes.c_int
+        L.orc_nf4_codes.argtypes = [_P, _I64, _P]
+        L.orc_e4m3_decode.argtypes = [ctypes.c_uint8]
+        L.orc_e4m3_decode.restype = ctypes.c_float
+        L.orc_e4m3_encode.argtypes = [ctypes.c_float]
+        L.orc_e4m3_encode.restype = ctypes.c_uint8
+        L.orc_bf16_rne.argtypes = [ctypes.c_float]
+        L.orc_bf16_rne.restype = ctypes.c_uint16
+        L.orc_scale_mean.argtypes = [_P, _I64]
+        L.orc_scale_mean.restype = ctypes.c_float
+        L.orc_quantize.argtypes = [_P, _I64, ctypes.c_int, _P, _P, _P, _P, _P]
+        L.orc_quantize.restype = ctypes.c_int
+        L.orc_dequantize.argtypes = [_P, _I64, ctypes.c_int, _P, _P, _P, _P, _P, _P]
+        L.orc_lora_down.argtypes = [_P, _P, _I64, ctypes.c_int, _P, _I64, _P]
+        L.orc_qlora_fwd.argtypes = [_P, _I64, _I64, _P, _P, _P, ctypes.c_int,
+                                    ctypes.c_double, _P, _I64, _P, _P]
+        L.orc_lora_up_grad.argtypes = [_P, _P, _I64, ctypes.c_int, _P, _I64, _P]
+        L.orc_qlora_dx.argtypes = [_P, _I64, _I64, _P, _P, _P, ctypes.c_int,
+                                   ctypes.c_double, _P, _I64, _P, _P]
+        L.orc_adapter_grads.argtypes = [_P, _P, _P, _P, _I64, _I64, _I64,
+                                        ctypes.c_int, ctypes.c_double, _P, _P]
+        L.orc_num_threads.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _ptr(a: np.ndarray | None):
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"], "oracle arrays must be contiguous"
+    return a.ctypes.data
+
+
+def _bf16_bits(a) -> np.ndarray:
+    """bf16 data as uint16 bit patterns (numpy uint16 or a torch bf16 tensor)."""
+    if isinstance(a, np.ndarray):
+        assert a.dtype == np.uint16
+        return np.ascontiguousarray(a)
+    import torch  # only to read torch bf16 tensors handed over by tests
+    assert a.dtype == torch.bfloat16
+    return np.ascontiguousarray(a.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16))
+
+
+def num_threads() -> int:
+    return int(lib().orc_num_threads())
+
+
+# ---------------------------------------------------------------- codebook
+def codebook() -> np.ndarray:
+    out = np.zeros(16, np.float32)
+    lib().orc_codebook(_ptr(out))
+    return out
+
+
+def nf4_codes(n: np.ndarray) -> np.ndarray:
+    n = np.ascontiguousarray(n, dtype=np.float32)
+    out = np.empty(n.size, np.uint8)
+    lib().orc_nf4_codes(_ptr(n), n.size, _ptr(out))
+    return out.reshape(n.shape)
+
+
+def e4m3_encode(x: float) -> int:
+    return int(lib().orc_e4m3_encode(float(x)))
+
+
+def e4m3_decode(q: int) -> float:
+    return float(lib().orc_e4m3_decode(int(q)))
+
+
+def bf16_rne(v: float) -> int:
+    return int(lib().orc_bf16_rne(float(v)))
+
+
+def scale_mean(absmax: np.ndarray) -> np.float32:
+    a = np.ascontiguousarray(absmax, dtype=np.float32)
+    return np.float32(lib().orc_scale_mean(_ptr(a), a.size))
+
+
+# ---------------------------------------------------------------- quantize
+@dataclass
+class State:
+    packed: np.ndarray   # uint8 [32*nb]
+    absmax: np.ndarray   # float32 [nb]   first-level scales (DQ-off state)
+    qscale: np.ndarray   # uint8 [nb]     E4M3FN codes (DQ state)
+    scale2: np.ndarray   # float32 [ng]
+    offset: np.float32   # mean of the first-level scales
+    rows: int
+    cols: int
+    double_quant: bool
+
+    @property
+    def n(self) -> int:
+        return self.rows * self.cols
+
+
+def quantize(W: np.ndarray, double_quant: bool = True) -> State:
+    """NF4 block-64 quantisation (+ double quantisation) of an fp32 array.
+
+    Raises ValueError on empty or non-finite input, like the page's listing.
+    """
+    W = np.ascontiguousarray(W, dtype=np.float32)
+    rows, cols = (W.shape if W.ndim == 2 else (1, W.size))
+    n = W.size
+    nb = max((n + 63) // 64, 1)
+    ng = (nb + 255) // 256
+    packed = np.zeros(32 * nb, np.uint8)
+    absmax = np.zeros(nb, np.float32)
+    qscale = np.zeros(nb, np.uint8)
+    scale2 = np.zeros(ng, np.float32)
+    offset = np.zeros(1, np.float32)
+    st = lib().orc_quantize(_ptr(W), n, int(bool(double_quant)), _ptr(packed), _ptr(absmax),
+                            _ptr(qscale), _ptr(scale2), _ptr(offset))
+    if st == EINVAL:
+        raise ValueError("quantizer input: empty")
+    if st == ENONFINITE:
+        raise ValueError("quantizer input: non-finite")
+    return State(packed, absmax, qscale, scale2, offset[0], rows, cols, bool(double_quant))
+
+
+def dequantize(s: State, want_f32: bool = True, want_bf16: bool = True):
+    """Returns (fp32 [rows, cols] or None, bf16 bits uint16 [rows, cols] or None)."""
+    n = s.n
+    f32 = np.empty(n, np.float32) if want_f32 else None
+    b16 = np.empty(n, np.uint16) if want_bf16 else None
+    off = np.array([s.offset], np.float32)
+    lib().orc_dequantize(_ptr(s.packed), n, int(s.double_quant), _ptr(s.absmax), _ptr(s.qscale),
+                         _ptr(s.scale2), _ptr(off), _ptr(f32), _ptr(b16))
+    shape = (s.rows, s.cols)
+    return (f32.reshape(shape) if f32 is not None else None,
+            b16.reshape(shape) if b16 is not None else None)
+
+
+def codes_of(s: State) -> np.ndarray:
+    """Unpacked 4-bit codes (uint8 [32*nb*2]) of a state."""
+    p = s.packed
+    c = np.empty(2 * p.size, np.uint8)
+    c[0::2] = p & 15
+    c[1::2] = p >> 4
+    return c
+
+
+# ---------------------------------------------------------------- linear
+def _rows_arg(rows):
+    if rows is None:
+        return None
+    return np.ascontiguousarray(rows, dtype=np.int64)
+
+
+def lora_down(X, A, rows=None) -> np.ndarray:
+    Xb, Ab = _bf16_bits(X), _bf16_bits(A)
+    M, K = Xb.shape
+    r = Ab.shape[0]
+    rr = _rows_arg(rows)
+    nrows = M if rr is None else rr.size
+    u = np.empty((nrows, r), np.float64)
+    lib().orc_lora_down(_ptr(Xb), _ptr(Ab), K, r, _ptr(rr), nrows, _ptr(u))
+    return u
+
+
+def qlora_fwd(Wd: np.ndarray, X, A, B, s: float, rows=None):
+    """Y = X W'^T + s (X A^T) B^T in fp64 for the listed rows (all if None).
+
+    Returns (Y [nrows, N] fp64, u [nrows, r] fp64)."""
+    Wd = np.ascontiguousarray(Wd, dtype=np.float32)
+    Xb, Ab, Bb = _bf16_bits(X), _bf16_bits(A), _bf16_bits(B)
+    N, K = Wd.shape
+    M = Xb.shape[0]
+    r = Ab.shape[0]
+    assert Xb.shape[1] == K and Ab.shape == (r, K) and Bb.shape == (N, r)
+    rr = _rows_arg(rows)
+    nrows = M if rr is None else rr.size
+    Y = np.empty((nrows, N), np.float64)
+    u = np.empty((nrows, r), np.float64)
+    lib().orc_qlora_fwd(_ptr(Wd), N, K, _ptr(Xb), _ptr(Ab), _ptr(Bb), r, float(s), _ptr(rr),
+                        nrows, _ptr(Y), _ptr(u))
+    return Y, u
+
+
+def lora_up_grad(G, B, rows=None) -> np.ndarray:
+    Gb, Bb = _bf16_bits(G), _bf16_bits(B)
+    M, N = Gb.shape
+    r = Bb.shape[1]
+    rr = _rows_arg(rows)
+    nrows = M if rr is None else rr.size
+    v = np.empty((nrows, r), np.float64)
+    lib().orc_lora_up_grad(_ptr(Gb), _ptr(Bb), N, r, _ptr(rr), nrows, _ptr(v))
+    return v
+
+
+def qlora_dx(Wd: np.ndarray, G, A, B, s: float, rows=None):
+    """dX = G W' + s (G B) A in fp64 for the listed rows.  Returns (dX, v)."""
+    Wd = np.ascontiguousarray(Wd, dtype=np.float32)
+    Gb, Ab, Bb = _bf16_bits(G), _bf16_bits(A), _bf16_bits(B)
+    N, K = Wd.shape
+    M = Gb.shape[0]
+    r = Ab.shape[0]
+    assert Gb.shape[1] == N and Ab.shape == (r, K) and Bb.shape == (N, r)
+    rr = _rows_arg(rows)
+    nrows = M if rr is None else rr.size
+    dX = np.empty((nrows, K), np.float64)
+    v = np.empty((nrows, r), np.float64)
+    lib().orc_qlora_dx(_ptr(Wd), N, K, _ptr(Gb), _ptr(Ab), _ptr(Bb), r, float(s), _ptr(rr),
+                       nrows, _ptr(dX), _ptr(v))
+    return dX, v
+
+
+def adapter_grads(X, G, A, B, s: float):
+    """dA = s (G B)^T X [r, K] and dB = s G^T (X A^T) [N, r], fp64, over all rows."""
+    Xb, Gb, Ab, Bb = _bf16_bits(X), _bf16_bits(G), _bf16_bits(A), _bf16_bits(B)
+    M, K = Xb.shape
+    N = Gb.shape[1]
+    r = Ab.shape[0]
+    u = lora_down(Xb, Ab)
+    v = lora_up_grad(Gb, Bb)
+    dA = np.empty((r, K), np.float64)
+    dB = np.empty((N, r), np.float64)
+    lib().orc_adapter_grads(_ptr(Xb), _ptr(Gb), _ptr(u), _ptr(v), M, N, K, r, float(s),
+                            _ptr(dA), _ptr(dB))
+    return dA, dB
+
+
+def rel_frobenius(out, ref) -> float:
+    out = np.asarray(out, np.float64)
+    ref = np.asarray(ref, np.float64)
+    den = np.linalg.norm(ref)
+    num = np.linalg.norm(out - ref)
+    return float(num / den) if den > 0 else float(num)
