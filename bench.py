@@ -1,0 +1,373 @@
+"""Benchmark of the QLoRA NF4 hot path on one MI355X.
+
+One step = one pass of the whole hot path over one synthetic batch of the
+training-shaped workload (W 4096x4096 fp32 ~ N(0, 0.02), x and dY bf16
+[8192, 4096] ~ N(0, 1), rank-16 bf16 adapters ~ N(0, 0.01), alpha 32):
+    nf4_quantize_dq -> nf4_dequantize (bf16) -> qlora_linear_fwd -> qlora_linear_bwd
+The headline value is the fwd+bwd algorithmic FLOPs of the step divided by
+the wall time of the whole step (quantize and dequantize included).
+Also printed in the same JSON line: the roofline of the dominant kernel,
+the CPU oracle on a bounded sample, and per-kernel-group rates for the other
+workloads (dequantize/quantize 4096x4096, decode forward, one decoder layer).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+
+
+# ----------------------------------------------------------------- accounting
+def fwd_flops(M, N, K, r):
+    """Algorithmic FLOPs of y = x W'^T + s (x A^T) B^T (dequant not counted)."""
+    return 2 * M * N * K + 2 * M * r * (K + N)
+
+
+def bwd_flops(M, N, K, r):
+    """dX = G W' + s (G B) A, dB = s G^T u, dA = s v^T x (u saved by fwd)."""
+    return 2 * M * N * K + 2 * M * r * (N + K) + 2 * M * N * r + 2 * M * K * r
+
+
+def state_bytes(rows, cols):
+    n = rows * cols
+    nb = (n + 63) // 64
+    ng = (nb + 255) // 256
+    return 32 * nb + nb + 4 * ng + 4
+
+
+def dequant_bytes(rows, cols, out_bytes=2):
+    return state_bytes(rows, cols) + out_bytes * rows * cols
+
+
+def quant_bytes(rows, cols):
+    return 4 * rows * cols + state_bytes(rows, cols)
+
+
+def decode_bytes(rows, cols, M, r):
+    """Algorithmic HBM bytes of one decode forward: the NF4 state, x, A, B, y."""
+    return state_bytes(rows, cols) + 2 * M * cols + 2 * r * cols + 2 * rows * r + 2 * M * rows
+
+
+def throughput(work, seconds):
+    if not (math.isfinite(seconds) and seconds > 0):
+        raise ValueError("invalid elapsed time")
+    return work / seconds
+
+
+def measure(step, batches, tokens, clock, sync, warmup):
+    """Warmup excluded, synchronize, clock, run the measured batches,
+    synchronize, clock; returns (seconds, work units).  (The measurement
+    order of the page-2 measurement reference, without its allocator
+    counters.)"""
+    if type(warmup) is not int or warmup < 0 or len(batches) <= warmup:
+        raise ValueError("warmup and a non-empty measured suffix are required")
+    for b in batches[:warmup]:
+        step(b)
+    sync()
+    t0 = clock()
+    for b in batches[warmup:]:
+        step(b)
+    sync()
+    elapsed = clock() - t0
+    if not (math.isfinite(elapsed) and elapsed > 0):
+        raise ValueError("invalid elapsed time")
+    return elapsed, sum(tokens(b) for b in batches[warmup:])
+
+
+# ----------------------------------------------------------------- GPU helpers
+def _bf16(torch, a):
+    import numpy as np
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def _event_time_ms(torch, fn, iters):
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for i in range(iters):
+        fn(i)
+    e1.record(st)
+    e1.synchronize()
+    return e0.elapsed_time(e1) / iters
+
+
+def _median_min(xs):
+    s = sorted(xs)
+    return s[len(s) // 2], s[0]
+
+
+def bench_train(torch, qn, wl, steps, warmup):
+    cfg = wl.CONFIGS[4]
+    N, K, M, r, alpha = cfg["rows"], cfg["cols"], cfg["M"], cfg["r"], cfg["alpha"]
+    W, x, A, B, dY = wl.linear_inputs(N, K, M, r, cfg=4)
+    Wd = torch.from_numpy(W).cuda()
+    xd, Ad, Bd, Gd = (_bf16(torch, a) for a in (x, A, B, dY))
+    st = qn.empty_state(N, K, "cuda")
+    L = qn.load_library()
+    qws = torch.empty(L.nf4_quantize_dq_workspace(N, K), dtype=torch.uint8, device="cuda")
+    fws = torch.empty(L.qlora_linear_workspace(M, N, K, r, 0), dtype=torch.uint8, device="cuda")
+    bws = torch.empty(L.qlora_linear_workspace(M, N, K, r, 1), dtype=torch.uint8, device="cuda")
+    wbf = torch.empty((N, K), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+
+    def step(_):
+        qn.nf4_quantize_dq(Wd, out=st, workspace=qws)
+        qn.nf4_dequantize(st, torch.bfloat16, out=wbf)
+        _, u = qn.qlora_linear_fwd(st, xd, Ad, Bd, alpha, y=y, workspace=fws)
+        qn.qlora_linear_bwd(st, xd, Gd, Ad, Bd, alpha, u, workspace=bws)
+
+    batches = list(range(warmup + steps))
+    secs, nsteps = measure(step, batches, lambda b: 1, time.perf_counter,
+                           torch.cuda.synchronize, warmup)
+    flops = fwd_flops(M, N, K, r) + bwd_flops(M, N, K, r)
+    res = dict(seconds=secs, steps=nsteps, ms_per_step=1e3 * secs / nsteps,
+               tflops=flops * nsteps / secs / 1e12, flops_per_step=flops)
+
+    # dominant kernels: time the forward and backward calls with HIP events on
+    # the stream the library launches on (torch's current stream)
+    u = torch.empty((M, r), dtype=torch.float32, device="cuda")
+
+    def fwd(_):
+        L.qlora_linear_fwd(qn.ctypes.byref(st.c_struct()), xd.data_ptr(), M, Ad.data_ptr(),
+                           Bd.data_ptr(), r, float(alpha), y.data_ptr(), u.data_ptr(),
+                           fws.data_ptr(), fws.numel(), torch.cuda.current_stream().cuda_stream)
+
+    dX = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+    dA = torch.empty((r, K), dtype=torch.float32, device="cuda")
+    dB = torch.empty((N, r), dtype=torch.float32, device="cuda")
+
+    def bwd(_):
+        L.qlora_linear_bwd(qn.ctypes.byref(st.c_struct()), xd.data_ptr(), Gd.data_ptr(), M,
+                           Ad.data_ptr(), Bd.data_ptr(), r, float(alpha), u.data_ptr(),
+                           dX.data_ptr(), dA.data_ptr(), dB.data_ptr(), bws.data_ptr(),
+                           bws.numel(), torch.cuda.current_stream().cuda_stream)
+
+    for f in (fwd, bwd):
+        f(0)
+    torch.cuda.synchronize()
+    fwd_ms = [_event_time_ms(torch, fwd, 20) for _ in range(5)]
+    bwd_ms = [_event_time_ms(torch, bwd, 20) for _ in range(5)]
+    res["fwd_call_ms"] = _median_min(fwd_ms)
+    res["bwd_call_ms"] = _median_min(bwd_ms)
+    res["fwd_flops"] = fwd_flops(M, N, K, r)
+    res["bwd_flops"] = bwd_flops(M, N, K, r)
+    return res
+
+
+def bench_extras(torch, qn, wl):
+    import numpy as np
+    L = qn.load_library()
+    out = {}
+    # quantize + dequantize of the 4096x4096 outlier weight, rotated copies
+    W2 = torch.from_numpy(wl.outlier_weight()).cuda()
+    R = 12
+    states = [qn.nf4_quantize_dq(W2) for _ in range(R)]
+    outs = [torch.empty((4096, 4096), dtype=torch.bfloat16, device="cuda") for _ in range(R)]
+    torch.cuda.synchronize()
+    ms = [_event_time_ms(torch, lambda i: qn.nf4_dequantize(states[i % R], torch.bfloat16,
+                                                             out=outs[i % R]), 48)
+          for _ in range(5)]
+    med, mn = _median_min(ms)
+    nbytes = dequant_bytes(4096, 4096, 2)
+    out["dequant_bf16_4096x4096"] = dict(ms=med, ms_min=mn, bytes=nbytes,
+                                         GBs=nbytes / med / 1e6,
+                                         hbm_frac=nbytes / med / 1e6 / HBM_PEAK_GBS)
+    outs32 = [torch.empty((4096, 4096), dtype=torch.float32, device="cuda") for _ in range(6)]
+    ms = [_event_time_ms(torch, lambda i: qn.nf4_dequantize(states[i % 6], torch.float32,
+                                                             out=outs32[i % 6]), 24)
+          for _ in range(5)]
+    med, mn = _median_min(ms)
+    nbytes = dequant_bytes(4096, 4096, 4)
+    out["dequant_f32_4096x4096"] = dict(ms=med, ms_min=mn, bytes=nbytes,
+                                        GBs=nbytes / med / 1e6,
+                                        hbm_frac=nbytes / med / 1e6 / HBM_PEAK_GBS)
+    del outs, outs32
+    # quantize: the call synchronizes (non-finite check), so this is the
+    # call's wall time including that round trip
+    Ws = [torch.from_numpy(wl.weight(4096, 4096, 90 + i)).cuda() for i in range(4)]
+    qws = torch.empty(L.nf4_quantize_dq_workspace(4096, 4096), dtype=torch.uint8, device="cuda")
+    for i in range(3):
+        qn.nf4_quantize_dq(Ws[i % 4], out=states[i % R], workspace=qws)
+    t0 = time.perf_counter()
+    n_q = 40
+    for i in range(n_q):
+        qn.nf4_quantize_dq(Ws[i % 4], out=states[i % R], workspace=qws)
+    torch.cuda.synchronize()
+    q_ms = (time.perf_counter() - t0) * 1e3 / n_q
+    nbytes = quant_bytes(4096, 4096)
+    out["quantize_dq_call_4096x4096"] = dict(ms=q_ms, bytes=nbytes, GBs=nbytes / q_ms / 1e6,
+                                             note="wall time per call incl. its stream sync")
+    del Ws, states, W2
+    torch.cuda.empty_cache()
+
+    # decode forward 14336x4096, M = 1, 4, 16, rotated weight copies
+    cfg = wl.CONFIGS[3]
+    N, K, r, alpha = cfg["rows"], cfg["cols"], cfg["r"], cfg["alpha"]
+    Wq = torch.from_numpy(wl.weight(N, K, wl.SEED_W + 3)).cuda()
+    base = qn.nf4_quantize_dq(Wq)
+    R = 20
+    copies = [qn.NF4State(base.packed.clone(), base.qscale.clone(), base.scale2.clone(),
+                          base.offset.clone(), N, K) for _ in range(R)]
+    del Wq
+    A = _bf16(torch, wl.normal_bf16((r, K), wl.SEED_A + 3, 0.01))
+    B = _bf16(torch, wl.normal_bf16((N, r), wl.SEED_B + 3, 0.01))
+    dec = {}
+    for M in cfg["Ms"]:
+        x = _bf16(torch, wl.normal_bf16((M, K), wl.SEED_X + 3, 1.0))
+        ws = torch.empty(L.qlora_linear_workspace(M, N, K, r, 0), dtype=torch.uint8, device="cuda")
+        ys = [torch.empty((M, N), dtype=torch.bfloat16, device="cuda") for _ in range(R)]
+        us = [torch.empty((M, r), dtype=torch.float32, device="cuda") for _ in range(R)]
+        stream = torch.cuda.current_stream().cuda_stream
+        structs = [c.c_struct() for c in copies]
+
+        def call(i):
+            L.qlora_linear_fwd(qn.ctypes.byref(structs[i % R]), x.data_ptr(), M, A.data_ptr(),
+                               B.data_ptr(), r, float(alpha), ys[i % R].data_ptr(),
+                               us[i % R].data_ptr(), ws.data_ptr(), ws.numel(), stream)
+        call(0)
+        torch.cuda.synchronize()
+        ms = [_event_time_ms(torch, call, 100) for _ in range(5)]
+        med, mn = _median_min(ms)
+        nbytes = decode_bytes(N, K, M, r)
+        dec[f"M{M}"] = dict(ms=med, ms_min=mn, bytes=nbytes, GBs=nbytes / med / 1e6,
+                            hbm_frac=nbytes / med / 1e6 / HBM_PEAK_GBS)
+    out["decode_fwd_14336x4096"] = dec
+    del copies, base
+    torch.cuda.empty_cache()
+
+    # one decoder layer's seven linears, M = 4096, fwd + bwd
+    cfg = wl.CONFIGS[5]
+    M, r, alpha = cfg["M"], cfg["r"], cfg["alpha"]
+    layers = []
+    for idx, (name, N, K) in enumerate(wl.DECODER_LINEARS):
+        W, x, A, B, G = wl.linear_inputs(N, K, M, r, cfg=5, index=idx)
+        st = qn.nf4_quantize_dq(torch.from_numpy(W).cuda())
+        layers.append(dict(st=st, x=_bf16(torch, x), A=_bf16(torch, A), B=_bf16(torch, B),
+                           G=_bf16(torch, G), N=N, K=K,
+                           fws=torch.empty(L.qlora_linear_workspace(M, N, K, r, 0),
+                                           dtype=torch.uint8, device="cuda"),
+                           bws=torch.empty(L.qlora_linear_workspace(M, N, K, r, 1),
+                                           dtype=torch.uint8, device="cuda"),
+                           y=torch.empty((M, N), dtype=torch.bfloat16, device="cuda")))
+
+    def layer_step(_):
+        for d in layers:
+            _, u = qn.qlora_linear_fwd(d["st"], d["x"], d["A"], d["B"], alpha, y=d["y"],
+                                       workspace=d["fws"])
+            qn.qlora_linear_bwd(d["st"], d["x"], d["G"], d["A"], d["B"], alpha, u,
+                                workspace=d["bws"])
+    layer_step(0)
+    torch.cuda.synchronize()
+    ms = [_event_time_ms(torch, layer_step, 3) for _ in range(5)]
+    med, mn = _median_min(ms)
+    flops = sum(fwd_flops(M, d["N"], d["K"], r) + bwd_flops(M, d["N"], d["K"], r) for d in layers)
+    out["decoder_layer_7_linears_M4096"] = dict(ms=med, ms_min=mn, flops=flops,
+                                                TFLOPs=flops / med / 1e9,
+                                                mfma_frac=flops / med / 1e9 / BF16_PEAK_TFLOPS,
+                                                adapter_params=wl.adapter_params(r=r))
+    del layers
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline(wl):
+    """The oracle, untuned, on a bounded sample of the training workload:
+    forward and input-gradient rows for a row sample, adapter gradients over
+    a row block; reported as sampled FLOPs per second."""
+    import numpy as np
+    import oracle
+    cfg = wl.CONFIGS[4]
+    N, K, M, r, alpha = cfg["rows"], cfg["cols"], cfg["M"], cfg["r"], cfg["alpha"]
+    W, x, A, B, dY = wl.linear_inputs(N, K, M, r, cfg=4)
+    s = alpha / r
+    rows = np.arange(0, M, M // 64)[:64]
+    mb = 1024
+    t0 = time.perf_counter()
+    st = oracle.quantize(W)
+    Wd, _ = oracle.dequantize(st, want_bf16=False)
+    t_q = time.perf_counter() - t0
+    t1 = time.perf_counter()
+    oracle.qlora_fwd(Wd, x, A, B, s, rows=rows)
+    oracle.qlora_dx(Wd, dY, A, B, s, rows=rows)
+    oracle.adapter_grads(x[:mb], dY[:mb], A, B, s)
+    t_lin = time.perf_counter() - t1
+    nr = len(rows)
+    flops = (fwd_flops(nr, N, K, r) + 2 * nr * N * K + 2 * nr * r * (N + K)
+             + 2 * mb * r * (K + N) + 2 * mb * N * r + 2 * mb * K * r)
+    return dict(value=flops / t_lin / 1e12, unit="TFLOP/s", cores=oracle.num_threads(),
+                kind="oracle",
+                sample=(f"fp64 oracle: y and dX rows for {nr} of {M} rows, dA/dB over {mb} "
+                        f"rows, at 4096x4096 r=16 ({flops / 1e9:.1f} GFLOP in {t_lin:.1f} s); "
+                        f"quantize+dequantize 4096x4096 took {t_q:.2f} s"),
+                seconds=t_lin)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-extras", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only: the hot path is measured "
+                                   "on one MI355X; multi-GPU sharding is a design note, not "
+                                   "built", "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+    import quantized_fine_tuning_nf4_amd as qn
+    import workloads as wl
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    qn.load_library()
+    print(f"[bench] training step: {args.warmup} warmup + {args.steps} timed", file=sys.stderr,
+          flush=True)
+    tr = bench_train(torch, qn, wl, args.steps, args.warmup)
+    fwd_med = tr["fwd_call_ms"][0]
+    bwd_med = tr["bwd_call_ms"][0]
+    fwd_tf = tr["fwd_flops"] / fwd_med / 1e9
+    roof = dict(bound="mfma", kernel="k_qgemm_fwd (call: lora-down + fused dequant GEMM)",
+                achieved=fwd_tf, peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                frac=fwd_tf / BF16_PEAK_TFLOPS, traffic=None,
+                launch_ms=fwd_med, flops_per_launch=tr["fwd_flops"],
+                bwd_call=dict(ms=bwd_med, TFLOPs=tr["bwd_flops"] / bwd_med / 1e9,
+                              frac=tr["bwd_flops"] / bwd_med / 1e9 / BF16_PEAK_TFLOPS))
+    extras = {}
+    if not args.no_extras:
+        print("[bench] extras", file=sys.stderr, flush=True)
+        extras = bench_extras(torch, qn, wl)
+    cpu = None
+    if not args.no_cpu:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(wl)
+    line = {
+        "metric": "QLoRA linear fwd+bwd TFLOP/s and NF4 dequant GB/s, % of MI355X roofline",
+        "value": tr["tflops"], "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": tr["ms_per_step"], "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "train_fwd_bwd_4096x4096_M8192", "rows": 4096, "cols": 4096,
+                   "M": 8192, "r": 16, "alpha": 32,
+                   "step": "nf4_quantize_dq + nf4_dequantize(bf16) + qlora_linear_fwd + "
+                           "qlora_linear_bwd", "flops_per_step": tr["flops_per_step"]},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "extras": extras,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

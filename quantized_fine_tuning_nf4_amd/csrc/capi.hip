@@ -1,0 +1,272 @@
+// C ABI of the QLoRA NF4 library: argument checks, workspace layout and
+// launch order.  Every call checks its arguments on the host first and
+// launches nothing on error.
+#include <hip/hip_runtime.h>
+
+#include <cstring>
+
+#include "../../include/qlora_nf4.h"
+#include "qn_device.h"
+#include "qn_internal.h"
+
+namespace {
+
+using namespace qn;
+
+// Carves 256-byte aligned pieces out of a caller workspace; with a null
+// base it only measures.
+struct Carver {
+  char* base;
+  size_t used = 0;
+  explicit Carver(void* b) : base(static_cast<char*>(b)) {}
+  template <typename T>
+  T* take(size_t count) {
+    used = (used + 255) & ~size_t(255);
+    T* p = base ? reinterpret_cast<T*>(base + used) : nullptr;
+    used += count * sizeof(T);
+    return p;
+  }
+};
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int64_t blocks_of(int64_t n) { return (n + kBlock - 1) / kBlock; }
+int64_t groups_of(int64_t nb) { return (nb + kGroup - 1) / kGroup; }
+int64_t pow2_at_least(int64_t v) {
+  int64_t p = 1;
+  while (p < v) p *= 2;
+  return p;
+}
+
+qn_status from_hip(hipError_t e) { return e == hipSuccess ? QN_OK : QN_EDEVICE; }
+
+struct QuantWs {
+  float* absmax;
+  double* part;
+  int64_t part_len;
+  int* flag;
+};
+
+QuantWs carve_quant(Carver& c, int64_t n) {
+  const int64_t nb = blocks_of(n), ng = groups_of(nb);
+  QuantWs w;
+  w.absmax = c.take<float>(nb);
+  w.part_len = pow2_at_least(ng);
+  w.part = c.take<double>(w.part_len);
+  w.flag = c.take<int>(1);
+  return w;
+}
+
+qn_status check_state(const qn_nf4dq* w) {
+  if (!w || !w->packed || !w->qscale || !w->scale2 || !w->offset) return QN_EINVAL;
+  if (w->rows < 1 || w->cols < 1) return QN_EINVAL;
+  if (w->rows > (INT64_MAX / 2) / w->cols) return QN_EINVAL;
+  if (!aligned16(w->packed) || !aligned16(w->qscale) || !aligned16(w->scale2) ||
+      !aligned16(w->offset))
+    return QN_EALIGN;
+  return QN_OK;
+}
+
+qn_status check_linear(const qn_nf4dq* w, int64_t M, int r) {
+  qn_status s = check_state(w);
+  if (s != QN_OK) return s;
+  if (w->cols % kBlock != 0 || w->rows % 8 != 0) return QN_EINVAL;
+  if (r < 1 || r > 64) return QN_EINVAL;
+  if (M < 0) return QN_EINVAL;
+  return QN_OK;
+}
+
+WState to_state(const qn_nf4dq* w) {
+  return WState{w->packed, w->qscale, w->scale2, w->offset, w->rows, w->cols};
+}
+
+struct FwdWs {
+  float* u;      // [M, r] when the caller gives no u_out
+  float* upart;  // [S, M, r] when S > 1
+  int S;
+};
+
+FwdWs carve_fwd(Carver& c, int64_t M, int64_t cols, int r, bool need_u) {
+  FwdWs f;
+  f.S = thin_nt_slices(M, cols);
+  f.u = need_u ? c.take<float>((size_t)M * r) : nullptr;
+  f.upart = f.S > 1 ? c.take<float>((size_t)f.S * M * r) : nullptr;
+  return f;
+}
+
+struct BwdWs {
+  FwdWs fu;      // recomputed u (if not saved)
+  uint16_t* Bt;  // [r, rows]
+  float* v;      // [M, r]
+  float* vpart;  // [Sv, M, r]
+  int Sv;
+  float* dBpart;  // [Sb, rows, r]
+  int Sb;
+  float* dApart;  // [Sa, cols, r]
+  int Sa;
+};
+
+BwdWs carve_bwd(Carver& c, int64_t M, int64_t rows, int64_t cols, int r, bool need_u) {
+  BwdWs b;
+  if (need_u) {
+    b.fu = carve_fwd(c, M, cols, r, true);
+  } else {
+    b.fu = FwdWs{nullptr, nullptr, 1};
+  }
+  b.Bt = c.take<uint16_t>((size_t)r * rows);
+  b.Sv = thin_nt_slices(M, rows);
+  b.v = c.take<float>((size_t)M * r);
+  b.vpart = b.Sv > 1 ? c.take<float>((size_t)b.Sv * M * r) : nullptr;
+  b.Sb = thin_tn_slices(M, rows);
+  b.dBpart = c.take<float>((size_t)b.Sb * rows * r);
+  b.Sa = thin_tn_slices(M, cols);
+  b.dApart = c.take<float>((size_t)b.Sa * cols * r);
+  return b;
+}
+
+}  // namespace
+
+extern "C" {
+
+int qn_abi_version(void) { return QN_ABI_VERSION; }
+
+const char* qn_status_str(qn_status s) {
+  switch (s) {
+    case QN_OK: return "ok";
+    case QN_EINVAL: return "invalid argument";
+    case QN_ENONFINITE: return "non-finite value in the weight";
+    case QN_EALIGN: return "pointer not 16-byte aligned";
+    case QN_EWORKSPACE: return "workspace too small";
+    case QN_EDEVICE: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+void qn_nf4_codebook(float out[16]) {
+  for (int k = 0; k < 16; ++k) {
+    uint32_t b = kNF4Bits[k];
+    std::memcpy(&out[k], &b, 4);
+  }
+}
+
+size_t nf4_quantize_dq_workspace(int64_t rows, int64_t cols) {
+  if (rows < 1 || cols < 1 || rows > INT64_MAX / 2 / cols) return 0;
+  Carver c(nullptr);
+  carve_quant(c, rows * cols);
+  return c.used;
+}
+
+qn_status nf4_quantize_dq(const float* W, int64_t rows, int64_t cols, uint8_t* packed,
+                          uint8_t* qscale, float* scale2, float* offset, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  if (!W || !packed || !qscale || !scale2 || !offset || !workspace) return QN_EINVAL;
+  if (rows < 1 || cols < 1 || rows > INT64_MAX / 2 / cols) return QN_EINVAL;
+  if (!aligned16(W) || !aligned16(packed) || !aligned16(qscale) || !aligned16(scale2) ||
+      !aligned16(offset) || (reinterpret_cast<uintptr_t>(workspace) & 255u))
+    return QN_EALIGN;
+  const int64_t n = rows * cols;
+  if (workspace_bytes < nf4_quantize_dq_workspace(rows, cols)) return QN_EWORKSPACE;
+  Carver c(workspace);
+  QuantWs ws = carve_quant(c, n);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_quantize(W, n, packed, qscale, scale2, offset, ws.absmax, ws.part,
+                                 ws.part_len, ws.flag, st);
+  if (e != hipSuccess) return QN_EDEVICE;
+  int bad = 0;
+  e = hipMemcpyAsync(&bad, ws.flag, sizeof(int), hipMemcpyDeviceToHost, st);
+  if (e != hipSuccess) return QN_EDEVICE;
+  e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return QN_EDEVICE;
+  return bad ? QN_ENONFINITE : QN_OK;
+}
+
+qn_status nf4_dequantize(const qn_nf4dq* w, qn_dtype out_dtype, void* out, void* stream) {
+  qn_status s = check_state(w);
+  if (s != QN_OK) return s;
+  if (!out || (out_dtype != QN_F32 && out_dtype != QN_BF16)) return QN_EINVAL;
+  if (!aligned16(out)) return QN_EALIGN;
+  return from_hip(launch_dequant(w->packed, w->qscale, w->scale2, w->offset, w->rows * w->cols,
+                                 out_dtype == QN_BF16, out, static_cast<hipStream_t>(stream)));
+}
+
+size_t qlora_linear_workspace(int64_t M, int64_t rows, int64_t cols, int r, int backward) {
+  if (M < 0 || rows < 1 || cols < 1 || r < 1 || r > 64) return 0;
+  Carver c(nullptr);
+  if (backward)
+    carve_bwd(c, M, rows, cols, r, true);
+  else
+    carve_fwd(c, M, cols, r, true);
+  return c.used;
+}
+
+qn_status qlora_linear_fwd(const qn_nf4dq* w, const uint16_t* x, int64_t M, const uint16_t* A,
+                           const uint16_t* B, int r, float alpha, uint16_t* y, float* u_out,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  qn_status s = check_linear(w, M, r);
+  if (s != QN_OK) return s;
+  if (M == 0) return QN_OK;
+  if (!x || !A || !B || !y) return QN_EINVAL;
+  if (!aligned16(x) || !aligned16(A) || !aligned16(B) || !aligned16(y) ||
+      (u_out && !aligned16(u_out)))
+    return QN_EALIGN;
+  Carver probe(nullptr);
+  carve_fwd(probe, M, w->cols, r, u_out == nullptr);
+  if (probe.used > 0) {
+    if (!workspace) return QN_EINVAL;
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u) return QN_EALIGN;
+    if (workspace_bytes < probe.used) return QN_EWORKSPACE;
+  }
+  Carver c(workspace);
+  FwdWs f = carve_fwd(c, M, w->cols, r, u_out == nullptr);
+  float* u = u_out ? u_out : f.u;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const float scale = alpha / (float)r;
+  hipError_t e = launch_thin_nt(x, A, M, w->cols, r, u, f.upart, f.S, st);
+  if (e == hipSuccess) e = launch_qgemm_fwd(to_state(w), x, M, u, B, r, scale, y, st);
+  return from_hip(e);
+}
+
+qn_status qlora_linear_bwd(const qn_nf4dq* w, const uint16_t* x, const uint16_t* dY, int64_t M,
+                           const uint16_t* A, const uint16_t* B, int r, float alpha,
+                           const float* u_saved, uint16_t* dX, float* dA, float* dB,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  qn_status s = check_linear(w, M, r);
+  if (s != QN_OK) return s;
+  if (!A || !B || !dA || !dB) return QN_EINVAL;
+  if (M > 0 && (!x || !dY)) return QN_EINVAL;
+  if (!aligned16(x) || !aligned16(dY) || !aligned16(A) || !aligned16(B) || !aligned16(dA) ||
+      !aligned16(dB) || (dX && !aligned16(dX)) || (u_saved && !aligned16(u_saved)))
+    return QN_EALIGN;
+  const int64_t N = w->rows, K = w->cols;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (M == 0) {
+    // empty batch: the gradients of the adapters are zero
+    hipError_t e = launch_fill_zero(dA, (int64_t)r * K, st);
+    if (e == hipSuccess) e = launch_fill_zero(dB, N * (int64_t)r, st);
+    return from_hip(e);
+  }
+  Carver probe(nullptr);
+  carve_bwd(probe, M, N, K, r, u_saved == nullptr);
+  if (!workspace) return QN_EINVAL;
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u) return QN_EALIGN;
+  if (workspace_bytes < probe.used) return QN_EWORKSPACE;
+  Carver c(workspace);
+  BwdWs b = carve_bwd(c, M, N, K, r, u_saved == nullptr);
+  const float scale = alpha / (float)r;
+  hipError_t e = hipSuccess;
+  const float* u = u_saved;
+  if (!u) {
+    e = launch_thin_nt(x, A, M, K, r, b.fu.u, b.fu.upart, b.fu.S, st);
+    u = b.fu.u;
+  }
+  // v = G B, through B^T so both operands are contiguous along the reduction
+  if (e == hipSuccess) e = launch_transpose_b(B, N, r, b.Bt, st);
+  if (e == hipSuccess) e = launch_thin_nt(dY, b.Bt, M, N, r, b.v, b.vpart, b.Sv, st);
+  if (e == hipSuccess && dX)
+    e = launch_qgemm_dx(to_state(w), dY, M, b.v, A, r, scale, dX, st);
+  if (e == hipSuccess) e = launch_thin_tn(dY, u, M, N, r, scale, dB, false, b.dBpart, b.Sb, st);
+  if (e == hipSuccess) e = launch_thin_tn(x, b.v, M, K, r, scale, dA, true, b.dApart, b.Sa, st);
+  return from_hip(e);
+}
+
+}  // extern "C"

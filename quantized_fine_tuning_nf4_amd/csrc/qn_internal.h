@@ -1,0 +1,53 @@
+// Host-side launchers of the HIP kernels (one translation unit each).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qn {
+
+hipError_t launch_quantize(const float* W, int64_t n, uint8_t* packed, uint8_t* qscale,
+                           float* scale2, float* offset, float* ws_absmax, double* ws_part,
+                           int64_t part_len, int* ws_flag, hipStream_t st);
+
+hipError_t launch_dequant(const uint8_t* packed, const uint8_t* qscale, const float* scale2,
+                          const float* offset, int64_t n, bool bf16, void* out, hipStream_t st);
+
+// Weight state as the kernels take it.
+struct WState {
+  const uint8_t* packed;
+  const uint8_t* qscale;
+  const float* scale2;
+  const float* offset;
+  int64_t rows, cols;
+};
+
+// out[M, r] (fp32) = sum over S slices of Z[M, P] * T[r, P]^T.  When S > 1
+// the slices are written to part[S][M][r] and summed in slice order into
+// out; S == 1 writes out directly.
+hipError_t launch_thin_nt(const uint16_t* Z, const uint16_t* T, int64_t M, int64_t P, int r,
+                          float* out, float* part, int S, hipStream_t st);
+int thin_nt_slices(int64_t M, int64_t P);
+
+// p[0..n) = 0 (a kernel, so it may sit in a captured graph).
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st);
+
+// Bt[r, N] = B[N, r]^T (bf16).
+hipError_t launch_transpose_b(const uint16_t* B, int64_t N, int r, uint16_t* Bt, hipStream_t st);
+
+// out = s * Z^T V reduced over the M rows: Z bf16 [M, P], V fp32 [M, r];
+// transposed == false: out fp32 [P, r]; true: out fp32 [r, P].  Split over
+// S row slices, partials part[S][P][r], summed in slice order.
+hipError_t launch_thin_tn(const uint16_t* Z, const float* V, int64_t M, int64_t P, int r,
+                          float s, float* out, bool transposed, float* part, int S,
+                          hipStream_t st);
+int thin_tn_slices(int64_t M, int64_t P);
+
+// Y[M, N] bf16 = X[M, K] * W'[N, K]^T + s * u[M, r] * B[N, r]^T.
+hipError_t launch_qgemm_fwd(const WState& w, const uint16_t* X, int64_t M, const float* u,
+                            const uint16_t* B, int r, float s, uint16_t* Y, hipStream_t st);
+
+// dX[M, K] bf16 = G[M, N] * W'[N, K] + s * v[M, r] * A[r, K].
+hipError_t launch_qgemm_dx(const WState& w, const uint16_t* G, int64_t M, const float* v,
+                           const uint16_t* A, int r, float s, uint16_t* dX, hipStream_t st);
+
+}  // namespace qn

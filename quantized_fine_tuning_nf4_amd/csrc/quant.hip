@@ -1,0 +1,294 @@
+// NF4 block-64 quantisation with double quantisation, and dequantisation,
+// for gfx950.
+//
+// What is computed (pages: "QLoRA: NF4 storage, gradients and local
+// integration", section "Exact CPU teaching quantizer and adapter gradient
+// path"; "QLoRA Deep Dive: 4-bit NormalFloat & Double Quantization
+// Internals", section "2. Squeezing More Memory: Double Quantization (DQ)"):
+//   blocks of 64 consecutive weights (flattened row-major, tail zero-padded),
+//   s_b = max|w|, n = RN32(w / s_b) (a zero block divides by 1),
+//   code = nearest NF4 level, ties to the lower code, two codes per byte with
+//   the even element in the low nibble;
+//   mu = mean of all s_b (fixed fp64 stride-halving tree), d_b = s_b - mu,
+//   per 256 scales C2 = max|d_b|, s2 = C2 / 448, q_b = E4M3FN(d_b / s2).
+//   dequant: s'_b = fmaf(e4m3(q_b), s2, mu), w' = L[c] * s'_b.
+//
+// Exact code search without a division.  code(w) = #{k : RN32(w/s) > t_k}
+// where t_k is the largest fp32 not above the k-th midpoint of adjacent
+// levels (a value that lands exactly on a midpoint is not above it, so ties
+// go to the lower code).  RN32(x) > t_k holds exactly when x exceeds the
+// midpoint mu_k between t_k and the next fp32 up: a quotient of two fp32
+// numbers is never exactly such a midpoint, so there is no tie to break.
+// x > mu_k is w > mu_k * s; mu_k has 25 significant bits and s 24, so the
+// product is exact in fp64 and the comparison is exact.  Which mu_k to test
+// is found from an approximate quotient q = w * rcp(s) and a table of 65
+// buckets of width 1/32 on [-1, 1]: every bucket holds at most one t_k and
+// every t_k lies at least 1.6e-3 from a bucket edge, far beyond the error of
+// q, so the bucket is right even when q and the true quotient straddle an
+// edge.
+#include "qn_device.h"
+#include "qn_internal.h"
+
+namespace qn {
+
+struct CodeLut {
+  double mu;  // midpoint to compare against (4.0: bucket holds no threshold)
+  int c0;     // code of the bucket's lower part
+  int pad;
+};
+
+__device__ __forceinline__ float f32_next_up(float t) {
+  uint32_t b = as_u32(t);
+  return as_f32(t > 0.f ? b + 1u : b - 1u);
+}
+__device__ __forceinline__ float f32_next_down(float t) {
+  uint32_t b = as_u32(t);
+  return as_f32(t > 0.f ? b - 1u : b + 1u);
+}
+
+// Entry j covers quotients in [(j-32)/32, (j-31)/32).
+__device__ void build_code_lut(CodeLut* lut, int j) {
+  const double lo = (double)(j - 32) * 0.03125, hi = (double)(j - 31) * 0.03125;
+  int c0 = 0;
+  double mu = 4.0;
+  for (int k = 0; k < 15; ++k) {
+    // exact midpoint of two adjacent levels, then its round-down to fp32
+    double m = ((double)as_f32(kNF4Bits[k]) + (double)as_f32(kNF4Bits[k + 1])) * 0.5;
+    float t = (float)m;
+    if ((double)t > m) t = f32_next_down(t);
+    if ((double)t < lo) {
+      ++c0;
+    } else if ((double)t < hi) {
+      mu = ((double)t + (double)f32_next_up(t)) * 0.5;
+    }
+  }
+  lut[j].mu = mu;
+  lut[j].c0 = c0;
+  lut[j].pad = 0;
+}
+
+// Max of v over each row of 16 lanes (DPP: xor 1, xor 2, half-row mirror,
+// row mirror).
+__device__ __forceinline__ uint32_t row16_max(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, false));
+  return v;
+}
+
+__device__ __forceinline__ uint32_t nf4_code(float w, double s64, double rs,
+                                             const CodeLut* lut) {
+  const double w64 = (double)w;
+  int idx = (int)__builtin_fma(w64 * rs, 32.0, 32.0);
+  idx = min(max(idx, 0), 64);
+  const CodeLut e = lut[idx];
+  return (uint32_t)e.c0 + (w64 > e.mu * s64 ? 1u : 0u);
+}
+
+// Pass 1.  One workgroup per group of 256 blocks (16384 weights); wave w
+// owns blocks 64w..64w+63 of the group, and at step j its 64 lanes read
+// 1 KB: four blocks, 16 lanes x float4 per block.
+__global__ __launch_bounds__(256) void k_quant_blocks(
+    const float* __restrict__ W, int64_t n, int64_t nb, uint8_t* __restrict__ packed,
+    float* __restrict__ absmax, double* __restrict__ part, int* __restrict__ bad) {
+  __shared__ CodeLut lut[65];
+  __shared__ double tree[kGroup];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  if (tid < 65) build_code_lut(lut, tid);
+
+  const int64_t g = blockIdx.x;
+  const int64_t e_wave = (g * kGroup + wave * 64) * kBlock;
+  const bool full = (g + 1) * (int64_t)(kGroup * kBlock) <= n;
+  float4 v[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int64_t e = e_wave + j * 256 + lane * 4;
+    if (full) {
+      v[j] = *reinterpret_cast<const float4*>(W + e);
+    } else {
+      v[j].x = e + 0 < n ? W[e + 0] : 0.f;
+      v[j].y = e + 1 < n ? W[e + 1] : 0.f;
+      v[j].z = e + 2 < n ? W[e + 2] : 0.f;
+      v[j].w = e + 3 < n ? W[e + 3] : 0.f;
+    }
+  }
+  __syncthreads();  // code table ready
+
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const uint32_t a0 = as_u32(v[j].x) & 0x7fffffffu, a1 = as_u32(v[j].y) & 0x7fffffffu;
+    const uint32_t a2 = as_u32(v[j].z) & 0x7fffffffu, a3 = as_u32(v[j].w) & 0x7fffffffu;
+    // |w| bit patterns order like the values; NaN/Inf sort above all finite
+    const uint32_t m = row16_max(max(max(a0, a1), max(a2, a3)));
+    if (m >= 0x7f800000u) *bad = 1;
+    const float s = as_f32(m);
+    const int slot = wave * 64 + 4 * j + (lane >> 4);
+    const int64_t b = g * kGroup + slot;
+    if ((lane & 15) == 0) {
+      if (b < nb) absmax[b] = s;
+      tree[slot] = (b < nb) ? (double)s : 0.0;
+    }
+    const double s64 = s > 0.f ? (double)s : 1.0;
+    const double rs = __builtin_amdgcn_rcp(s64);
+    const uint32_t c0 = nf4_code(v[j].x, s64, rs, lut), c1 = nf4_code(v[j].y, s64, rs, lut);
+    const uint32_t c2 = nf4_code(v[j].z, s64, rs, lut), c3 = nf4_code(v[j].w, s64, rs, lut);
+    if (b < nb) {
+      const int64_t e = e_wave + j * 256 + lane * 4;
+      *reinterpret_cast<uint16_t*>(packed + e / 2) =
+          (uint16_t)(c0 | (c1 << 4) | (c2 << 8) | (c3 << 12));
+    }
+  }
+  __syncthreads();
+  // fixed-order fp64 partial sum of this group's 256 scale slots
+  for (int h = kGroup / 2; h >= 1; h >>= 1) {
+    if (tid < h) tree[tid] += tree[tid + h];
+    __syncthreads();
+  }
+  if (tid == 0) part[g] = tree[0];
+}
+
+// Pass 2.  mu = RN32(S / nb), S = stride-halving tree over the group partials
+// zero-padded to len (a power of two).  One workgroup; the leading levels of
+// a long tree run in global memory, the last 2048 in LDS.
+__global__ __launch_bounds__(1024) void k_quant_mean(double* __restrict__ part, int64_t ng,
+                                                     int64_t len, int64_t nb,
+                                                     float* __restrict__ offset) {
+  __shared__ double t[2048];
+  const int tid = threadIdx.x;
+  int64_t h = len / 2;
+  for (; h >= 2048; h /= 2) {
+    for (int64_t j = tid; j < h; j += 1024) {
+      const double a = j < ng ? part[j] : 0.0;
+      const double b = j + h < ng ? part[j + h] : 0.0;
+      part[j] = a + b;
+    }
+    __threadfence();
+    __syncthreads();
+  }
+  const int64_t active = (len >= 2048) ? 2048 : len;  // == 2h unless len == 1
+  const int64_t valid = ng < active ? ng : active;
+  for (int64_t i = tid; i < active; i += 1024) t[i] = i < valid ? part[i] : 0.0;
+  __syncthreads();
+  for (h = active / 2; h >= 1; h /= 2) {
+    for (int64_t j = tid; j < h; j += 1024) t[j] += t[j + h];
+    __syncthreads();
+  }
+  if (tid == 0) *offset = (float)(t[0] / (double)nb);
+}
+
+// Pass 3.  One workgroup per group: d_b, C2, s2 and the E4M3 codes.
+__global__ __launch_bounds__(256) void k_quant_dq(const float* __restrict__ absmax, int64_t nb,
+                                                  const float* __restrict__ offset,
+                                                  uint8_t* __restrict__ qscale,
+                                                  float* __restrict__ scale2) {
+  __shared__ float red[4];
+  const int tid = threadIdx.x;
+  const int64_t b = (int64_t)blockIdx.x * kGroup + tid;
+  const float mu = *offset;
+  const float d = (b < nb) ? absmax[b] - mu : 0.f;
+  float a = __builtin_fabsf(d);
+  for (int o = 32; o >= 1; o >>= 1) a = fmaxf(a, __shfl_xor(a, o));
+  if ((tid & 63) == 0) red[tid >> 6] = a;
+  __syncthreads();
+  const float c2 = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float s2 = c2 / kE4M3Max;
+  const float x = (s2 > 0.f) ? d / s2 : 0.f;
+  if (b < nb) qscale[b] = (uint8_t)f32_to_e4m3(x);
+  if (tid == 0) scale2[blockIdx.x] = s2;
+}
+
+hipError_t launch_quantize(const float* W, int64_t n, uint8_t* packed, uint8_t* qscale,
+                           float* scale2, float* offset, float* ws_absmax, double* ws_part,
+                           int64_t part_len, int* ws_flag, hipStream_t st) {
+  const int64_t nb = (n + kBlock - 1) / kBlock;
+  const int64_t ng = (nb + kGroup - 1) / kGroup;
+  hipError_t e = hipMemsetAsync(ws_flag, 0, sizeof(int), st);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_quant_blocks, dim3((unsigned)ng), dim3(256), 0, st, W, n, nb, packed,
+                     ws_absmax, ws_part, ws_flag);
+  hipLaunchKernelGGL(k_quant_mean, dim3(1), dim3(1024), 0, st, ws_part, ng, part_len, nb,
+                     offset);
+  hipLaunchKernelGGL(k_quant_dq, dim3((unsigned)ng), dim3(256), 0, st, ws_absmax, nb, offset,
+                     qscale, scale2);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Dequantisation.  Thread-chunk c covers CH consecutive weights (CH = 8 for
+// bf16 output: one u32 of codes in, 16 B out; CH = 4 for fp32: one u16 in,
+// 16 B out).  A workgroup's 256 threads take 256 consecutive chunks, so
+// loads and stores are contiguous; each thread does UNROLL chunks.
+template <bool BF16>
+__global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ packed,
+                                                 const uint8_t* __restrict__ qscale,
+                                                 const float* __restrict__ scale2,
+                                                 const float* __restrict__ offset, int64_t n,
+                                                 void* __restrict__ out) {
+  constexpr int CH = BF16 ? 8 : 4;
+  constexpr int UNROLL = 4;
+  __shared__ float lut[16];
+  if (threadIdx.x < 16) lut[threadIdx.x] = as_f32(kNF4Bits[threadIdx.x]);
+  const int64_t nchunk = (n + CH - 1) / CH;
+  const int64_t c_first = (int64_t)blockIdx.x * 256 * UNROLL + threadIdx.x;
+  const float mu = *offset;
+  uint32_t p[UNROLL];
+  float sc[UNROLL];
+#pragma unroll
+  for (int i = 0; i < UNROLL; ++i) {
+    const int64_t c = c_first + i * 256;
+    if (c < nchunk) {
+      if (BF16)
+        p[i] = *reinterpret_cast<const uint32_t*>(packed + c * 4);
+      else
+        p[i] = *reinterpret_cast<const uint16_t*>(packed + c * 2);
+      const int64_t b = c * CH / kBlock;
+      sc[i] = dq_scale(qscale[b], scale2[b / kGroup], mu);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < UNROLL; ++i) {
+    const int64_t c = c_first + i * 256;
+    if (c >= nchunk) continue;
+    float w[CH];
+#pragma unroll
+    for (int k = 0; k < CH; ++k) w[k] = lut[(p[i] >> (4 * k)) & 15u] * sc[i];
+    const int64_t e = c * CH;
+    if (BF16) {
+      uint16_t* o = reinterpret_cast<uint16_t*>(out) + e;
+      if (e + CH <= n) {
+        u32x4 q = {pack_bf16x2(w[0], w[1]), pack_bf16x2(w[2], w[3]), pack_bf16x2(w[4], w[5]),
+                   pack_bf16x2(w[6], w[7])};
+        *reinterpret_cast<u32x4*>(o) = q;
+      } else {
+        for (int k = 0; k < CH && e + k < n; ++k)
+          o[k] = (uint16_t)(pack_bf16x2(w[k], 0.f) & 0xffffu);
+      }
+    } else {
+      float* o = reinterpret_cast<float*>(out) + e;
+      if (e + CH <= n) {
+        *reinterpret_cast<float4*>(o) = make_float4(w[0], w[1], w[2], w[3]);
+      } else {
+        for (int k = 0; k < CH && e + k < n; ++k) o[k] = w[k];
+      }
+    }
+  }
+}
+
+hipError_t launch_dequant(const uint8_t* packed, const uint8_t* qscale, const float* scale2,
+                          const float* offset, int64_t n, bool bf16, void* out, hipStream_t st) {
+  const int CH = bf16 ? 8 : 4;
+  const int64_t nchunk = (n + CH - 1) / CH;
+  const int64_t per_wg = 256 * 4;
+  const unsigned grid = (unsigned)((nchunk + per_wg - 1) / per_wg);
+  if (bf16)
+    hipLaunchKernelGGL(k_dequant<true>, dim3(grid), dim3(256), 0, st, packed, qscale, scale2,
+                       offset, n, out);
+  else
+    hipLaunchKernelGGL(k_dequant<false>, dim3(grid), dim3(256), 0, st, packed, qscale, scale2,
+                       offset, n, out);
+  return hipGetLastError();
+}
+
+}  // namespace qn

@@ -1,0 +1,123 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every function include/qlora_nf4.h declares, and rejects bad arguments on the
+host before any launch."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from tests import _golden
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def qn():
+    import quantized_fine_tuning_nf4_amd as qn
+    qn.load_library()
+    return qn
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "qlora_nf4.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\**\s*([a-z_][a-z0-9_]*)\s*\(",
+                       src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_four_calls():
+    names = declared_functions()
+    for f in ["nf4_quantize_dq", "nf4_dequantize", "qlora_linear_fwd", "qlora_linear_bwd"]:
+        assert f in names
+
+
+def test_library_exports_every_declared_symbol(qn):
+    names = declared_functions()
+    L = qn.load_library()
+    for f in names:
+        assert hasattr(L, f), f
+    assert sorted(qn.EXPORTS) == names
+
+
+def test_abi_version_and_status_strings(qn):
+    L = qn.load_library()
+    assert L.qn_abi_version() == 1
+    for s in range(6):
+        assert len(L.qn_status_str(s)) > 0
+    assert L.qn_status_str(0) == b"ok"
+
+
+def test_library_codebook_equals_page_table(qn):
+    lit = np.array(_golden.values("nf4_codebook_page2.txt"), np.float32)
+    assert np.array_equal(np.array(qn.codebook(), np.float32), lit)
+
+
+def test_workspace_sizes(qn):
+    L = qn.load_library()
+    # absmax fp32 [nb] | fp64 partials [pow2(ng)] | flag, 256-aligned pieces
+    nb, ng = 262144, 1024
+    want = nb * 4 + ng * 8 + 4
+    assert L.nf4_quantize_dq_workspace(4096, 4096) == want
+    assert L.nf4_quantize_dq_workspace(0, 5) == 0
+    assert L.qlora_linear_workspace(8192, 4096, 4096, 16, 0) >= 8192 * 16 * 4
+    b = L.qlora_linear_workspace(8192, 4096, 4096, 16, 1)
+    assert b >= 8192 * 16 * 4 * 2 + 16 * 4096 * 2
+    assert L.qlora_linear_workspace(1, 8, 64, 65, 0) == 0
+
+
+FAKE = 1 << 20  # a non-null, 256-aligned address that is never dereferenced
+
+
+def _state(rows, cols, packed=FAKE):
+    from quantized_fine_tuning_nf4_amd import _NF4DQ
+    return _NF4DQ(packed, FAKE, FAKE, FAKE, rows, cols)
+
+
+def test_argument_errors_are_host_side(qn):
+    L = qn.load_library()
+    EINVAL, EALIGN, EWS = qn.QN_EINVAL, qn.QN_EALIGN, qn.QN_EWORKSPACE
+    # quantize
+    assert L.nf4_quantize_dq(None, 4, 4, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == EINVAL
+    assert L.nf4_quantize_dq(FAKE, 0, 4, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == EINVAL
+    assert L.nf4_quantize_dq(FAKE + 4, 4, 4, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == EALIGN
+    assert L.nf4_quantize_dq(FAKE, 4, 4, FAKE, FAKE, FAKE, FAKE, FAKE + 16, 1 << 20, None) == EALIGN
+    assert L.nf4_quantize_dq(FAKE, 4096, 4096, FAKE, FAKE, FAKE, FAKE, FAKE, 100, None) == EWS
+    # dequantize
+    s = _state(0, 64)
+    assert L.nf4_dequantize(ctypes.byref(s), 1, FAKE, None) == EINVAL
+    s = _state(8, 64, packed=FAKE + 2)
+    assert L.nf4_dequantize(ctypes.byref(s), 1, FAKE, None) == EALIGN
+    s = _state(8, 64)
+    assert L.nf4_dequantize(ctypes.byref(s), 7, FAKE, None) == EINVAL
+    assert L.nf4_dequantize(None, 1, FAKE, None) == EINVAL
+    # linear: cols % 64, rows % 8, rank range, M < 0, nulls, alignment, workspace
+    for rows, cols, r, M in [(8, 65, 4, 2), (12, 64, 4, 2), (8, 64, 0, 2), (8, 64, 65, 2),
+                             (8, 64, 4, -1)]:
+        s = _state(rows, cols)
+        assert L.qlora_linear_fwd(ctypes.byref(s), FAKE, M, FAKE, FAKE, r, 8.0, FAKE, None, FAKE,
+                                  1 << 20, None) == EINVAL
+        assert L.qlora_linear_bwd(ctypes.byref(s), FAKE, FAKE, M, FAKE, FAKE, r, 8.0, None,
+                                  FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == EINVAL
+    s = _state(8, 64)
+    assert L.qlora_linear_fwd(ctypes.byref(s), None, 2, FAKE, FAKE, 4, 8.0, FAKE, None, FAKE,
+                              1 << 20, None) == EINVAL
+    assert L.qlora_linear_fwd(ctypes.byref(s), FAKE + 8, 2, FAKE, FAKE, 4, 8.0, FAKE, None, FAKE,
+                              1 << 20, None) == EALIGN
+    assert L.qlora_linear_fwd(ctypes.byref(s), FAKE, 2, FAKE, FAKE, 4, 8.0, FAKE, None, FAKE,
+                              10, None) == EWS
+    assert L.qlora_linear_bwd(ctypes.byref(s), FAKE, FAKE, 2, FAKE, FAKE, 4, 8.0, None, FAKE,
+                              FAKE, FAKE, FAKE, 10, None) == EWS
+    assert L.qlora_linear_bwd(ctypes.byref(s), FAKE, FAKE, 2, FAKE, FAKE, 4, 8.0, None, FAKE,
+                              None, FAKE, FAKE, 1 << 20, None) == EINVAL
+    # M == 0 forward is a no-op that touches nothing
+    assert L.qlora_linear_fwd(ctypes.byref(s), None, 0, None, None, 4, 8.0, None, None, None, 0,
+                              None) == qn.QN_OK
+
+
+def test_binding_rejects_cpu_tensors(qn):
+    import torch
+    with pytest.raises(ValueError):
+        qn.nf4_quantize_dq(torch.zeros(4, 64))

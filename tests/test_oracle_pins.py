@@ -90,9 +90,8 @@ def test_code_search_random_and_special(orc):
     assert np.array_equal(orc.nf4_codes(vals), nearest_exact(vals))
 
 
-@pytest.mark.slow
 def test_code_search_exhaustive_fp32(orc):
-    """Every fp32 in [-1, 1] (about 2.13e9 values)."""
+    """Every fp32 in [-1, 1] (about 2.13e9 values; ~30 s on 8 cores)."""
     one = int(np.float32(1.0).view(np.uint32))
     chunk = 1 << 25
     for sign in (0, 0x80000000):
