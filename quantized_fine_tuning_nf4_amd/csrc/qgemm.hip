@@ -22,6 +22,8 @@
 // order is used for both operands, so the hardware's internal k order does
 // not matter.  Accumulator register v of lane l holds row
 // 8(v/4) + 4(l/32) + v%4, column l%32 of the 32x32 tile.
+#include <type_traits>
+
 #include "qn_device.h"
 #include "qn_internal.h"
 
@@ -171,12 +173,12 @@ __global__ __launch_bounds__(64 * WM * WN) void k_qgemm_fwd(
   float wscale;
   auto load_w = [&](int64_t kb) {
     const uint8_t* p = wp + kb * 32;
-    if (SPT == 4) {
+    if constexpr (SPT == 4) {
       const u32x4 a = *reinterpret_cast<const u32x4*>(p);
       const u32x4 b = *reinterpret_cast<const u32x4*>(p + 16);
       wreg[0] = a[0]; wreg[1] = a[1]; wreg[2] = a[2]; wreg[3] = a[3];
       wreg[4] = b[0]; wreg[5] = b[1]; wreg[6] = b[2]; wreg[7] = b[3];
-    } else if (SPT == 2) {
+    } else if constexpr (SPT == 2) {
       const u32x4 a = *reinterpret_cast<const u32x4*>(p);
       wreg[0] = a[0]; wreg[1] = a[1]; wreg[2] = a[2]; wreg[3] = a[3];
     } else {
@@ -448,7 +450,7 @@ hipError_t launch_qgemm_fwd(const WState& w, const uint16_t* X, int64_t M, const
   switch (pick(M, w.rows)) {
     case 0: return run_fwd<1, 4, 1, 1>(w, X, M, u, B, r, s, Y, st);
     case 1: return run_fwd<2, 2, 2, 2>(w, X, M, u, B, r, s, Y, st);
-    default: return run_fwd<2, 2, 4, 4>(w, X, M, u, B, r, s, Y, st);
+    default: return launch_qgemm_big(false, w, X, M, u, B, r, s, Y, st);
   }
 }
 
@@ -457,7 +459,7 @@ hipError_t launch_qgemm_dx(const WState& w, const uint16_t* G, int64_t M, const 
   switch (pick(M, w.cols)) {
     case 0: return run_dx<1, 4, 1, 1>(w, G, M, v, A, r, s, dX, st);
     case 1: return run_dx<2, 2, 2, 2>(w, G, M, v, A, r, s, dX, st);
-    default: return run_dx<2, 2, 4, 4>(w, G, M, v, A, r, s, dX, st);
+    default: return launch_qgemm_big(true, w, G, M, v, A, r, s, dX, st);
   }
 }
 

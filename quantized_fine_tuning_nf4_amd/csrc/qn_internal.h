@@ -46,6 +46,11 @@ int thin_tn_slices(int64_t M, int64_t P);
 hipError_t launch_qgemm_fwd(const WState& w, const uint16_t* X, int64_t M, const float* u,
                             const uint16_t* B, int r, float s, uint16_t* Y, hipStream_t st);
 
+// The 256 x 256-tile kernels for large batches (dx: the dX product).
+hipError_t launch_qgemm_big(bool dx, const WState& w, const uint16_t* Act, int64_t M,
+                            const float* V, const uint16_t* L, int r, float s, uint16_t* Out,
+                            hipStream_t st);
+
 // dX[M, K] bf16 = G[M, N] * W'[N, K] + s * v[M, r] * A[r, K].
 hipError_t launch_qgemm_dx(const WState& w, const uint16_t* G, int64_t M, const float* v,
                            const uint16_t* A, int r, float s, uint16_t* dX, hipStream_t st);
