@@ -80,17 +80,27 @@ WState to_state(const qn_nf4dq* w) {
   return WState{w->packed, w->qscale, w->scale2, w->offset, w->rows, w->cols};
 }
 
+// Large batches (enough 256 x 256 output tiles to fill the chip) take the
+// weight through a bf16 copy in the workspace and a plain bf16 GEMM; smaller
+// ones dequantize inside the GEMM.
+bool dense_path(int64_t M, int64_t out_cols) {
+  return M > 0 && ((M + 255) / 256) * ((out_cols + 255) / 256) >= 240;
+}
+int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
+
 struct FwdWs {
   float* u;      // [M, r] when the caller gives no u_out
   float* upart;  // [S, M, r] when S > 1
   int S;
+  uint16_t* wd;  // [rows, cols] bf16 Qhat(W) (dense path)
 };
 
-FwdWs carve_fwd(Carver& c, int64_t M, int64_t cols, int r, bool need_u) {
+FwdWs carve_fwd(Carver& c, int64_t M, int64_t rows, int64_t cols, int r, bool need_u) {
   FwdWs f;
   f.S = thin_nt_slices(M, cols);
   f.u = need_u ? c.take<float>((size_t)M * r) : nullptr;
   f.upart = f.S > 1 ? c.take<float>((size_t)f.S * M * r) : nullptr;
+  f.wd = dense_path(M, rows) ? c.take<uint16_t>((size_t)rows * cols) : nullptr;
   return f;
 }
 
@@ -104,14 +114,17 @@ struct BwdWs {
   int Sb;
   float* dApart;  // [Sa, cols, r]
   int Sa;
+  uint16_t* wt;   // [cols, ldt] bf16 Qhat(W)^T (dense path)
+  int64_t ldt;
+  uint16_t* At;   // [cols, r] A^T (dense path)
 };
 
 BwdWs carve_bwd(Carver& c, int64_t M, int64_t rows, int64_t cols, int r, bool need_u) {
   BwdWs b;
   if (need_u) {
-    b.fu = carve_fwd(c, M, cols, r, true);
+    b.fu = carve_fwd(c, M, 0, cols, r, true);
   } else {
-    b.fu = FwdWs{nullptr, nullptr, 1};
+    b.fu = FwdWs{nullptr, nullptr, 1, nullptr};
   }
   b.Bt = c.take<uint16_t>((size_t)r * rows);
   b.Sv = thin_nt_slices(M, rows);
@@ -121,6 +134,10 @@ BwdWs carve_bwd(Carver& c, int64_t M, int64_t rows, int64_t cols, int r, bool ne
   b.dBpart = c.take<float>((size_t)b.Sb * rows * r);
   b.Sa = thin_tn_slices(M, cols);
   b.dApart = c.take<float>((size_t)b.Sa * cols * r);
+  b.ldt = round_up(rows, 32);
+  const bool dense = dense_path(M, cols);
+  b.wt = dense ? c.take<uint16_t>((size_t)cols * b.ldt) : nullptr;
+  b.At = dense ? c.take<uint16_t>((size_t)cols * r) : nullptr;
   return b;
 }
 
@@ -195,7 +212,7 @@ size_t qlora_linear_workspace(int64_t M, int64_t rows, int64_t cols, int r, int 
   if (backward)
     carve_bwd(c, M, rows, cols, r, true);
   else
-    carve_fwd(c, M, cols, r, true);
+    carve_fwd(c, M, rows, cols, r, true);
   return c.used;
 }
 
@@ -210,19 +227,26 @@ qn_status qlora_linear_fwd(const qn_nf4dq* w, const uint16_t* x, int64_t M, cons
       (u_out && !aligned16(u_out)))
     return QN_EALIGN;
   Carver probe(nullptr);
-  carve_fwd(probe, M, w->cols, r, u_out == nullptr);
+  carve_fwd(probe, M, w->rows, w->cols, r, u_out == nullptr);
   if (probe.used > 0) {
     if (!workspace) return QN_EINVAL;
     if (reinterpret_cast<uintptr_t>(workspace) & 255u) return QN_EALIGN;
     if (workspace_bytes < probe.used) return QN_EWORKSPACE;
   }
   Carver c(workspace);
-  FwdWs f = carve_fwd(c, M, w->cols, r, u_out == nullptr);
+  FwdWs f = carve_fwd(c, M, w->rows, w->cols, r, u_out == nullptr);
   float* u = u_out ? u_out : f.u;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const float scale = alpha / (float)r;
-  hipError_t e = launch_thin_nt(x, A, M, w->cols, r, u, f.upart, f.S, st);
-  if (e == hipSuccess) e = launch_qgemm_fwd(to_state(w), x, M, u, B, r, scale, y, st);
+  const int64_t N = w->rows, K = w->cols;
+  hipError_t e = launch_thin_nt(x, A, M, K, r, u, f.upart, f.S, st);
+  if (f.wd) {
+    if (e == hipSuccess)
+      e = launch_dequant(w->packed, w->qscale, w->scale2, w->offset, N * K, true, f.wd, st);
+    if (e == hipSuccess) e = launch_gemm_nt(x, K, K, f.wd, K, M, N, u, B, r, scale, y, st);
+  } else if (e == hipSuccess) {
+    e = launch_qgemm_fwd(to_state(w), x, M, u, B, r, scale, y, st);
+  }
   return from_hip(e);
 }
 
@@ -262,8 +286,16 @@ qn_status qlora_linear_bwd(const qn_nf4dq* w, const uint16_t* x, const uint16_t*
   // v = G B, through B^T so both operands are contiguous along the reduction
   if (e == hipSuccess) e = launch_transpose_b(B, N, r, b.Bt, st);
   if (e == hipSuccess) e = launch_thin_nt(dY, b.Bt, M, N, r, b.v, b.vpart, b.Sv, st);
-  if (e == hipSuccess && dX)
-    e = launch_qgemm_dx(to_state(w), dY, M, b.v, A, r, scale, dX, st);
+  if (e == hipSuccess && dX) {
+    if (b.wt) {
+      e = launch_dequant_t(w->packed, w->qscale, w->scale2, w->offset, N, K, b.wt, b.ldt, st);
+      if (e == hipSuccess) e = launch_transpose_b(A, r, (int)K, b.At, st);
+      if (e == hipSuccess)
+        e = launch_gemm_nt(dY, N, N, b.wt, b.ldt, M, K, b.v, b.At, r, scale, dX, st);
+    } else {
+      e = launch_qgemm_dx(to_state(w), dY, M, b.v, A, r, scale, dX, st);
+    }
+  }
   if (e == hipSuccess) e = launch_thin_tn(dY, u, M, N, r, scale, dB, false, b.dBpart, b.Sb, st);
   if (e == hipSuccess) e = launch_thin_tn(x, b.v, M, K, r, scale, dA, true, b.dApart, b.Sa, st);
   return from_hip(e);

@@ -12,6 +12,19 @@ hipError_t launch_quantize(const float* W, int64_t n, uint8_t* packed, uint8_t* 
 hipError_t launch_dequant(const uint8_t* packed, const uint8_t* qscale, const float* scale2,
                           const float* offset, int64_t n, bool bf16, void* out, hipStream_t st);
 
+// out[k][n] = Qhat(W)[n][k] as bf16 with row length ldt (ldt % 8 == 0,
+// ldt >= rows); zero for rows <= n < ldt.  cols % 64 == 0.
+hipError_t launch_dequant_t(const uint8_t* packed, const uint8_t* qscale, const float* scale2,
+                            const float* offset, int64_t rows, int64_t cols, uint16_t* out,
+                            int64_t ldt, hipStream_t st);
+
+// C[M, Nc] bf16 = A[M, R] (row stride lda) * Bm[Nc, :R]^T (row stride ldb,
+// ldb % 32 == 0, zero in columns R..ldb) + s * V[M, r] * L[Nc, r]^T.
+// lda >= R, R % 8 == 0, Nc % 8 == 0; 16-byte aligned pointers.
+hipError_t launch_gemm_nt(const uint16_t* A, int64_t lda, int64_t R, const uint16_t* Bm,
+                          int64_t ldb, int64_t M, int64_t Nc, const float* V, const uint16_t* L,
+                          int r, float s, uint16_t* C, hipStream_t st);
+
 // Weight state as the kernels take it.
 struct WState {
   const uint8_t* packed;

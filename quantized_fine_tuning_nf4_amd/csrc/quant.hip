@@ -291,4 +291,59 @@ hipError_t launch_dequant(const uint8_t* packed, const uint8_t* qscale, const fl
   return hipGetLastError();
 }
 
+
+// Transposed dequantization for the dX product: out[k][n] (bf16, row length
+// ldt >= rows, ldt % 8 == 0) = Qhat(W)[n][k], zero for rows <= n < ldt.
+// Workgroup (bx, kb): rows n0 = 64 bx .. +63 of block column kb; thread t
+// dequantizes 16 codes (row n0 + t/4, elements 16 (t%4) ..) into an LDS tile
+// [k][n], which is written out as 16-byte row pieces.
+__global__ __launch_bounds__(256) void k_dequant_t(const uint8_t* __restrict__ packed,
+                                                   const uint8_t* __restrict__ qscale,
+                                                   const float* __restrict__ scale2,
+                                                   const float* __restrict__ offset, int64_t rows,
+                                                   int64_t cols, uint16_t* __restrict__ out,
+                                                   int64_t ldt) {
+  constexpr int LDT = 72;  // 64 + 8 pad
+  __shared__ float lut[16];
+  __shared__ __attribute__((aligned(16))) uint16_t tile[64][LDT];
+  const int t = threadIdx.x;
+  if (t < 16) lut[t] = as_f32(kNF4Bits[t]);
+  const int64_t n0 = (int64_t)blockIdx.x * 64, kb = blockIdx.y;
+  const int64_t kblocks = cols / kBlock;
+  const int nl = t >> 2, q = t & 3;
+  const int64_t n = n0 + nl;
+  uint2 p = make_uint2(0u, 0u);
+  float sc = 0.f;
+  if (n < rows) {
+    p = *reinterpret_cast<const uint2*>(packed + n * (cols / 2) + kb * 32 + 8 * q);
+    const int64_t b = n * kblocks + kb;
+    sc = dq_scale(qscale[b], scale2[b / kGroup], *offset);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const uint32_t word = e < 8 ? p.x : p.y;
+    const float w = lut[(word >> (4 * (e & 7))) & 15u] * sc;
+    tile[16 * q + e][nl] = (uint16_t)(pack_bf16x2(w, 0.f) & 0xffffu);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int c = t + 256 * h, k = c >> 3, n8 = c & 7;
+    const int64_t col = n0 + 8 * n8;
+    if (col < ldt)
+      *reinterpret_cast<u32x4*>(out + (kb * 64 + k) * ldt + col) =
+          *reinterpret_cast<const u32x4*>(&tile[k][8 * n8]);
+  }
+}
+
+hipError_t launch_dequant_t(const uint8_t* packed, const uint8_t* qscale, const float* scale2,
+                            const float* offset, int64_t rows, int64_t cols, uint16_t* out,
+                            int64_t ldt, hipStream_t st) {
+  const dim3 grid((unsigned)((ldt + 63) / 64), (unsigned)(cols / kBlock));
+  hipLaunchKernelGGL(k_dequant_t, grid, dim3(256), 0, st, packed, qscale, scale2, offset, rows,
+                     cols, out, ldt);
+  return hipGetLastError();
+}
+
 }  // namespace qn

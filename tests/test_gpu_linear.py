@@ -92,7 +92,8 @@ def test_tiny_config(qn):
     (8, 64, 1, 1),          # smallest legal shapes
     (520, 576, 300, 16),    # 128x128 tiles, ragged M / N / K tiles
     (1032, 320, 130, 64),   # rank 64: four 16-wide adapter steps
-    (7680, 256, 2085, 8),   # 256x256 tiles (>= 240 of them), ragged M
+    (7680, 256, 2085, 8),   # forward through the bf16 copy + dense GEMM, ragged M
+    (3848, 3840, 4100, 5),  # dense forward and dX: ragged M, N % 32 == 8, rank 5
 ])
 def test_ragged_shapes(qn, rows, cols, M, r):
     c = Case(rows, cols, M, r, 2.0 * r, seed=rows + cols + M)
@@ -134,15 +135,19 @@ def test_zero_weight_isolates_lora_term(qn):
     check_fwd_bwd(qn, c, "zero weight")
 
 
-def test_one_hot_rows_read_dequantized_weight_exactly(qn):
+@pytest.mark.parametrize("rows,cols,M", [
+    (1024, 512, 300),    # dequantization inside the GEMM
+    (4096, 4096, 3840),  # bf16 copies of the weight and its transpose + dense GEMM
+])
+def test_one_hot_rows_read_dequantized_weight_exactly(qn, rows, cols, M):
     """B = 0 and x rows = e_k: y[m, :] = bf16(W'[:, k]) exactly; A = 0 and G
     rows = e_n: dX[m, :] = bf16(W'[n, :]) exactly (through the MFMA path)."""
-    rows, cols = 1024, 512
-    c = Case(rows, cols, 300, 16, 32.0, seed=13)
+    say(f"[linear] one-hot rows={rows} cols={cols} M={M}")
+    c = Case(rows, cols, M, 16, 32.0, seed=13)
     _, Wb = oracle.dequantize(oracle.quantize(c.W))
-    ks = np.arange(300) * 7 % cols
-    x = np.zeros((300, cols), np.uint16)
-    x[np.arange(300), ks] = 0x3F80  # bf16 1.0
+    ks = np.arange(M) * 7 % cols
+    x = np.zeros((M, cols), np.uint16)
+    x[np.arange(M), ks] = 0x3F80  # bf16 1.0
     c.x = x
     c.B[:] = 0
     st, xd, A, B, G = c.dev(qn)
@@ -151,9 +156,9 @@ def test_one_hot_rows_read_dequantized_weight_exactly(qn):
     got = y.float().cpu().numpy()
     want = wl.bf16_bits_to_f32(Wb[:, ks].T)
     assert np.array_equal(got, want)
-    ns = np.arange(300) * 5 % rows
-    g = np.zeros((300, rows), np.uint16)
-    g[np.arange(300), ns] = 0x3F80
+    ns = np.arange(M) * 5 % rows
+    g = np.zeros((M, rows), np.uint16)
+    g[np.arange(M), ns] = 0x3F80
     c.A[:] = 0
     st, xd, A, B, _ = c.dev(qn)
     dX, _, _ = qn.qlora_linear_bwd(st, xd, bf16_dev(g), A, bf16_dev(c.B), c.alpha, None)
