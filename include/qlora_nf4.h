@@ -143,6 +143,18 @@ qn_status qlora_linear_bwd(const qn_nf4dq* w, const uint16_t* x, const uint16_t*
                            const float* u_saved, uint16_t* dX, float* dA, float* dB,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/* Dense LoRA linear on an already dequantized weight -- the forward's product
+ * once Qhat(W) is held in bf16 (page 2, paragraph after the listing):
+ *   y [M, rows] bf16 = X W^T + (alpha/r) V L^T
+ * with X bf16 [M, cols], W bf16 [rows, cols] (e.g. from nf4_dequantize),
+ * V fp32 [M, r] (u = X A^T, as qlora_linear_fwd returns it) and L bf16
+ * [rows, r] (the adapter B).  Large-batch forwards run exactly this product
+ * after dequantizing into their workspace.  Shape rules as qlora_linear_fwd;
+ * no workspace; M == 0: no work. */
+qn_status lora_linear_bf16(const uint16_t* x, int64_t M, const uint16_t* W, int64_t rows,
+                           int64_t cols, const float* V, const uint16_t* L, int r, float alpha,
+                           uint16_t* y, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -28,7 +28,7 @@ QN_F32, QN_BF16 = 0, 1
 
 EXPORTS = ["qn_abi_version", "qn_status_str", "qn_nf4_codebook", "nf4_quantize_dq_workspace",
            "nf4_quantize_dq", "nf4_dequantize", "qlora_linear_workspace", "qlora_linear_fwd",
-           "qlora_linear_bwd"]
+           "qlora_linear_bwd", "lora_linear_bf16"]
 
 
 class QNError(RuntimeError):
@@ -74,6 +74,8 @@ def load_library(path: str = LIB_PATH):
     L.qlora_linear_bwd.argtypes = [ctypes.POINTER(_NF4DQ), P, P, I64, P, P, ctypes.c_int,
                                    ctypes.c_float, P, P, P, P, P, SZ, P]
     L.qlora_linear_bwd.restype = ctypes.c_int
+    L.lora_linear_bf16.argtypes = [P, I64, P, I64, I64, P, P, ctypes.c_int, ctypes.c_float, P, P]
+    L.lora_linear_bf16.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -244,6 +246,28 @@ def qlora_linear_bwd(st: NF4State, x: torch.Tensor, dY: torch.Tensor, A: torch.T
                               dB.data_ptr(), workspace.data_ptr(), workspace.numel(),
                               _stream(x.device)))
     return dX, dA, dB
+
+
+def lora_linear_bf16(x: torch.Tensor, W: torch.Tensor, V: torch.Tensor, L_: torch.Tensor,
+                     alpha: float, y: torch.Tensor | None = None) -> torch.Tensor:
+    """y = x W^T + (alpha/r) V L_^T on a bf16 weight W [d_out, d_in] (for
+    example nf4_dequantize's output); V fp32 [M, r] (u), L_ bf16 [d_out, r]."""
+    L = load_library()
+    x = _dev(x, torch.bfloat16, "x")
+    W = _dev(W, torch.bfloat16, "W")
+    V = _dev(V, torch.float32, "V")
+    L_ = _dev(L_, torch.bfloat16, "L")
+    if x.dim() != 2 or W.dim() != 2 or x.shape[1] != W.shape[1]:
+        raise ValueError("x must be [M, d_in] and W [d_out, d_in]")
+    M, (rows, cols) = x.shape[0], W.shape
+    r = V.shape[1] if V.dim() == 2 else -1
+    if V.shape != (M, r) or L_.shape != (rows, r):
+        raise ValueError("V must be [M, r] and L [d_out, r]")
+    if y is None:
+        y = torch.empty((M, rows), dtype=torch.bfloat16, device=x.device)
+    _check(L.lora_linear_bf16(x.data_ptr(), M, W.data_ptr(), rows, cols, V.data_ptr(),
+                              L_.data_ptr(), r, float(alpha), y.data_ptr(), _stream(x.device)))
+    return y
 
 
 class _QLoRAFn(torch.autograd.Function):

@@ -10,7 +10,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libqlora_nf4.so")
-SOURCES = ["quant.hip", "lora.hip", "qgemm.hip", "qgemm_big.hip", "gemm_bf16.hip", "capi.hip"]
+SOURCES = ["quant.hip", "lora.hip", "qgemm.hip", "gemm_bf16.hip", "decode.hip", "capi.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -93,6 +93,9 @@ struct FwdWs {
   float* upart;  // [S, M, r] when S > 1
   int S;
   uint16_t* wd;  // [rows, cols] bf16 Qhat(W) (dense path)
+  float* dpart;  // [dS, M, rows] decode partial sums (decode path)
+  float* dupart; // [dS, M, r] decode partials of u
+  int dS;
 };
 
 FwdWs carve_fwd(Carver& c, int64_t M, int64_t rows, int64_t cols, int r, bool need_u) {
@@ -101,6 +104,9 @@ FwdWs carve_fwd(Carver& c, int64_t M, int64_t rows, int64_t cols, int r, bool ne
   f.u = need_u ? c.take<float>((size_t)M * r) : nullptr;
   f.upart = f.S > 1 ? c.take<float>((size_t)f.S * M * r) : nullptr;
   f.wd = dense_path(M, rows) ? c.take<uint16_t>((size_t)rows * cols) : nullptr;
+  f.dS = rows > 0 ? decode_slices(M, rows, cols) : 0;
+  f.dpart = f.dS > 0 ? c.take<float>((size_t)f.dS * M * rows) : nullptr;
+  f.dupart = f.dS > 0 ? c.take<float>((size_t)f.dS * M * r) : nullptr;
   return f;
 }
 
@@ -124,7 +130,7 @@ BwdWs carve_bwd(Carver& c, int64_t M, int64_t rows, int64_t cols, int r, bool ne
   if (need_u) {
     b.fu = carve_fwd(c, M, 0, cols, r, true);
   } else {
-    b.fu = FwdWs{nullptr, nullptr, 1, nullptr};
+    b.fu = FwdWs{nullptr, nullptr, 1, nullptr, nullptr, nullptr, 0};
   }
   b.Bt = c.take<uint16_t>((size_t)r * rows);
   b.Sv = thin_nt_slices(M, rows);
@@ -239,6 +245,9 @@ qn_status qlora_linear_fwd(const qn_nf4dq* w, const uint16_t* x, int64_t M, cons
   hipStream_t st = static_cast<hipStream_t>(stream);
   const float scale = alpha / (float)r;
   const int64_t N = w->rows, K = w->cols;
+  if (f.dpart)  // decode-sized batch: u and the product in two kernels
+    return from_hip(launch_decode_fwd(to_state(w), x, M, A, B, r, scale, y, u, f.dpart,
+                                      f.dupart, f.dS, st));
   hipError_t e = launch_thin_nt(x, A, M, K, r, u, f.upart, f.S, st);
   if (f.wd) {
     if (e == hipSuccess)
@@ -299,6 +308,19 @@ qn_status qlora_linear_bwd(const qn_nf4dq* w, const uint16_t* x, const uint16_t*
   if (e == hipSuccess) e = launch_thin_tn(dY, u, M, N, r, scale, dB, false, b.dBpart, b.Sb, st);
   if (e == hipSuccess) e = launch_thin_tn(x, b.v, M, K, r, scale, dA, true, b.dApart, b.Sa, st);
   return from_hip(e);
+}
+
+qn_status lora_linear_bf16(const uint16_t* x, int64_t M, const uint16_t* W, int64_t rows,
+                           int64_t cols, const float* V, const uint16_t* L, int r, float alpha,
+                           uint16_t* y, void* stream) {
+  if (rows < 1 || cols < 1 || M < 0 || r < 1 || r > 64) return QN_EINVAL;
+  if (cols % kBlock != 0 || rows % 8 != 0) return QN_EINVAL;
+  if (M == 0) return QN_OK;
+  if (!x || !W || !V || !L || !y) return QN_EINVAL;
+  if (!aligned16(x) || !aligned16(W) || !aligned16(V) || !aligned16(L) || !aligned16(y))
+    return QN_EALIGN;
+  return from_hip(launch_gemm_nt(x, cols, cols, W, cols, M, rows, V, L, r, alpha / (float)r, y,
+                                 static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

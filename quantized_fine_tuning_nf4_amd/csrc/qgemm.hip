@@ -434,33 +434,22 @@ hipError_t run_dx(const WState& w, const uint16_t* G, int64_t M, const float* v,
   return hipGetLastError();
 }
 
-// Tile choice: 256x256 when that still gives about one tile per CU, else
-// 128x128, and a 32-row tile for decode-sized batches.
-int pick(int64_t M, int64_t Ncols) {
-  const int64_t t256 = ((M + 255) / 256) * ((Ncols + 255) / 256);
-  if (M <= 32) return 0;
-  if (t256 >= 240) return 2;
-  return 1;
-}
+// Tile choice: a 32-row tile for decode-sized batches, else 128x128 (larger
+// batches go through the bf16 copy of the weight and the dense GEMM).
+int pick(int64_t M) { return M <= 32 ? 0 : 1; }
 
 }  // namespace
 
 hipError_t launch_qgemm_fwd(const WState& w, const uint16_t* X, int64_t M, const float* u,
                             const uint16_t* B, int r, float s, uint16_t* Y, hipStream_t st) {
-  switch (pick(M, w.rows)) {
-    case 0: return run_fwd<1, 4, 1, 1>(w, X, M, u, B, r, s, Y, st);
-    case 1: return run_fwd<2, 2, 2, 2>(w, X, M, u, B, r, s, Y, st);
-    default: return launch_qgemm_big(false, w, X, M, u, B, r, s, Y, st);
-  }
+  if (pick(M) == 0) return run_fwd<1, 4, 1, 1>(w, X, M, u, B, r, s, Y, st);
+  return run_fwd<2, 2, 2, 2>(w, X, M, u, B, r, s, Y, st);
 }
 
 hipError_t launch_qgemm_dx(const WState& w, const uint16_t* G, int64_t M, const float* v,
                            const uint16_t* A, int r, float s, uint16_t* dX, hipStream_t st) {
-  switch (pick(M, w.cols)) {
-    case 0: return run_dx<1, 4, 1, 1>(w, G, M, v, A, r, s, dX, st);
-    case 1: return run_dx<2, 2, 2, 2>(w, G, M, v, A, r, s, dX, st);
-    default: return launch_qgemm_big(true, w, G, M, v, A, r, s, dX, st);
-  }
+  if (pick(M) == 0) return run_dx<1, 4, 1, 1>(w, G, M, v, A, r, s, dX, st);
+  return run_dx<2, 2, 2, 2>(w, G, M, v, A, r, s, dX, st);
 }
 
 }  // namespace qn

@@ -26,6 +26,11 @@ hipError_t launch_gemm_nt(const uint16_t* A, int64_t lda, int64_t R, const uint1
                           int r, float s, uint16_t* C, hipStream_t st);
 
 // Weight state as the kernels take it.
+struct WState;
+// Decode-sized forward (M <= 16, cols % 1024 == 0): number of K slices, or
+// 0 when the decode kernels do not apply.
+int decode_slices(int64_t M, int64_t rows, int64_t cols);
+
 struct WState {
   const uint8_t* packed;
   const uint8_t* qscale;
@@ -55,14 +60,15 @@ hipError_t launch_thin_tn(const uint16_t* Z, const float* V, int64_t M, int64_t 
                           hipStream_t st);
 int thin_tn_slices(int64_t M, int64_t P);
 
+// Decode forward, u = X A^T included (written to u_out [M, r]); workspace
+// part [S, M, rows] and upart [S, M, r] fp32, S = decode_slices(...).
+hipError_t launch_decode_fwd(const WState& w, const uint16_t* X, int64_t M, const uint16_t* A,
+                             const uint16_t* B, int r, float s, uint16_t* Y, float* u_out,
+                             float* part, float* upart, int S, hipStream_t st);
+
 // Y[M, N] bf16 = X[M, K] * W'[N, K]^T + s * u[M, r] * B[N, r]^T.
 hipError_t launch_qgemm_fwd(const WState& w, const uint16_t* X, int64_t M, const float* u,
                             const uint16_t* B, int r, float s, uint16_t* Y, hipStream_t st);
-
-// The 256 x 256-tile kernels for large batches (dx: the dX product).
-hipError_t launch_qgemm_big(bool dx, const WState& w, const uint16_t* Act, int64_t M,
-                            const float* V, const uint16_t* L, int r, float s, uint16_t* Out,
-                            hipStream_t st);
 
 // dX[M, K] bf16 = G[M, N] * W'[N, K] + s * v[M, r] * A[r, K].
 hipError_t launch_qgemm_dx(const WState& w, const uint16_t* G, int64_t M, const float* v,

@@ -115,6 +115,14 @@ def test_argument_errors_are_host_side(qn):
     # M == 0 forward is a no-op that touches nothing
     assert L.qlora_linear_fwd(ctypes.byref(s), None, 0, None, None, 4, 8.0, None, None, None, 0,
                               None) == qn.QN_OK
+    # dense LoRA linear on a bf16 weight: same shape rules, alignment, nulls
+    for rows, cols, r, M in [(8, 65, 4, 2), (12, 64, 4, 2), (8, 64, 0, 2), (8, 64, 65, 2),
+                             (8, 64, 4, -1), (0, 64, 4, 2)]:
+        assert L.lora_linear_bf16(FAKE, M, FAKE, rows, cols, FAKE, FAKE, r, 8.0, FAKE,
+                                  None) == EINVAL
+    assert L.lora_linear_bf16(FAKE, 2, None, 8, 64, FAKE, FAKE, 4, 8.0, FAKE, None) == EINVAL
+    assert L.lora_linear_bf16(FAKE, 2, FAKE, 8, 64, FAKE + 4, FAKE, 4, 8.0, FAKE, None) == EALIGN
+    assert L.lora_linear_bf16(None, 0, None, 8, 64, None, None, 4, 8.0, None, None) == qn.QN_OK
 
 
 def test_binding_rejects_cpu_tensors(qn):
