@@ -145,8 +145,11 @@ def bench_train(torch, qn, wl, steps, warmup):
     wbf = torch.empty((N, K), dtype=torch.bfloat16, device="cuda")
     y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
 
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+
     def step(_):
-        qn.nf4_quantize_dq(Wd, out=st, workspace=qws)
+        # asynchronous non-finite report: no host round trip inside the step
+        qn.nf4_quantize_dq(Wd, out=st, workspace=qws, nonfinite=flag)
         qn.nf4_dequantize(st, torch.bfloat16, out=wbf)
         _, u = qn.qlora_linear_fwd(st, xd, Ad, Bd, alpha, y=y, workspace=fws)
         qn.qlora_linear_bwd(st, xd, Gd, Ad, Bd, alpha, u, workspace=bws)
@@ -154,6 +157,8 @@ def bench_train(torch, qn, wl, steps, warmup):
     batches = list(range(warmup + steps))
     secs, nsteps = measure(step, batches, lambda b: 1, time.perf_counter,
                            torch.cuda.synchronize, warmup)
+    if int(flag.item()) != 0:
+        raise RuntimeError("quantizer reported non-finite input")
     flops = fwd_flops(M, N, K, r) + bwd_flops(M, N, K, r)
     res = dict(seconds=secs, steps=nsteps, ms_per_step=1e3 * secs / nsteps,
                tflops=flops * nsteps / secs / 1e12, flops_per_step=flops)
@@ -482,8 +487,8 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "train_fwd_bwd_4096x4096_M8192", "rows": 4096, "cols": 4096,
                    "M": 8192, "r": 16, "alpha": 32,
-                   "step": "nf4_quantize_dq + nf4_dequantize(bf16) + qlora_linear_fwd + "
-                           "qlora_linear_bwd", "flops_per_step": tr["flops_per_step"]},
+                   "step": "nf4_quantize_dq (device non-finite flag) + nf4_dequantize(bf16) + "
+                           "qlora_linear_fwd + qlora_linear_bwd", "flops_per_step": tr["flops_per_step"]},
         "roofline": roof,
         "cpu_baseline": cpu,
         "extras": extras,

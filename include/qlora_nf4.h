@@ -51,8 +51,9 @@
  *     from the caller as `workspace` (sizes from the *_workspace functions;
  *     256-byte aligned).  Device pointers must be 16-byte aligned.
  *   - `stream` is a hipStream_t (NULL: the null stream).  All calls are
- *     stream-ordered and asynchronous, except nf4_quantize_dq, which
- *     synchronizes `stream` so that it can report non-finite input.
+ *     stream-ordered and asynchronous, except nf4_quantize_dq without a
+ *     `nonfinite` flag pointer, which synchronizes `stream` so that it can
+ *     report non-finite input in its return value.
  *   - Arguments are checked on the host before any launch; on error nothing
  *     is launched.  QN_EINVAL: bad size or null required pointer;
  *     QN_EALIGN: misaligned pointer; QN_EWORKSPACE: workspace too small;
@@ -70,7 +71,7 @@
 extern "C" {
 #endif
 
-#define QN_ABI_VERSION 1
+#define QN_ABI_VERSION 2
 
 typedef enum {
   QN_OK = 0,
@@ -108,11 +109,16 @@ size_t nf4_quantize_dq_workspace(int64_t rows, int64_t cols);
 /* Quantize W [rows, cols] fp32 to NF4 with double quantisation (see top of
  * file for the steps and the state layout).  rows, cols >= 1; W 16-byte
  * aligned.  Writes packed [32*nb], qscale [nb], scale2 [ng], offset [1].
- * Synchronizes `stream`; returns QN_ENONFINITE when W holds a NaN or an
- * infinity (the outputs are then unspecified). */
+ * Non-finite input (a NaN or an infinity in W; the outputs are then
+ * unspecified) is reported in one of two ways:
+ *   nonfinite == NULL: the call synchronizes `stream` and returns
+ *     QN_ENONFINITE;
+ *   nonfinite = a device int (4-byte aligned): the call stays asynchronous
+ *     and writes 1 (non-finite input) or 0 there, stream-ordered; the caller
+ *     must read it before trusting the state. */
 qn_status nf4_quantize_dq(const float* W, int64_t rows, int64_t cols, uint8_t* packed,
-                          uint8_t* qscale, float* scale2, float* offset, void* workspace,
-                          size_t workspace_bytes, void* stream);
+                          uint8_t* qscale, float* scale2, float* offset, int* nonfinite,
+                          void* workspace, size_t workspace_bytes, void* stream);
 
 /* Dequantize w into out [rows, cols]: fp32 (QN_F32) or bf16 bit patterns
  * (QN_BF16, round to nearest even of the fp32 value). */

@@ -62,7 +62,7 @@ def load_library(path: str = LIB_PATH):
     L.qn_nf4_codebook.argtypes = [P]
     L.nf4_quantize_dq_workspace.argtypes = [I64, I64]
     L.nf4_quantize_dq_workspace.restype = SZ
-    L.nf4_quantize_dq.argtypes = [P, I64, I64, P, P, P, P, P, SZ, P]
+    L.nf4_quantize_dq.argtypes = [P, I64, I64, P, P, P, P, P, P, SZ, P]
     L.nf4_quantize_dq.restype = ctypes.c_int
     L.nf4_dequantize.argtypes = [ctypes.POINTER(_NF4DQ), ctypes.c_int, P, P]
     L.nf4_dequantize.restype = ctypes.c_int
@@ -150,9 +150,12 @@ def empty_state(rows: int, cols: int, device) -> NF4State:
 
 
 def nf4_quantize_dq(W: torch.Tensor, out: NF4State | None = None,
-                    workspace: torch.Tensor | None = None) -> NF4State:
+                    workspace: torch.Tensor | None = None,
+                    nonfinite: torch.Tensor | None = None) -> NF4State:
     """NF4 block-64 quantisation + double quantisation of an fp32 weight
-    [d_out, d_in] (a 1-D tensor is one row).  Raises QNError on NaN/Inf."""
+    [d_out, d_in] (a 1-D tensor is one row).  Without `nonfinite` the call
+    synchronizes and raises QNError on NaN/Inf; with `nonfinite` (an int32
+    CUDA tensor of one element) it stays asynchronous and writes 1 or 0 there."""
     L = load_library()
     W = _dev(W, torch.float32, "W")
     rows, cols = (W.shape[0], W.shape[1]) if W.dim() == 2 else (1, W.numel())
@@ -162,9 +165,13 @@ def nf4_quantize_dq(W: torch.Tensor, out: NF4State | None = None,
     ws_bytes = L.nf4_quantize_dq_workspace(rows, cols)
     ws = workspace if workspace is not None else torch.empty(max(ws_bytes, 1), dtype=torch.uint8,
                                                              device=W.device)
+    if nonfinite is not None:
+        _dev(nonfinite, torch.int32, "nonfinite")
+        if nonfinite.numel() != 1:
+            raise ValueError("nonfinite must hold one int32")
     _check(L.nf4_quantize_dq(W.data_ptr(), rows, cols, st.packed.data_ptr(),
                              st.qscale.data_ptr(), st.scale2.data_ptr(), st.offset.data_ptr(),
-                             ws.data_ptr(), ws.numel(), _stream(W.device)))
+                             _ptr(nonfinite), ws.data_ptr(), ws.numel(), _stream(W.device)))
     return st
 
 

@@ -44,7 +44,8 @@ struct QuantWs {
   float* absmax;
   double* part;
   int64_t part_len;
-  int* flag;
+  int* bad;   // [ng] per-group flags
+  int* flag;  // the synchronous call's flag
 };
 
 QuantWs carve_quant(Carver& c, int64_t n) {
@@ -53,6 +54,7 @@ QuantWs carve_quant(Carver& c, int64_t n) {
   w.absmax = c.take<float>(nb);
   w.part_len = pow2_at_least(ng);
   w.part = c.take<double>(w.part_len);
+  w.bad = c.take<int>(ng);
   w.flag = c.take<int>(1);
   return w;
 }
@@ -118,8 +120,10 @@ struct BwdWs {
   int Sv;
   float* dBpart;  // [Sb, rows, r]
   int Sb;
+  uint16_t* su;   // [2][rp][Mpb] (s u)^T high and remainder parts
   float* dApart;  // [Sa, cols, r]
   int Sa;
+  uint16_t* sv;   // [2][rp][Mpa] (s v)^T
   uint16_t* wt;   // [cols, ldt] bf16 Qhat(W)^T (dense path)
   int64_t ldt;
   uint16_t* At;   // [cols, r] A^T (dense path)
@@ -136,10 +140,13 @@ BwdWs carve_bwd(Carver& c, int64_t M, int64_t rows, int64_t cols, int r, bool ne
   b.Sv = thin_nt_slices(M, rows);
   b.v = c.take<float>((size_t)M * r);
   b.vpart = b.Sv > 1 ? c.take<float>((size_t)b.Sv * M * r) : nullptr;
-  b.Sb = thin_tn_slices(M, rows);
+  const int64_t rp = 16 * ((r + 15) / 16);
+  b.Sb = thin_tn_slices(M, rows, r);
   b.dBpart = c.take<float>((size_t)b.Sb * rows * r);
-  b.Sa = thin_tn_slices(M, cols);
+  b.su = c.take<uint16_t>((size_t)2 * rp * thin_tn_rows_padded(M, rows, r));
+  b.Sa = thin_tn_slices(M, cols, r);
   b.dApart = c.take<float>((size_t)b.Sa * cols * r);
+  b.sv = c.take<uint16_t>((size_t)2 * rp * thin_tn_rows_padded(M, cols, r));
   b.ldt = round_up(rows, 32);
   const bool dense = dense_path(M, cols);
   b.wt = dense ? c.take<uint16_t>((size_t)cols * b.ldt) : nullptr;
@@ -180,12 +187,13 @@ size_t nf4_quantize_dq_workspace(int64_t rows, int64_t cols) {
 }
 
 qn_status nf4_quantize_dq(const float* W, int64_t rows, int64_t cols, uint8_t* packed,
-                          uint8_t* qscale, float* scale2, float* offset, void* workspace,
-                          size_t workspace_bytes, void* stream) {
+                          uint8_t* qscale, float* scale2, float* offset, int* nonfinite,
+                          void* workspace, size_t workspace_bytes, void* stream) {
   if (!W || !packed || !qscale || !scale2 || !offset || !workspace) return QN_EINVAL;
   if (rows < 1 || cols < 1 || rows > INT64_MAX / 2 / cols) return QN_EINVAL;
   if (!aligned16(W) || !aligned16(packed) || !aligned16(qscale) || !aligned16(scale2) ||
-      !aligned16(offset) || (reinterpret_cast<uintptr_t>(workspace) & 255u))
+      !aligned16(offset) || (reinterpret_cast<uintptr_t>(workspace) & 255u) ||
+      (reinterpret_cast<uintptr_t>(nonfinite) & 3u))
     return QN_EALIGN;
   const int64_t n = rows * cols;
   if (workspace_bytes < nf4_quantize_dq_workspace(rows, cols)) return QN_EWORKSPACE;
@@ -193,8 +201,9 @@ qn_status nf4_quantize_dq(const float* W, int64_t rows, int64_t cols, uint8_t* p
   QuantWs ws = carve_quant(c, n);
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = launch_quantize(W, n, packed, qscale, scale2, offset, ws.absmax, ws.part,
-                                 ws.part_len, ws.flag, st);
+                                 ws.part_len, ws.bad, nonfinite ? nonfinite : ws.flag, st);
   if (e != hipSuccess) return QN_EDEVICE;
+  if (nonfinite) return QN_OK;  // asynchronous: the caller reads the flag
   int bad = 0;
   e = hipMemcpyAsync(&bad, ws.flag, sizeof(int), hipMemcpyDeviceToHost, st);
   if (e != hipSuccess) return QN_EDEVICE;
@@ -305,8 +314,12 @@ qn_status qlora_linear_bwd(const qn_nf4dq* w, const uint16_t* x, const uint16_t*
       e = launch_qgemm_dx(to_state(w), dY, M, b.v, A, r, scale, dX, st);
     }
   }
-  if (e == hipSuccess) e = launch_thin_tn(dY, u, M, N, r, scale, dB, false, b.dBpart, b.Sb, st);
-  if (e == hipSuccess) e = launch_thin_tn(x, b.v, M, K, r, scale, dA, true, b.dApart, b.Sa, st);
+  if (e == hipSuccess)
+    e = launch_prep_svt(u, M, thin_tn_rows_padded(M, N, r), r, scale, b.su, st);
+  if (e == hipSuccess) e = launch_thin_tn(dY, b.su, M, N, r, dB, false, b.dBpart, b.Sb, st);
+  if (e == hipSuccess)
+    e = launch_prep_svt(b.v, M, thin_tn_rows_padded(M, K, r), r, scale, b.sv, st);
+  if (e == hipSuccess) e = launch_thin_tn(x, b.sv, M, K, r, dA, true, b.dApart, b.Sa, st);
   return from_hip(e);
 }
 

@@ -36,69 +36,88 @@ __device__ __forceinline__ u32x4 load8(const uint16_t* row, int64_t p, int64_t P
 
 }  // namespace
 
-// out[M, r] = Z[M, P] T[r, P]^T.  Workgroup (mt, s): rows 16mt..16mt+15,
-// columns of slice s; its four waves take consecutive quarters of the slice
-// and their sums are added in wave order.  MFMA lane l holds row l%16 and
-// the eight columns 8(l/16).. of each 32-wide step; the k order inside a step
-// is the same for both operands, so the product is the plain dot product.
+// out[M, r] = Z[M, P] T[r, P]^T over column slice s.  Workgroup (mt, s):
+// rows 64mt .. 64mt+63, wave w rows 16w .. +15, all columns of the slice.
+// MFMA lane l holds row l%16 and the eight columns 8(l/16).. of each 32-wide
+// step of both operands (rows of Z and of T are contiguous along the
+// reduction).  U steps' loads are issued before their MFMAs.  Columns past
+// the slice load as zero (P is a multiple of 8).  NJ = ceil(r/16).
+template <int NJ>
 __global__ __launch_bounds__(kThreads) void k_thin_nt(const uint16_t* __restrict__ Z,
                                                       const uint16_t* __restrict__ T, int64_t M,
                                                       int64_t P, int r, int64_t slice,
                                                       float* __restrict__ out) {
-  __shared__ float red[4][4][16][17];
+  constexpr int U = NJ <= 2 ? 8 : 4;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int64_t m0 = (int64_t)blockIdx.x * 16;
-  const int64_t p_begin = (int64_t)blockIdx.y * slice;
-  const int64_t quarter = slice / 4;
-  const int64_t pw0 = p_begin + wave * quarter;
-  const int64_t pw1 = min(pw0 + quarter, P);
-  const int nj = (r + 15) / 16;
-  const int64_t m = min(m0 + (lane & 15), M - 1);
-  const uint16_t* zrow = Z + m * P;
-  f32x4 acc[4] = {};
-  // uniform trip count; columns at or past pw1 load as zero (P and the
-  // quarter bounds are multiples of 8, so a chunk is all in or all out)
-  for (int64_t ps = pw0; ps < pw1; ps += 32) {
-    const int64_t p = ps + 8 * (lane >> 4);
-    const bf16x8 a = as_bf16x8(p < pw1 ? load8(zrow, p, pw1) : u32x4{0, 0, 0, 0});
+  const int g = lane >> 4, l16 = lane & 15;
+  const int64_t mw = (int64_t)blockIdx.x * 64 + 16 * wave;  // first row of the wave
+  const int64_t m = min(mw + l16, M - 1);
+  const int64_t pb = (int64_t)blockIdx.y * slice, pe = min(pb + slice, P);
+  const int steps = (int)((pe - pb + 31) / 32);
+  const uint16_t* zp = Z + m * P + pb + 8 * g;
+  const uint16_t* tp[NJ];
 #pragma unroll
-    for (int jt = 0; jt < 4; ++jt) {
-      if (jt < nj) {
-        const int j = jt * 16 + (lane & 15);
-        const u32x4 bv = (j < r && p < pw1) ? load8(T + (int64_t)j * P, p, P) : u32x4{0, 0, 0, 0};
-        acc[jt] = mfma16(a, as_bf16x8(bv), acc[jt]);
-      }
+  for (int jt = 0; jt < NJ; ++jt) tp[jt] = T + (int64_t)min(16 * jt + l16, r - 1) * P + pb + 8 * g;
+  const int64_t lim = pe - pb - 8 * g;  // in-slice columns left for this lane's chunk
+  f32x4 acc[NJ] = {};
+  for (int s0 = 0; s0 < steps; s0 += U) {
+    u32x4 za[U], tb[U][NJ];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t off = 32 * (int64_t)(s0 + u);
+      const bool ok = off < lim;
+      const int64_t o = ok ? off : 0;
+      za[u] = *reinterpret_cast<const u32x4*>(zp + o);
+#pragma unroll
+      for (int jt = 0; jt < NJ; ++jt) tb[u][jt] = *reinterpret_cast<const u32x4*>(tp[jt] + o);
+      if (!ok) za[u] = u32x4{0u, 0u, 0u, 0u};
     }
-  }
-  // 16x16 result: lane l holds column l%16, rows 4(l/16)+i
 #pragma unroll
-  for (int jt = 0; jt < 4; ++jt)
-    if (jt < nj)
-      for (int i = 0; i < 4; ++i) red[wave][jt][4 * (lane >> 4) + i][lane & 15] = acc[jt][i];
-  __syncthreads();
-  for (int e = tid; e < 16 * r; e += kThreads) {
-    const int row = e / r, j = e % r;
-    const int jt = j / 16, jj = j % 16;
-    const float s = ((red[0][jt][row][jj] + red[1][jt][row][jj]) + red[2][jt][row][jj]) +
-                    red[3][jt][row][jj];
-    if (m0 + row < M) out[((int64_t)blockIdx.y * M + m0 + row) * r + j] = s;
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int jt = 0; jt < NJ; ++jt) {
+        u32x4 b = tb[u][jt];
+        if (16 * jt + l16 >= r) b = u32x4{0u, 0u, 0u, 0u};
+        acc[jt] = mfma16(as_bf16x8(za[u]), as_bf16x8(b), acc[jt]);
+      }
+  }
+  // lane l: column j = 16jt + l%16, rows mw + 4(l/16) + i
+  float* dst = out + (int64_t)blockIdx.y * M * r;
+#pragma unroll
+  for (int jt = 0; jt < NJ; ++jt) {
+    const int j = 16 * jt + l16;
+    if (j >= r) continue;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t row = mw + 4 * g + i;
+      if (row < M) dst[row * r + j] = acc[jt][i];
+    }
   }
 }
 
-// out[i] = sum over s of part[s][i], in slice order.
+// out[i] = sum over s of part[s][i], added in slice order (loads issued
+// eight at a time).
 __global__ void k_sum_slices(const float* __restrict__ part, int64_t count, int S,
                              float* __restrict__ out) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= count) return;
   float acc = part[i];
-  for (int s = 1; s < S; ++s) acc += part[(int64_t)s * count + i];
+  for (int s0 = 1; s0 < S; s0 += 8) {
+    float v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = s0 + k < S ? part[(int64_t)(s0 + k) * count + i] : 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (s0 + k < S) acc += v[k];
+  }
   out[i] = acc;
 }
 
+// Column slices (multiples of 128 columns) so that about 512 workgroups run.
 int thin_nt_slices(int64_t M, int64_t P) {
-  const int64_t mt = (M + 15) / 16;
-  int64_t S = 512 / (mt > 0 ? mt : 1);
-  const int64_t smax = P / 256 > 0 ? P / 256 : 1;
+  const int64_t mt = M > 0 ? (M + 63) / 64 : 1;
+  int64_t S = (512 + mt - 1) / mt;
+  const int64_t smax = (P + 127) / 128;
   if (S > smax) S = smax;
   if (S < 1) S = 1;
   return (int)S;
@@ -106,12 +125,16 @@ int thin_nt_slices(int64_t M, int64_t P) {
 
 hipError_t launch_thin_nt(const uint16_t* Z, const uint16_t* T, int64_t M, int64_t P, int r,
                           float* out, float* part, int S, hipStream_t st) {
-  // slice width: a multiple of 128 so each wave's quarter is whole 32-steps
   int64_t slice = (P + S - 1) / S;
   slice = (slice + 127) / 128 * 128;
-  const dim3 grid((unsigned)((M + 15) / 16), (unsigned)S);
-  hipLaunchKernelGGL(k_thin_nt, grid, dim3(kThreads), 0, st, Z, T, M, P, r, slice,
-                     S > 1 ? part : out);
+  const dim3 grid((unsigned)((M + 63) / 64), (unsigned)S);
+  float* dst = S > 1 ? part : out;
+  switch ((r + 15) / 16) {
+    case 1: hipLaunchKernelGGL(k_thin_nt<1>, grid, dim3(kThreads), 0, st, Z, T, M, P, r, slice, dst); break;
+    case 2: hipLaunchKernelGGL(k_thin_nt<2>, grid, dim3(kThreads), 0, st, Z, T, M, P, r, slice, dst); break;
+    case 3: hipLaunchKernelGGL(k_thin_nt<3>, grid, dim3(kThreads), 0, st, Z, T, M, P, r, slice, dst); break;
+    default: hipLaunchKernelGGL(k_thin_nt<4>, grid, dim3(kThreads), 0, st, Z, T, M, P, r, slice, dst); break;
+  }
   if (S > 1) {
     const int64_t count = M * r;
     hipLaunchKernelGGL(k_sum_slices, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, st,
@@ -147,104 +170,232 @@ hipError_t launch_transpose_b(const uint16_t* B, int64_t N, int r, uint16_t* Bt,
   return hipGetLastError();
 }
 
-// part[s][p][j] = sum over the rows m of slice s of Z[m, p] * (s*V[m, j]).
-// Workgroup (pt, s): 64 columns p0..p0+63; wave w owns columns 16w..16w+15.
-// Each 32-row step stages Z^T (64 x 32) and (sV)^T split in bf16 high and
-// remainder parts (r x 32) in LDS, so that both MFMA operands read eight
-// consecutive rows from one LDS row.
-__global__ __launch_bounds__(kThreads) void k_thin_tn(const uint16_t* __restrict__ Z,
-                                                      const float* __restrict__ V, int64_t M,
-                                                      int64_t P, int r, float scale,
-                                                      int64_t slice, float* __restrict__ part) {
-  constexpr int LD = 40;  // 32 rows + 8 pad (bf16) per LDS row: 80 B
-  __shared__ __attribute__((aligned(16))) uint16_t zt[64][LD];
-  __shared__ __attribute__((aligned(16))) uint16_t vh[64][LD];
-  __shared__ __attribute__((aligned(16))) uint16_t vl[64][LD];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int64_t p0 = (int64_t)blockIdx.x * 64;
+// (s V)^T split into bf16 high and remainder parts: vt[0][j][m] (high) and
+// vt[1][j][m] (remainder) for j < rp = 16 ceil(r/16) and m < Mp; zero for
+// j >= r or m >= M.
+__global__ void k_prep_svt(const float* __restrict__ V, int64_t M, int64_t Mp, int r, int rp,
+                           float scale, uint16_t* __restrict__ vt) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t count = (int64_t)rp * Mp;
+  if (i >= count) return;
+  const int64_t j = i / Mp, m = i % Mp;
+  const float x = (j < r && m < M) ? scale * V[m * r + j] : 0.f;
+  const uint32_t h = pack_bf16x2(x, 0.f) & 0xffffu;
+  vt[i] = (uint16_t)h;
+  vt[count + i] = (uint16_t)(pack_bf16x2(x - bf16_lo(h), 0.f) & 0xffffu);
+}
+
+namespace {
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef short v4s __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ rsrc_t make_rs(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(lo | (hi << 32)), 0,
+                                           __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000);
+}
+__device__ __forceinline__ void dma16(rsrc_t rs, uint32_t voff, uint32_t soff, uint8_t* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)lds, 16, voff, soff, 0, 0);
+}
+
+constexpr int TN_COLS = 128;             // columns of Z per workgroup
+constexpr int TN_ROWB = TN_COLS * 2;     // 256 B per staged row
+constexpr int TN_STAGE = 32 * TN_ROWB;   // 8 KB: 32 rows per step
+constexpr int TN_NST = 4;
+
+}  // namespace
+
+// part[z][p][j] = sum over the rows m of slice z of Z[m, p] * (sV)[m, j]
+// (a transposed product: the reduction runs down the columns of Z).
+// Workgroup (pt, z): columns 128 pt .. +127, wave w: 32w .. 32w+31 (two
+// 16-column MFMA tiles).  32 rows of Z per step go global -> LDS by buffer
+// loads four steps deep (row y's 16-byte chunk c at unit c ^ 2(y & 3)); the A
+// operand (16 columns x 32 rows) is read transposed with ds_read_b64_tr_b16,
+// lane t of a 16-lane group addressing row 4h + t/4, columns 4(t%4)..+3, so
+// that lane t receives column t, four consecutive rows.  The B operand is
+// (sV)^T high and remainder parts, staged in LDS for the whole slice.
+__global__ __launch_bounds__(kThreads) void k_thin_tn(
+    const uint16_t* __restrict__ Z, int64_t M, int64_t P, const uint16_t* __restrict__ vt,
+    int64_t Mp, int r, int64_t slice, float* __restrict__ part) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int nj = (r + 15) / 16;
+  const int64_t p0 = (int64_t)blockIdx.x * TN_COLS;
   const int64_t mb = (int64_t)blockIdx.y * slice;
   const int64_t me = min(mb + slice, M);
-  const int nj = (r + 15) / 16;
-  f32x4 acc[4] = {};
-  for (int64_t m = mb; m < me; m += 32) {
-    {  // Z rows m..m+31, columns p0..p0+63 -> zt[p][row]
-      const int row = tid >> 3, c = tid & 7;
-      const int64_t mm = m + row, pp = p0 + 8 * c;
-      u32x4 v = {0, 0, 0, 0};
-      if (mm < me && pp < P) v = load8(Z + mm * P, pp, P);
-      for (int h = 0; h < 4; ++h) {
-        zt[8 * c + 2 * h][row] = (uint16_t)(v[h] & 0xffffu);
-        zt[8 * c + 2 * h + 1][row] = (uint16_t)(v[h] >> 16);
-      }
+  const int steps = (int)((me - mb + 31) / 32);
+  uint8_t* zst = smem;                          // TN_NST stages of Z
+  uint8_t* vst = smem + TN_NST * TN_STAGE;      // [2][16 nj][slice] bf16
+  const int64_t vrow = slice * 2;               // bytes per staged (sV)^T row
+
+  // ---- (sV)^T for the slice: 2 * 16nj rows of `slice` bf16, 16-B chunks
+  {
+    const int chunks = (int)(slice / 8);
+    const rsrc_t rv = make_rs(vt, (uint32_t)(2 * 16 * nj * Mp * 2));
+    const int total = 2 * 16 * nj * chunks;     // multiple of 64 (slice % 32 == 0)
+    for (int c0 = 64 * wave; c0 < total; c0 += 256) {
+      const int c = c0 + lane, row = c / chunks, q = c % chunks;  // row: part * 16nj + j
+      dma16(rv, (uint32_t)((row * Mp + mb + 8 * q) * 2), 0, vst + (int64_t)(c0 / 64) * 1024);
     }
-    for (int e = tid; e < 32 * 16 * nj; e += kThreads) {  // (sV)^T, zero past r / rows
-      const int row = e / (16 * nj), j = e % (16 * nj);
-      const int64_t mm = m + row;
-      const float x = (mm < me && j < r) ? scale * V[mm * r + j] : 0.f;
-      const uint32_t hi = pack_bf16x2(x, 0.f) & 0xffffu;
-      const float rem = x - bf16_lo(hi);
-      vh[j][row] = (uint16_t)hi;
-      vl[j][row] = (uint16_t)(pack_bf16x2(rem, 0.f) & 0xffffu);
+  }
+  // ---- Z loads: instruction i (0..7) of a step covers rows 4i..4i+3; wave w
+  // issues i = 2w, 2w+1; lane l -> row 4i + l/16, unit l%16, source chunk
+  // (l%16) ^ 2(row & 3).  Rows past M repeat row M-1 (their sV is zero);
+  // columns past P repeat the last chunk (their outputs are not stored).
+  const rsrc_t rz = make_rs(Z, (uint32_t)(M * P * 2));
+  uint32_t zoff[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int i = 2 * wave + h, row = 4 * i + (lane >> 4);
+    const int chunk = (lane & 15) ^ (2 * (row & 3));
+    const int64_t col = min(p0 + 8 * chunk, P - 8);
+    zoff[h] = (uint32_t)(col * 2);
+    (void)row;
+  }
+  auto load_z = [&](int st, int stage) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int i = 2 * wave + h, row = 4 * i + (lane >> 4);
+      const int64_t m = min(mb + 32 * (int64_t)st + row, M - 1);
+      dma16(rz, zoff[h] + (uint32_t)(m * P * 2), 0, zst + stage * TN_STAGE + 1024 * i);
     }
-    __syncthreads();
-    const int kk = 8 * (lane >> 4);
-    const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&zt[16 * wave + (lane & 15)][kk]));
+  };
+  for (int k = 0; k < TN_NST - 1; ++k) load_z(min(k, steps - 1), k);
+  asm volatile("s_waitcnt vmcnt(4)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+
+  // transposed-read addresses: lane l, group g = l/16, t = l%16; p-tile pt,
+  // half h: row 8g + 4h + t/4, column 32w + 16pt + 4(t%4)
+  const int g = lane >> 4, t = lane & 15;
+  int aoff[2][2];
+#pragma unroll
+  for (int pt = 0; pt < 2; ++pt)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int row = 8 * g + 4 * h + (t >> 2);
+      const int col = 32 * wave + 16 * pt + 4 * (t & 3);
+      aoff[pt][h] = row * TN_ROWB + 16 * ((col >> 3) ^ (2 * (row & 3))) + 2 * (col & 7);
+    }
+  f32x4 acc[2][4] = {};
+  for (int st = 0; st < steps; ++st) {
+    const int stage = st % TN_NST;
+    load_z(min(st + TN_NST - 1, steps - 1), (st + TN_NST - 1) % TN_NST);
+    const uint8_t* zs = zst + stage * TN_STAGE;
+    bf16x8 a[2];
+#pragma unroll
+    for (int pt = 0; pt < 2; ++pt) {
+      const v4s x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) v4s*)(zs + aoff[pt][0]));
+      const v4s x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) v4s*)(zs + aoff[pt][1]));
+      const u32x2 l2 = __builtin_bit_cast(u32x2, x0), h2 = __builtin_bit_cast(u32x2, x1);
+      a[pt] = as_bf16x8(u32x4{l2[0], l2[1], h2[0], h2[1]});
+    }
 #pragma unroll
     for (int jt = 0; jt < 4; ++jt) {
       if (jt < nj) {
-        const int j = 16 * jt + (lane & 15);
-        const bf16x8 bh = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&vh[j][kk]));
-        const bf16x8 bl = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&vl[j][kk]));
-        acc[jt] = mfma16(a, bh, acc[jt]);
-        acc[jt] = mfma16(a, bl, acc[jt]);
+        // B operand: column j = 16jt + l%16, rows 8g..8g+7 of the step
+        const int64_t off = (int64_t)(16 * jt + t) * vrow + (32 * (int64_t)st + 8 * g) * 2;
+        const bf16x8 bh = as_bf16x8(*reinterpret_cast<const u32x4*>(vst + off));
+        const bf16x8 bl = as_bf16x8(*reinterpret_cast<const u32x4*>(vst + 16 * nj * vrow + off));
+#pragma unroll
+        for (int pt = 0; pt < 2; ++pt) {
+          acc[pt][jt] = mfma16(a[pt], bh, acc[pt][jt]);
+          acc[pt][jt] = mfma16(a[pt], bl, acc[pt][jt]);
+        }
       }
     }
-    __syncthreads();
+    // step st+1's loads (issued 3 steps ago) have landed everywhere before
+    // anyone reads them or overwrites this stage
+    asm volatile("s_waitcnt vmcnt(4)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   }
-  // lane l: column j = 16jt + l%16, rows p = 16w + 4(l/16) + i
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // lane: column j = 16jt + l%16, rows p = 16pt + 4(l/16) + i of the wave
   float* dst = part + (int64_t)blockIdx.y * P * r;
 #pragma unroll
   for (int jt = 0; jt < 4; ++jt) {
-    if (jt >= nj) continue;
-    const int j = 16 * jt + (lane & 15);
-    if (j >= r) continue;
-    for (int i = 0; i < 4; ++i) {
-      const int64_t p = p0 + 16 * wave + 4 * (lane >> 4) + i;
-      if (p < P) dst[p * r + j] = acc[jt][i];
-    }
+    const int j = 16 * jt + t;
+    if (jt >= nj || j >= r) continue;
+#pragma unroll
+    for (int pt = 0; pt < 2; ++pt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t p = p0 + 32 * wave + 16 * pt + 4 * g + i;
+        if (p < P) dst[p * r + j] = acc[pt][jt][i];
+      }
   }
 }
 
-// out = sum over slices of part (slice order); transposed: out[j][p].
+// out = sum over slices of part, added in slice order (loads issued eight
+// at a time); transposed: out[j][p], thread index running along p.
 __global__ void k_sum_slices_tn(const float* __restrict__ part, int64_t P, int r, int S,
                                 bool transposed, float* __restrict__ out) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t count = P * r;
-  if (i >= count) return;
+  if (t >= count) return;
+  // element index into part[s] ([P][r]) and into out
+  const int64_t i = transposed ? (t % P) * r + t / P : t;
   float acc = part[i];
-  for (int s = 1; s < S; ++s) acc += part[(int64_t)s * count + i];
-  if (transposed)
-    out[(i % r) * P + i / r] = acc;
-  else
-    out[i] = acc;
+  for (int s0 = 1; s0 < S; s0 += 8) {
+    float v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = s0 + k < S ? part[(int64_t)(s0 + k) * count + i] : 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (s0 + k < S) acc += v[k];
+  }
+  out[t] = acc;
 }
 
-int thin_tn_slices(int64_t M, int64_t P) {
-  const int64_t pt = (P + 63) / 64;
-  int64_t S = 512 / (pt > 0 ? pt : 1);
-  const int64_t smax = (M + 255) / 256;
-  if (S > smax) S = smax;
-  if (S < 1) S = 1;
-  return (int)S;
-}
-
-hipError_t launch_thin_tn(const uint16_t* Z, const float* V, int64_t M, int64_t P, int r,
-                          float s, float* out, bool transposed, float* part, int S,
-                          hipStream_t st) {
+// Slices of the M rows for the transposed products: enough workgroups to
+// fill the chip, a multiple of 32 rows each, and the slice's (sV)^T (2 parts
+// x 16 ceil(r/16) rows) in at most 32 KB of LDS.
+int64_t thin_tn_slice_rows(int64_t M, int64_t P, int r) {
+  const int nj = (r + 15) / 16;
+  const int64_t pt = (P + TN_COLS - 1) / TN_COLS;
+  int64_t S = (512 + pt - 1) / pt;
   int64_t slice = (M + S - 1) / S;
   slice = (slice + 31) / 32 * 32;
-  const dim3 grid((unsigned)((P + 63) / 64), (unsigned)S);
-  hipLaunchKernelGGL(k_thin_tn, grid, dim3(kThreads), 0, st, Z, V, M, P, r, s, slice, part);
+  const int64_t cap = 32768 / (2 * 16 * nj * 2) / 32 * 32;  // 512 / nj
+  if (slice > cap) slice = cap;
+  if (slice < 32) slice = 32;
+  return slice;
+}
+
+int thin_tn_slices(int64_t M, int64_t P, int r) {
+  const int64_t slice = thin_tn_slice_rows(M, P, r);
+  return (int)((M + slice - 1) / slice);
+}
+
+// Row length of the staged (sV)^T: every slice's rows exist (zero past M).
+int64_t thin_tn_rows_padded(int64_t M, int64_t P, int r) {
+  return (int64_t)thin_tn_slices(M, P, r) * thin_tn_slice_rows(M, P, r);
+}
+
+hipError_t launch_prep_svt(const float* V, int64_t M, int64_t Mp, int r, float s, uint16_t* vt,
+                           hipStream_t st) {
+  const int rp = 16 * ((r + 15) / 16);
+  const int64_t count = (int64_t)rp * Mp;
+  hipLaunchKernelGGL(k_prep_svt, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, st, V, M,
+                     Mp, r, rp, s, vt);
+  return hipGetLastError();
+}
+
+hipError_t launch_thin_tn(const uint16_t* Z, const uint16_t* vt, int64_t M, int64_t P, int r,
+                          float* out, bool transposed, float* part, int S, hipStream_t st) {
+  const int64_t slice = thin_tn_slice_rows(M, P, r);
+  const int nj = (r + 15) / 16;
+  const size_t lds = (size_t)TN_NST * TN_STAGE + (size_t)2 * 16 * nj * slice * 2;
+  static hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(k_thin_tn), hipFuncAttributeMaxDynamicSharedMemorySize,
+      (int)(TN_NST * TN_STAGE + 32768));
+  if (attr != hipSuccess) return attr;
+  const dim3 grid((unsigned)((P + TN_COLS - 1) / TN_COLS), (unsigned)S);
+  hipLaunchKernelGGL(k_thin_tn, grid, dim3(kThreads), lds, st, Z, M, P, vt,
+                     thin_tn_rows_padded(M, P, r), r, slice, part);
   const int64_t count = P * r;
   hipLaunchKernelGGL(k_sum_slices_tn, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, st,
                      part, P, r, S, transposed, out);

@@ -5,9 +5,11 @@
 
 namespace qn {
 
+// ws_bad [ng] per-group non-finite flags; *flag = 1 when any weight is NaN
+// or infinite, else 0 (written by the last kernel; no clearing needed).
 hipError_t launch_quantize(const float* W, int64_t n, uint8_t* packed, uint8_t* qscale,
                            float* scale2, float* offset, float* ws_absmax, double* ws_part,
-                           int64_t part_len, int* ws_flag, hipStream_t st);
+                           int64_t part_len, int* ws_bad, int* flag, hipStream_t st);
 
 hipError_t launch_dequant(const uint8_t* packed, const uint8_t* qscale, const float* scale2,
                           const float* offset, int64_t n, bool bf16, void* out, hipStream_t st);
@@ -52,13 +54,20 @@ hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st);
 // Bt[r, N] = B[N, r]^T (bf16).
 hipError_t launch_transpose_b(const uint16_t* B, int64_t N, int r, uint16_t* Bt, hipStream_t st);
 
-// out = s * Z^T V reduced over the M rows: Z bf16 [M, P], V fp32 [M, r];
+// vt [2][rp][Mp] bf16 = high and remainder parts of (s V)^T, V fp32 [M, r],
+// rp = 16 ceil(r/16), zero for j >= r or m >= M.
+hipError_t launch_prep_svt(const float* V, int64_t M, int64_t Mp, int r, float s, uint16_t* vt,
+                           hipStream_t st);
+
+// out = Z^T (sV) reduced over the M rows: Z bf16 [M, P], vt from
+// launch_prep_svt with Mp = thin_tn_rows_padded(M, P, r);
 // transposed == false: out fp32 [P, r]; true: out fp32 [r, P].  Split over
-// S row slices, partials part[S][P][r], summed in slice order.
-hipError_t launch_thin_tn(const uint16_t* Z, const float* V, int64_t M, int64_t P, int r,
-                          float s, float* out, bool transposed, float* part, int S,
-                          hipStream_t st);
-int thin_tn_slices(int64_t M, int64_t P);
+// S = thin_tn_slices(M, P, r) row slices, partials part[S][P][r], summed in
+// slice order.  P % 8 == 0.
+hipError_t launch_thin_tn(const uint16_t* Z, const uint16_t* vt, int64_t M, int64_t P, int r,
+                          float* out, bool transposed, float* part, int S, hipStream_t st);
+int thin_tn_slices(int64_t M, int64_t P, int r);
+int64_t thin_tn_rows_padded(int64_t M, int64_t P, int r);
 
 // Decode forward, u = X A^T included (written to u_out [M, r]); workspace
 // part [S, M, rows] and upart [S, M, r] fp32, S = decode_slices(...).

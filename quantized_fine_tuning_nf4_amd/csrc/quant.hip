@@ -94,8 +94,10 @@ __global__ __launch_bounds__(256) void k_quant_blocks(
     float* __restrict__ absmax, double* __restrict__ part, int* __restrict__ bad) {
   __shared__ CodeLut lut[65];
   __shared__ double tree[kGroup];
+  __shared__ int s_bad;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   if (tid < 65) build_code_lut(lut, tid);
+  if (tid == 0) s_bad = 0;
 
   const int64_t g = blockIdx.x;
   const int64_t e_wave = (g * kGroup + wave * 64) * kBlock;
@@ -121,7 +123,7 @@ __global__ __launch_bounds__(256) void k_quant_blocks(
     const uint32_t a2 = as_u32(v[j].z) & 0x7fffffffu, a3 = as_u32(v[j].w) & 0x7fffffffu;
     // |w| bit patterns order like the values; NaN/Inf sort above all finite
     const uint32_t m = row16_max(max(max(a0, a1), max(a2, a3)));
-    if (m >= 0x7f800000u) *bad = 1;
+    if (m >= 0x7f800000u) s_bad = 1;
     const float s = as_f32(m);
     const int slot = wave * 64 + 4 * j + (lane >> 4);
     const int64_t b = g * kGroup + slot;
@@ -145,7 +147,10 @@ __global__ __launch_bounds__(256) void k_quant_blocks(
     if (tid < h) tree[tid] += tree[tid + h];
     __syncthreads();
   }
-  if (tid == 0) part[g] = tree[0];
+  if (tid == 0) {
+    part[g] = tree[0];
+    bad[g] = s_bad;  // every group writes its flag: no clearing pass needed
+  }
 }
 
 // Pass 2.  mu = RN32(S / nb), S = stride-halving tree over the group partials
@@ -153,9 +158,19 @@ __global__ __launch_bounds__(256) void k_quant_blocks(
 // a long tree run in global memory, the last 2048 in LDS.
 __global__ __launch_bounds__(1024) void k_quant_mean(double* __restrict__ part, int64_t ng,
                                                      int64_t len, int64_t nb,
-                                                     float* __restrict__ offset) {
+                                                     float* __restrict__ offset,
+                                                     const int* __restrict__ bad,
+                                                     int* __restrict__ flag) {
   __shared__ double t[2048];
+  __shared__ int s_any;
   const int tid = threadIdx.x;
+  if (tid == 0) s_any = 0;
+  __syncthreads();
+  {  // any group with a non-finite weight
+    int any = 0;
+    for (int64_t j = tid; j < ng; j += 1024) any |= bad[j];
+    if (any) s_any = 1;
+  }
   int64_t h = len / 2;
   for (; h >= 2048; h /= 2) {
     for (int64_t j = tid; j < h; j += 1024) {
@@ -174,7 +189,10 @@ __global__ __launch_bounds__(1024) void k_quant_mean(double* __restrict__ part, 
     for (int64_t j = tid; j < h; j += 1024) t[j] += t[j + h];
     __syncthreads();
   }
-  if (tid == 0) *offset = (float)(t[0] / (double)nb);
+  if (tid == 0) {
+    *offset = (float)(t[0] / (double)nb);
+    *flag = s_any;
+  }
 }
 
 // Pass 3.  One workgroup per group: d_b, C2, s2 and the E4M3 codes.
@@ -200,15 +218,13 @@ __global__ __launch_bounds__(256) void k_quant_dq(const float* __restrict__ absm
 
 hipError_t launch_quantize(const float* W, int64_t n, uint8_t* packed, uint8_t* qscale,
                            float* scale2, float* offset, float* ws_absmax, double* ws_part,
-                           int64_t part_len, int* ws_flag, hipStream_t st) {
+                           int64_t part_len, int* ws_bad, int* flag, hipStream_t st) {
   const int64_t nb = (n + kBlock - 1) / kBlock;
   const int64_t ng = (nb + kGroup - 1) / kGroup;
-  hipError_t e = hipMemsetAsync(ws_flag, 0, sizeof(int), st);
-  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_quant_blocks, dim3((unsigned)ng), dim3(256), 0, st, W, n, nb, packed,
-                     ws_absmax, ws_part, ws_flag);
+                     ws_absmax, ws_part, ws_bad);
   hipLaunchKernelGGL(k_quant_mean, dim3(1), dim3(1024), 0, st, ws_part, ng, part_len, nb,
-                     offset);
+                     offset, ws_bad, flag);
   hipLaunchKernelGGL(k_quant_dq, dim3((unsigned)ng), dim3(256), 0, st, ws_absmax, nb, offset,
                      qscale, scale2);
   return hipGetLastError();

@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol(qn):
 
 def test_abi_version_and_status_strings(qn):
     L = qn.load_library()
-    assert L.qn_abi_version() == 1
+    assert L.qn_abi_version() == 2
     for s in range(6):
         assert len(L.qn_status_str(s)) > 0
     assert L.qn_status_str(0) == b"ok"
@@ -57,15 +57,19 @@ def test_library_codebook_equals_page_table(qn):
 
 def test_workspace_sizes(qn):
     L = qn.load_library()
-    # absmax fp32 [nb] | fp64 partials [pow2(ng)] | flag, 256-aligned pieces
+    # absmax fp32 [nb] | fp64 partials [pow2(ng)] | group flags int [ng] | flag,
+    # 256-aligned pieces
     nb, ng = 262144, 1024
-    want = nb * 4 + ng * 8 + 4
+    want = nb * 4 + ng * 8 + ng * 4 + 4
     assert L.nf4_quantize_dq_workspace(4096, 4096) == want
     assert L.nf4_quantize_dq_workspace(0, 5) == 0
     assert L.qlora_linear_workspace(8192, 4096, 4096, 16, 0) >= 8192 * 16 * 4
     b = L.qlora_linear_workspace(8192, 4096, 4096, 16, 1)
     assert b >= 8192 * 16 * 4 * 2 + 16 * 4096 * 2
     assert L.qlora_linear_workspace(1, 8, 64, 65, 0) == 0
+    # an empty batch is legal: its workspace query must not fault on the host
+    assert L.qlora_linear_workspace(0, 4096, 4096, 16, 0) == 0
+    assert L.qlora_linear_workspace(0, 4096, 4096, 16, 1) >= 0
 
 
 FAKE = 1 << 20  # a non-null, 256-aligned address that is never dereferenced
@@ -80,11 +84,13 @@ def test_argument_errors_are_host_side(qn):
     L = qn.load_library()
     EINVAL, EALIGN, EWS = qn.QN_EINVAL, qn.QN_EALIGN, qn.QN_EWORKSPACE
     # quantize
-    assert L.nf4_quantize_dq(None, 4, 4, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == EINVAL
-    assert L.nf4_quantize_dq(FAKE, 0, 4, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == EINVAL
-    assert L.nf4_quantize_dq(FAKE + 4, 4, 4, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == EALIGN
-    assert L.nf4_quantize_dq(FAKE, 4, 4, FAKE, FAKE, FAKE, FAKE, FAKE + 16, 1 << 20, None) == EALIGN
-    assert L.nf4_quantize_dq(FAKE, 4096, 4096, FAKE, FAKE, FAKE, FAKE, FAKE, 100, None) == EWS
+    q = L.nf4_quantize_dq
+    assert q(None, 4, 4, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 20, None) == EINVAL
+    assert q(FAKE, 0, 4, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 20, None) == EINVAL
+    assert q(FAKE + 4, 4, 4, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 20, None) == EALIGN
+    assert q(FAKE, 4, 4, FAKE, FAKE, FAKE, FAKE, None, FAKE + 16, 1 << 20, None) == EALIGN
+    assert q(FAKE, 4, 4, FAKE, FAKE, FAKE, FAKE, FAKE + 2, FAKE, 1 << 20, None) == EALIGN
+    assert q(FAKE, 4096, 4096, FAKE, FAKE, FAKE, FAKE, None, FAKE, 100, None) == EWS
     # dequantize
     s = _state(0, 64)
     assert L.nf4_dequantize(ctypes.byref(s), 1, FAKE, None) == EINVAL

@@ -128,6 +128,30 @@ def test_quant_rejects_nonfinite(qn):
     check_quant(qn, wl.weight(64, 256, seed=6), "after non-finite")
 
 
+def test_quant_async_flag(qn):
+    """With a device flag the call does not synchronize; the flag reads 1 for
+    non-finite input, 0 otherwise, and the state equals the synchronous one."""
+    import torch
+    flag = torch.full((1,), 7, dtype=torch.int32, device="cuda")
+    W = wl.weight(512, 1024, seed=8)
+    st_sync = qn.nf4_quantize_dq(f32_dev(W))
+    st = qn.nf4_quantize_dq(f32_dev(W), nonfinite=flag)
+    torch.cuda.synchronize()
+    assert int(flag.item()) == 0
+    a, b = state_np(st_sync), state_np(st)
+    for k in ("packed", "qscale", "scale2", "offset"):
+        assert np.array_equal(a[k], b[k]), k
+    for bad in (np.nan, np.inf):
+        Wb = W.copy()
+        Wb[300, 1000] = bad
+        qn.nf4_quantize_dq(f32_dev(Wb), nonfinite=flag)
+        torch.cuda.synchronize()
+        assert int(flag.item()) == 1
+    qn.nf4_quantize_dq(f32_dev(W), nonfinite=flag)
+    torch.cuda.synchronize()
+    assert int(flag.item()) == 0
+
+
 def test_quant_deterministic(qn):
     W = f32_dev(wl.weight(2048, 4096, seed=9))
     a = state_np(qn.nf4_quantize_dq(W))
