@@ -60,6 +60,11 @@
  *     QN_EDEVICE: a HIP runtime call failed (no device, launch failure).
  *   - Calls that overlap on one stream are ordered; calls on different
  *     streams that share a workspace race.
+ *   - Decode-sized forwards (1 <= M <= 16, r <= 16, cols % 1024 == 0) run as
+ *     one kernel whose column slices meet through arrival counters in the
+ *     library's static device memory: 64 slots per device, one per call,
+ *     taken round robin and left at zero when the call ends.  More than 64
+ *     such calls executing at the same time on one device would race.
  */
 #ifndef QLORA_NF4_H
 #define QLORA_NF4_H

@@ -14,6 +14,8 @@
 // 64g + 16w .. +15), blocks z*nbs .. (z+1)*nbs-1 of every row; X's slice is
 // staged in LDS once for the four waves.  Partial sums go to part[z][m][n];
 // a second kernel adds the slices, the LoRA term and rounds to bf16.
+#include <atomic>
+
 #include "qn_device.h"
 #include "qn_internal.h"
 
@@ -207,6 +209,340 @@ __global__ __launch_bounds__(T) void k_decode_finish(const float* __restrict__ p
   Y[m * N + n] = (uint16_t)(pack_bf16x2(__builtin_fmaf(s, lora, acc), 0.f) & 0xffffu);
 }
 
+// ---------------------------------------------------------------------------
+// One-kernel decode forward over tiles of (band of 16 RGT rows) x (slice of
+// 1024 columns), one workgroup of 16 waves each:
+//   - wave w owns block pair w % 8 of the slice and the band's row groups of
+//     parity w / 8; its X and A fragments are loaded once;
+//   - a unit of work is one 16-row group of the wave's block pair: 16 rows x
+//     64 bytes of codes, which the wave itself moves into its own LDS ring by
+//     one direct-to-LDS load (lane t: row t / 4, 16-byte chunk
+//     (t % 4) ^ ((row / 2) % 4), so that the MFMA-layout reads below are
+//     free of bank conflicts).  Each wave runs its own pipeline, NST - 1
+//     units in flight, with no barrier in the main loop;
+//   - lane (l16, g4) reads bytes 16 g4 .. +15 of row l16's block pair; two
+//     v_permlane32_swap regroup the dwords so that each MFMA operand holds
+//     one block (the per-block scale stays after the MFMA), koff1/koff2 give
+//     the code positions each lane group carries;
+//   - a code byte becomes its bf16 pair through a 256-entry LDS table in 32
+//     copies (entry e of copy c at byte 256 e + 4 c, copy = lane % 32): the
+//     32 lanes of a bank cycle never collide; v_perm_b32 forms the address;
+//   - the waves' sums meet in LDS; the tile's partial y and its part of
+//     u = X A^T go to the workspace through device-coherent stores; the last
+//     tile of a band to arrive (an arrival counter per band) adds the slices
+//     in slice order with device-coherent loads, adds s u B^T and writes bf16
+//     y, so the result does not depend on the order of arrival.  Counters
+//     live in a per-device table, one row per call slot, and are returned to
+//     zero by the tile that finishes the band.
+constexpr int TT = 1024;
+constexpr int NWV = TT / 64;       // waves
+constexpr int NPR = 8;             // block pairs per slice
+constexpr int KSL = 1024;          // columns per slice
+constexpr int RGM = 16;            // row groups per band, at most
+constexpr int RPW = RGM / 2;       // row groups per wave, at most
+constexpr int NST = 5;             // ring slots per wave (NST - 1 units in flight)
+constexpr int UB = 1024;           // bytes per unit: 16 rows x 64 B
+constexpr int L_TAB = 0, L_RING = 65536, L_U = L_RING + NWV * NST * UB;
+constexpr int L_URED = L_U + 16 * 17 * 4, L_QS = L_URED + NPR * 4 * 64 * 4;
+constexpr int L_S2 = L_QS + RGM * 16 * 16, L_FLAG = L_S2 + RGM * 16 * 4;
+constexpr int L_TOTAL = L_FLAG + 16;
+constexpr int kSlots = 64, kMaxBands = 1024;
+static_assert(NPR * RGM * 4 * 64 * 4 <= L_U, "reduction buffer overlaps");
+static_assert(L_TOTAL <= 160 * 1024, "LDS");
+
+__device__ unsigned g_band_arrivals[kSlots * kMaxBands];
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rs(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(lo | (hi << 32)), 0,
+                                           __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000);
+}
+
+__device__ __forceinline__ uint32_t tab_pair(const uint8_t* tab, uint32_t w, uint32_t base, int i) {
+  // byte address 256 * (byte i of w) + base, base = 4 (lane % 32)
+  const uint32_t a = __builtin_amdgcn_perm(w, base, 0x0c0c0000u | ((4u + (uint32_t)i) << 8));
+  return *reinterpret_cast<const uint32_t*>(tab + a);
+}
+__device__ __forceinline__ bf16x8 tab_pairs4(const uint8_t* tab, uint32_t w, uint32_t base) {
+  return as_bf16x8(u32x4{tab_pair(tab, w, base, 0), tab_pair(tab, w, base, 1),
+                         tab_pair(tab, w, base, 2), tab_pair(tab, w, base, 3)});
+}
+// Device-coherent 16-byte store / load (cache policy sc1, the device
+// scope): the access goes to the level shared by every XCD, never leaving a
+// stale or dirty line in one XCD's L2, so no cache-wide write-back or
+// invalidate is needed around it.
+constexpr int kDeviceScope = 16;  // sc1
+__device__ __forceinline__ void st_dev4(rsrc_t rs, uint32_t off, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, off, 0, kDeviceScope);
+}
+__device__ __forceinline__ f32x4 ld_dev4(rsrc_t rs, uint32_t off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kDeviceScope));
+}
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__global__ __launch_bounds__(TT, 1) void k_decode_tile(
+    const uint8_t* __restrict__ packed, const uint8_t* __restrict__ qscale,
+    const float* __restrict__ scale2, const float* __restrict__ offset,
+    const uint16_t* __restrict__ X, int64_t M, int64_t N, int64_t K,
+    const uint16_t* __restrict__ Aad, const uint16_t* __restrict__ Bad, int r, float s, int rgt,
+    int S, unsigned* __restrict__ arrivals, float* __restrict__ part, float* __restrict__ upart,
+    uint16_t* __restrict__ Y, float* __restrict__ u_out) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[L_TOTAL];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int pr = wave & (NPR - 1), par = wave / NPR;
+  const int l16 = lane & 15, g4 = lane >> 4;
+  const int band = blockIdx.x / S, z = blockIdx.x % S;
+  const int BR = 16 * rgt;
+  const int64_t n0 = (int64_t)band * BR;
+  const int nrows = (int)min((int64_t)BR, N - n0);
+  const int64_t kb = K / 64;
+  const int64_t col0 = (int64_t)z * KSL + 128 * pr;  // first column of the wave's pair
+
+  // ---- small loads first (their waits then never wait for the code stream)
+  const float lo_level = as_f32(kNF4Bits[(tid >> 5) & 15]);
+  const int koff1 = 32 * (g4 & 1) + ((g4 >> 1) ? 16 : 8);
+  const int koff2 = 32 * (g4 & 1) + ((g4 >> 1) ? 24 : 0);
+  // rows past M / r read the last valid row: finite values in outputs never stored
+  const uint16_t* xrow = X + (int64_t)min(l16, (int)M - 1) * K + col0;
+  const uint16_t* arow = Aad + (int64_t)min(l16, r - 1) * K + col0;
+  bf16x8 xf[2][2], af[2][2];
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    xf[b][0] = as_bf16x8(*reinterpret_cast<const u32x4*>(xrow + 64 * b + koff1));
+    xf[b][1] = as_bf16x8(*reinterpret_cast<const u32x4*>(xrow + 64 * b + koff2));
+    af[b][0] = as_bf16x8(*reinterpret_cast<const u32x4*>(arow + 64 * b + koff1));
+    af[b][1] = as_bf16x8(*reinterpret_cast<const u32x4*>(arow + 64 * b + koff2));
+  }
+  // the band's scales for this slice, straight into LDS (direct-to-LDS
+  // loads: nothing waits for them before the code stream is issued): the 16
+  // scale codes of each row (thread t: row t / 4, bytes 4 (t % 4) ..) and
+  // each row's second-level scale (rows past the band read its last row)
+  {
+    const int row = min(tid >> 2, nrows - 1);
+    const rsrc_t rq = make_rs(qscale + n0 * kb + (int64_t)z * (KSL / 64),
+                              (uint32_t)((int64_t)(nrows - 1) * kb + KSL / 64));
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rq, (__attribute__((address_space(3))) void*)(smem + L_QS + 256 * wave), 4,
+        (uint32_t)(row * kb + 4 * (tid & 3)), 0, 0, 0);
+    if (wave < RGM * 16 / 64) {
+      const rsrc_t r2 = make_rs(scale2, (uint32_t)((N * kb + kGroup - 1) / kGroup * 4));
+      const int64_t b2 = (n0 + min(tid, nrows - 1)) * kb + (int64_t)z * (KSL / 64);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          r2, (__attribute__((address_space(3))) void*)(smem + L_S2 + 256 * wave), 4,
+          (uint32_t)(b2 / kGroup * 4), 0, 0, 0);
+    }
+  }
+
+  // ---- the wave's code stream: unit i = row group par + 2 i.  The
+  // descriptor of a unit starts at its first row and ends at the band's end,
+  // so rows past the band (and units past the last) read zeros without
+  // touching memory; the lane offset is fixed.
+  const int drow = lane >> 2;
+  const uint32_t voff = (uint32_t)drow * (uint32_t)(K / 2) + (uint32_t)z * (KSL / 2) +
+                        64u * (uint32_t)pr + 16u * (uint32_t)((lane & 3) ^ ((drow >> 1) & 3));
+  uint8_t* ring = smem + L_RING + wave * NST * UB;
+  auto dma_unit = [&](int i) {
+    const int rg = par + 2 * i;
+    const int64_t left = max((int64_t)0, (int64_t)nrows - 16 * rg);
+    const rsrc_t rs = make_rs(packed + (n0 + min((int64_t)16 * rg, (int64_t)nrows)) * (K / 2),
+                              (uint32_t)(left * (K / 2)));
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rs, (__attribute__((address_space(3))) void*)(ring + (i % NST) * UB), 16, voff, 0, 0, 0);
+  };
+#pragma unroll
+  for (int i = 0; i < NST - 1; ++i) dma_unit(i);
+
+  // ---- tables (while the loads are in flight): thread tid fills copy
+  // tid % 32 of the entries with low nibble tid / 32 % 16 and high nibble
+  // hi = tid / 512 (mod 2); hi is a constant in each branch, so the levels
+  // are immediates (no loads that would wait behind the code stream)
+  static_assert(TT == 1024, "table fill assumes 1024 threads");
+  uint32_t* tab32 = reinterpret_cast<uint32_t*>(smem + L_TAB);
+  const int hi_par = __builtin_amdgcn_readfirstlane(tid >> 9);  // wave-uniform
+  uint32_t* trow = tab32 + ((tid >> 5) & 15) * 64 + (tid & 31);
+#pragma unroll
+  for (int hi = 0; hi < 16; ++hi)
+    if ((hi & 1) == hi_par) trow[hi * 16 * 64] = pack_bf16x2(lo_level, as_f32(kNF4Bits[hi]));
+  // tables and scales ready (everything but the NST - 1 code units in
+  // flight has landed); the code stream stays in flight across the barrier
+  wait_vm<NST - 1>();
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  const uint8_t* tab = smem + L_TAB;
+  const uint32_t tbase = 4u * (lane & 31);
+  const float mu = *offset;
+  const int rd = 16 * (4 * l16 + (g4 ^ ((l16 >> 1) & 3)));  // this lane's chunk in a unit
+  // the block scales of the wave's two blocks for row l16 of each of its
+  // row groups, once: s'_b = fma(e4m3(q_b), s2, mu)
+  float sca[RPW], scb[RPW];
+#pragma unroll
+  for (int i = 0; i < RPW; ++i) {
+    const int row = 16 * (par + 2 * i) + l16;
+    const uint32_t qs = *reinterpret_cast<const uint16_t*>(smem + L_QS + 16 * row + 2 * pr);
+    const float s2 = reinterpret_cast<const float*>(smem + L_S2)[row];
+    sca[i] = dq_scale(qs & 0xffu, s2, mu);
+    scb[i] = dq_scale((qs >> 8) & 0xffu, s2, mu);
+  }
+
+  f32x4 acc[RPW];
+#pragma unroll
+  for (int i = 0; i < RPW; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < RPW; ++i) {
+    if (par + 2 * i >= rgt) continue;
+    wait_vm<NST - 2>();  // unit i landed; units i + 1 .. i + NST - 2 still fly
+    const u32x4 c = *reinterpret_cast<const u32x4*>(ring + (i % NST) * UB + rd);
+    // unit i + NST - 1 goes into the slot of unit i - 1, whose read is done
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    dma_unit(i + NST - 1);
+    const auto h = __builtin_amdgcn_permlane32_swap(c[1], c[2], false, false);
+    const auto l = __builtin_amdgcn_permlane32_swap(c[0], c[3], false, false);
+    const float sa = sca[i], sb = scb[i];
+    f32x4 t = mfma16(xf[0][0], tab_pairs4(tab, h[0], tbase), f32x4{0.f, 0.f, 0.f, 0.f});
+    t = mfma16(xf[0][1], tab_pairs4(tab, l[0], tbase), t);
+    f32x4 t2 = mfma16(xf[1][0], tab_pairs4(tab, h[1], tbase), f32x4{0.f, 0.f, 0.f, 0.f});
+    t2 = mfma16(xf[1][1], tab_pairs4(tab, l[1], tbase), t2);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      acc[i][v] = __builtin_fmaf(sa, t[v], acc[i][v]);
+      acc[i][v] = __builtin_fmaf(sb, t2[v], acc[i][v]);
+    }
+  }
+  f32x4 uacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    uacc = mfma16(xf[b][0], af[b][0], uacc);
+    uacc = mfma16(xf[b][1], af[b][1], uacc);
+  }
+  wait_vm<0>();  // the trailing unit loads land before their LDS is reused
+
+  // ---- the waves' sums: lane (l16, g4) slot v holds row 16 rg + l16, m = 4 g4 + v
+  __syncthreads();
+  float* s_red = reinterpret_cast<float*>(smem);            // [pair][rg][v][lane]
+  float* s_ured = reinterpret_cast<float*>(smem + L_URED);  // [pair][v][lane]
+#pragma unroll
+  for (int i = 0; i < RPW; ++i) {
+    const int rg = par + 2 * i;
+    if (rg < rgt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) s_red[((pr * RGM + rg) * 4 + v) * 64 + lane] = acc[i][v];
+  }
+  if (par == 0)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) s_ured[(pr * 4 + v) * 64 + lane] = uacc[v];
+  __syncthreads();
+  // partial sums of this tile: thread (m = tid / 64, rows 4 (tid % 64) ..
+  // + 3), one 16-byte store; part rows are Np = N rounded up to 4 long
+  const int64_t Np = (N + 3) & ~(int64_t)3;
+  const rsrc_t rpart = make_rs(part, (uint32_t)((int64_t)S * M * Np * 4));
+  const rsrc_t rupart = make_rs(upart, (uint32_t)((int64_t)gridDim.x * 256 * 4));
+  const int om = tid >> 6, orow = 4 * (tid & 63);
+  if (om < M && orow < nrows) {
+    const f32x4* red4 = reinterpret_cast<const f32x4*>(s_red);
+    f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int p = 0; p < NPR; ++p)
+      a += red4[(((p * RGM + (orow >> 4)) * 4 + (om & 3)) * 64 + (orow & 15) + 16 * (om >> 2)) / 4];
+    st_dev4(rpart, (uint32_t)((((int64_t)z * M + om) * Np + n0 + orow) * 4), a);
+  }
+  if (tid < 64) {
+    // u partial: [m][j] for m = tid / 4, j = 4 (tid % 4) .. + 3
+    const int m = tid >> 2, j = 4 * (tid & 3);
+    f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int p = 0; p < NPR; ++p)
+      a += *reinterpret_cast<const f32x4*>(s_ured + (p * 4 + (m & 3)) * 64 + j + 16 * (m >> 2));
+    st_dev4(rupart, (uint32_t)((((int64_t)band * S + z) * 256 + 16 * m + j) * 4), a);
+  }
+
+  // ---- arrival; the last tile of the band finishes it.  Every wave's
+  // device-coherent stores have completed (vmcnt(0)) before the barrier, so
+  // they precede the arrival; the finishing tile reads them with
+  // device-coherent loads after it has seen all S arrivals.
+  wait_vm<0>();
+  __syncthreads();
+  int* s_flag = reinterpret_cast<int*>(smem + L_FLAG);
+  if (tid == 0) {
+    const unsigned old =
+        __hip_atomic_fetch_add(arrivals + band, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_flag[0] = old == (unsigned)(S - 1);
+  }
+  __syncthreads();
+  if (!s_flag[0]) return;
+  // ---- finishing the band: every load goes out before the first is used
+  // (the band's B rows into LDS, the u partials, this thread's S partial
+  // sums), then the sums run in slice order
+  // B of the band, transposed into LDS (the ring is free): s_bt[j][row],
+  // row pitch BTP, zero for j >= r; a thread later reads four consecutive
+  // rows of one j at once
+  constexpr int BTP = RGM * 16 + 8;
+  uint16_t* s_bt = reinterpret_cast<uint16_t*>(smem + L_RING);
+  for (int e = tid; e < BR * 16; e += TT) {
+    const int row = e >> 4, j = e & 15;
+    const int64_t n = n0 + min(row, nrows - 1);
+    s_bt[j * BTP + row] = j < r ? Bad[n * r + min(j, r - 1)] : (uint16_t)0;
+  }
+  float* s_u = reinterpret_cast<float*>(smem + L_U);  // [16][17]
+  f32x4 ua = {0.f, 0.f, 0.f, 0.f}, ya = {0.f, 0.f, 0.f, 0.f};
+  const bool yok = om < M && orow < nrows;
+  for (int z0 = 0; z0 < S; z0 += 4) {
+    f32x4 uv[4], yv[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int zz = z0 + q;
+      uv[q] = (zz < S && tid < 64)
+                  ? ld_dev4(rupart, (uint32_t)((((int64_t)band * S + zz) * 256 + 4 * tid) * 4))
+                  : f32x4{0.f, 0.f, 0.f, 0.f};
+      yv[q] = (zz < S && yok)
+                  ? ld_dev4(rpart, (uint32_t)((((int64_t)zz * M + om) * Np + n0 + orow) * 4))
+                  : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (z0 + q < S) {
+        ua += uv[q];
+        ya += yv[q];
+      }
+  }
+  if (tid < 64) {
+    // u[m][j], m = tid / 4, j = 4 (tid % 4) + q, summed in slice order
+    const int m = tid >> 2, j0 = 4 * (tid & 3);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      s_u[m * 17 + j0 + q] = ua[q];
+      if (band == 0 && m < M && j0 + q < r) u_out[m * r + j0 + q] = ua[q];
+    }
+  }
+  if (tid == 0)  // every tile of the band has arrived: ready for the next call
+    __hip_atomic_store(arrivals + band, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();  // s_u, s_bt
+  if (yok) {
+    float lora[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const u32x2 b4 = *reinterpret_cast<const u32x2*>(s_bt + j * BTP + orow);
+      const float uj = s_u[om * 17 + j];
+      lora[0] = __builtin_fmaf(uj, bf16_lo(b4[0]), lora[0]);
+      lora[1] = __builtin_fmaf(uj, bf16_hi(b4[0]), lora[1]);
+      lora[2] = __builtin_fmaf(uj, bf16_lo(b4[1]), lora[2]);
+      lora[3] = __builtin_fmaf(uj, bf16_hi(b4[1]), lora[3]);
+    }
+    uint16_t yo[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      yo[q] = (uint16_t)(pack_bf16x2(__builtin_fmaf(s, lora[q], ya[q]), 0.f) & 0xffffu);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (orow + q < nrows) Y[om * N + n0 + orow + q] = yo[q];
+  }
+}
+
 }  // namespace
 
 int decode_slices(int64_t M, int64_t N, int64_t K) {
@@ -214,6 +550,50 @@ int decode_slices(int64_t M, int64_t N, int64_t K) {
   (void)N;
   if (M < 1 || M > 16 || K % 1024 != 0) return 0;
   return (int)(K / 1024);
+}
+
+DecodeTiles decode_tiles(int64_t M, int64_t N, int64_t K, int r) {
+  DecodeTiles t{0, 0, 0};
+  if (M < 1 || M > 16 || r < 1 || r > 16 || N < 1 || K < KSL || K % KSL != 0) return t;
+  static int cus = [] {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 0;
+    return n;
+  }();
+  if (cus <= 0) return t;
+  const int64_t S = K / KSL, groups = (N + 15) / 16;
+  const int64_t per_slice = max((int64_t)1, (int64_t)cus / S);
+  const int64_t rgt = min((int64_t)RGM, (groups + per_slice - 1) / per_slice);
+  const int64_t bands = (N + 16 * rgt - 1) / (16 * rgt);
+  if (bands > kMaxBands || bands * S > (int64_t)1 << 30) return t;
+  t.rgt = (int)rgt;
+  t.S = (int)S;
+  t.bands = (int)bands;
+  return t;
+}
+
+hipError_t launch_decode_tile(const WState& w, const uint16_t* X, int64_t M, const uint16_t* A,
+                              const uint16_t* B, int r, float s, uint16_t* Y, float* u_out,
+                              const DecodeTiles& t, float* part, float* upart, hipStream_t st) {
+  const int64_t N = w.rows, K = w.cols;
+  if (t.rgt < 1 || t.rgt > RGM || t.S != K / KSL || t.bands < 1 || t.bands > kMaxBands ||
+      (int64_t)t.bands * 16 * t.rgt < N || M < 1 || M > 16 || r < 1 || r > 16)
+    return hipErrorInvalidValue;
+  static unsigned* table = [] {
+    void* p = nullptr;
+    return hipGetSymbolAddress(&p, HIP_SYMBOL(g_band_arrivals)) == hipSuccess
+               ? static_cast<unsigned*>(p)
+               : nullptr;
+  }();
+  if (!table) return hipErrorInvalidSymbol;
+  static std::atomic<unsigned> next_slot{0};
+  unsigned* arrivals = table + (size_t)(next_slot.fetch_add(1) % kSlots) * kMaxBands;
+  hipLaunchKernelGGL(k_decode_tile, dim3((unsigned)(t.bands * t.S)), dim3(TT), 0, st, w.packed,
+                     w.qscale, w.scale2, w.offset, X, M, N, K, A, B, r, s, t.rgt, t.S, arrivals,
+                     part, upart, Y, u_out);
+  return hipGetLastError();
 }
 
 hipError_t launch_decode_fwd(const WState& w, const uint16_t* X, int64_t M, const uint16_t* A,

@@ -75,6 +75,20 @@ hipError_t launch_decode_fwd(const WState& w, const uint16_t* X, int64_t M, cons
                              const uint16_t* B, int r, float s, uint16_t* Y, float* u_out,
                              float* part, float* upart, int S, hipStream_t st);
 
+// One-kernel decode forward (M <= 16, r <= 16, cols % 1024 == 0): tiles of
+// 16 rgt rows x 1024 columns; S = cols / 1024 slices, `bands` row bands.
+// rgt == 0 when it does not apply.  Workspace: part [S, M, rows rounded up
+// to 4] and upart [bands, S, 256] fp32, 16-byte aligned.  Writes Y and u_out.  Calls on one device share
+// a table of 64 call slots of arrival counters (taken round robin): more than
+// 64 such calls in flight at once on one device would race.
+struct DecodeTiles {
+  int rgt, S, bands;
+};
+DecodeTiles decode_tiles(int64_t M, int64_t rows, int64_t cols, int r);
+hipError_t launch_decode_tile(const WState& w, const uint16_t* X, int64_t M, const uint16_t* A,
+                              const uint16_t* B, int r, float s, uint16_t* Y, float* u_out,
+                              const DecodeTiles& t, float* part, float* upart, hipStream_t st);
+
 // Y[M, N] bf16 = X[M, K] * W'[N, K]^T + s * u[M, r] * B[N, r]^T.
 hipError_t launch_qgemm_fwd(const WState& w, const uint16_t* X, int64_t M, const float* u,
                             const uint16_t* B, int r, float s, uint16_t* Y, hipStream_t st);

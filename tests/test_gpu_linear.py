@@ -111,8 +111,13 @@ def test_decode_config(qn, M):
 
 
 @pytest.mark.parametrize("rows,cols,M,r", [
-    (4096, 14336, 3, 16),   # decode kernels, 14 K slices
-    (1000, 1024, 5, 7),     # one slice, partial 64-row group, odd rank
+    (4096, 14336, 3, 16),   # one-kernel decode: 14 slices, 240-row bands
+    (8200, 2048, 7, 5),     # one-kernel decode: 2 slices, 80-row bands, ragged last band
+    (16384, 4096, 16, 16),  # one-kernel decode: 4 slices, 256-row bands (the widest)
+    (9000, 4096, 2, 13),    # one-kernel decode: 9 row groups per band, rank 13
+    (1040, 3072, 1, 1),     # one-kernel decode: one row group per band, rank 1
+    (1000, 1024, 5, 7),     # one slice, partial row group, odd rank
+    (2048, 2048, 8, 32),    # rank 32: the two-kernel decode (u by extra workgroups)
     (264, 192, 9, 5),       # cols % 1024 != 0: the 32-row fused GEMM instead
 ])
 def test_decode_shapes(qn, rows, cols, M, r):
@@ -248,16 +253,36 @@ def test_autograd_module(qn):
     assert rel_err(mod.lora_B.grad.float().cpu().numpy(), dB_ref) <= 1e-2
 
 
-def test_decode_forward_in_a_graph_replays_exactly(qn):
+@pytest.mark.parametrize("rows,M", [(14336, 4), (4096, 16), (1040, 1)])
+def test_decode_calls_sharing_a_workspace_see_fresh_inputs(qn, rows, M):
+    """Successive decode forwards through one workspace (partial sums of the
+    previous call still in it) give exactly what separate workspaces give."""
+    c = Case(rows, 4096, M, 16, 32.0, seed=33)
+    st, x1, A, B, _ = c.dev(qn)
+    x2 = bf16_dev(wl.normal_bf16((M, 4096), 34, 1.0))
+    ref1, _ = qn.qlora_linear_fwd(st, x1, A, B, c.alpha)
+    ref2, _ = qn.qlora_linear_fwd(st, x2, A, B, c.alpha)
+    L = qn.load_library()
+    ws = torch.zeros(max(L.qlora_linear_workspace(M, rows, 4096, 16, 0), 1), dtype=torch.uint8,
+                     device="cuda")
+    for xin, ref in ((x1, ref1), (x2, ref2), (x1, ref1), (x2, ref2)):
+        y, _ = qn.qlora_linear_fwd(st, xin, A, B, c.alpha, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(y, ref)
+
+
+@pytest.mark.parametrize("rows", [4096, 14336])
+def test_decode_forward_in_a_graph_replays_exactly(qn, rows):
     """The decode forward captured in a HIP graph: every replay, with eager
-    work between replays, equals the eager result bit for bit."""
-    c = Case(4096, 4096, 4, 16, 32.0, seed=21)
+    work between replays, equals the eager result bit for bit (the band sums
+    do not depend on the order in which tiles arrive)."""
+    c = Case(rows, 4096, 4, 16, 32.0, seed=21)
     st, x, A, B, _ = c.dev(qn)
     y_ref, u_ref = qn.qlora_linear_fwd(st, x, A, B, c.alpha)
     y = torch.empty_like(y_ref)
     u = torch.empty_like(u_ref)
     L = qn.load_library()
-    ws = torch.empty(L.qlora_linear_workspace(4, 4096, 4096, 16, 0), dtype=torch.uint8,
+    ws = torch.empty(L.qlora_linear_workspace(4, rows, 4096, 16, 0), dtype=torch.uint8,
                      device="cuda")
     s = st.c_struct()
     torch.cuda.synchronize()
