@@ -25,17 +25,16 @@
 // buckets of width 1/32 on [-1, 1]: every bucket holds at most one t_k and
 // every t_k lies at least 1.6e-3 from a bucket edge, far beyond the error of
 // q, so the bucket is right even when q and the true quotient straddle an
-// edge.
+// edge.  The table holds, per bucket, mu_k (or 4.0 when the bucket holds no
+// threshold) with the bucket's lower code c0 in the four low bits of the
+// fp64 pattern (mu_k has 25 significant bits, so those bits are zero), in 16
+// copies (bucket j, copy c at entry 16 j + c; lane l reads copy l % 16) so
+// that the 16 lanes a 64-bit LDS read serves per cycle never collide.
 #include "qn_device.h"
 #include "qn_internal.h"
 
 namespace qn {
 
-struct CodeLut {
-  double mu;  // midpoint to compare against (4.0: bucket holds no threshold)
-  int c0;     // code of the bucket's lower part
-  int pad;
-};
 
 __device__ __forceinline__ float f32_next_up(float t) {
   uint32_t b = as_u32(t);
@@ -46,8 +45,10 @@ __device__ __forceinline__ float f32_next_down(float t) {
   return as_f32(t > 0.f ? b - 1u : b + 1u);
 }
 
-// Entry j covers quotients in [(j-32)/32, (j-31)/32).
-__device__ void build_code_lut(CodeLut* lut, int j) {
+// Entry j covers quotients in [(j-32)/32, (j-31)/32): mu (4.0: the bucket
+// holds no threshold) with c0, the code of the bucket's lower part, in its
+// four low bits.
+__device__ uint64_t code_lut_entry(int j) {
   const double lo = (double)(j - 32) * 0.03125, hi = (double)(j - 31) * 0.03125;
   int c0 = 0;
   double mu = 4.0;
@@ -62,9 +63,7 @@ __device__ void build_code_lut(CodeLut* lut, int j) {
       mu = ((double)t + (double)f32_next_up(t)) * 0.5;
     }
   }
-  lut[j].mu = mu;
-  lut[j].c0 = c0;
-  lut[j].pad = 0;
+  return __builtin_bit_cast(uint64_t, mu) | (uint64_t)c0;
 }
 
 // Max of v over each row of 16 lanes (DPP: xor 1, xor 2, half-row mirror,
@@ -78,35 +77,35 @@ __device__ __forceinline__ uint32_t row16_max(uint32_t v) {
 }
 
 __device__ __forceinline__ uint32_t nf4_code(float w, double s64, double rs,
-                                             const CodeLut* lut) {
+                                             const uint64_t* lut_copy) {
   const double w64 = (double)w;
   int idx = (int)__builtin_fma(w64 * rs, 32.0, 32.0);
   idx = min(max(idx, 0), 64);
-  const CodeLut e = lut[idx];
-  return (uint32_t)e.c0 + (w64 > e.mu * s64 ? 1u : 0u);
+  const uint64_t e = lut_copy[16 * idx];
+  const double mu = __builtin_bit_cast(double, e & ~(uint64_t)15);
+  return (uint32_t)(e & 15u) + (w64 > mu * s64 ? 1u : 0u);
 }
 
 // Pass 1.  One workgroup per group of 256 blocks (16384 weights); wave w
 // owns blocks 64w..64w+63 of the group, and at step j its 64 lanes read
-// 1 KB: four blocks, 16 lanes x float4 per block.
-__global__ __launch_bounds__(256) void k_quant_blocks(
-    const float* __restrict__ W, int64_t n, int64_t nb, uint8_t* __restrict__ packed,
-    float* __restrict__ absmax, double* __restrict__ part, int* __restrict__ bad) {
-  __shared__ CodeLut lut[65];
-  __shared__ double tree[kGroup];
-  __shared__ int s_bad;
+// 1 KB: four blocks, 16 lanes x float4 per block.  The body is instantiated
+// for whole groups (every load unconditional, all 16 in flight at once) and
+// for the tail group (element-wise bounds); the kernel branches once, around
+// the whole body, so no loaded value meets a branch join (which would make
+// the compiler wait for every load there).
+template <bool FULL>
+__device__ __forceinline__ void quant_group(const float* __restrict__ W, int64_t n, int64_t nb,
+                                            uint8_t* __restrict__ packed,
+                                            float* __restrict__ absmax, double* tree,
+                                            const uint64_t* lut, int* s_bad) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  if (tid < 65) build_code_lut(lut, tid);
-  if (tid == 0) s_bad = 0;
-
   const int64_t g = blockIdx.x;
   const int64_t e_wave = (g * kGroup + wave * 64) * kBlock;
-  const bool full = (g + 1) * (int64_t)(kGroup * kBlock) <= n;
   float4 v[16];
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     const int64_t e = e_wave + j * 256 + lane * 4;
-    if (full) {
+    if (FULL) {
       v[j] = *reinterpret_cast<const float4*>(W + e);
     } else {
       v[j].x = e + 0 < n ? W[e + 0] : 0.f;
@@ -115,32 +114,53 @@ __global__ __launch_bounds__(256) void k_quant_blocks(
       v[j].w = e + 3 < n ? W[e + 3] : 0.f;
     }
   }
-  __syncthreads();  // code table ready
-
+  // code table ready (LDS-only barrier: the loads above stay in flight)
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  const uint64_t* lc = lut + (lane & 15);
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     const uint32_t a0 = as_u32(v[j].x) & 0x7fffffffu, a1 = as_u32(v[j].y) & 0x7fffffffu;
     const uint32_t a2 = as_u32(v[j].z) & 0x7fffffffu, a3 = as_u32(v[j].w) & 0x7fffffffu;
     // |w| bit patterns order like the values; NaN/Inf sort above all finite
     const uint32_t m = row16_max(max(max(a0, a1), max(a2, a3)));
-    if (m >= 0x7f800000u) s_bad = 1;
+    if (m >= 0x7f800000u) *s_bad = 1;
     const float s = as_f32(m);
     const int slot = wave * 64 + 4 * j + (lane >> 4);
     const int64_t b = g * kGroup + slot;
     if ((lane & 15) == 0) {
-      if (b < nb) absmax[b] = s;
-      tree[slot] = (b < nb) ? (double)s : 0.0;
+      if (FULL || b < nb) absmax[b] = s;
+      tree[slot] = (FULL || b < nb) ? (double)s : 0.0;
     }
     const double s64 = s > 0.f ? (double)s : 1.0;
     const double rs = __builtin_amdgcn_rcp(s64);
-    const uint32_t c0 = nf4_code(v[j].x, s64, rs, lut), c1 = nf4_code(v[j].y, s64, rs, lut);
-    const uint32_t c2 = nf4_code(v[j].z, s64, rs, lut), c3 = nf4_code(v[j].w, s64, rs, lut);
-    if (b < nb) {
+    const uint32_t c0 = nf4_code(v[j].x, s64, rs, lc), c1 = nf4_code(v[j].y, s64, rs, lc);
+    const uint32_t c2 = nf4_code(v[j].z, s64, rs, lc), c3 = nf4_code(v[j].w, s64, rs, lc);
+    if (FULL || b < nb) {
       const int64_t e = e_wave + j * 256 + lane * 4;
       *reinterpret_cast<uint16_t*>(packed + e / 2) =
           (uint16_t)(c0 | (c1 << 4) | (c2 << 8) | (c3 << 12));
     }
   }
+}
+
+__global__ __launch_bounds__(256) void k_quant_blocks(
+    const float* __restrict__ W, int64_t n, int64_t nb, uint8_t* __restrict__ packed,
+    float* __restrict__ absmax, double* __restrict__ part, int* __restrict__ bad) {
+  __shared__ uint64_t lut[65 * 16];
+  __shared__ double tree[kGroup];
+  __shared__ int s_bad;
+  const int tid = threadIdx.x;
+  if (tid < 65) {
+    const uint64_t e = code_lut_entry(tid);
+#pragma unroll
+    for (int c = 0; c < 16; ++c) lut[16 * tid + c] = e;
+  }
+  if (tid == 0) s_bad = 0;
+  const int64_t g = blockIdx.x;
+  if ((g + 1) * (int64_t)(kGroup * kBlock) <= n)
+    quant_group<true>(W, n, nb, packed, absmax, tree, lut, &s_bad);
+  else
+    quant_group<false>(W, n, nb, packed, absmax, tree, lut, &s_bad);
   __syncthreads();
   // fixed-order fp64 partial sum of this group's 256 scale slots
   for (int h = kGroup / 2; h >= 1; h >>= 1) {
