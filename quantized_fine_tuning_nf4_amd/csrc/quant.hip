@@ -254,46 +254,50 @@ hipError_t launch_quantize(const float* W, int64_t n, uint8_t* packed, uint8_t* 
 // Dequantisation.  Thread-chunk c covers CH consecutive weights (CH = 8 for
 // bf16 output: one u32 of codes in, 16 B out; CH = 4 for fp32: one u16 in,
 // 16 B out).  A workgroup's 256 threads take 256 consecutive chunks, so
-// loads and stores are contiguous; each thread does UNROLL chunks.
-template <bool BF16>
-__global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ packed,
-                                                 const uint8_t* __restrict__ qscale,
-                                                 const float* __restrict__ scale2,
-                                                 const float* __restrict__ offset, int64_t n,
-                                                 void* __restrict__ out) {
+// loads and stores are contiguous; each thread does UNROLL chunks, all of
+// whose loads (codes, scale code, second-level scale) go out before the first
+// is used.  Whole workgroups (every chunk in range) take unconditional
+// loads; only the last workgroup checks bounds, and the kernel branches once
+// around the whole body, so no loaded value meets a branch join.
+template <bool BF16, bool FULL>
+__device__ __forceinline__ void dequant_chunks(const uint8_t* __restrict__ packed,
+                                               const uint8_t* __restrict__ qscale,
+                                               const float* __restrict__ scale2,
+                                               const float* __restrict__ offset, int64_t n,
+                                               void* __restrict__ out, const float* lut) {
   constexpr int CH = BF16 ? 8 : 4;
   constexpr int UNROLL = 4;
-  __shared__ float lut[16];
-  if (threadIdx.x < 16) lut[threadIdx.x] = as_f32(kNF4Bits[threadIdx.x]);
   const int64_t nchunk = (n + CH - 1) / CH;
   const int64_t c_first = (int64_t)blockIdx.x * 256 * UNROLL + threadIdx.x;
-  const float mu = *offset;
-  uint32_t p[UNROLL];
-  float sc[UNROLL];
+  uint32_t p[UNROLL], qb[UNROLL];
+  float s2[UNROLL];
 #pragma unroll
   for (int i = 0; i < UNROLL; ++i) {
-    const int64_t c = c_first + i * 256;
-    if (c < nchunk) {
-      if (BF16)
-        p[i] = *reinterpret_cast<const uint32_t*>(packed + c * 4);
-      else
-        p[i] = *reinterpret_cast<const uint16_t*>(packed + c * 2);
-      const int64_t b = c * CH / kBlock;
-      sc[i] = dq_scale(qscale[b], scale2[b / kGroup], mu);
-    }
+    const int64_t c = FULL ? c_first + i * 256 : min(c_first + i * 256, nchunk - 1);
+    if (BF16)
+      p[i] = *reinterpret_cast<const uint32_t*>(packed + c * 4);
+    else
+      p[i] = *reinterpret_cast<const uint16_t*>(packed + c * 2);
+    const int64_t b = c * CH / kBlock;
+    qb[i] = qscale[b];
+    s2[i] = scale2[b / kGroup];
   }
-  __syncthreads();
+  const float mu = *offset;
+  __builtin_amdgcn_sched_barrier(0);  // every load issues before the first use
+  // the level table is ready (LDS-only barrier: the loads stay in flight)
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 #pragma unroll
   for (int i = 0; i < UNROLL; ++i) {
     const int64_t c = c_first + i * 256;
-    if (c >= nchunk) continue;
+    if (!FULL && c >= nchunk) continue;
+    const float sc = dq_scale(qb[i], s2[i], mu);
     float w[CH];
 #pragma unroll
-    for (int k = 0; k < CH; ++k) w[k] = lut[(p[i] >> (4 * k)) & 15u] * sc[i];
+    for (int k = 0; k < CH; ++k) w[k] = lut[(p[i] >> (4 * k)) & 15u] * sc;
     const int64_t e = c * CH;
     if (BF16) {
       uint16_t* o = reinterpret_cast<uint16_t*>(out) + e;
-      if (e + CH <= n) {
+      if (FULL || e + CH <= n) {
         u32x4 q = {pack_bf16x2(w[0], w[1]), pack_bf16x2(w[2], w[3]), pack_bf16x2(w[4], w[5]),
                    pack_bf16x2(w[6], w[7])};
         *reinterpret_cast<u32x4*>(o) = q;
@@ -303,13 +307,35 @@ __global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ pac
       }
     } else {
       float* o = reinterpret_cast<float*>(out) + e;
-      if (e + CH <= n) {
+      if (FULL || e + CH <= n) {
         *reinterpret_cast<float4*>(o) = make_float4(w[0], w[1], w[2], w[3]);
       } else {
         for (int k = 0; k < CH && e + k < n; ++k) o[k] = w[k];
       }
     }
   }
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ packed,
+                                                 const uint8_t* __restrict__ qscale,
+                                                 const float* __restrict__ scale2,
+                                                 const float* __restrict__ offset, int64_t n,
+                                                 void* __restrict__ out) {
+  constexpr int CH = BF16 ? 8 : 4;
+  constexpr int UNROLL = 4;
+  __shared__ float lut[16];
+  if (threadIdx.x < 16) {  // from immediates: no load that the first weight loads would queue behind
+    uint32_t v = kNF4Bits[0];
+#pragma unroll
+    for (int k = 1; k < 16; ++k) v = threadIdx.x == k ? kNF4Bits[k] : v;
+    lut[threadIdx.x] = as_f32(v);
+  }
+  const int64_t last_elem = ((int64_t)blockIdx.x + 1) * 256 * UNROLL * CH;  // one past
+  if (last_elem <= n)
+    dequant_chunks<BF16, true>(packed, qscale, scale2, offset, n, out, lut);
+  else
+    dequant_chunks<BF16, false>(packed, qscale, scale2, offset, n, out, lut);
 }
 
 hipError_t launch_dequant(const uint8_t* packed, const uint8_t* qscale, const float* scale2,
