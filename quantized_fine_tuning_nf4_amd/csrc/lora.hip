@@ -95,6 +95,100 @@ __global__ __launch_bounds__(kThreads) void k_thin_nt(const uint16_t* __restrict
   }
 }
 
+// r <= 16: the same product with T's slice (rows 0..15, zero past r)
+// staged in LDS once per workgroup (row pitch 64 steps + 16 bytes, so the
+// 16-byte reads of 8 consecutive rows fall in distinct bank groups), and Z
+// streamed through registers two batches of TN1_U steps deep: the loads of
+// batch b + 1 are in flight while batch b is multiplied.  Columns past the
+// slice read as zero (selected at use, so no load waits at a branch).
+constexpr int TN1_U = 4;
+constexpr int64_t kThinNt1MaxSlice = 2048;
+__global__ __launch_bounds__(kThreads) void k_thin_nt1(const uint16_t* __restrict__ Z,
+                                                       const uint16_t* __restrict__ T, int64_t M,
+                                                       int64_t P, int r, int64_t slice,
+                                                       float* __restrict__ out) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int g = lane >> 4, l16 = lane & 15;
+  const int64_t mw = (int64_t)blockIdx.x * 64 + 16 * wave;
+  const int64_t m = min(mw + l16, M - 1);
+  const int64_t pb = (int64_t)blockIdx.y * slice, pe = min(pb + slice, P);
+  const int64_t width = pe - pb;
+  const int steps = (int)((width + 31) / 32);
+  const int nb = (steps + TN1_U - 1) / TN1_U;
+  const int pitch = steps * 64 + 16;
+  const uint16_t* zp = Z + m * P + pb + 8 * g;
+  const int64_t lim = width - 8 * g;  // in-slice columns left for this lane's chunk
+  u32x4 za[2][TN1_U];
+  auto load_batch = [&](int buf, int b) {
+#pragma unroll
+    for (int u = 0; u < TN1_U; ++u) {
+      const int64_t off = 32 * (int64_t)(TN1_U * b + u);
+      za[buf][u] = *reinterpret_cast<const u32x4*>(zp + (off < lim ? off : 0));
+    }
+  };
+  {
+    // stage T: eight 16-byte chunks per thread per pass, every load issued
+    // before the first is used (clamped addresses; zero selected at the LDS
+    // write for rows past r and columns past the slice); the first Z batch
+    // goes out behind the first pass
+    const int cpr = steps * 4;  // 16-byte chunks per staged row
+    const int total = 16 * cpr;
+    for (int e0 = 0; e0 < total; e0 += 8 * kThreads) {
+      u32x4 tv[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int e = min(e0 + q * kThreads + tid, total - 1);
+        const int j = e / cpr, c = e - j * cpr;
+        const int64_t col = min(8 * (int64_t)c, width - 8);
+        tv[q] = *reinterpret_cast<const u32x4*>(T + (int64_t)min(j, r - 1) * P + pb + col);
+      }
+      if (e0 == 0) load_batch(0, 0);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int e = e0 + q * kThreads + tid;
+        if (e < total) {
+          const int j = e / cpr, c = e - j * cpr;
+          const bool ok = j < r && 8 * (int64_t)c < width;
+          *reinterpret_cast<u32x4*>(smem + j * pitch + 16 * c) = ok ? tv[q] : u32x4{0u, 0u, 0u, 0u};
+        }
+      }
+    }
+  }
+  // LDS-only barrier: the first Z batch stays in flight
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  const uint8_t* trow = smem + l16 * pitch + 16 * g;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  auto compute_batch = [&](int buf, int b) {
+#pragma unroll
+    for (int u = 0; u < TN1_U; ++u) {
+      const int st = TN1_U * b + u;
+      if (st < steps) {
+        const u32x4 z = 32 * (int64_t)st < lim ? za[buf][u] : u32x4{0u, 0u, 0u, 0u};
+        const u32x4 t = *reinterpret_cast<const u32x4*>(trow + 64 * st);
+        acc = mfma16(as_bf16x8(z), as_bf16x8(t), acc);
+      }
+    }
+  };
+  for (int b = 0; b < nb; b += 2) {
+    if (b + 1 < nb) load_batch(1, b + 1);
+    compute_batch(0, b);
+    if (b + 1 < nb) {
+      if (b + 2 < nb) load_batch(0, b + 2);
+      compute_batch(1, b + 1);
+    }
+  }
+  // lane l: column j = l%16, rows mw + 4(l/16) + i
+  float* dst = out + (int64_t)blockIdx.y * M * r;
+  if (l16 < r) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t row = mw + 4 * g + i;
+      if (row < M) dst[row * r + l16] = acc[i];
+    }
+  }
+}
+
 // out[i] = sum over s of part[s][i], added in slice order (loads issued
 // eight at a time).
 __global__ void k_sum_slices(const float* __restrict__ part, int64_t count, int S,
@@ -129,11 +223,21 @@ hipError_t launch_thin_nt(const uint16_t* Z, const uint16_t* T, int64_t M, int64
   slice = (slice + 127) / 128 * 128;
   const dim3 grid((unsigned)((M + 63) / 64), (unsigned)S);
   float* dst = S > 1 ? part : out;
+  if (r <= 16 && slice <= kThinNt1MaxSlice) {
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(k_thin_nt1), hipFuncAttributeMaxDynamicSharedMemorySize,
+        (int)(16 * (kThinNt1MaxSlice * 2 + 16)));
+    if (attr != hipSuccess) return attr;
+    const int steps = (int)((slice + 31) / 32);
+    const size_t lds = (size_t)16 * (steps * 64 + 16);
+    hipLaunchKernelGGL(k_thin_nt1, grid, dim3(kThreads), lds, st, Z, T, M, P, r, slice, dst);
+  } else {
   switch ((r + 15) / 16) {
     case 1: hipLaunchKernelGGL(k_thin_nt<1>, grid, dim3(kThreads), 0, st, Z, T, M, P, r, slice, dst); break;
     case 2: hipLaunchKernelGGL(k_thin_nt<2>, grid, dim3(kThreads), 0, st, Z, T, M, P, r, slice, dst); break;
     case 3: hipLaunchKernelGGL(k_thin_nt<3>, grid, dim3(kThreads), 0, st, Z, T, M, P, r, slice, dst); break;
     default: hipLaunchKernelGGL(k_thin_nt<4>, grid, dim3(kThreads), 0, st, Z, T, M, P, r, slice, dst); break;
+  }
   }
   if (S > 1) {
     const int64_t count = M * r;
