@@ -154,7 +154,7 @@ BwdWs carve_bwd(Carver& c, int64_t M, int64_t rows, int64_t cols, int r, bool ne
   b.Sa = thin_tn_slices(M, cols, r);
   b.dApart = c.take<float>((size_t)b.Sa * cols * r);
   b.sv = c.take<uint16_t>((size_t)2 * rp * thin_tn_rows_padded(M, cols, r));
-  b.ldt = round_up(rows, 32);
+  b.ldt = round_up(rows, 64);
   const bool dense = dense_path(M, cols);
   b.wt = dense ? c.take<uint16_t>((size_t)cols * b.ldt) : nullptr;
   b.At = dense ? c.take<uint16_t>((size_t)cols * r) : nullptr;

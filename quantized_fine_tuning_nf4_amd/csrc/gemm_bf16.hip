@@ -7,18 +7,22 @@
 // storage, gradients and local integration" (paragraph after the teaching
 // listing), once the weight has been dequantized to bf16 in a workspace.
 //
-// Workgroup tile 256 x 256, four waves (2 x 2), each wave 128 x 128 as 4 x 4
-// tiles of v_mfma_f32_32x32x16_bf16 (256 accumulators).  A step covers 32
-// reduction elements; both operands are brought from global memory straight
-// into LDS by buffer loads (no registers), four stages deep: the loads of
-// step s+3 are issued at the start of step s, and the barrier ending step s
-// guarantees step s+2, so the fragments of step s+1 are read during step s.
-// LDS rows are 64 bytes (four 16-byte chunks); chunk c of row y sits at unit
-// c ^ ((y >> 2) & 3), which keeps 16 consecutive rows read at one chunk on
-// distinct banks.  Reduction order inside a step: lane group g = lane/32 and
-// substep ks take elements 16 ks + 8 g + 0..7 (chunk 2 ks + g) of both
-// operands.  Rows of A past its length R are clamped onto its last chunk;
-// Bm is zero there (its rows are padded to a multiple of 32 with zeros).
+// Workgroup tile 256 x 256, four waves (2 x 2), each wave 128 x 128 as 8 x 8
+// tiles of v_mfma_f32_16x16x32_bf16 (256 accumulators, pinned in AGPRs).  On
+// gfx950 this shape keeps a higher shader clock under load than the 32x32x16
+// one at the same issue rate.  A step covers 64 reduction elements: both
+// operands go from global memory straight into LDS by buffer loads, each
+// load instruction filling eight whole 128-byte rows (one cache line per row
+// and step), two stages deep.  A step is multiplied in two halves of 32; the
+// fragments of the next half are read from LDS while the current half's
+// MFMAs run (A in place, B in a second set).  The loads of step s+2 go out
+// during the second half of step s into step s's stage, whose last fragments
+// were read during its first half; the end of the first half of step s+1
+// waits for them.  Chunk c (16 bytes) of LDS row y sits at unit
+// c ^ ((y >> 1) & 7), which keeps the sixteen rows of one fragment read on
+// distinct banks.  Rows of A past its length R are moved back onto its last
+// chunk; Bm is zero there (its rows are padded to a multiple of 64 with
+// zeros).
 #include <type_traits>
 
 #include "qn_device.h"
@@ -27,10 +31,10 @@
 namespace qn {
 namespace {
 
-constexpr int BM = 256, BN = 256, BK = 32, NST = 4, T = 256;
-constexpr int ROWB = BK * 2;            // bytes per tile row per stage
-constexpr int OPB = 256 * ROWB;         // bytes per operand per stage (16 KB)
-constexpr int STB = 2 * OPB;            // bytes per stage
+constexpr int BM = 256, BN = 256, BK = 64, NST = 2, T = 256;
+constexpr int ROWB = BK * 2;            // bytes per tile row per stage (one cache line)
+constexpr int OPB = 256 * ROWB;         // bytes per operand per stage (32 KB)
+constexpr int STB = 2 * OPB;            // bytes per stage (64 KB)
 constexpr int OUTP = 128 * 2 + 16;      // epilogue staging row pitch (bytes)
 constexpr int OUTW = 128 * OUTP;        // staging bytes per wave
 constexpr size_t LDS_BYTES = (size_t)NST * STB > (size_t)4 * OUTW ? (size_t)NST * STB
@@ -39,8 +43,10 @@ constexpr size_t LDS_BYTES = (size_t)NST * STB > (size_t)4 * OUTW ? (size_t)NST 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
-__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+// the same product with the accumulator pinned in AGPRs (destination tied to
+// the addend); the caller keeps dependent reads of c away from it
+__device__ __forceinline__ void mfma16_acc(bf16x8 a, bf16x8 b, f32x4& c) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
 }
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
@@ -60,10 +66,6 @@ __device__ __forceinline__ void dma16(rsrc_t rs, uint32_t voff, uint32_t soff, u
 __device__ __forceinline__ void barrier_lds() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
-// all but the newest step's eight loads have landed
-__device__ __forceinline__ void wait_all_but_one_step() {
-  asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-}
 __device__ __forceinline__ void wait_all_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 __global__ __launch_bounds__(T, 1) void k_gemm_nt(
@@ -72,7 +74,7 @@ __global__ __launch_bounds__(T, 1) void k_gemm_nt(
     const uint16_t* __restrict__ L, int r, float s, uint16_t* __restrict__ C, int tiles_m,
     int tiles_c) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
 
@@ -97,130 +99,133 @@ __global__ __launch_bounds__(T, 1) void k_gemm_nt(
   const int64_t m0 = (int64_t)tm * BM, c0 = (int64_t)tc * BN;
   const int64_t mrows = min((int64_t)BM, M - m0), ncols = min((int64_t)BN, Nc - c0);
 
-  // ---- loads: instruction i of wave w covers tile rows 64w + 16i + l/4,
-  // stored unit l%4, source chunk (l%4) ^ ((row >> 2) & 3).
+  // ---- loads: a stage holds 64 reduction elements (128-byte rows, one
+  // cache line per row and step).  Load instruction i (0..7) of wave w covers
+  // rows 64w + 8i + l/8 of an operand; lane l fills unit l%8 of its row with
+  // source chunk (l%8) ^ ((row >> 1) & 7), so the 1 KB it writes is
+  // contiguous and the sixteen rows a fragment read touches sit on distinct
+  // banks.
   const rsrc_t rsA = make_rs(A + m0 * lda, (uint32_t)(mrows * lda * 2));
   const rsrc_t rsB = make_rs(Bm + c0 * ldb, (uint32_t)(ncols * ldb * 2));
-  const int chunk = (lane & 3) ^ ((lane >> 4) & 3);
-  uint32_t aoff[4], boff[4];
+  uint32_t aoff[8], boff[8];
+  int achunk[8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t row = 64 * wave + 16 * i + (lane >> 2);
+  for (int i = 0; i < 8; ++i) {
+    const int64_t row = 64 * wave + 8 * i + (lane >> 3);
+    const int chunk = (lane & 7) ^ (int)((row >> 1) & 7);
+    achunk[i] = chunk;
     aoff[i] = (uint32_t)((min(row, mrows - 1) * lda + 8 * chunk) * 2);
     boff[i] = (uint32_t)((min(row, ncols - 1) * ldb + 8 * chunk) * 2);
   }
-  // A's reduction tail: columns past R are clamped onto the row's last chunk
-  auto a_back = [&](int st) {
-    const int64_t k = (int64_t)st * BK + 8 * chunk;
+  // A's reduction tail: a chunk past R is moved back onto the row's last
+  // chunk (its Bm partner is zero)
+  auto a_back = [&](int st, int i) {
+    const int64_t k = (int64_t)st * BK + 8 * achunk[i];
     return (uint32_t)(2 * (k - min(k, R - 8)));
   };
-  // load q (0..7) of step st into its stage: q < 4 A rows, else B rows
-  auto load_one = [&](int q, int st, int stage, uint32_t back) {
-    uint8_t* d = smem + stage * STB + (q >= 4 ? OPB : 0) + wave * 4096 + 1024 * (q & 3);
+  // load q (0..15) of step st: q < 8 A rows, else B rows
+  auto load_one = [&](int q, int st, int stage) {
+    uint8_t* d = smem + stage * STB + (q >= 8 ? OPB : 0) + wave * 8192 + 1024 * (q & 7);
     const uint32_t so = (uint32_t)st * (BK * 2);
-    if (q < 4)
-      dma16(rsA, aoff[q] - back, so, d);
+    if (q < 8)
+      dma16(rsA, aoff[q] - a_back(st, q), so, d);
     else
-      dma16(rsB, boff[q - 4], so, d);
-  };
-  auto load_step = [&](int st, int stage) {
-    const uint32_t back = a_back(st);
-#pragma unroll
-    for (int q = 0; q < 8; ++q) load_one(q, st, stage, back);
+      dma16(rsB, boff[q - 8], so, d);
   };
 
-  // ---- fragment reads: row 32t + l32 of a 32-row tile, chunk 2 ks + g
+  // ---- fragment reads (v_mfma_f32_16x16x32_bf16): tile t of the wave's 128
+  // rows, half h of the stage: lane l reads row 16t + l%16 at chunk
+  // 4h + l/16 (eight consecutive reduction elements)
+  const int l16 = lane & 15, g4 = lane >> 4;
   int roff[2];
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks) roff[ks] = l32 * ROWB + 16 * ((2 * ks + g) ^ ((l32 >> 2) & 3));
+  for (int h = 0; h < 2; ++h) roff[h] = l16 * ROWB + 16 * ((4 * h + g4) ^ ((l16 >> 1) & 7));
   const int abase = wm * 128 * ROWB, bbase = OPB + wn * 128 * ROWB;
-  auto frag = [&](int stage, int opbase, int t, int ks) {
-    return as_bf16x8(*reinterpret_cast<const u32x4*>(smem + stage * STB + opbase + t * 32 * ROWB +
-                                                     roff[ks]));
+  auto frag = [&](int stage, int opbase, int t, int h) {
+    return as_bf16x8(*reinterpret_cast<const u32x4*>(smem + stage * STB + opbase + t * 16 * ROWB +
+                                                     roff[h]));
   };
 
-  f32x16 acc[4][4];
+  f32x4 acc[8][8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{};
 
-  // fragment sets: X holds substep 0, Y substep 1
-  bf16x8 xa[4], xb[4], ya[4], yb[4];
+  // A fragments are replaced in place once their row of MFMAs has issued;
+  // B fragments come in two sets (first and second half of a stage)
+  bf16x8 fa[8], fb[2][8];
 
-  // ---- prologue: steps 0, 1, 2 in flight; 0 and 1 landed
+  // ---- prologue: steps 0 and 1 in flight, 0 landed
 #pragma unroll
-  for (int k = 0; k < 3; ++k) load_step(min(k, steps - 1), k);
-  asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  for (int k = 0; k < 2; ++k)
+#pragma unroll
+    for (int q = 0; q < 16; ++q) load_one(q, min(k, steps - 1), k);
+  asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
   barrier_lds();
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    xa[t] = frag(0, abase, t, 0);
-    xb[t] = frag(0, bbase, t, 0);
+  for (int t = 0; t < 8; ++t) {
+    fa[t] = frag(0, abase, t, 0);
+    fb[0][t] = frag(0, bbase, t, 0);
   }
 
-  // ---- one step on stage P: 32 MFMAs in two substeps; during substep 0 the
-  // Y set is read (substep 1 of this step), during substep 1 the X set (substep
-  // 0 of the next step, whose data the previous barrier guaranteed).
-  auto body = [&](auto p_t, int st) {
-    constexpr int P = decltype(p_t)::value, PN = (P + 1) % NST, PL = (P + 3) % NST;
-    // the loads of step st+3 are spread over the step, one per four MFMAs,
-    // so that the wave never waits on a full address queue
-    const int lst = min(st + 3, steps - 1);
-    const uint32_t lback = a_back(lst);
+  // ---- half h of step st on stage P: 64 MFMAs.  Half 0 reads half 1's
+  // fragments from the same stage, then waits for step st+1 (sent during
+  // half 1 of step st-1) and meets the other waves: after that barrier no
+  // wave reads stage P again.  Half 1 reads the next step's first half from
+  // the other stage and sends the sixteen loads of step st+2 into stage P.
+  // Half 1 needs no barrier of its own: the next half 0 reads only data that
+  // every wave waited for before the barrier above, and writes none.
+  auto half = [&](auto p_t, auto h_t, int st) {
+    constexpr int P = decltype(p_t)::value, H = decltype(h_t)::value;
+    constexpr int RS = H == 0 ? P : (P + 1) % NST;  // stage of the fragments read ahead
+    constexpr int RH = H ^ 1;                       // their half
+    const int lst = min(st + 2, steps - 1);
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+    for (int i = 0; i < 8; ++i) {
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const int i = c >> 1, j0 = 2 * (c & 1);
-        bf16x8* ca = ks == 0 ? xa : ya;
-        bf16x8* cb = ks == 0 ? xb : yb;
-        acc[i][j0] = mfma32(cb[j0], ca[i], acc[i][j0]);
-        acc[i][j0 + 1] = mfma32(cb[j0 + 1], ca[i], acc[i][j0 + 1]);
-        // one read per MFMA pair into the other set
-        const int t = c >> 1;
-        if ((c & 1) == 0) load_one(4 * ks + (c >> 1), lst, PL, lback);
-        if (ks == 0) {
-          if (c & 1) yb[t] = frag(P, bbase, t, 1);
-          else ya[t] = frag(P, abase, t, 1);
-        } else {
-          if (c & 1) xb[t] = frag(PN, bbase, t, 0);
-          else xa[t] = frag(PN, abase, t, 0);
-        }
-        __builtin_amdgcn_sched_barrier(0);
+      for (int j = 0; j < 8; ++j) {
+        mfma16_acc(fb[H][j], fa[i], acc[i][j]);
+        if (j == 1) fb[RH][i] = frag(RS, bbase, i, RH);
+        if (H == 1 && (j == 3 || j == 6)) load_one(2 * i + (j == 6), lst, P);
       }
+      fa[i] = frag(RS, abase, i, RH);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    wait_all_but_one_step();
-    barrier_lds();
+    if (H == 0) {
+      wait_all_loads();
+      barrier_lds();
+    }
   };
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
-  using S2 = std::integral_constant<int, 2>;
-  using S3 = std::integral_constant<int, 3>;
   int st = 0;
-  for (; st + 4 <= steps; st += 4) {
-    body(S0{}, st);
-    body(S1{}, st + 1);
-    body(S2{}, st + 2);
-    body(S3{}, st + 3);
+  for (; st + 2 <= steps; st += 2) {
+    half(S0{}, S0{}, st);
+    half(S0{}, S1{}, st);
+    half(S1{}, S0{}, st + 1);
+    half(S1{}, S1{}, st + 1);
   }
-  if (st < steps) body(S0{}, st);
-  if (st + 1 < steps) body(S1{}, st + 1);
-  if (st + 2 < steps) body(S2{}, st + 2);
+  if (st < steps) {
+    half(S0{}, S0{}, st);
+    half(S0{}, S1{}, st);
+  }
   // every wave's loads have landed and all reads are done before the stages
   // are reused for the output staging below
   wait_all_loads();
   barrier_lds();
 
-  // ---- LoRA term: acc += (s V) L^T, 16 ranks at a time; s V enters as a
-  // bf16 high part and a bf16 remainder.
+  // ---- LoRA term: acc += (s V) L^T, 16 ranks per MFMA reduction of 32: lane
+  // group g4 < 2 carries the bf16 high part of s V, g4 >= 2 its remainder,
+  // both against the same eight ranks 8(g4 & 1) .. +7 of L.
   const bool vec = (r % 8) == 0;
+  const bool lo_part = g4 >= 2;
   for (int j0 = 0; j0 < r; j0 += 16) {
-    const int jl = j0 + 8 * g;
-    bf16x8 lh[4];
+    const int jl = j0 + 8 * (g4 & 1);
+    bf16x8 lh[8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t col = min(c0 + wn * 128 + 32 * j + l32, Nc - 1);
+    for (int j = 0; j < 8; ++j) {
+      const int64_t col = min(c0 + wn * 128 + 16 * j + l16, Nc - 1);
       const uint16_t* lp = L + col * r;
       if (vec) {
         lh[j] = jl < r ? as_bf16x8(*reinterpret_cast<const u32x4*>(lp + jl)) : bf16x8{};
@@ -232,69 +237,51 @@ __global__ __launch_bounds__(T, 1) void k_gemm_nt(
                                 e[6] | (e[7] << 16)});
       }
     }
-    float vr[4][8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t m = min(m0 + wm * 128 + 32 * i + l32, M - 1);
+    for (int i = 0; i < 8; ++i) {
+      const int64_t m = min(m0 + wm * 128 + 16 * i + l16, M - 1);
       const float* vp = V + m * r;
+      float vr[8];
       if (vec && jl < r) {
         const f32x4 v0 = *reinterpret_cast<const f32x4*>(vp + jl);
         const f32x4 v1 = *reinterpret_cast<const f32x4*>(vp + jl + 4);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          vr[i][q] = v0[q];
-          vr[i][4 + q] = v1[q];
+          vr[q] = v0[q];
+          vr[4 + q] = v1[q];
         }
       } else {
 #pragma unroll
-        for (int q = 0; q < 8; ++q) vr[i][q] = jl + q < r ? vp[min(jl + q, r - 1)] : 0.f;
+        for (int q = 0; q < 8; ++q) vr[q] = jl + q < r ? vp[min(jl + q, r - 1)] : 0.f;
       }
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint32_t h[4], lo[4];
+      uint32_t w[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const float x0 = s * vr[i][2 * q], x1 = s * vr[i][2 * q + 1];
-        h[q] = pack_bf16x2(x0, x1);
-        lo[q] = pack_bf16x2(x0 - bf16_lo(h[q]), x1 - bf16_hi(h[q]));
+        const float x0 = s * vr[2 * q], x1 = s * vr[2 * q + 1];
+        const uint32_t h = pack_bf16x2(x0, x1);
+        w[q] = lo_part ? pack_bf16x2(x0 - bf16_lo(h), x1 - bf16_hi(h)) : h;
       }
-      const bf16x8 ah = as_bf16x8(u32x4{h[0], h[1], h[2], h[3]});
-      const bf16x8 al = as_bf16x8(u32x4{lo[0], lo[1], lo[2], lo[3]});
+      const bf16x8 av = as_bf16x8(u32x4{w[0], w[1], w[2], w[3]});
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        acc[i][j] = mfma32(lh[j], ah, acc[i][j]);
-        acc[i][j] = mfma32(lh[j], al, acc[i][j]);
-      }
+      for (int j = 0; j < 8; ++j) mfma16_acc(lh[j], av, acc[i][j]);
     }
   }
 
-  // ---- store.  Tile (i, j) is held transposed: lane l has row 32i + l%32 and
-  // columns 32j + 8q + 4(l/32) + e in register 4q + e.  Swapping lanes 32..63
-  // of one register with lanes 0..31 of another gives each lane eight
-  // consecutive columns 32j + 16p + 8(l/32) .. +7 of pair p, which go to the
-  // wave's LDS staging tile; the
-  // tile then leaves as rows of 256 contiguous bytes, four rows per store.
-  // The staging tiles overlap the stages, freed by the barrier above.
+  // ---- store.  Tile (i, j) is held transposed: lane l has row 16i + l%16
+  // and columns 16j + 4(l/16) .. +3 in its four registers; they go to the
+  // wave's LDS staging tile as 8 bytes, and the tile then leaves as rows of
+  // 256 contiguous bytes, four rows per store.  The staging tiles overlap the
+  // stages, freed by the barrier above.
   uint8_t* stg = smem + wave * OUTW;
+  // the last products' results are complete before they are read
+  asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < 8; ++i) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-#pragma unroll
-      for (int pr = 0; pr < 2; ++pr) {
-        const f32x16& c = acc[i][j];
-        const int q0 = 2 * pr, q1 = 2 * pr + 1;
-        const auto s0 = __builtin_amdgcn_permlane32_swap(pack_bf16x2(c[4 * q0], c[4 * q0 + 1]),
-                                                         pack_bf16x2(c[4 * q1], c[4 * q1 + 1]),
-                                                         false, false);
-        const auto s1 = __builtin_amdgcn_permlane32_swap(pack_bf16x2(c[4 * q0 + 2], c[4 * q0 + 3]),
-                                                         pack_bf16x2(c[4 * q1 + 2], c[4 * q1 + 3]),
-                                                         false, false);
-        const int col = 32 * j + 16 * pr + 8 * g;
-        *reinterpret_cast<u32x4*>(stg + (32 * i + l32) * OUTP + 2 * col) =
-            u32x4{s0[0], s1[0], s0[1], s1[1]};
-      }
+    for (int j = 0; j < 8; ++j) {
+      const f32x4& c = acc[i][j];
+      *reinterpret_cast<u32x2*>(stg + (16 * i + l16) * OUTP + 2 * (16 * j + 4 * g4)) =
+          u32x2{pack_bf16x2(c[0], c[1]), pack_bf16x2(c[2], c[3])};
     }
   }
   // (a wave's LDS accesses execute in order, so its reads see its writes)
@@ -320,6 +307,7 @@ hipError_t launch_gemm_nt(const uint16_t* A, int64_t lda, int64_t R, const uint1
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS_BYTES);
   if (attr != hipSuccess) return attr;
   if (M <= 0) return hipSuccess;
+  if (ldb % BK != 0 || R < 8 || R > ldb) return hipErrorInvalidValue;
   const int64_t tm = (M + BM - 1) / BM, tc = (Nc + BN - 1) / BN;
   const int steps = (int)(ldb / BK);
   hipLaunchKernelGGL(k_gemm_nt, dim3((unsigned)(tm * tc)), dim3(T), LDS_BYTES, st, A, lda, R, Bm,

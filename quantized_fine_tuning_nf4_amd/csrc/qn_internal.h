@@ -21,7 +21,7 @@ hipError_t launch_dequant_t(const uint8_t* packed, const uint8_t* qscale, const 
                             int64_t ldt, hipStream_t st);
 
 // C[M, Nc] bf16 = A[M, R] (row stride lda) * Bm[Nc, :R]^T (row stride ldb,
-// ldb % 32 == 0, zero in columns R..ldb) + s * V[M, r] * L[Nc, r]^T.
+// ldb % 64 == 0, zero in columns R..ldb) + s * V[M, r] * L[Nc, r]^T.
 // lda >= R, R % 8 == 0, Nc % 8 == 0; 16-byte aligned pointers.
 hipError_t launch_gemm_nt(const uint16_t* A, int64_t lda, int64_t R, const uint16_t* Bm,
                           int64_t ldb, int64_t M, int64_t Nc, const float* V, const uint16_t* L,
