@@ -127,10 +127,8 @@ struct BwdWs {
   int Sv;
   float* dBpart;  // [Sb, rows, r]
   int Sb;
-  uint16_t* su;   // [2][rp][Mpb] (s u)^T high and remainder parts
   float* dApart;  // [Sa, cols, r]
   int Sa;
-  uint16_t* sv;   // [2][rp][Mpa] (s v)^T
   uint16_t* wt;   // [cols, ldt] bf16 Qhat(W)^T (dense path)
   int64_t ldt;
   uint16_t* At;   // [cols, r] A^T (dense path)
@@ -147,13 +145,10 @@ BwdWs carve_bwd(Carver& c, int64_t M, int64_t rows, int64_t cols, int r, bool ne
   b.Sv = thin_nt_slices(M, rows);
   b.v = c.take<float>((size_t)M * r);
   b.vpart = b.Sv > 1 ? c.take<float>((size_t)b.Sv * M * r) : nullptr;
-  const int64_t rp = 16 * ((r + 15) / 16);
   b.Sb = thin_tn_slices(M, rows, r);
   b.dBpart = c.take<float>((size_t)b.Sb * rows * r);
-  b.su = c.take<uint16_t>((size_t)2 * rp * thin_tn_rows_padded(M, rows, r));
   b.Sa = thin_tn_slices(M, cols, r);
   b.dApart = c.take<float>((size_t)b.Sa * cols * r);
-  b.sv = c.take<uint16_t>((size_t)2 * rp * thin_tn_rows_padded(M, cols, r));
   b.ldt = round_up(rows, 64);
   const bool dense = dense_path(M, cols);
   b.wt = dense ? c.take<uint16_t>((size_t)cols * b.ldt) : nullptr;
@@ -267,10 +262,14 @@ qn_status qlora_linear_fwd(const qn_nf4dq* w, const uint16_t* x, int64_t M, cons
   if (f.dpart)  // decode-sized batch: u and the product in two kernels
     return from_hip(launch_decode_fwd(to_state(w), x, M, A, B, r, scale, y, u, f.dpart,
                                       f.dupart, f.dS, st));
-  hipError_t e = launch_thin_nt(x, A, M, K, r, u, f.upart, f.S, st);
+  // dense path: the slices of u are added by spare workgroups of the
+  // dequantization launch that follows
+  const bool fold = f.wd && f.S > 1;
+  hipError_t e = launch_thin_nt(x, A, M, K, r, u, f.upart, f.S, st, !fold);
   if (f.wd) {
     if (e == hipSuccess)
-      e = launch_dequant(w->packed, w->qscale, w->scale2, w->offset, N * K, true, f.wd, st);
+      e = launch_dequant(w->packed, w->qscale, w->scale2, w->offset, N * K, true, f.wd, st,
+                         fold ? SliceSum{f.upart, M * (int64_t)r, f.S, u} : SliceSum{});
     if (e == hipSuccess) e = launch_gemm_nt(x, K, K, f.wd, K, M, N, u, B, r, scale, y, st);
   } else if (e == hipSuccess) {
     e = launch_qgemm_fwd(to_state(w), x, M, u, B, r, scale, y, st);
@@ -311,25 +310,28 @@ qn_status qlora_linear_bwd(const qn_nf4dq* w, const uint16_t* x, const uint16_t*
     e = launch_thin_nt(x, A, M, K, r, b.fu.u, b.fu.upart, b.fu.S, st);
     u = b.fu.u;
   }
-  // v = G B, through B^T so both operands are contiguous along the reduction
-  if (e == hipSuccess) e = launch_transpose_b(B, N, r, b.Bt, st);
+  // Qhat(W)^T for the dense dX product, with A^T and B^T made by spare
+  // workgroups of the same launch; B^T alone otherwise.  v = G B goes
+  // through B^T so both operands are contiguous along the reduction.
+  const bool dense_dx = dX && b.wt;
+  if (e == hipSuccess) {
+    if (dense_dx)
+      e = launch_dequant_t(w->packed, w->qscale, w->scale2, w->offset, N, K, b.wt, b.ldt,
+                           AdapterTransposes{A, b.At, K, B, b.Bt, N, r}, st);
+    else
+      e = launch_transpose_b(B, N, r, b.Bt, st);
+  }
   if (e == hipSuccess) e = launch_thin_nt(dY, b.Bt, M, N, r, b.v, b.vpart, b.Sv, st);
   if (e == hipSuccess && dX) {
-    if (b.wt) {
-      e = launch_dequant_t(w->packed, w->qscale, w->scale2, w->offset, N, K, b.wt, b.ldt, st);
-      if (e == hipSuccess) e = launch_transpose_b(A, r, (int)K, b.At, st);
-      if (e == hipSuccess)
-        e = launch_gemm_nt(dY, N, N, b.wt, b.ldt, M, K, b.v, b.At, r, scale, dX, st);
-    } else {
+    if (dense_dx)
+      e = launch_gemm_nt(dY, N, N, b.wt, b.ldt, M, K, b.v, b.At, r, scale, dX, st);
+    else
       e = launch_qgemm_dx(to_state(w), dY, M, b.v, A, r, scale, dX, st);
-    }
   }
+  // dB = s G^T u and dA = s v^T X in one launch (and their slice sums in one)
   if (e == hipSuccess)
-    e = launch_prep_svt(u, M, thin_tn_rows_padded(M, N, r), r, scale, b.su, st);
-  if (e == hipSuccess) e = launch_thin_tn(dY, b.su, M, N, r, dB, false, b.dBpart, b.Sb, st);
-  if (e == hipSuccess)
-    e = launch_prep_svt(b.v, M, thin_tn_rows_padded(M, K, r), r, scale, b.sv, st);
-  if (e == hipSuccess) e = launch_thin_tn(x, b.sv, M, K, r, dA, true, b.dApart, b.Sa, st);
+    e = launch_thin_tn2(ThinTn{dY, u, N, dB, false, b.dBpart},
+                        ThinTn{x, b.v, K, dA, true, b.dApart}, M, r, scale, st);
   return from_hip(e);
 }
 

@@ -7,6 +7,8 @@
 //                                     sums are added in slice order.
 // All use v_mfma_f32_16x16x32_bf16; fp32 operands (u, v) enter the MFMA as a
 // bf16 high part plus a bf16 remainder, so they keep ~16 significant bits.
+#include <algorithm>
+
 #include "qn_device.h"
 #include "qn_internal.h"
 
@@ -189,22 +191,11 @@ __global__ __launch_bounds__(kThreads) void k_thin_nt1(const uint16_t* __restric
   }
 }
 
-// out[i] = sum over s of part[s][i], added in slice order (loads issued
-// eight at a time).
+// out[i] = sum over s of part[s][i], added in slice order.
 __global__ void k_sum_slices(const float* __restrict__ part, int64_t count, int S,
                              float* __restrict__ out) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= count) return;
-  float acc = part[i];
-  for (int s0 = 1; s0 < S; s0 += 8) {
-    float v[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) v[k] = s0 + k < S ? part[(int64_t)(s0 + k) * count + i] : 0.f;
-#pragma unroll
-    for (int k = 0; k < 8; ++k)
-      if (s0 + k < S) acc += v[k];
-  }
-  out[i] = acc;
+  if (i < count) out[i] = slice_sum(part, count, S, i);
 }
 
 // Column slices (multiples of 128 columns) so that about 512 workgroups run.
@@ -218,7 +209,7 @@ int thin_nt_slices(int64_t M, int64_t P) {
 }
 
 hipError_t launch_thin_nt(const uint16_t* Z, const uint16_t* T, int64_t M, int64_t P, int r,
-                          float* out, float* part, int S, hipStream_t st) {
+                          float* out, float* part, int S, hipStream_t st, bool sum) {
   int64_t slice = (P + S - 1) / S;
   slice = (slice + 127) / 128 * 128;
   const dim3 grid((unsigned)((M + 63) / 64), (unsigned)S);
@@ -239,7 +230,7 @@ hipError_t launch_thin_nt(const uint16_t* Z, const uint16_t* T, int64_t M, int64
     default: hipLaunchKernelGGL(k_thin_nt<4>, grid, dim3(kThreads), 0, st, Z, T, M, P, r, slice, dst); break;
   }
   }
-  if (S > 1) {
+  if (S > 1 && sum) {
     const int64_t count = M * r;
     hipLaunchKernelGGL(k_sum_slices, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, st,
                        part, count, S, out);
@@ -274,21 +265,6 @@ hipError_t launch_transpose_b(const uint16_t* B, int64_t N, int r, uint16_t* Bt,
   return hipGetLastError();
 }
 
-// (s V)^T split into bf16 high and remainder parts: vt[0][j][m] (high) and
-// vt[1][j][m] (remainder) for j < rp = 16 ceil(r/16) and m < Mp; zero for
-// j >= r or m >= M.
-__global__ void k_prep_svt(const float* __restrict__ V, int64_t M, int64_t Mp, int r, int rp,
-                           float scale, uint16_t* __restrict__ vt) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t count = (int64_t)rp * Mp;
-  if (i >= count) return;
-  const int64_t j = i / Mp, m = i % Mp;
-  const float x = (j < r && m < M) ? scale * V[m * r + j] : 0.f;
-  const uint32_t h = pack_bf16x2(x, 0.f) & 0xffffu;
-  vt[i] = (uint16_t)h;
-  vt[count + i] = (uint16_t)(pack_bf16x2(x - bf16_lo(h), 0.f) & 0xffffu);
-}
-
 namespace {
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -313,22 +289,42 @@ constexpr int TN_NST = 4;
 
 }  // namespace
 
-// part[z][p][j] = sum over the rows m of slice z of Z[m, p] * (sV)[m, j]
-// (a transposed product: the reduction runs down the columns of Z).
-// Workgroup (pt, z): columns 128 pt .. +127, wave w: 32w .. 32w+31 (two
-// 16-column MFMA tiles).  32 rows of Z per step go global -> LDS by buffer
-// loads four steps deep (row y's 16-byte chunk c at unit c ^ 2(y & 3)); the A
-// operand (16 columns x 32 rows) is read transposed with ds_read_b64_tr_b16,
-// lane t of a 16-lane group addressing row 4h + t/4, columns 4(t%4)..+3, so
-// that lane t receives column t, four consecutive rows.  The B operand is
-// (sV)^T high and remainder parts, staged in LDS for the whole slice.
-__global__ __launch_bounds__(kThreads) void k_thin_tn(
-    const uint16_t* __restrict__ Z, int64_t M, int64_t P, const uint16_t* __restrict__ vt,
-    int64_t Mp, int r, int64_t slice, float* __restrict__ part) {
+// part[z][p][j] = sum over the rows m of slice z of Z[m, p] * (s V)[m, j]
+// (a transposed product: the reduction runs down the columns of Z).  Two
+// independent products (dB and dA of one backward) share the launch: grid x
+// runs over the column tiles of job 0, then those of job 1.  Workgroup
+// (pt, z): columns 128 pt .. +127, wave w: 32w .. 32w+31 (two 16-column MFMA
+// tiles).  32 rows of Z per step go global -> LDS by buffer loads four steps
+// deep (row y's 16-byte chunk c at unit c ^ 2(y & 3)); the A operand (16
+// columns x 32 rows) is read transposed with ds_read_b64_tr_b16, lane t of a
+// 16-lane group addressing row 4h + t/4, columns 4(t%4)..+3, so that lane t
+// receives column t, four consecutive rows.  The B operand is (s V)^T for the
+// slice, built in LDS from the fp32 V as a bf16 high part and a bf16
+// remainder (zero for j >= r and m >= M).
+struct TnJob {
+  const uint16_t* Z;  // [M, P] bf16
+  const float* V;     // [M, r] fp32
+  int64_t P;
+  int64_t slice;      // rows per slice, a multiple of 32
+  int S;              // slices
+  int tiles;          // column tiles of 128
+  float* part;        // [S, P, r]
+};
+
+__global__ __launch_bounds__(kThreads) void k_thin_tn(TnJob j0, TnJob j1, int64_t M, int r,
+                                                      float s) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const bool second = (int)blockIdx.x >= j0.tiles;
+  const uint16_t* Z = second ? j1.Z : j0.Z;
+  const float* V = second ? j1.V : j0.V;
+  const int64_t P = second ? j1.P : j0.P;
+  const int64_t slice = second ? j1.slice : j0.slice;
+  const int S = second ? j1.S : j0.S;
+  float* part = second ? j1.part : j0.part;
+  if ((int)blockIdx.y >= S) return;
   const int nj = (r + 15) / 16;
-  const int64_t p0 = (int64_t)blockIdx.x * TN_COLS;
+  const int64_t p0 = (int64_t)((int)blockIdx.x - (second ? j0.tiles : 0)) * TN_COLS;
   const int64_t mb = (int64_t)blockIdx.y * slice;
   const int64_t me = min(mb + slice, M);
   const int steps = (int)((me - mb + 31) / 32);
@@ -336,14 +332,22 @@ __global__ __launch_bounds__(kThreads) void k_thin_tn(
   uint8_t* vst = smem + TN_NST * TN_STAGE;      // [2][16 nj][slice] bf16
   const int64_t vrow = slice * 2;               // bytes per staged (sV)^T row
 
-  // ---- (sV)^T for the slice: 2 * 16nj rows of `slice` bf16, 16-B chunks
+  // ---- (sV)^T: thread -> a pair of rows m, m+1 and 16 ranks; the fp32 reads
+  // go out before the Z loads, the LDS writes (one word per rank: rows m and
+  // m+1) after them.  At most 256 units: slice <= 512 / nj.
+  const int npairs = (int)(slice / 2), units = npairs * nj;
+  const int pm = tid % npairs, jg = tid / npairs;
+  const int64_t m = mb + 2 * pm;
+  // (unconditional, clamped reads: no load waits at a branch join)
+  float va[16], vb[16];
   {
-    const int chunks = (int)(slice / 8);
-    const rsrc_t rv = make_rs(vt, (uint32_t)(2 * 16 * nj * Mp * 2));
-    const int total = 2 * 16 * nj * chunks;     // multiple of 64 (slice % 32 == 0)
-    for (int c0 = 64 * wave; c0 < total; c0 += 256) {
-      const int c = c0 + lane, row = c / chunks, q = c % chunks;  // row: part * 16nj + j
-      dma16(rv, (uint32_t)((row * Mp + mb + 8 * q) * 2), 0, vst + (int64_t)(c0 / 64) * 1024);
+    const float* r0 = V + min(m, M - 1) * r;
+    const float* r1 = V + min(m + 1, M - 1) * r;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int jj = min(16 * jg + q, r - 1);
+      va[q] = r0[jj];
+      vb[q] = r1[jj];
     }
   }
   // ---- Z loads: instruction i (0..7) of a step covers rows 4i..4i+3; wave w
@@ -358,17 +362,28 @@ __global__ __launch_bounds__(kThreads) void k_thin_tn(
     const int chunk = (lane & 15) ^ (2 * (row & 3));
     const int64_t col = min(p0 + 8 * chunk, P - 8);
     zoff[h] = (uint32_t)(col * 2);
-    (void)row;
   }
   auto load_z = [&](int st, int stage) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int i = 2 * wave + h, row = 4 * i + (lane >> 4);
-      const int64_t m = min(mb + 32 * (int64_t)st + row, M - 1);
-      dma16(rz, zoff[h] + (uint32_t)(m * P * 2), 0, zst + stage * TN_STAGE + 1024 * i);
+      const int64_t mm = min(mb + 32 * (int64_t)st + row, M - 1);
+      dma16(rz, zoff[h] + (uint32_t)(mm * P * 2), 0, zst + stage * TN_STAGE + 1024 * i);
     }
   };
   for (int k = 0; k < TN_NST - 1; ++k) load_z(min(k, steps - 1), k);
+  if (tid < units) {
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int j = 16 * jg + q;
+      const float x0 = (j < r && m < M) ? s * va[q] : 0.f;
+      const float x1 = (j < r && m + 1 < M) ? s * vb[q] : 0.f;
+      const uint32_t h = pack_bf16x2(x0, x1);
+      const uint32_t lo = pack_bf16x2(x0 - bf16_lo(h), x1 - bf16_hi(h));
+      *reinterpret_cast<uint32_t*>(vst + j * vrow + 4 * pm) = h;
+      *reinterpret_cast<uint32_t*>(vst + (16 * nj + j) * vrow + 4 * pm) = lo;
+    }
+  }
   asm volatile("s_waitcnt vmcnt(4)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
   // transposed-read addresses: lane l, group g = l/16, t = l%16; p-tile pt,
@@ -434,24 +449,27 @@ __global__ __launch_bounds__(kThreads) void k_thin_tn(
 }
 
 // out = sum over slices of part, added in slice order (loads issued eight
-// at a time); transposed: out[j][p], thread index running along p.
-__global__ void k_sum_slices_tn(const float* __restrict__ part, int64_t P, int r, int S,
-                                bool transposed, float* __restrict__ out) {
-  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t count = P * r;
+// at a time), for the two products of one launch: threads 0 .. P0 r - 1
+// produce job 0's output, the rest job 1's.  transposed: out[j][p], thread
+// index running along p.
+struct TnSum {
+  const float* part;
+  int64_t P;
+  int S;
+  bool transposed;
+  float* out;
+};
+__global__ void k_sum_slices_tn(TnSum a, TnSum b, int r) {
+  int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t count_a = a.P * r;
+  const bool second = t >= count_a;
+  const TnSum& J = second ? b : a;
+  if (second) t -= count_a;
+  const int64_t count = J.P * r;
   if (t >= count) return;
   // element index into part[s] ([P][r]) and into out
-  const int64_t i = transposed ? (t % P) * r + t / P : t;
-  float acc = part[i];
-  for (int s0 = 1; s0 < S; s0 += 8) {
-    float v[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) v[k] = s0 + k < S ? part[(int64_t)(s0 + k) * count + i] : 0.f;
-#pragma unroll
-    for (int k = 0; k < 8; ++k)
-      if (s0 + k < S) acc += v[k];
-  }
-  out[t] = acc;
+  const int64_t i = J.transposed ? (t % J.P) * r + t / J.P : t;
+  J.out[t] = slice_sum(J.part, count, J.S, i);
 }
 
 // Slices of the M rows for the transposed products: enough workgroups to
@@ -474,35 +492,46 @@ int thin_tn_slices(int64_t M, int64_t P, int r) {
   return (int)((M + slice - 1) / slice);
 }
 
-// Row length of the staged (sV)^T: every slice's rows exist (zero past M).
-int64_t thin_tn_rows_padded(int64_t M, int64_t P, int r) {
-  return (int64_t)thin_tn_slices(M, P, r) * thin_tn_slice_rows(M, P, r);
-}
-
-hipError_t launch_prep_svt(const float* V, int64_t M, int64_t Mp, int r, float s, uint16_t* vt,
+hipError_t launch_thin_tn2(const ThinTn& a, const ThinTn& b, int64_t M, int r, float s,
                            hipStream_t st) {
-  const int rp = 16 * ((r + 15) / 16);
-  const int64_t count = (int64_t)rp * Mp;
-  hipLaunchKernelGGL(k_prep_svt, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, st, V, M,
-                     Mp, r, rp, s, vt);
-  return hipGetLastError();
-}
-
-hipError_t launch_thin_tn(const uint16_t* Z, const uint16_t* vt, int64_t M, int64_t P, int r,
-                          float* out, bool transposed, float* part, int S, hipStream_t st) {
-  const int64_t slice = thin_tn_slice_rows(M, P, r);
-  const int nj = (r + 15) / 16;
-  const size_t lds = (size_t)TN_NST * TN_STAGE + (size_t)2 * 16 * nj * slice * 2;
   static hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(k_thin_tn), hipFuncAttributeMaxDynamicSharedMemorySize,
       (int)(TN_NST * TN_STAGE + 32768));
   if (attr != hipSuccess) return attr;
-  const dim3 grid((unsigned)((P + TN_COLS - 1) / TN_COLS), (unsigned)S);
-  hipLaunchKernelGGL(k_thin_tn, grid, dim3(kThreads), lds, st, Z, M, P, vt,
-                     thin_tn_rows_padded(M, P, r), r, slice, part);
-  const int64_t count = P * r;
+  const int nj = (r + 15) / 16;
+  TnJob job[2];
+  const ThinTn* in[2] = {&a, &b};
+  int64_t slice_max = 32;
+  int s_max = 1;
+  for (int k = 0; k < 2; ++k) {
+    const ThinTn& x = *in[k];
+    TnJob& j = job[k];
+    j.Z = x.Z;
+    j.V = x.V;
+    j.P = x.P;
+    j.slice = thin_tn_slice_rows(M, x.P, r);
+    j.S = thin_tn_slices(M, x.P, r);
+    j.tiles = x.Z ? (int)((x.P + TN_COLS - 1) / TN_COLS) : 0;
+    j.part = x.part;
+    if (j.tiles > 0) {
+      slice_max = std::max(slice_max, j.slice);
+      s_max = std::max(s_max, j.S);
+    }
+  }
+  const int tiles = job[0].tiles + job[1].tiles;
+  if (tiles == 0) return hipSuccess;
+  const size_t lds = (size_t)TN_NST * TN_STAGE + (size_t)2 * 16 * nj * slice_max * 2;
+  hipLaunchKernelGGL(k_thin_tn, dim3((unsigned)tiles, (unsigned)s_max), dim3(kThreads), lds, st,
+                     job[0], job[1], M, r, s);
+  TnSum sum[2];
+  int64_t count = 0;
+  for (int k = 0; k < 2; ++k) {
+    const ThinTn& x = *in[k];
+    sum[k] = TnSum{x.part, x.Z ? x.P : 0, job[k].S, x.transposed, x.out};
+    count += sum[k].P * r;
+  }
   hipLaunchKernelGGL(k_sum_slices_tn, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, st,
-                     part, P, r, S, transposed, out);
+                     sum[0], sum[1], r);
   return hipGetLastError();
 }
 

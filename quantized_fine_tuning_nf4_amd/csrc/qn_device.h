@@ -40,6 +40,22 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 __device__ __forceinline__ float bf16_lo(uint32_t p) { return as_f32(p << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t p) { return as_f32(p & 0xffff0000u); }
 
+// sum over s < S of part[s * count + i], added in slice order (loads issued
+// eight at a time)
+__device__ __forceinline__ float slice_sum(const float* __restrict__ part, int64_t count, int S,
+                                           int64_t i) {
+  float acc = part[i];
+  for (int s0 = 1; s0 < S; s0 += 8) {
+    float v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = s0 + k < S ? part[(int64_t)(s0 + k) * count + i] : 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (s0 + k < S) acc += v[k];
+  }
+  return acc;
+}
+
 // OCP FP8 E4M3FN byte -> fp32 (exact).  Exponent bias 7, three mantissa
 // bits, subnormals m * 2^-9; the NaN pattern is never produced here.
 __device__ __forceinline__ float e4m3_to_f32(uint32_t q) {

@@ -11,14 +11,39 @@ hipError_t launch_quantize(const float* W, int64_t n, uint8_t* packed, uint8_t* 
                            float* scale2, float* offset, float* ws_absmax, double* ws_part,
                            int64_t part_len, int* ws_bad, int* flag, hipStream_t st);
 
+// out = sum over S slices of part[S][count] (slice order); count == 0: none.
+struct SliceSum {
+  const float* part;
+  int64_t count;
+  int S;
+  float* out;
+};
+
+// n weights -> bf16 or fp32 out; the slice sum ss (independent of the
+// weight) runs in spare workgroups of the same launch.
 hipError_t launch_dequant(const uint8_t* packed, const uint8_t* qscale, const float* scale2,
-                          const float* offset, int64_t n, bool bf16, void* out, hipStream_t st);
+                          const float* offset, int64_t n, bool bf16, void* out, hipStream_t st,
+                          const SliceSum& ss = SliceSum{nullptr, 0, 0, nullptr});
+
+// Adapter transposes done by spare workgroups of another launch:
+// At [K, r] = A[r, K]^T and Bt [r, N] = B[N, r]^T (bf16); a null A or B
+// skips that one.
+struct AdapterTransposes {
+  const uint16_t* A;
+  uint16_t* At;
+  int64_t K;
+  const uint16_t* B;
+  uint16_t* Bt;
+  int64_t N;
+  int r;
+};
 
 // out[k][n] = Qhat(W)[n][k] as bf16 with row length ldt (ldt % 8 == 0,
-// ldt >= rows); zero for rows <= n < ldt.  cols % 64 == 0.
+// ldt >= rows); zero for rows <= n < ldt.  cols % 64 == 0.  The transposes
+// in tj run in the same launch.
 hipError_t launch_dequant_t(const uint8_t* packed, const uint8_t* qscale, const float* scale2,
                             const float* offset, int64_t rows, int64_t cols, uint16_t* out,
-                            int64_t ldt, hipStream_t st);
+                            int64_t ldt, const AdapterTransposes& tj, hipStream_t st);
 
 // C[M, Nc] bf16 = A[M, R] (row stride lda) * Bm[Nc, :R]^T (row stride ldb,
 // ldb % 64 == 0, zero in columns R..ldb) + s * V[M, r] * L[Nc, r]^T.
@@ -44,8 +69,9 @@ struct WState {
 // out[M, r] (fp32) = sum over S slices of Z[M, P] * T[r, P]^T.  When S > 1
 // the slices are written to part[S][M][r] and summed in slice order into
 // out; S == 1 writes out directly.
+// sum == false leaves the slices in part for the caller to add.
 hipError_t launch_thin_nt(const uint16_t* Z, const uint16_t* T, int64_t M, int64_t P, int r,
-                          float* out, float* part, int S, hipStream_t st);
+                          float* out, float* part, int S, hipStream_t st, bool sum = true);
 int thin_nt_slices(int64_t M, int64_t P);
 
 // p[0..n) = 0 (a kernel, so it may sit in a captured graph).
@@ -54,20 +80,24 @@ hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st);
 // Bt[r, N] = B[N, r]^T (bf16).
 hipError_t launch_transpose_b(const uint16_t* B, int64_t N, int r, uint16_t* Bt, hipStream_t st);
 
-// vt [2][rp][Mp] bf16 = high and remainder parts of (s V)^T, V fp32 [M, r],
-// rp = 16 ceil(r/16), zero for j >= r or m >= M.
-hipError_t launch_prep_svt(const float* V, int64_t M, int64_t Mp, int r, float s, uint16_t* vt,
-                           hipStream_t st);
-
-// out = Z^T (sV) reduced over the M rows: Z bf16 [M, P], vt from
-// launch_prep_svt with Mp = thin_tn_rows_padded(M, P, r);
-// transposed == false: out fp32 [P, r]; true: out fp32 [r, P].  Split over
-// S = thin_tn_slices(M, P, r) row slices, partials part[S][P][r], summed in
+// One transposed adapter product out = Z^T (s V), reduced over the M rows:
+// Z bf16 [M, P] (null: no product), V fp32 [M, r]; transposed == false:
+// out fp32 [P, r]; true: out fp32 [r, P].  Split over
+// thin_tn_slices(M, P, r) row slices with partials part[S][P][r], summed in
 // slice order.  P % 8 == 0.
-hipError_t launch_thin_tn(const uint16_t* Z, const uint16_t* vt, int64_t M, int64_t P, int r,
-                          float* out, bool transposed, float* part, int S, hipStream_t st);
+struct ThinTn {
+  const uint16_t* Z;
+  const float* V;
+  int64_t P;
+  float* out;
+  bool transposed;
+  float* part;
+};
+// Two such products (same M, r and s) in one launch, their slice sums in a
+// second.
+hipError_t launch_thin_tn2(const ThinTn& a, const ThinTn& b, int64_t M, int r, float s,
+                           hipStream_t st);
 int thin_tn_slices(int64_t M, int64_t P, int r);
-int64_t thin_tn_rows_padded(int64_t M, int64_t P, int r);
 
 // Decode forward, u = X A^T included (written to u_out [M, r]); workspace
 // part [S, M, rows] and upart [S, M, r] fp32, S = decode_slices(...).

@@ -321,9 +321,16 @@ __global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ pac
                                                  const uint8_t* __restrict__ qscale,
                                                  const float* __restrict__ scale2,
                                                  const float* __restrict__ offset, int64_t n,
-                                                 void* __restrict__ out) {
+                                                 void* __restrict__ out, SliceSum ss,
+                                                 unsigned dq_blocks) {
   constexpr int CH = BF16 ? 8 : 4;
   constexpr int UNROLL = 4;
+  if (blockIdx.x >= dq_blocks) {
+    // workgroups past the weight: a slice sum from the preceding launch
+    const int64_t i = (int64_t)(blockIdx.x - dq_blocks) * blockDim.x + threadIdx.x;
+    if (i < ss.count) ss.out[i] = slice_sum(ss.part, ss.count, ss.S, i);
+    return;
+  }
   __shared__ float lut[16];
   if (threadIdx.x < 16) {  // from immediates: no load that the first weight loads would queue behind
     uint32_t v = kNF4Bits[0];
@@ -339,23 +346,27 @@ __global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ pac
 }
 
 hipError_t launch_dequant(const uint8_t* packed, const uint8_t* qscale, const float* scale2,
-                          const float* offset, int64_t n, bool bf16, void* out, hipStream_t st) {
+                          const float* offset, int64_t n, bool bf16, void* out, hipStream_t st,
+                          const SliceSum& ss) {
   const int CH = bf16 ? 8 : 4;
   const int64_t nchunk = (n + CH - 1) / CH;
   const int64_t per_wg = 256 * 4;
   const unsigned grid = (unsigned)((nchunk + per_wg - 1) / per_wg);
+  const unsigned extra = ss.count > 0 ? (unsigned)((ss.count + 255) / 256) : 0u;
   if (bf16)
-    hipLaunchKernelGGL(k_dequant<true>, dim3(grid), dim3(256), 0, st, packed, qscale, scale2,
-                       offset, n, out);
+    hipLaunchKernelGGL(k_dequant<true>, dim3(grid + extra), dim3(256), 0, st, packed, qscale,
+                       scale2, offset, n, out, ss, grid);
   else
-    hipLaunchKernelGGL(k_dequant<false>, dim3(grid), dim3(256), 0, st, packed, qscale, scale2,
-                       offset, n, out);
+    hipLaunchKernelGGL(k_dequant<false>, dim3(grid + extra), dim3(256), 0, st, packed, qscale,
+                       scale2, offset, n, out, ss, grid);
   return hipGetLastError();
 }
 
 
 // Transposed dequantization for the dX product: out[k][n] (bf16, row length
-// ldt >= rows, ldt % 8 == 0) = Qhat(W)[n][k], zero for rows <= n < ldt.
+// ldt >= rows, ldt % 8 == 0) = Qhat(W)[n][k], zero for rows <= n < ldt.  An
+// extra row of workgroups (when asked) transposes the adapters for the same
+// backward, which saves their launches.
 // Workgroup (bx, kb): rows n0 = 64 bx .. +63 of block column kb; thread t
 // dequantizes 16 codes (row n0 + t/4, elements 16 (t%4) ..) into an LDS tile
 // [k][n], which is written out as 16-byte row pieces.
@@ -364,11 +375,27 @@ __global__ __launch_bounds__(256) void k_dequant_t(const uint8_t* __restrict__ p
                                                    const float* __restrict__ scale2,
                                                    const float* __restrict__ offset, int64_t rows,
                                                    int64_t cols, uint16_t* __restrict__ out,
-                                                   int64_t ldt) {
+                                                   int64_t ldt, AdapterTransposes tj) {
   constexpr int LDT = 72;  // 64 + 8 pad
   __shared__ float lut[16];
   __shared__ __attribute__((aligned(16))) uint16_t tile[64][LDT];
   const int t = threadIdx.x;
+  if ((int64_t)blockIdx.y == cols / kBlock) {
+    // the extra row of workgroups: adapter transposes At [K, r] = A^T and
+    // Bt [r, N] = B^T, grid-strided
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    const int64_t na = tj.A ? (int64_t)tj.r * tj.K : 0, nb = tj.B ? tj.N * tj.r : 0;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + t; i < na + nb; i += stride) {
+      if (i < na) {
+        const int64_t k = i / tj.r, j = i % tj.r;
+        tj.At[i] = tj.A[j * tj.K + k];
+      } else {
+        const int64_t e = i - na, j = e / tj.N, n = e % tj.N;
+        tj.Bt[e] = tj.B[n * tj.r + j];
+      }
+    }
+    return;
+  }
   if (t < 16) lut[t] = as_f32(kNF4Bits[t]);
   const int64_t n0 = (int64_t)blockIdx.x * 64, kb = blockIdx.y;
   const int64_t kblocks = cols / kBlock;
@@ -401,10 +428,11 @@ __global__ __launch_bounds__(256) void k_dequant_t(const uint8_t* __restrict__ p
 
 hipError_t launch_dequant_t(const uint8_t* packed, const uint8_t* qscale, const float* scale2,
                             const float* offset, int64_t rows, int64_t cols, uint16_t* out,
-                            int64_t ldt, hipStream_t st) {
-  const dim3 grid((unsigned)((ldt + 63) / 64), (unsigned)(cols / kBlock));
+                            int64_t ldt, const AdapterTransposes& tj, hipStream_t st) {
+  const bool extra = tj.A || tj.B;
+  const dim3 grid((unsigned)((ldt + 63) / 64), (unsigned)(cols / kBlock + (extra ? 1 : 0)));
   hipLaunchKernelGGL(k_dequant_t, grid, dim3(256), 0, st, packed, qscale, scale2, offset, rows,
-                     cols, out, ldt);
+                     cols, out, ldt, tj);
   return hipGetLastError();
 }
 
