@@ -127,8 +127,10 @@ struct BwdWs {
   int Sv;
   float* dBpart;  // [Sb, rows, r]
   int Sb;
+  uint16_t* su;   // [2][rp][Mpb] (s u)^T high and remainder parts
   float* dApart;  // [Sa, cols, r]
   int Sa;
+  uint16_t* sv;   // [2][rp][Mpa] (s v)^T
   uint16_t* wt;   // [cols, ldt] bf16 Qhat(W)^T (dense path)
   int64_t ldt;
   uint16_t* At;   // [cols, r] A^T (dense path)
@@ -145,10 +147,13 @@ BwdWs carve_bwd(Carver& c, int64_t M, int64_t rows, int64_t cols, int r, bool ne
   b.Sv = thin_nt_slices(M, rows);
   b.v = c.take<float>((size_t)M * r);
   b.vpart = b.Sv > 1 ? c.take<float>((size_t)b.Sv * M * r) : nullptr;
+  const int64_t rp = 16 * ((r + 15) / 16);
   b.Sb = thin_tn_slices(M, rows, r);
   b.dBpart = c.take<float>((size_t)b.Sb * rows * r);
+  b.su = c.take<uint16_t>((size_t)2 * rp * thin_tn_rows_padded(M, rows, r));
   b.Sa = thin_tn_slices(M, cols, r);
   b.dApart = c.take<float>((size_t)b.Sa * cols * r);
+  b.sv = c.take<uint16_t>((size_t)2 * rp * thin_tn_rows_padded(M, cols, r));
   b.ldt = round_up(rows, 64);
   const bool dense = dense_path(M, cols);
   b.wt = dense ? c.take<uint16_t>((size_t)cols * b.ldt) : nullptr;
@@ -310,18 +315,45 @@ qn_status qlora_linear_bwd(const qn_nf4dq* w, const uint16_t* x, const uint16_t*
     e = launch_thin_nt(x, A, M, K, r, b.fu.u, b.fu.upart, b.fu.S, st);
     u = b.fu.u;
   }
-  // Qhat(W)^T for the dense dX product, with A^T and B^T made by spare
-  // workgroups of the same launch; B^T alone otherwise.  v = G B goes
-  // through B^T so both operands are contiguous along the reduction.
+  // v = G B as slices (added below); the product takes B as stored when it
+  // can, else B^T made first
+  const bool b_rows = thin_nt_rows_ok(M, N, r);
+  if (e == hipSuccess && !b_rows) {
+    BwdAux t{};
+    t.B = B;
+    t.Bt = b.Bt;
+    t.N = N;
+    t.r = r;
+    e = launch_bwd_aux(t, st);
+  }
+  if (e == hipSuccess)
+    e = launch_thin_nt(dY, b_rows ? B : b.Bt, M, N, r, b.v, b.vpart, b.Sv, st, false, b_rows);
+  // the small jobs: v's slice sum, (s u)^T and (s v)^T split for the
+  // transposed products, A^T for the dense dX product; in spare workgroups of
+  // the transposed dequantization when there is one
   const bool dense_dx = dX && b.wt;
+  BwdAux aux{};
+  aux.A = A;
+  aux.At = dense_dx ? b.At : nullptr;
+  aux.K = K;
+  aux.u = u;
+  aux.su = b.su;
+  aux.Mpu = thin_tn_rows_padded(M, N, r);
+  aux.vpart = b.vpart;
+  aux.Sv = b.Sv;
+  aux.v = b.v;
+  aux.sv = b.sv;
+  aux.Mpv = thin_tn_rows_padded(M, K, r);
+  aux.M = M;
+  aux.r = r;
+  aux.s = scale;
   if (e == hipSuccess) {
     if (dense_dx)
-      e = launch_dequant_t(w->packed, w->qscale, w->scale2, w->offset, N, K, b.wt, b.ldt,
-                           AdapterTransposes{A, b.At, K, B, b.Bt, N, r}, st);
+      e = launch_dequant_t(w->packed, w->qscale, w->scale2, w->offset, N, K, b.wt, b.ldt, aux,
+                           st);
     else
-      e = launch_transpose_b(B, N, r, b.Bt, st);
+      e = launch_bwd_aux(aux, st);
   }
-  if (e == hipSuccess) e = launch_thin_nt(dY, b.Bt, M, N, r, b.v, b.vpart, b.Sv, st);
   if (e == hipSuccess && dX) {
     if (dense_dx)
       e = launch_gemm_nt(dY, N, N, b.wt, b.ldt, M, K, b.v, b.At, r, scale, dX, st);
@@ -330,8 +362,8 @@ qn_status qlora_linear_bwd(const qn_nf4dq* w, const uint16_t* x, const uint16_t*
   }
   // dB = s G^T u and dA = s v^T X in one launch (and their slice sums in one)
   if (e == hipSuccess)
-    e = launch_thin_tn2(ThinTn{dY, u, N, dB, false, b.dBpart},
-                        ThinTn{x, b.v, K, dA, true, b.dApart}, M, r, scale, st);
+    e = launch_thin_tn2(ThinTn{dY, b.su, N, dB, false, b.dBpart},
+                        ThinTn{x, b.sv, K, dA, true, b.dApart}, M, r, st);
   return from_hip(e);
 }
 

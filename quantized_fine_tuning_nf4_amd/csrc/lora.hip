@@ -105,6 +105,7 @@ __global__ __launch_bounds__(kThreads) void k_thin_nt(const uint16_t* __restrict
 // slice read as zero (selected at use, so no load waits at a branch).
 constexpr int TN1_U = 4;
 constexpr int64_t kThinNt1MaxSlice = 2048;
+template <int TMODE>
 __global__ __launch_bounds__(kThreads) void k_thin_nt1(const uint16_t* __restrict__ Z,
                                                        const uint16_t* __restrict__ T, int64_t M,
                                                        int64_t P, int r, int64_t slice,
@@ -129,7 +130,7 @@ __global__ __launch_bounds__(kThreads) void k_thin_nt1(const uint16_t* __restric
       za[buf][u] = *reinterpret_cast<const u32x4*>(zp + (off < lim ? off : 0));
     }
   };
-  {
+  if constexpr (TMODE == 0) {
     // stage T: eight 16-byte chunks per thread per pass, every load issued
     // before the first is used (clamped addresses; zero selected at the LDS
     // write for rows past r and columns past the slice); the first Z batch
@@ -153,6 +154,51 @@ __global__ __launch_bounds__(kThreads) void k_thin_nt1(const uint16_t* __restric
           const int j = e / cpr, c = e - j * cpr;
           const bool ok = j < r && 8 * (int64_t)c < width;
           *reinterpret_cast<u32x4*>(smem + j * pitch + 16 * c) = ok ? tv[q] : u32x4{0u, 0u, 0u, 0u};
+        }
+      }
+    }
+  } else {
+    // stage T given as its transpose Tr [P, r] (the adapter B as stored): a
+    // thread takes a pair of columns (two rows of Tr, r <= 16 values each),
+    // loads them (unconditional, clamped), sends the first Z batch, then
+    // writes one word per rank (the pair's two values) to LDS; zero for
+    // ranks >= r and columns past the slice
+    const int pairs = steps * 16;
+    for (int p0 = 0; p0 < pairs; p0 += 4 * kThreads) {
+      uint32_t v[4][16];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int pp = min(p0 + k * kThreads + tid, pairs - 1);
+        const int64_t c0 = min(pb + 2 * (int64_t)pp, P - 1), c1 = min(c0 + 1, P - 1);
+        if constexpr (TMODE == 1) {
+          const u32x4* s0 = reinterpret_cast<const u32x4*>(T + c0 * 16);
+          const u32x4* s1 = reinterpret_cast<const u32x4*>(T + c1 * 16);
+          const u32x4 a0 = s0[0], a1 = s0[1], b0 = s1[0], b1 = s1[1];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            v[k][2 * q] = (a0[q] & 0xffffu) | (b0[q] << 16);
+            v[k][2 * q + 1] = (a0[q] >> 16) | (b0[q] & 0xffff0000u);
+            v[k][8 + 2 * q] = (a1[q] & 0xffffu) | (b1[q] << 16);
+            v[k][8 + 2 * q + 1] = (a1[q] >> 16) | (b1[q] & 0xffff0000u);
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const int jj = min(j, r - 1);
+            v[k][j] = (uint32_t)T[c0 * r + jj] | ((uint32_t)T[c1 * r + jj] << 16);
+          }
+        }
+      }
+      if (p0 == 0) load_batch(0, 0);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int pp = p0 + k * kThreads + tid;
+        if (pp < pairs) {
+          const int64_t col = 2 * (int64_t)pp;
+          const uint32_t keep = (col < width ? 0xffffu : 0u) | (col + 1 < width ? 0xffff0000u : 0u);
+#pragma unroll
+          for (int j = 0; j < 16; ++j)
+            *reinterpret_cast<uint32_t*>(smem + j * pitch + 4 * pp) = j < r ? (v[k][j] & keep) : 0u;
         }
       }
     }
@@ -198,6 +244,17 @@ __global__ void k_sum_slices(const float* __restrict__ part, int64_t count, int 
   if (i < count) out[i] = slice_sum(part, count, S, i);
 }
 
+// Column slice of launch_thin_nt (a multiple of 128).
+int64_t thin_nt_slice(int64_t P, int S) {
+  const int64_t slice = (P + S - 1) / S;
+  return (slice + 127) / 128 * 128;
+}
+
+// Whether launch_thin_nt takes T as its transpose [P, r] for this shape.
+bool thin_nt_rows_ok(int64_t M, int64_t P, int r) {
+  return r <= 16 && thin_nt_slice(P, thin_nt_slices(M, P)) <= kThinNt1MaxSlice;
+}
+
 // Column slices (multiples of 128 columns) so that about 512 workgroups run.
 int thin_nt_slices(int64_t M, int64_t P) {
   const int64_t mt = M > 0 ? (M + 63) / 64 : 1;
@@ -209,20 +266,33 @@ int thin_nt_slices(int64_t M, int64_t P) {
 }
 
 hipError_t launch_thin_nt(const uint16_t* Z, const uint16_t* T, int64_t M, int64_t P, int r,
-                          float* out, float* part, int S, hipStream_t st, bool sum) {
-  int64_t slice = (P + S - 1) / S;
-  slice = (slice + 127) / 128 * 128;
+                          float* out, float* part, int S, hipStream_t st, bool sum, bool t_rows) {
+  const int64_t slice = thin_nt_slice(P, S);
   const dim3 grid((unsigned)((M + 63) / 64), (unsigned)S);
   float* dst = S > 1 ? part : out;
   if (r <= 16 && slice <= kThinNt1MaxSlice) {
-    static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(k_thin_nt1), hipFuncAttributeMaxDynamicSharedMemorySize,
-        (int)(16 * (kThinNt1MaxSlice * 2 + 16)));
-    if (attr != hipSuccess) return attr;
+    const int mode = !t_rows ? 0 : r == 16 ? 1 : 2;
+    static const hipError_t attr[3] = {
+        hipFuncSetAttribute(reinterpret_cast<const void*>(k_thin_nt1<0>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)(16 * (kThinNt1MaxSlice * 2 + 16))),
+        hipFuncSetAttribute(reinterpret_cast<const void*>(k_thin_nt1<1>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)(16 * (kThinNt1MaxSlice * 2 + 16))),
+        hipFuncSetAttribute(reinterpret_cast<const void*>(k_thin_nt1<2>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)(16 * (kThinNt1MaxSlice * 2 + 16)))};
+    if (attr[mode] != hipSuccess) return attr[mode];
     const int steps = (int)((slice + 31) / 32);
     const size_t lds = (size_t)16 * (steps * 64 + 16);
-    hipLaunchKernelGGL(k_thin_nt1, grid, dim3(kThreads), lds, st, Z, T, M, P, r, slice, dst);
+    if (mode == 0)
+      hipLaunchKernelGGL(k_thin_nt1<0>, grid, dim3(kThreads), lds, st, Z, T, M, P, r, slice, dst);
+    else if (mode == 1)
+      hipLaunchKernelGGL(k_thin_nt1<1>, grid, dim3(kThreads), lds, st, Z, T, M, P, r, slice, dst);
+    else
+      hipLaunchKernelGGL(k_thin_nt1<2>, grid, dim3(kThreads), lds, st, Z, T, M, P, r, slice, dst);
   } else {
+    if (t_rows) return hipErrorInvalidValue;  // the general kernel takes T as [r, P]
   switch ((r + 15) / 16) {
     case 1: hipLaunchKernelGGL(k_thin_nt<1>, grid, dim3(kThreads), 0, st, Z, T, M, P, r, slice, dst); break;
     case 2: hipLaunchKernelGGL(k_thin_nt<2>, grid, dim3(kThreads), 0, st, Z, T, M, P, r, slice, dst); break;
@@ -249,19 +319,15 @@ hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st) {
   return hipGetLastError();
 }
 
-__global__ void k_transpose_b(const uint16_t* __restrict__ B, int64_t N, int r,
-                              uint16_t* __restrict__ Bt) {
+__global__ void k_bwd_aux(BwdAux a) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= N * r) return;
-  const int64_t n = i / r;
-  const int j = (int)(i % r);
-  Bt[(int64_t)j * N + n] = B[i];
+  if (i < bwd_aux_count(a)) bwd_aux_at(a, i);
 }
 
-hipError_t launch_transpose_b(const uint16_t* B, int64_t N, int r, uint16_t* Bt, hipStream_t st) {
-  const int64_t count = N * r;
-  hipLaunchKernelGGL(k_transpose_b, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, st, B, N,
-                     r, Bt);
+hipError_t launch_bwd_aux(const BwdAux& a, hipStream_t st) {
+  const int64_t count = bwd_aux_count(a);
+  if (count == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_bwd_aux, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
@@ -298,26 +364,27 @@ constexpr int TN_NST = 4;
 // deep (row y's 16-byte chunk c at unit c ^ 2(y & 3)); the A operand (16
 // columns x 32 rows) is read transposed with ds_read_b64_tr_b16, lane t of a
 // 16-lane group addressing row 4h + t/4, columns 4(t%4)..+3, so that lane t
-// receives column t, four consecutive rows.  The B operand is (s V)^T for the
-// slice, built in LDS from the fp32 V as a bf16 high part and a bf16
-// remainder (zero for j >= r and m >= M).
+// receives column t, four consecutive rows.  The B operand is (s V)^T as a
+// bf16 high part and a bf16 remainder (made beforehand, see BwdAux), staged
+// in LDS for the whole slice.
 struct TnJob {
-  const uint16_t* Z;  // [M, P] bf16
-  const float* V;     // [M, r] fp32
+  const uint16_t* Z;   // [M, P] bf16
+  const uint16_t* vt;  // [2][16 ceil(r/16)][Mp] (s V)^T high and remainder parts
+  int64_t Mp;
   int64_t P;
-  int64_t slice;      // rows per slice, a multiple of 32
-  int S;              // slices
-  int tiles;          // column tiles of 128
-  float* part;        // [S, P, r]
+  int64_t slice;       // rows per slice, a multiple of 32
+  int S;               // slices
+  int tiles;           // column tiles of 128
+  float* part;         // [S, P, r]
 };
 
-__global__ __launch_bounds__(kThreads) void k_thin_tn(TnJob j0, TnJob j1, int64_t M, int r,
-                                                      float s) {
+__global__ __launch_bounds__(kThreads) void k_thin_tn(TnJob j0, TnJob j1, int64_t M, int r) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const bool second = (int)blockIdx.x >= j0.tiles;
   const uint16_t* Z = second ? j1.Z : j0.Z;
-  const float* V = second ? j1.V : j0.V;
+  const uint16_t* vt = second ? j1.vt : j0.vt;
+  const int64_t Mp = second ? j1.Mp : j0.Mp;
   const int64_t P = second ? j1.P : j0.P;
   const int64_t slice = second ? j1.slice : j0.slice;
   const int S = second ? j1.S : j0.S;
@@ -332,22 +399,14 @@ __global__ __launch_bounds__(kThreads) void k_thin_tn(TnJob j0, TnJob j1, int64_
   uint8_t* vst = smem + TN_NST * TN_STAGE;      // [2][16 nj][slice] bf16
   const int64_t vrow = slice * 2;               // bytes per staged (sV)^T row
 
-  // ---- (sV)^T: thread -> a pair of rows m, m+1 and 16 ranks; the fp32 reads
-  // go out before the Z loads, the LDS writes (one word per rank: rows m and
-  // m+1) after them.  At most 256 units: slice <= 512 / nj.
-  const int npairs = (int)(slice / 2), units = npairs * nj;
-  const int pm = tid % npairs, jg = tid / npairs;
-  const int64_t m = mb + 2 * pm;
-  // (unconditional, clamped reads: no load waits at a branch join)
-  float va[16], vb[16];
+  // ---- (sV)^T for the slice: 2 * 16nj rows of `slice` bf16, 16-B chunks
   {
-    const float* r0 = V + min(m, M - 1) * r;
-    const float* r1 = V + min(m + 1, M - 1) * r;
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int jj = min(16 * jg + q, r - 1);
-      va[q] = r0[jj];
-      vb[q] = r1[jj];
+    const int chunks = (int)(slice / 8);
+    const rsrc_t rv = make_rs(vt, (uint32_t)(2 * 16 * nj * Mp * 2));
+    const int total = 2 * 16 * nj * chunks;     // multiple of 64 (slice % 32 == 0)
+    for (int c0 = 64 * wave; c0 < total; c0 += 256) {
+      const int c = c0 + lane, row = c / chunks, q = c % chunks;  // row: part * 16nj + j
+      dma16(rv, (uint32_t)((row * Mp + mb + 8 * q) * 2), 0, vst + (int64_t)(c0 / 64) * 1024);
     }
   }
   // ---- Z loads: instruction i (0..7) of a step covers rows 4i..4i+3; wave w
@@ -372,18 +431,6 @@ __global__ __launch_bounds__(kThreads) void k_thin_tn(TnJob j0, TnJob j1, int64_
     }
   };
   for (int k = 0; k < TN_NST - 1; ++k) load_z(min(k, steps - 1), k);
-  if (tid < units) {
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int j = 16 * jg + q;
-      const float x0 = (j < r && m < M) ? s * va[q] : 0.f;
-      const float x1 = (j < r && m + 1 < M) ? s * vb[q] : 0.f;
-      const uint32_t h = pack_bf16x2(x0, x1);
-      const uint32_t lo = pack_bf16x2(x0 - bf16_lo(h), x1 - bf16_hi(h));
-      *reinterpret_cast<uint32_t*>(vst + j * vrow + 4 * pm) = h;
-      *reinterpret_cast<uint32_t*>(vst + (16 * nj + j) * vrow + 4 * pm) = lo;
-    }
-  }
   asm volatile("s_waitcnt vmcnt(4)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
   // transposed-read addresses: lane l, group g = l/16, t = l%16; p-tile pt,
@@ -492,7 +539,12 @@ int thin_tn_slices(int64_t M, int64_t P, int r) {
   return (int)((M + slice - 1) / slice);
 }
 
-hipError_t launch_thin_tn2(const ThinTn& a, const ThinTn& b, int64_t M, int r, float s,
+// Row length of the staged (sV)^T: every slice's rows exist (zero past M).
+int64_t thin_tn_rows_padded(int64_t M, int64_t P, int r) {
+  return (int64_t)thin_tn_slices(M, P, r) * thin_tn_slice_rows(M, P, r);
+}
+
+hipError_t launch_thin_tn2(const ThinTn& a, const ThinTn& b, int64_t M, int r,
                            hipStream_t st) {
   static hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(k_thin_tn), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -507,7 +559,8 @@ hipError_t launch_thin_tn2(const ThinTn& a, const ThinTn& b, int64_t M, int r, f
     const ThinTn& x = *in[k];
     TnJob& j = job[k];
     j.Z = x.Z;
-    j.V = x.V;
+    j.vt = x.vt;
+    j.Mp = thin_tn_rows_padded(M, x.P, r);
     j.P = x.P;
     j.slice = thin_tn_slice_rows(M, x.P, r);
     j.S = thin_tn_slices(M, x.P, r);
@@ -522,7 +575,7 @@ hipError_t launch_thin_tn2(const ThinTn& a, const ThinTn& b, int64_t M, int r, f
   if (tiles == 0) return hipSuccess;
   const size_t lds = (size_t)TN_NST * TN_STAGE + (size_t)2 * 16 * nj * slice_max * 2;
   hipLaunchKernelGGL(k_thin_tn, dim3((unsigned)tiles, (unsigned)s_max), dim3(kThreads), lds, st,
-                     job[0], job[1], M, r, s);
+                     job[0], job[1], M, r);
   TnSum sum[2];
   int64_t count = 0;
   for (int k = 0; k < 2; ++k) {

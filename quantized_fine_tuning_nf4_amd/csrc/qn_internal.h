@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "qn_device.h"
+
 namespace qn {
 
 // ws_bad [ng] per-group non-finite flags; *flag = 1 when any weight is NaN
@@ -25,25 +27,91 @@ hipError_t launch_dequant(const uint8_t* packed, const uint8_t* qscale, const fl
                           const float* offset, int64_t n, bool bf16, void* out, hipStream_t st,
                           const SliceSum& ss = SliceSum{nullptr, 0, 0, nullptr});
 
-// Adapter transposes done by spare workgroups of another launch:
-// At [K, r] = A[r, K]^T and Bt [r, N] = B[N, r]^T (bf16); a null A or B
-// skips that one.
-struct AdapterTransposes {
-  const uint16_t* A;
-  uint16_t* At;
-  int64_t K;
+// Small backward jobs, run by spare workgroups of another launch or alone:
+//   Bt [r, N] = B[N, r]^T and At [K, r] = A[r, K]^T (bf16);
+//   su = (s u)^T and sv = (s v)^T, each [2][16 ceil(r/16)][Mp] bf16 (high
+//   parts, then remainders; zero for j >= r or m >= M), u and v fp32 [M, r];
+//   when Sv > 1, v is first written as the slice sum of vpart [Sv][M][r].
+// A null destination skips its job.  One thread per output element.
+struct BwdAux {
   const uint16_t* B;
   uint16_t* Bt;
   int64_t N;
+  const uint16_t* A;
+  uint16_t* At;
+  int64_t K;
+  const float* u;
+  uint16_t* su;
+  int64_t Mpu;
+  const float* vpart;
+  int Sv;
+  float* v;
+  uint16_t* sv;
+  int64_t Mpv;
+  int64_t M;
   int r;
+  float s;
 };
+__host__ __device__ inline int64_t bwd_aux_count(const BwdAux& a) {
+  const int64_t rp = 16 * ((a.r + 15) / 16);
+  return (a.Bt ? a.N * a.r : 0) + (a.At ? a.K * a.r : 0) + (a.su ? rp * a.Mpu : 0) +
+         (a.sv ? rp * a.Mpv : 0);
+}
+// element i of the concatenated jobs (Bt, At, su, sv in that order)
+__device__ inline void bwd_aux_at(const BwdAux& a, int64_t i) {
+  const int64_t rp = 16 * ((a.r + 15) / 16);
+  const int64_t nb = a.Bt ? a.N * a.r : 0;
+  if (i < nb) {
+    const int64_t j = i / a.N, n = i % a.N;
+    a.Bt[i] = a.B[n * a.r + j];
+    return;
+  }
+  i -= nb;
+  const int64_t na = a.At ? a.K * a.r : 0;
+  if (i < na) {
+    const int64_t k = i / a.r, j = i % a.r;
+    a.At[i] = a.A[j * a.K + k];
+    return;
+  }
+  i -= na;
+  const int64_t nu = a.su ? rp * a.Mpu : 0;
+  uint16_t* dst;
+  int64_t count;
+  float x = 0.f;
+  if (i < nu) {
+    const int64_t j = i / a.Mpu, m = i % a.Mpu;
+    if (j < a.r && m < a.M) x = a.s * a.u[m * a.r + j];
+    dst = a.su;
+    count = nu;
+  } else {
+    i -= nu;
+    const int64_t j = i / a.Mpv, m = i % a.Mpv;
+    if (j < a.r && m < a.M) {
+      const int64_t e = m * a.r + j;
+      float val;
+      if (a.Sv > 1) {
+        val = slice_sum(a.vpart, a.M * a.r, a.Sv, e);
+        a.v[e] = val;
+      } else {
+        val = a.v[e];
+      }
+      x = a.s * val;
+    }
+    dst = a.sv;
+    count = rp * a.Mpv;
+  }
+  const uint32_t h = pack_bf16x2(x, 0.f) & 0xffffu;
+  dst[i] = (uint16_t)h;
+  dst[count + i] = (uint16_t)(pack_bf16x2(x - bf16_lo(h), 0.f) & 0xffffu);
+}
+hipError_t launch_bwd_aux(const BwdAux& a, hipStream_t st);
 
 // out[k][n] = Qhat(W)[n][k] as bf16 with row length ldt (ldt % 8 == 0,
-// ldt >= rows); zero for rows <= n < ldt.  cols % 64 == 0.  The transposes
-// in tj run in the same launch.
+// ldt >= rows); zero for rows <= n < ldt.  cols % 64 == 0.  The jobs of
+// aux run in extra workgroups of the same launch.
 hipError_t launch_dequant_t(const uint8_t* packed, const uint8_t* qscale, const float* scale2,
                             const float* offset, int64_t rows, int64_t cols, uint16_t* out,
-                            int64_t ldt, const AdapterTransposes& tj, hipStream_t st);
+                            int64_t ldt, const BwdAux& aux, hipStream_t st);
 
 // C[M, Nc] bf16 = A[M, R] (row stride lda) * Bm[Nc, :R]^T (row stride ldb,
 // ldb % 64 == 0, zero in columns R..ldb) + s * V[M, r] * L[Nc, r]^T.
@@ -69,35 +137,36 @@ struct WState {
 // out[M, r] (fp32) = sum over S slices of Z[M, P] * T[r, P]^T.  When S > 1
 // the slices are written to part[S][M][r] and summed in slice order into
 // out; S == 1 writes out directly.
-// sum == false leaves the slices in part for the caller to add.
+// sum == false leaves the slices in part for the caller to add.  t_rows:
+// T is given as its transpose [P, r] (r <= 16 only).
 hipError_t launch_thin_nt(const uint16_t* Z, const uint16_t* T, int64_t M, int64_t P, int r,
-                          float* out, float* part, int S, hipStream_t st, bool sum = true);
+                          float* out, float* part, int S, hipStream_t st, bool sum = true,
+                          bool t_rows = false);
 int thin_nt_slices(int64_t M, int64_t P);
+bool thin_nt_rows_ok(int64_t M, int64_t P, int r);
 
 // p[0..n) = 0 (a kernel, so it may sit in a captured graph).
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st);
 
-// Bt[r, N] = B[N, r]^T (bf16).
-hipError_t launch_transpose_b(const uint16_t* B, int64_t N, int r, uint16_t* Bt, hipStream_t st);
 
 // One transposed adapter product out = Z^T (s V), reduced over the M rows:
-// Z bf16 [M, P] (null: no product), V fp32 [M, r]; transposed == false:
-// out fp32 [P, r]; true: out fp32 [r, P].  Split over
-// thin_tn_slices(M, P, r) row slices with partials part[S][P][r], summed in
-// slice order.  P % 8 == 0.
+// Z bf16 [M, P] (null: no product), vt = (s V)^T split as BwdAux makes it
+// with Mp = thin_tn_rows_padded(M, P, r); transposed == false: out fp32
+// [P, r]; true: out fp32 [r, P].  Split over thin_tn_slices(M, P, r) row
+// slices with partials part[S][P][r], summed in slice order.  P % 8 == 0.
 struct ThinTn {
   const uint16_t* Z;
-  const float* V;
+  const uint16_t* vt;
   int64_t P;
   float* out;
   bool transposed;
   float* part;
 };
-// Two such products (same M, r and s) in one launch, their slice sums in a
+// Two such products (same M and r) in one launch, their slice sums in a
 // second.
-hipError_t launch_thin_tn2(const ThinTn& a, const ThinTn& b, int64_t M, int r, float s,
-                           hipStream_t st);
+hipError_t launch_thin_tn2(const ThinTn& a, const ThinTn& b, int64_t M, int r, hipStream_t st);
 int thin_tn_slices(int64_t M, int64_t P, int r);
+int64_t thin_tn_rows_padded(int64_t M, int64_t P, int r);
 
 // Decode forward, u = X A^T included (written to u_out [M, r]); workspace
 // part [S, M, rows] and upart [S, M, r] fp32, S = decode_slices(...).

@@ -364,8 +364,8 @@ hipError_t launch_dequant(const uint8_t* packed, const uint8_t* qscale, const fl
 
 
 // Transposed dequantization for the dX product: out[k][n] (bf16, row length
-// ldt >= rows, ldt % 8 == 0) = Qhat(W)[n][k], zero for rows <= n < ldt.  An
-// extra row of workgroups (when asked) transposes the adapters for the same
+// ldt >= rows, ldt % 8 == 0) = Qhat(W)[n][k], zero for rows <= n < ldt.
+// Extra rows of workgroups (when asked) run the small jobs of the same
 // backward, which saves their launches.
 // Workgroup (bx, kb): rows n0 = 64 bx .. +63 of block column kb; thread t
 // dequantizes 16 codes (row n0 + t/4, elements 16 (t%4) ..) into an LDS tile
@@ -375,25 +375,16 @@ __global__ __launch_bounds__(256) void k_dequant_t(const uint8_t* __restrict__ p
                                                    const float* __restrict__ scale2,
                                                    const float* __restrict__ offset, int64_t rows,
                                                    int64_t cols, uint16_t* __restrict__ out,
-                                                   int64_t ldt, AdapterTransposes tj) {
+                                                   int64_t ldt, BwdAux aux) {
   constexpr int LDT = 72;  // 64 + 8 pad
   __shared__ float lut[16];
   __shared__ __attribute__((aligned(16))) uint16_t tile[64][LDT];
   const int t = threadIdx.x;
-  if ((int64_t)blockIdx.y == cols / kBlock) {
-    // the extra row of workgroups: adapter transposes At [K, r] = A^T and
-    // Bt [r, N] = B^T, grid-strided
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    const int64_t na = tj.A ? (int64_t)tj.r * tj.K : 0, nb = tj.B ? tj.N * tj.r : 0;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + t; i < na + nb; i += stride) {
-      if (i < na) {
-        const int64_t k = i / tj.r, j = i % tj.r;
-        tj.At[i] = tj.A[j * tj.K + k];
-      } else {
-        const int64_t e = i - na, j = e / tj.N, n = e % tj.N;
-        tj.Bt[e] = tj.B[n * tj.r + j];
-      }
-    }
+  if ((int64_t)blockIdx.y >= cols / kBlock) {
+    // the extra rows of workgroups: the small backward jobs
+    const int64_t i =
+        (((int64_t)blockIdx.y - cols / kBlock) * gridDim.x + blockIdx.x) * blockDim.x + t;
+    if (i < bwd_aux_count(aux)) bwd_aux_at(aux, i);
     return;
   }
   if (t < 16) lut[t] = as_f32(kNF4Bits[t]);
@@ -428,11 +419,12 @@ __global__ __launch_bounds__(256) void k_dequant_t(const uint8_t* __restrict__ p
 
 hipError_t launch_dequant_t(const uint8_t* packed, const uint8_t* qscale, const float* scale2,
                             const float* offset, int64_t rows, int64_t cols, uint16_t* out,
-                            int64_t ldt, const AdapterTransposes& tj, hipStream_t st) {
-  const bool extra = tj.A || tj.B;
-  const dim3 grid((unsigned)((ldt + 63) / 64), (unsigned)(cols / kBlock + (extra ? 1 : 0)));
+                            int64_t ldt, const BwdAux& aux, hipStream_t st) {
+  const int64_t gx = (ldt + 63) / 64, per_row = gx * 256;
+  const int64_t extra = (bwd_aux_count(aux) + per_row - 1) / per_row;
+  const dim3 grid((unsigned)gx, (unsigned)(cols / kBlock + extra));
   hipLaunchKernelGGL(k_dequant_t, grid, dim3(256), 0, st, packed, qscale, scale2, offset, rows,
-                     cols, out, ldt, tj);
+                     cols, out, ldt, aux);
   return hipGetLastError();
 }
 
