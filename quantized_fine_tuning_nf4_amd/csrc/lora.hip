@@ -8,6 +8,7 @@
 // All use v_mfma_f32_16x16x32_bf16; fp32 operands (u, v) enter the MFMA as a
 // bf16 high part plus a bf16 remainder, so they keep ~16 significant bits.
 #include <algorithm>
+#include <type_traits>
 
 #include "qn_device.h"
 #include "qn_internal.h"
@@ -349,8 +350,7 @@ __device__ __forceinline__ void dma16(rsrc_t rs, uint32_t voff, uint32_t soff, u
 }
 
 constexpr int TN_COLS = 128;             // columns of Z per workgroup
-constexpr int TN_ROWB = TN_COLS * 2;     // 256 B per staged row
-constexpr int TN_STAGE = 32 * TN_ROWB;   // 8 KB: 32 rows per step
+constexpr int TN_ROWB = TN_COLS * 2;     // 256 B per staged Z row
 constexpr int TN_NST = 4;
 
 }  // namespace
@@ -360,16 +360,17 @@ constexpr int TN_NST = 4;
 // independent products (dB and dA of one backward) share the launch: grid x
 // runs over the column tiles of job 0, then those of job 1.  Workgroup
 // (pt, z): columns 128 pt .. +127, wave w: 32w .. 32w+31 (two 16-column MFMA
-// tiles).  32 rows of Z per step go global -> LDS by buffer loads four steps
-// deep (row y's 16-byte chunk c at unit c ^ 2(y & 3)); the A operand (16
+// tiles).  A step is 32 rows: their Z (8 KB) and their (s V)^T high and
+// remainder parts (2 x 16 NJ rows of 64 B) go global -> LDS by buffer loads
+// into one stage, four stages deep, every wave issuing 2 + 2 NJ loads per
+// step.
+// Z row y's 16-byte chunk c sits at unit c ^ 2(y & 3); the A operand (16
 // columns x 32 rows) is read transposed with ds_read_b64_tr_b16, lane t of a
 // 16-lane group addressing row 4h + t/4, columns 4(t%4)..+3, so that lane t
-// receives column t, four consecutive rows.  The B operand is (s V)^T as a
-// bf16 high part and a bf16 remainder (made beforehand, see BwdAux), staged
-// in LDS for the whole slice.
+// receives column t, four consecutive rows.  NJ = ceil(r/16).
 struct TnJob {
   const uint16_t* Z;   // [M, P] bf16
-  const uint16_t* vt;  // [2][16 ceil(r/16)][Mp] (s V)^T high and remainder parts
+  const uint16_t* vt;  // [2][16 NJ][Mp] (s V)^T high and remainder parts
   int64_t Mp;
   int64_t P;
   int64_t slice;       // rows per slice, a multiple of 32
@@ -378,7 +379,11 @@ struct TnJob {
   float* part;         // [S, P, r]
 };
 
+template <int NJ>
 __global__ __launch_bounds__(kThreads) void k_thin_tn(TnJob j0, TnJob j1, int64_t M, int r) {
+  constexpr int ZB = 32 * TN_ROWB;             // Z bytes per stage
+  constexpr int VB = 2 * 16 * NJ * 64;         // (sV)^T bytes per stage
+  constexpr int SB = ZB + VB;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const bool second = (int)blockIdx.x >= j0.tiles;
@@ -390,30 +395,20 @@ __global__ __launch_bounds__(kThreads) void k_thin_tn(TnJob j0, TnJob j1, int64_
   const int S = second ? j1.S : j0.S;
   float* part = second ? j1.part : j0.part;
   if ((int)blockIdx.y >= S) return;
-  const int nj = (r + 15) / 16;
   const int64_t p0 = (int64_t)((int)blockIdx.x - (second ? j0.tiles : 0)) * TN_COLS;
   const int64_t mb = (int64_t)blockIdx.y * slice;
   const int64_t me = min(mb + slice, M);
   const int steps = (int)((me - mb + 31) / 32);
-  uint8_t* zst = smem;                          // TN_NST stages of Z
-  uint8_t* vst = smem + TN_NST * TN_STAGE;      // [2][16 nj][slice] bf16
-  const int64_t vrow = slice * 2;               // bytes per staged (sV)^T row
 
-  // ---- (sV)^T for the slice: 2 * 16nj rows of `slice` bf16, 16-B chunks
-  {
-    const int chunks = (int)(slice / 8);
-    const rsrc_t rv = make_rs(vt, (uint32_t)(2 * 16 * nj * Mp * 2));
-    const int total = 2 * 16 * nj * chunks;     // multiple of 64 (slice % 32 == 0)
-    for (int c0 = 64 * wave; c0 < total; c0 += 256) {
-      const int c = c0 + lane, row = c / chunks, q = c % chunks;  // row: part * 16nj + j
-      dma16(rv, (uint32_t)((row * Mp + mb + 8 * q) * 2), 0, vst + (int64_t)(c0 / 64) * 1024);
-    }
-  }
   // ---- Z loads: instruction i (0..7) of a step covers rows 4i..4i+3; wave w
   // issues i = 2w, 2w+1; lane l -> row 4i + l/16, unit l%16, source chunk
   // (l%16) ^ 2(row & 3).  Rows past M repeat row M-1 (their sV is zero);
   // columns past P repeat the last chunk (their outputs are not stored).
+  // (sV)^T loads: 4 of its 64-byte rows per 4-byte-per-lane instruction
+  // (lane l: row 4q + l/16, word l%16), instruction q = 2 NJ w + k of the
+  // step (all lanes active: no branch around a load into LDS).
   const rsrc_t rz = make_rs(Z, (uint32_t)(M * P * 2));
+  const rsrc_t rv = make_rs(vt, (uint32_t)(2 * 16 * NJ * Mp * 2));
   uint32_t zoff[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
@@ -422,16 +417,35 @@ __global__ __launch_bounds__(kThreads) void k_thin_tn(TnJob j0, TnJob j1, int64_
     const int64_t col = min(p0 + 8 * chunk, P - 8);
     zoff[h] = (uint32_t)(col * 2);
   }
-  auto load_z = [&](int st, int stage) {
+  uint32_t voff[2 * NJ];
+#pragma unroll
+  for (int k = 0; k < 2 * NJ; ++k) {
+    const int q = 2 * NJ * wave + k, row = 4 * q + (lane >> 4);
+    voff[k] = (uint32_t)((row * Mp + mb) * 2 + 4 * (lane & 15));
+  }
+  auto load_step = [&](int st, int stage) {
+    uint8_t* base = smem + stage * SB;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int i = 2 * wave + h, row = 4 * i + (lane >> 4);
       const int64_t mm = min(mb + 32 * (int64_t)st + row, M - 1);
-      dma16(rz, zoff[h] + (uint32_t)(mm * P * 2), 0, zst + stage * TN_STAGE + 1024 * i);
+      dma16(rz, zoff[h] + (uint32_t)(mm * P * 2), 0, base + 1024 * i);
     }
+#pragma unroll
+    for (int k = 0; k < 2 * NJ; ++k)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(base + ZB + 256 * (2 * NJ * wave + k)),
+                                               4, voff[k] + (uint32_t)(64 * st), 0, 0, 0);
   };
-  for (int k = 0; k < TN_NST - 1; ++k) load_z(min(k, steps - 1), k);
-  asm volatile("s_waitcnt vmcnt(4)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  // all but the two newest steps' loads have landed
+  auto wait_two = [&]() {
+    if constexpr (NJ == 1) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    else if constexpr (NJ == 2) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+    else if constexpr (NJ == 3) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(20)" ::: "memory");
+  };
+  for (int k = 0; k < TN_NST - 1; ++k) load_step(min(k, steps - 1), k);
+  wait_two();
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
   // transposed-read addresses: lane l, group g = l/16, t = l%16; p-tile pt,
   // half h: row 8g + 4h + t/4, column 32w + 16pt + 4(t%4)
@@ -445,46 +459,68 @@ __global__ __launch_bounds__(kThreads) void k_thin_tn(TnJob j0, TnJob j1, int64_
       const int col = 32 * wave + 16 * pt + 4 * (t & 3);
       aoff[pt][h] = row * TN_ROWB + 16 * ((col >> 3) ^ (2 * (row & 3))) + 2 * (col & 7);
     }
-  f32x4 acc[2][4] = {};
-  for (int st = 0; st < steps; ++st) {
-    const int stage = st % TN_NST;
-    load_z(min(st + TN_NST - 1, steps - 1), (st + TN_NST - 1) % TN_NST);
-    const uint8_t* zs = zst + stage * TN_STAGE;
+  f32x4 acc[2][NJ] = {};
+  // one step on stage P (a constant, so that the compiler sees the loads of
+  // step st+3 and this step's LDS reads touch different stages)
+  auto body = [&](auto p_t, int st) {
+    constexpr int P = decltype(p_t)::value;
+    load_step(min(st + TN_NST - 1, steps - 1), (P + TN_NST - 1) % TN_NST);
+    const uint8_t* zs = smem + P * SB;
+    // the four transposed reads in one block that also waits for them (the
+    // compiler would otherwise treat them as possibly overlapping the loads
+    // in flight to the other stages and wait for all of those first)
+    const uint32_t zb = (uint32_t)reinterpret_cast<uintptr_t>(zs);
+    u32x2 x00, x01, x10, x11;
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %4\n\t"
+        "ds_read_b64_tr_b16 %1, %5\n\t"
+        "ds_read_b64_tr_b16 %2, %6\n\t"
+        "ds_read_b64_tr_b16 %3, %7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=v"(x00), "=v"(x01), "=v"(x10), "=v"(x11)
+        : "v"(zb + aoff[0][0]), "v"(zb + aoff[0][1]), "v"(zb + aoff[1][0]), "v"(zb + aoff[1][1])
+        : "memory");
     bf16x8 a[2];
+    a[0] = as_bf16x8(u32x4{x00[0], x00[1], x01[0], x01[1]});
+    a[1] = as_bf16x8(u32x4{x10[0], x10[1], x11[0], x11[1]});
 #pragma unroll
-    for (int pt = 0; pt < 2; ++pt) {
-      const v4s x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) v4s*)(zs + aoff[pt][0]));
-      const v4s x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) v4s*)(zs + aoff[pt][1]));
-      const u32x2 l2 = __builtin_bit_cast(u32x2, x0), h2 = __builtin_bit_cast(u32x2, x1);
-      a[pt] = as_bf16x8(u32x4{l2[0], l2[1], h2[0], h2[1]});
-    }
+    for (int jt = 0; jt < NJ; ++jt) {
+      // B operand: column j = 16jt + l%16, rows 8g..8g+7 of the step
+      const uint8_t* vs = zs + ZB + (16 * jt + t) * 64 + 16 * g;
+      const bf16x8 bh = as_bf16x8(*reinterpret_cast<const u32x4*>(vs));
+      const bf16x8 bl = as_bf16x8(*reinterpret_cast<const u32x4*>(vs + 16 * NJ * 64));
 #pragma unroll
-    for (int jt = 0; jt < 4; ++jt) {
-      if (jt < nj) {
-        // B operand: column j = 16jt + l%16, rows 8g..8g+7 of the step
-        const int64_t off = (int64_t)(16 * jt + t) * vrow + (32 * (int64_t)st + 8 * g) * 2;
-        const bf16x8 bh = as_bf16x8(*reinterpret_cast<const u32x4*>(vst + off));
-        const bf16x8 bl = as_bf16x8(*reinterpret_cast<const u32x4*>(vst + 16 * nj * vrow + off));
-#pragma unroll
-        for (int pt = 0; pt < 2; ++pt) {
-          acc[pt][jt] = mfma16(a[pt], bh, acc[pt][jt]);
-          acc[pt][jt] = mfma16(a[pt], bl, acc[pt][jt]);
-        }
+      for (int pt = 0; pt < 2; ++pt) {
+        acc[pt][jt] = mfma16(a[pt], bh, acc[pt][jt]);
+        acc[pt][jt] = mfma16(a[pt], bl, acc[pt][jt]);
       }
     }
     // step st+1's loads (issued 3 steps ago) have landed everywhere before
     // anyone reads them or overwrites this stage
-    asm volatile("s_waitcnt vmcnt(4)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    wait_two();
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  };
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+  using S3 = std::integral_constant<int, 3>;
+  int st = 0;
+  for (; st + 4 <= steps; st += 4) {
+    body(S0{}, st);
+    body(S1{}, st + 1);
+    body(S2{}, st + 2);
+    body(S3{}, st + 3);
   }
+  if (st < steps) body(S0{}, st);
+  if (st + 1 < steps) body(S1{}, st + 1);
+  if (st + 2 < steps) body(S2{}, st + 2);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   // lane: column j = 16jt + l%16, rows p = 16pt + 4(l/16) + i of the wave
   float* dst = part + (int64_t)blockIdx.y * P * r;
 #pragma unroll
-  for (int jt = 0; jt < 4; ++jt) {
+  for (int jt = 0; jt < NJ; ++jt) {
     const int j = 16 * jt + t;
-    if (jt >= nj || j >= r) continue;
+    if (j >= r) continue;
 #pragma unroll
     for (int pt = 0; pt < 2; ++pt)
 #pragma unroll
@@ -520,16 +556,13 @@ __global__ void k_sum_slices_tn(TnSum a, TnSum b, int r) {
 }
 
 // Slices of the M rows for the transposed products: enough workgroups to
-// fill the chip, a multiple of 32 rows each, and the slice's (sV)^T (2 parts
-// x 16 ceil(r/16) rows) in at most 32 KB of LDS.
+// fill the chip (about 512 per product), a multiple of 32 rows each.
 int64_t thin_tn_slice_rows(int64_t M, int64_t P, int r) {
-  const int nj = (r + 15) / 16;
+  (void)r;
   const int64_t pt = (P + TN_COLS - 1) / TN_COLS;
-  int64_t S = (512 + pt - 1) / pt;
+  const int64_t S = (512 + pt - 1) / pt;
   int64_t slice = (M + S - 1) / S;
   slice = (slice + 31) / 32 * 32;
-  const int64_t cap = 32768 / (2 * 16 * nj * 2) / 32 * 32;  // 512 / nj
-  if (slice > cap) slice = cap;
   if (slice < 32) slice = 32;
   return slice;
 }
@@ -546,14 +579,9 @@ int64_t thin_tn_rows_padded(int64_t M, int64_t P, int r) {
 
 hipError_t launch_thin_tn2(const ThinTn& a, const ThinTn& b, int64_t M, int r,
                            hipStream_t st) {
-  static hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(k_thin_tn), hipFuncAttributeMaxDynamicSharedMemorySize,
-      (int)(TN_NST * TN_STAGE + 32768));
-  if (attr != hipSuccess) return attr;
   const int nj = (r + 15) / 16;
   TnJob job[2];
   const ThinTn* in[2] = {&a, &b};
-  int64_t slice_max = 32;
   int s_max = 1;
   for (int k = 0; k < 2; ++k) {
     const ThinTn& x = *in[k];
@@ -566,16 +594,18 @@ hipError_t launch_thin_tn2(const ThinTn& a, const ThinTn& b, int64_t M, int r,
     j.S = thin_tn_slices(M, x.P, r);
     j.tiles = x.Z ? (int)((x.P + TN_COLS - 1) / TN_COLS) : 0;
     j.part = x.part;
-    if (j.tiles > 0) {
-      slice_max = std::max(slice_max, j.slice);
-      s_max = std::max(s_max, j.S);
-    }
+    if (j.tiles > 0) s_max = std::max(s_max, j.S);
   }
   const int tiles = job[0].tiles + job[1].tiles;
   if (tiles == 0) return hipSuccess;
-  const size_t lds = (size_t)TN_NST * TN_STAGE + (size_t)2 * 16 * nj * slice_max * 2;
-  hipLaunchKernelGGL(k_thin_tn, dim3((unsigned)tiles, (unsigned)s_max), dim3(kThreads), lds, st,
-                     job[0], job[1], M, r);
+  const size_t lds = (size_t)TN_NST * (32 * TN_ROWB + 2 * 16 * nj * 64);
+  const dim3 grid((unsigned)tiles, (unsigned)s_max);
+  switch (nj) {
+    case 1: hipLaunchKernelGGL(k_thin_tn<1>, grid, dim3(kThreads), lds, st, job[0], job[1], M, r); break;
+    case 2: hipLaunchKernelGGL(k_thin_tn<2>, grid, dim3(kThreads), lds, st, job[0], job[1], M, r); break;
+    case 3: hipLaunchKernelGGL(k_thin_tn<3>, grid, dim3(kThreads), lds, st, job[0], job[1], M, r); break;
+    default: hipLaunchKernelGGL(k_thin_tn<4>, grid, dim3(kThreads), lds, st, job[0], job[1], M, r); break;
+  }
   TnSum sum[2];
   int64_t count = 0;
   for (int k = 0; k < 2; ++k) {
