@@ -477,7 +477,9 @@ __global__ __launch_bounds__(kThreads) void k_thin_tn(TnJob j0, TnJob j1, int64_
         "ds_read_b64_tr_b16 %2, %6\n\t"
         "ds_read_b64_tr_b16 %3, %7\n\t"
         "s_waitcnt lgkmcnt(0)"
-        : "=v"(x00), "=v"(x01), "=v"(x10), "=v"(x11)
+        // early-clobber: a result must not share a register with an address
+        // that a later read of the block still has to issue with
+        : "=&v"(x00), "=&v"(x01), "=&v"(x10), "=&v"(x11)
         : "v"(zb + aoff[0][0]), "v"(zb + aoff[0][1]), "v"(zb + aoff[1][0]), "v"(zb + aoff[1][1])
         : "memory");
     bf16x8 a[2];

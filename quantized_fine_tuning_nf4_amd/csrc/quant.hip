@@ -365,65 +365,92 @@ hipError_t launch_dequant(const uint8_t* packed, const uint8_t* qscale, const fl
 
 // Transposed dequantization for the dX product: out[k][n] (bf16, row length
 // ldt >= rows, ldt % 8 == 0) = Qhat(W)[n][k], zero for rows <= n < ldt.
-// Extra rows of workgroups (when asked) run the small jobs of the same
-// backward, which saves their launches.
-// Workgroup (bx, kb): rows n0 = 64 bx .. +63 of block column kb; thread t
-// dequantizes 16 codes (row n0 + t/4, elements 16 (t%4) ..) into an LDS tile
-// [k][n], which is written out as 16-byte row pieces.
+// Workgroup (bx, kq): rows n0 = 128 bx .. +127, columns 256 kq .. +255 (four
+// blocks, so every row's 128 bytes of codes come in whole; cols % 64 == 0,
+// columns past cols are not stored); wave q takes
+// block 4 kq + q, lane l rows n0 + 2l and n0 + 2l + 1, whose two values per
+// column go to the LDS tile [k][n] as one word; the tile leaves as 256-byte
+// row pieces.  Extra rows of workgroups (when asked) run the small jobs of the
+// same backward, which saves their launches.
+constexpr int DQT_N = 128, DQT_K = 256, DQT_PITCH = DQT_N * 2 + 16;
 __global__ __launch_bounds__(256) void k_dequant_t(const uint8_t* __restrict__ packed,
                                                    const uint8_t* __restrict__ qscale,
                                                    const float* __restrict__ scale2,
                                                    const float* __restrict__ offset, int64_t rows,
                                                    int64_t cols, uint16_t* __restrict__ out,
                                                    int64_t ldt, BwdAux aux) {
-  constexpr int LDT = 72;  // 64 + 8 pad
   __shared__ float lut[16];
-  __shared__ __attribute__((aligned(16))) uint16_t tile[64][LDT];
+  extern __shared__ __attribute__((aligned(16))) uint8_t tile[];  // [DQT_K][DQT_PITCH]
   const int t = threadIdx.x;
-  if ((int64_t)blockIdx.y >= cols / kBlock) {
+  const int64_t kq_count = (cols + DQT_K - 1) / DQT_K;
+  if ((int64_t)blockIdx.y >= kq_count) {
     // the extra rows of workgroups: the small backward jobs
     const int64_t i =
-        (((int64_t)blockIdx.y - cols / kBlock) * gridDim.x + blockIdx.x) * blockDim.x + t;
+        (((int64_t)blockIdx.y - kq_count) * gridDim.x + blockIdx.x) * blockDim.x + t;
     if (i < bwd_aux_count(aux)) bwd_aux_at(aux, i);
     return;
   }
-  if (t < 16) lut[t] = as_f32(kNF4Bits[t]);
-  const int64_t n0 = (int64_t)blockIdx.x * 64, kb = blockIdx.y;
+  if (t < 16) {  // from immediates: no load ahead of the code loads
+    uint32_t v = kNF4Bits[0];
+#pragma unroll
+    for (int k = 1; k < 16; ++k) v = t == k ? kNF4Bits[k] : v;
+    lut[t] = as_f32(v);
+  }
+  const int q = t >> 6, l = t & 63;
+  const int64_t n0 = (int64_t)blockIdx.x * DQT_N;
   const int64_t kblocks = cols / kBlock;
-  const int nl = t >> 2, q = t & 3;
-  const int64_t n = n0 + nl;
-  uint2 p = make_uint2(0u, 0u);
-  float sc = 0.f;
-  if (n < rows) {
-    p = *reinterpret_cast<const uint2*>(packed + n * (cols / 2) + kb * 32 + 8 * q);
-    const int64_t b = n * kblocks + kb;
-    sc = dq_scale(qscale[b], scale2[b / kGroup], *offset);
-  }
-  __syncthreads();
+  // a block past the last one (cols % 256 != 0) repeats the last block; its
+  // columns are not stored
+  const int64_t kb = min((int64_t)blockIdx.y * 4 + q, kblocks - 1);
+  const int64_t na = n0 + 2 * l, nb = na + 1;
+  const int64_t ra = min(na, rows - 1), rb = min(nb, rows - 1);
+  // unconditional, clamped loads (no wait at a branch join)
+  const u32x4* pa = reinterpret_cast<const u32x4*>(packed + ra * (cols / 2) + kb * 32);
+  const u32x4* pb = reinterpret_cast<const u32x4*>(packed + rb * (cols / 2) + kb * 32);
+  const u32x4 a0 = pa[0], a1 = pa[1], b0 = pb[0], b1 = pb[1];
+  const int64_t ba = ra * kblocks + kb, bb = rb * kblocks + kb;
+  const uint32_t qa = qscale[ba], qb = qscale[bb];
+  const float s2a = scale2[ba / kGroup], s2b = scale2[bb / kGroup], mu = *offset;
+  const float sa = na < rows ? dq_scale(qa, s2a, mu) : 0.f;
+  const float sb = nb < rows ? dq_scale(qb, s2b, mu) : 0.f;
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // lut ready
+  const uint32_t wa[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+  const uint32_t wb[8] = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+  uint8_t* trow = tile + (int64_t)(64 * q) * DQT_PITCH + 4 * l;
 #pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    const uint32_t word = e < 8 ? p.x : p.y;
-    const float w = lut[(word >> (4 * (e & 7))) & 15u] * sc;
-    tile[16 * q + e][nl] = (uint16_t)(pack_bf16x2(w, 0.f) & 0xffffu);
+  for (int e = 0; e < 64; ++e) {
+    const uint32_t ca = (wa[e >> 3] >> (4 * (e & 7))) & 15u;
+    const uint32_t cb = (wb[e >> 3] >> (4 * (e & 7))) & 15u;
+    uint32_t v = pack_bf16x2(lut[ca] * sa, lut[cb] * sb);
+    if (na >= rows) v &= 0xffff0000u;  // +0 past the last row
+    if (nb >= rows) v &= 0x0000ffffu;
+    *reinterpret_cast<uint32_t*>(trow + e * DQT_PITCH) = v;
   }
-  __syncthreads();
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  // 256 rows of 256 bytes: pass h, thread t -> row 16h + t/16, chunk t%16
+  const int c = t & 15;
+  const int64_t col = n0 + 8 * c;
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int c = t + 256 * h, k = c >> 3, n8 = c & 7;
-    const int64_t col = n0 + 8 * n8;
-    if (col < ldt)
-      *reinterpret_cast<u32x4*>(out + (kb * 64 + k) * ldt + col) =
-          *reinterpret_cast<const u32x4*>(&tile[k][8 * n8]);
+  for (int h = 0; h < 16; ++h) {
+    const int k = 16 * h + (t >> 4);
+    const u32x4 v = *reinterpret_cast<const u32x4*>(tile + k * DQT_PITCH + 16 * c);
+    const int64_t kk = (int64_t)blockIdx.y * DQT_K + k;
+    if (col < ldt && kk < cols) *reinterpret_cast<u32x4*>(out + kk * ldt + col) = v;
   }
 }
 
 hipError_t launch_dequant_t(const uint8_t* packed, const uint8_t* qscale, const float* scale2,
                             const float* offset, int64_t rows, int64_t cols, uint16_t* out,
                             int64_t ldt, const BwdAux& aux, hipStream_t st) {
-  const int64_t gx = (ldt + 63) / 64, per_row = gx * 256;
+  const size_t lds = (size_t)DQT_K * DQT_PITCH;
+  static const hipError_t attr =
+      hipFuncSetAttribute(reinterpret_cast<const void*>(k_dequant_t),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (attr != hipSuccess) return attr;
+  const int64_t gx = (ldt + DQT_N - 1) / DQT_N, per_row = gx * 256;
   const int64_t extra = (bwd_aux_count(aux) + per_row - 1) / per_row;
-  const dim3 grid((unsigned)gx, (unsigned)(cols / kBlock + extra));
-  hipLaunchKernelGGL(k_dequant_t, grid, dim3(256), 0, st, packed, qscale, scale2, offset, rows,
+  const dim3 grid((unsigned)gx, (unsigned)((cols + DQT_K - 1) / DQT_K + extra));
+  hipLaunchKernelGGL(k_dequant_t, grid, dim3(256), lds, st, packed, qscale, scale2, offset, rows,
                      cols, out, ldt, aux);
   return hipGetLastError();
 }

@@ -97,6 +97,8 @@ def test_tiny_config(qn):
     (1032, 320, 130, 64),   # rank 64: four 16-wide adapter steps
     (7680, 256, 2085, 8),   # forward through the bf16 copy + dense GEMM, ragged M
     (3848, 3840, 4100, 5),  # dense forward and dX: ragged M, N % 32 == 8, rank 5
+    (2056, 3904, 4100, 20), # dense dX: K % 256 == 64 (a partial column group in the
+                            # transposed dequantization), rank 20 (B^T made first)
 ])
 def test_ragged_shapes(qn, rows, cols, M, r):
     c = Case(rows, cols, M, r, 2.0 * r, seed=rows + cols + M)
@@ -217,6 +219,27 @@ def test_empty_batch(qn):
     dX, dA, dB = qn.qlora_linear_bwd(st, x, G, A, B, c.alpha, None)
     torch.cuda.synchronize()
     assert dX.shape == (0, 128) and not dA.any() and not dB.any()
+
+
+@pytest.mark.parametrize("rows,cols,M,r", [
+    (1024, 1024, 4100, 20),  # transposed products: 96-row slices (3-step tail), two rank groups
+    (2056, 1024, 4100, 17),  # 160-row slices (5 steps: tail after the unrolled loop)
+])
+def test_adapter_grads_repeat_identical(qn, rows, cols, M, r):
+    """dA and dB of repeated backward calls are bit-identical and match the
+    oracle (slice tails of the transposed products with more than 16 ranks)."""
+    c = Case(rows, cols, M, r, 2.0 * r, seed=rows + cols + r)
+    say(f"[linear] adapter-grad repeats: rows={rows} cols={cols} M={M} r={r}")
+    st, x, A, B, G = c.dev(qn)
+    _, u = qn.qlora_linear_fwd(st, x, A, B, c.alpha)
+    outs = [qn.qlora_linear_bwd(st, x, G, A, B, c.alpha, u) for _ in range(3)]
+    torch.cuda.synchronize()
+    for dX, dA, dB in outs[1:]:
+        assert torch.equal(dA, outs[0][1]) and torch.equal(dB, outs[0][2])
+    dA_ref, dB_ref = oracle.adapter_grads(c.x, c.G, c.A, c.B, c.s)
+    ea, eb = rel_err(outs[0][1].cpu().numpy(), dA_ref), rel_err(outs[0][2].cpu().numpy(), dB_ref)
+    say(f"  rel err dA={ea:.2e} dB={eb:.2e}")
+    assert ea <= REL_TOL and eb <= REL_TOL
 
 
 def test_deterministic_repeat(qn):
