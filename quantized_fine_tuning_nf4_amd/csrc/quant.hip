@@ -92,12 +92,15 @@ __device__ __forceinline__ uint32_t nf4_code(float w, double s64, double rs,
 // for whole groups (every load unconditional, all 16 in flight at once) and
 // for the tail group (element-wise bounds); the kernel branches once, around
 // the whole body, so no loaded value meets a branch join (which would make
-// the compiler wait for every load there).
+// the compiler wait for every load there).  In whole groups the codes gather
+// in LDS and leave as 16-byte pieces, and the 256 block scales leave in one
+// coalesced store at the end (2-byte and 4-lane stores per step cost more
+// than the code search).
 template <bool FULL>
 __device__ __forceinline__ void quant_group(const float* __restrict__ W, int64_t n, int64_t nb,
                                             uint8_t* __restrict__ packed,
                                             float* __restrict__ absmax, double* tree,
-                                            const uint64_t* lut, int* s_bad) {
+                                            const uint64_t* lut, int* s_bad, uint16_t* codes) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int64_t g = blockIdx.x;
   const int64_t e_wave = (g * kGroup + wave * 64) * kBlock;
@@ -128,17 +131,32 @@ __device__ __forceinline__ void quant_group(const float* __restrict__ W, int64_t
     const int slot = wave * 64 + 4 * j + (lane >> 4);
     const int64_t b = g * kGroup + slot;
     if ((lane & 15) == 0) {
-      if (FULL || b < nb) absmax[b] = s;
+      if (!FULL && b < nb) absmax[b] = s;
       tree[slot] = (FULL || b < nb) ? (double)s : 0.0;
     }
     const double s64 = s > 0.f ? (double)s : 1.0;
     const double rs = __builtin_amdgcn_rcp(s64);
     const uint32_t c0 = nf4_code(v[j].x, s64, rs, lc), c1 = nf4_code(v[j].y, s64, rs, lc);
     const uint32_t c2 = nf4_code(v[j].z, s64, rs, lc), c3 = nf4_code(v[j].w, s64, rs, lc);
-    if (FULL || b < nb) {
+    const uint16_t c16 = (uint16_t)(c0 | (c1 << 4) | (c2 << 8) | (c3 << 12));
+    if (FULL) {
+      codes[(wave * 16 + j) * 64 + lane] = c16;
+    } else if (b < nb) {
       const int64_t e = e_wave + j * 256 + lane * 4;
-      *reinterpret_cast<uint16_t*>(packed + e / 2) =
-          (uint16_t)(c0 | (c1 << 4) | (c2 << 8) | (c3 << 12));
+      *reinterpret_cast<uint16_t*>(packed + e / 2) = c16;
+    }
+  }
+  if (FULL) {
+    // the wave's 16 x 128 contiguous code bytes leave as 16-byte pieces (its
+    // own LDS writes above are visible to its reads: a wave's LDS accesses
+    // execute in order)
+    const uint8_t* cw = reinterpret_cast<const uint8_t*>(codes + wave * 16 * 64);
+    uint8_t* dst = packed + e_wave / 2;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int c = lane + 64 * h;  // 16-byte piece: iteration c / 8, offset 16 (c % 8)
+      *reinterpret_cast<u32x4*>(dst + (c >> 3) * 128 + 16 * (c & 7)) =
+          *reinterpret_cast<const u32x4*>(cw + 16 * c);
     }
   }
 }
@@ -148,6 +166,7 @@ __global__ __launch_bounds__(256) void k_quant_blocks(
     float* __restrict__ absmax, double* __restrict__ part, int* __restrict__ bad) {
   __shared__ uint64_t lut[65 * 16];
   __shared__ double tree[kGroup];
+  __shared__ __attribute__((aligned(16))) uint16_t codes[4 * 16 * 64];
   __shared__ int s_bad;
   const int tid = threadIdx.x;
   if (tid < 65) {
@@ -157,15 +176,19 @@ __global__ __launch_bounds__(256) void k_quant_blocks(
   }
   if (tid == 0) s_bad = 0;
   const int64_t g = blockIdx.x;
-  if ((g + 1) * (int64_t)(kGroup * kBlock) <= n)
-    quant_group<true>(W, n, nb, packed, absmax, tree, lut, &s_bad);
+  const bool full = (g + 1) * (int64_t)(kGroup * kBlock) <= n;
+  if (full)
+    quant_group<true>(W, n, nb, packed, absmax, tree, lut, &s_bad, codes);
   else
-    quant_group<false>(W, n, nb, packed, absmax, tree, lut, &s_bad);
-  __syncthreads();
+    quant_group<false>(W, n, nb, packed, absmax, tree, lut, &s_bad, codes);
+  // (LDS-only barriers from here: the code stores stay in flight)
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  // a whole group's 256 block scales leave in one coalesced store
+  if (full) absmax[g * kGroup + tid] = (float)tree[tid];
   // fixed-order fp64 partial sum of this group's 256 scale slots
   for (int h = kGroup / 2; h >= 1; h >>= 1) {
     if (tid < h) tree[tid] += tree[tid + h];
-    __syncthreads();
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   }
   if (tid == 0) {
     part[g] = tree[0];
@@ -215,15 +238,77 @@ __global__ __launch_bounds__(1024) void k_quant_mean(double* __restrict__ part, 
   }
 }
 
-// Pass 3.  One workgroup per group: d_b, C2, s2 and the E4M3 codes.
+// Pass 3.  One workgroup per group: d_b, C2, s2 and the E4M3 codes.  With
+// FUSED, passes 2 and 3 share the launch: every workgroup first forms the
+// same mu itself (the stride-halving tree over the group partials zero-padded
+// to len: levels of 256 entries and more inside each thread, then LDS, then
+// lane shuffles, with the same additions in the same order as
+// pass 2; up to 2048 groups), and workgroup 0 writes offset and the
+// non-finite flag.
+template <bool FUSED>
 __global__ __launch_bounds__(256) void k_quant_dq(const float* __restrict__ absmax, int64_t nb,
-                                                  const float* __restrict__ offset,
+                                                  float* __restrict__ offset,
                                                   uint8_t* __restrict__ qscale,
-                                                  float* __restrict__ scale2) {
+                                                  float* __restrict__ scale2,
+                                                  const double* __restrict__ part, int64_t ng,
+                                                  int64_t len, const int* __restrict__ bad,
+                                                  int* __restrict__ flag) {
   __shared__ float red[4];
+  __shared__ double t[128];
+  __shared__ int s_any;
   const int tid = threadIdx.x;
+  float mu;
+  if constexpr (FUSED) {
+    // thread tid holds entries tid + 256 q of the LDS stage (zero past it);
+    // levels h >= 256 pair entries of one thread, h = 128 and 64 go through
+    // LDS, h <= 32 through lane shuffles: t[j] + t[j + h] at every level,
+    // as in pass 2
+    // len <= 2048 here: one partial per stage entry
+    const int64_t active = len;
+    double v[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int64_t j = tid + 256 * q;
+      v[q] = 0.0;
+      if (256 * q < active && j < ng) v[q] = part[j];
+    }
+    int64_t h = active / 2;
+    for (; h >= 256; h /= 2) {
+      const int64_t qh = h / 256;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (q < qh) v[q] += v[q + qh];
+    }
+    double x = v[0];
+    for (; h >= 64; h /= 2) {
+      if (tid >= h && tid < 2 * h) t[tid - h] = x;
+      __syncthreads();
+      if (tid < h) x += t[tid];
+      __syncthreads();
+    }
+    for (; h >= 1; h /= 2) {
+      const double y = __shfl_down(x, (unsigned)h);
+      if (tid < h) x += y;
+    }
+    if (tid == 0) t[0] = x;
+    __syncthreads();
+    mu = (float)(t[0] / (double)nb);
+    if (blockIdx.x == 0) {  // workgroup 0: offset and the non-finite flag
+      int any = 0;
+      for (int64_t j = tid; j < ng; j += 256) any |= bad[j];
+      if (tid == 0) s_any = 0;
+      __syncthreads();
+      if (any) s_any = 1;
+      __syncthreads();
+      if (tid == 0) {
+        *offset = mu;
+        *flag = s_any;
+      }
+    }
+  } else {
+    mu = *offset;
+  }
   const int64_t b = (int64_t)blockIdx.x * kGroup + tid;
-  const float mu = *offset;
   const float d = (b < nb) ? absmax[b] - mu : 0.f;
   float a = __builtin_fabsf(d);
   for (int o = 32; o >= 1; o >>= 1) a = fmaxf(a, __shfl_xor(a, o));
@@ -243,10 +328,16 @@ hipError_t launch_quantize(const float* W, int64_t n, uint8_t* packed, uint8_t* 
   const int64_t ng = (nb + kGroup - 1) / kGroup;
   hipLaunchKernelGGL(k_quant_blocks, dim3((unsigned)ng), dim3(256), 0, st, W, n, nb, packed,
                      ws_absmax, ws_part, ws_bad);
-  hipLaunchKernelGGL(k_quant_mean, dim3(1), dim3(1024), 0, st, ws_part, ng, part_len, nb,
-                     offset, ws_bad, flag);
-  hipLaunchKernelGGL(k_quant_dq, dim3((unsigned)ng), dim3(256), 0, st, ws_absmax, nb, offset,
-                     qscale, scale2);
+  if (part_len <= 2048) {
+    // the mean inside the scale pass: one launch fewer
+    hipLaunchKernelGGL(k_quant_dq<true>, dim3((unsigned)ng), dim3(256), 0, st, ws_absmax, nb,
+                       offset, qscale, scale2, ws_part, ng, part_len, ws_bad, flag);
+  } else {
+    hipLaunchKernelGGL(k_quant_mean, dim3(1), dim3(1024), 0, st, ws_part, ng, part_len, nb,
+                       offset, ws_bad, flag);
+    hipLaunchKernelGGL(k_quant_dq<false>, dim3((unsigned)ng), dim3(256), 0, st, ws_absmax, nb,
+                       offset, qscale, scale2, ws_part, ng, part_len, ws_bad, flag);
+  }
   return hipGetLastError();
 }
 
