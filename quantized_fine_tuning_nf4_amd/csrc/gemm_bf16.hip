@@ -211,7 +211,11 @@ __global__ __launch_bounds__(T, 1) void k_gemm_nt(
     half(S0{}, S1{}, st);
   }
   // every wave's loads have landed and all reads are done before the stages
-  // are reused for the output staging below
+  // are reused for the output staging below; the last products' results are
+  // complete before any instruction the compiler places here (a register
+  // spill, say) reads an accumulator: it cannot see that the asm MFMAs write
+  // them
+  asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");
   wait_all_loads();
   barrier_lds();
 

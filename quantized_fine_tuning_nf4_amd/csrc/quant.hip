@@ -456,29 +456,32 @@ hipError_t launch_dequant(const uint8_t* packed, const uint8_t* qscale, const fl
 
 // Transposed dequantization for the dX product: out[k][n] (bf16, row length
 // ldt >= rows, ldt % 8 == 0) = Qhat(W)[n][k], zero for rows <= n < ldt.
-// Workgroup (bx, kq): rows n0 = 128 bx .. +127, columns 256 kq .. +255 (four
-// blocks, so every row's 128 bytes of codes come in whole; cols % 64 == 0,
-// columns past cols are not stored); wave q takes
-// block 4 kq + q, lane l rows n0 + 2l and n0 + 2l + 1, whose two values per
-// column go to the LDS tile [k][n] as one word; the tile leaves as 256-byte
-// row pieces.  Extra rows of workgroups (when asked) run the small jobs of the
-// same backward, which saves their launches.
-constexpr int DQT_N = 128, DQT_K = 256, DQT_PITCH = DQT_N * 2 + 16;
+// One-dimensional grid: the first `aux_wgs` workgroups run the small jobs of
+// the same backward (four elements per thread), so they share the machine
+// with the dequantization instead of trailing it; then one workgroup per
+// tile of 128 rows x 128 columns (two blocks; cols % 64 == 0, columns past
+// cols are not stored): wave q takes half q & 1 (32 columns) of block q >> 1,
+// lane l rows n0 + 2l and n0 + 2l + 1, whose two values per column go to the
+// LDS tile [k][n] as one word; the tile leaves as 256-byte row pieces.
+constexpr int DQT_N = 128, DQT_K = 128, DQT_PITCH = DQT_N * 2 + 16;
 __global__ __launch_bounds__(256) void k_dequant_t(const uint8_t* __restrict__ packed,
                                                    const uint8_t* __restrict__ qscale,
                                                    const float* __restrict__ scale2,
                                                    const float* __restrict__ offset, int64_t rows,
                                                    int64_t cols, uint16_t* __restrict__ out,
-                                                   int64_t ldt, BwdAux aux) {
+                                                   int64_t ldt, BwdAux aux, int aux_wgs,
+                                                   int gx) {
   __shared__ float lut[16];
-  extern __shared__ __attribute__((aligned(16))) uint8_t tile[];  // [DQT_K][DQT_PITCH]
+  __shared__ __attribute__((aligned(16))) uint8_t tile[DQT_K * DQT_PITCH];
   const int t = threadIdx.x;
-  const int64_t kq_count = (cols + DQT_K - 1) / DQT_K;
-  if ((int64_t)blockIdx.y >= kq_count) {
-    // the extra rows of workgroups: the small backward jobs
-    const int64_t i =
-        (((int64_t)blockIdx.y - kq_count) * gridDim.x + blockIdx.x) * blockDim.x + t;
-    if (i < bwd_aux_count(aux)) bwd_aux_at(aux, i);
+  if ((int)blockIdx.x < aux_wgs) {
+    const int64_t count = bwd_aux_count(aux), q4 = (count + 3) / 4;
+    const int64_t i0 = (int64_t)blockIdx.x * 256 + t;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int64_t i = i0 + q4 * k;
+      if (i0 < q4 && i < count) bwd_aux_at(aux, i);
+    }
     return;
   }
   if (t < 16) {  // from immediates: no load ahead of the code loads
@@ -487,45 +490,45 @@ __global__ __launch_bounds__(256) void k_dequant_t(const uint8_t* __restrict__ p
     for (int k = 1; k < 16; ++k) v = t == k ? kNF4Bits[k] : v;
     lut[t] = as_f32(v);
   }
+  const int d = (int)blockIdx.x - aux_wgs;
+  const int64_t kq = d / gx;
+  const int64_t n0 = (int64_t)(d - kq * gx) * DQT_N;
   const int q = t >> 6, l = t & 63;
-  const int64_t n0 = (int64_t)blockIdx.x * DQT_N;
   const int64_t kblocks = cols / kBlock;
-  // a block past the last one (cols % 256 != 0) repeats the last block; its
+  // a block past the last one (cols % 128 != 0) repeats the last block; its
   // columns are not stored
-  const int64_t kb = min((int64_t)blockIdx.y * 4 + q, kblocks - 1);
+  const int64_t kb = min(kq * 2 + (q >> 1), kblocks - 1);
+  const int kh = q & 1;
   const int64_t na = n0 + 2 * l, nb = na + 1;
   const int64_t ra = min(na, rows - 1), rb = min(nb, rows - 1);
   // unconditional, clamped loads (no wait at a branch join)
-  const u32x4* pa = reinterpret_cast<const u32x4*>(packed + ra * (cols / 2) + kb * 32);
-  const u32x4* pb = reinterpret_cast<const u32x4*>(packed + rb * (cols / 2) + kb * 32);
-  const u32x4 a0 = pa[0], a1 = pa[1], b0 = pb[0], b1 = pb[1];
+  const u32x4 a = *reinterpret_cast<const u32x4*>(packed + ra * (cols / 2) + kb * 32 + 16 * kh);
+  const u32x4 b = *reinterpret_cast<const u32x4*>(packed + rb * (cols / 2) + kb * 32 + 16 * kh);
   const int64_t ba = ra * kblocks + kb, bb = rb * kblocks + kb;
   const uint32_t qa = qscale[ba], qb = qscale[bb];
   const float s2a = scale2[ba / kGroup], s2b = scale2[bb / kGroup], mu = *offset;
   const float sa = na < rows ? dq_scale(qa, s2a, mu) : 0.f;
   const float sb = nb < rows ? dq_scale(qb, s2b, mu) : 0.f;
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // lut ready
-  const uint32_t wa[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-  const uint32_t wb[8] = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
-  uint8_t* trow = tile + (int64_t)(64 * q) * DQT_PITCH + 4 * l;
+  uint8_t* trow = tile + (int64_t)(64 * (q >> 1) + 32 * kh) * DQT_PITCH + 4 * l;
 #pragma unroll
-  for (int e = 0; e < 64; ++e) {
-    const uint32_t ca = (wa[e >> 3] >> (4 * (e & 7))) & 15u;
-    const uint32_t cb = (wb[e >> 3] >> (4 * (e & 7))) & 15u;
+  for (int e = 0; e < 32; ++e) {
+    const uint32_t ca = (a[e >> 3] >> (4 * (e & 7))) & 15u;
+    const uint32_t cb = (b[e >> 3] >> (4 * (e & 7))) & 15u;
     uint32_t v = pack_bf16x2(lut[ca] * sa, lut[cb] * sb);
     if (na >= rows) v &= 0xffff0000u;  // +0 past the last row
     if (nb >= rows) v &= 0x0000ffffu;
     *reinterpret_cast<uint32_t*>(trow + e * DQT_PITCH) = v;
   }
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  // 256 rows of 256 bytes: pass h, thread t -> row 16h + t/16, chunk t%16
+  // 128 rows of 256 bytes: pass h, thread t -> row 16h + t/16, chunk t%16
   const int c = t & 15;
   const int64_t col = n0 + 8 * c;
 #pragma unroll
-  for (int h = 0; h < 16; ++h) {
+  for (int h = 0; h < 8; ++h) {
     const int k = 16 * h + (t >> 4);
     const u32x4 v = *reinterpret_cast<const u32x4*>(tile + k * DQT_PITCH + 16 * c);
-    const int64_t kk = (int64_t)blockIdx.y * DQT_K + k;
+    const int64_t kk = kq * DQT_K + k;
     if (col < ldt && kk < cols) *reinterpret_cast<u32x4*>(out + kk * ldt + col) = v;
   }
 }
@@ -533,16 +536,10 @@ __global__ __launch_bounds__(256) void k_dequant_t(const uint8_t* __restrict__ p
 hipError_t launch_dequant_t(const uint8_t* packed, const uint8_t* qscale, const float* scale2,
                             const float* offset, int64_t rows, int64_t cols, uint16_t* out,
                             int64_t ldt, const BwdAux& aux, hipStream_t st) {
-  const size_t lds = (size_t)DQT_K * DQT_PITCH;
-  static const hipError_t attr =
-      hipFuncSetAttribute(reinterpret_cast<const void*>(k_dequant_t),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (attr != hipSuccess) return attr;
-  const int64_t gx = (ldt + DQT_N - 1) / DQT_N, per_row = gx * 256;
-  const int64_t extra = (bwd_aux_count(aux) + per_row - 1) / per_row;
-  const dim3 grid((unsigned)gx, (unsigned)((cols + DQT_K - 1) / DQT_K + extra));
-  hipLaunchKernelGGL(k_dequant_t, grid, dim3(256), lds, st, packed, qscale, scale2, offset, rows,
-                     cols, out, ldt, aux);
+  const int64_t gx = (ldt + DQT_N - 1) / DQT_N, gk = (cols + DQT_K - 1) / DQT_K;
+  const int64_t aux_wgs = ((bwd_aux_count(aux) + 3) / 4 + 255) / 256;
+  hipLaunchKernelGGL(k_dequant_t, dim3((unsigned)(aux_wgs + gx * gk)), dim3(256), 0, st, packed,
+                     qscale, scale2, offset, rows, cols, out, ldt, aux, (int)aux_wgs, (int)gx);
   return hipGetLastError();
 }
 
