@@ -101,13 +101,15 @@ struct FwdWs {
   DecodeTiles dt;  // one-kernel decode tiling (dt.rgt == 0: not used)
   float* tpart;    // [dt.S, M, rows] its partial sums
   float* tupart;   // [dt.bands, dt.S, 256] its partials of u
+  int dbr;         // rows per band of the whole-row decode kernel (0: not used)
 };
 
 FwdWs carve_fwd(Carver& c, int64_t M, int64_t rows, int64_t cols, int r, bool need_u) {
   FwdWs f;
-  f.dt = rows > 0 ? decode_tiles(M, rows, cols, r) : DecodeTiles{0, 0, 0};
-  f.dS = rows > 0 && f.dt.rgt == 0 ? decode_slices(M, rows, cols) : 0;
-  const bool decode = f.dt.rgt > 0 || f.dS > 0;  // u comes from the decode kernels
+  f.dbr = rows > 0 ? decode_rows_band(M, rows, cols, r) : 0;
+  f.dt = rows > 0 && f.dbr == 0 ? decode_tiles(M, rows, cols, r) : DecodeTiles{0, 0, 0};
+  f.dS = rows > 0 && f.dbr == 0 && f.dt.rgt == 0 ? decode_slices(M, rows, cols) : 0;
+  const bool decode = f.dbr > 0 || f.dt.rgt > 0 || f.dS > 0;  // u from the decode kernels
   f.S = thin_nt_slices(M, cols);
   f.u = need_u ? c.take<float>((size_t)M * r) : nullptr;
   f.upart = f.S > 1 && !decode ? c.take<float>((size_t)f.S * M * r) : nullptr;
@@ -261,7 +263,9 @@ qn_status qlora_linear_fwd(const qn_nf4dq* w, const uint16_t* x, int64_t M, cons
   hipStream_t st = static_cast<hipStream_t>(stream);
   const float scale = alpha / (float)r;
   const int64_t N = w->rows, K = w->cols;
-  if (f.dt.rgt > 0)  // decode-sized batch, one kernel
+  if (f.dbr > 0)  // decode-sized batch, whole rows per workgroup
+    return from_hip(launch_decode_rows(to_state(w), x, M, A, B, r, scale, y, u, f.dbr, st));
+  if (f.dt.rgt > 0)  // decode-sized batch, one kernel over column slices
     return from_hip(launch_decode_tile(to_state(w), x, M, A, B, r, scale, y, u, f.dt, f.tpart,
                                        f.tupart, st));
   if (f.dpart)  // decode-sized batch: u and the product in two kernels

@@ -543,6 +543,260 @@ __global__ __launch_bounds__(TT, 1) void k_decode_tile(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Whole-row decode forward (cols = 1024 PW, M <= 16, r <= 16): workgroup b
+// owns rows BR b .. BR b + BR - 1 (BR <= 64, at most four 16-row groups) and
+// every column, so each output is finished inside one workgroup: no partial
+// sums leave it and no workgroup waits for another.  Every workgroup forms
+// u = X A^T itself (A is r x cols bf16, read from L2 once the first
+// workgroups of an XCD have brought it in).  Eight waves (256 registers per
+// lane: the X and A fragments of a wave's columns stay in registers):
+//   - wave w owns block pairs w + 8 i (i < PW); a unit is one 16-row group
+//     of one of its pairs (16 rows x 64 B of codes), moved into the wave's
+//     LDS ring by one direct-to-LDS load in the layout of the sliced kernel
+//     above (same lane mapping, table and MFMA form);
+//   - order of issue, which is the order of completion: the band's scale
+//     codes, second-level scales and B rows (plain loads, written to LDS
+//     before the first barrier), X fragments, the first RS code units, A
+//     fragments; the remaining units refill the ring slot of the unit
+//     consumed RS steps earlier.  The wait for unit q counts the operations
+//     issued after it, a compile-time number;
+//   - after the main loop the waves' sums meet in LDS (sum over waves in wave
+//     order), u likewise; thread (m, row) adds s sum_j u[m][j] B[row][j] and
+//     stores bf16 y.  Workgroup 0 writes u.
+constexpr int RW_RG = 4;           // row groups per band
+constexpr int RW_BR = 16 * RW_RG;  // rows per band, at most
+constexpr int RW_RING_KB = 80;     // ring: 80 units of 1 KB, split among the waves
+constexpr int RW_TAB = 0, RW_RING = 65536, RW_QS = RW_RING + RW_RING_KB * UB;
+constexpr int RW_S2 = RW_QS + RW_BR * 64, RW_B = RW_S2 + 64 * 4, RW_E4 = RW_B + RW_BR * 16 * 2;
+constexpr int RW_TOTAL = RW_E4 + 256 * 4;
+static_assert(RW_TOTAL <= 160 * 1024, "LDS");
+static_assert(16 * RW_RG * 4 * 64 * 4 <= RW_RING, "wave sums overlap the ring");
+
+// operations issued after unit q of NU when it is awaited: RS units go out
+// first, then NA other loads; unit RS + k is issued after unit k is read
+template <int NU, int RS, int NA>
+constexpr int rw_after(int q) {
+  return q < RS ? (RS - 1 - q) + NA + (q < NU - RS ? q : (NU - RS > 0 ? NU - RS : 0))
+                : ((q - 1 < NU - RS - 1 ? q - 1 : NU - RS - 1) - q + RS);
+}
+
+// s_waitcnt vmcnt(n) for a count known after unrolling (0 past 39)
+__device__ __forceinline__ void wait_vm_n(int n) {
+  switch (n) {
+#define QN_W1(k) \
+  case k:        \
+    wait_vm<k>(); \
+    break;
+#define QN_W10(t) QN_W1(t##0) QN_W1(t##1) QN_W1(t##2) QN_W1(t##3) QN_W1(t##4) \
+                  QN_W1(t##5) QN_W1(t##6) QN_W1(t##7) QN_W1(t##8) QN_W1(t##9)
+    QN_W1(1) QN_W1(2) QN_W1(3) QN_W1(4) QN_W1(5) QN_W1(6) QN_W1(7) QN_W1(8) QN_W1(9)
+    QN_W10(1) QN_W10(2) QN_W10(3)
+#undef QN_W10
+#undef QN_W1
+    default:
+      wait_vm<0>();
+  }
+}
+
+template <int PW, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void k_decode_rows(
+    const uint8_t* __restrict__ packed, const uint8_t* __restrict__ qscale,
+    const float* __restrict__ scale2, const float* __restrict__ offset,
+    const uint16_t* __restrict__ X, int64_t M, int64_t N, const uint16_t* __restrict__ Aad,
+    const uint16_t* __restrict__ Bad, int r, float s, int br, uint16_t* __restrict__ Y,
+    float* __restrict__ u_out) {
+  constexpr int RW_T = 64 * NW, RW_W = NW;
+  constexpr int64_t K = 128 * NW * PW, kb = K / 64;
+  constexpr int NU = RW_RG * PW, RS = NU < RW_RING_KB / NW ? NU : RW_RING_KB / NW, NA = 4 * PW;
+  constexpr int PT = (RW_BR * 16 + RW_T - 1) / RW_T;  // small-load elements per thread
+  static_assert(rw_after<NU, RS, NA>(0) <= 39, "wait counts");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[RW_TOTAL];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, g4 = lane >> 4;
+  const int64_t n0 = (int64_t)blockIdx.x * br;
+  const int nrows = (int)min((int64_t)br, N - n0);
+
+  // ---- the band's scale codes (nrows * kb bytes), second-level scales and
+  // B rows: PT dwords / PT elements per thread
+  constexpr int QW = RW_BR * (int)kb / 4;  // dwords of scale codes, at most
+  static_assert(QW <= PT * RW_T && RW_BR * 16 <= PT * RW_T, "PT per thread");
+  const int64_t g0 = n0 * kb / kGroup;
+  const int ns2 = (int)(((n0 + nrows) * kb - 1) / kGroup - g0 + 1);
+  const int nq = nrows * (int)kb / 4, nb = nrows * r;
+  uint32_t qv[PT];
+  uint16_t bv[PT];
+#pragma unroll
+  for (int k = 0; k < PT; ++k) {
+    const int e = tid + RW_T * k;
+    qv[k] = e < nq ? reinterpret_cast<const uint32_t*>(qscale + n0 * kb)[e] : 0u;
+    bv[k] = e < nb ? Bad[n0 * r + e] : (uint16_t)0;
+  }
+  const float s2v = tid < ns2 ? scale2[g0 + tid] : 0.f;
+  // level of the low nibble tid / 32 % 16 = 2 (wave % 8) + bit 5 of the
+  // lane: a wave-uniform index (scalar loads, never queued behind the code
+  // stream) and a select
+  const int lsel = 2 * (wave & 7);
+  const float lo_level = as_f32((lane & 32) ? kNF4Bits[lsel + 1] : kNF4Bits[lsel]);
+
+  // ---- X fragments of the wave's pairs (rows past M read the last row)
+  const int koff1 = 32 * (g4 & 1) + ((g4 >> 1) ? 16 : 8);
+  const int koff2 = 32 * (g4 & 1) + ((g4 >> 1) ? 24 : 0);
+  const uint16_t* xrow = X + (int64_t)min(l16, (int)M - 1) * K + 128 * wave;
+  const uint16_t* arow = Aad + (int64_t)min(l16, r - 1) * K + 128 * wave;
+  constexpr int PS = 128 * NW;  // columns between a wave's pairs
+  bf16x8 xf[PW][2][2], af[PW][2][2];
+#pragma unroll
+  for (int i = 0; i < PW; ++i)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      xf[i][b][0] = as_bf16x8(*reinterpret_cast<const u32x4*>(xrow + PS * i + 64 * b + koff1));
+      xf[i][b][1] = as_bf16x8(*reinterpret_cast<const u32x4*>(xrow + PS * i + 64 * b + koff2));
+    }
+
+  // ---- the code stream: unit q = (row group q / PW, pair q % PW); rows past
+  // the band read zeros without touching memory
+  const int drow = lane >> 2;
+  const uint32_t voff = (uint32_t)drow * (uint32_t)(K / 2) + 64u * (uint32_t)wave +
+                        16u * (uint32_t)((lane & 3) ^ ((drow >> 1) & 3));
+  uint8_t* ring = smem + RW_RING + wave * RS * UB;
+  auto dma_unit = [&](int q) {
+    const int rg = q / PW, i = q % PW;
+    const int64_t left = max((int64_t)0, (int64_t)nrows - 16 * rg);
+    const rsrc_t rs = make_rs(packed + (n0 + min((int64_t)16 * rg, (int64_t)nrows)) * (K / 2),
+                              (uint32_t)(left * (K / 2)));
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rs, (__attribute__((address_space(3))) void*)(ring + (q % RS) * UB), 16,
+        voff + 64u * NW * (uint32_t)i, 0, 0, 0);
+  };
+#pragma unroll
+  for (int q = 0; q < RS; ++q) dma_unit(q);
+  // the A fragments go out after the first units and before any wait for
+  // them: the wait counts below rely on that order
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+#pragma unroll
+  for (int i = 0; i < PW; ++i)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      af[i][b][0] = as_bf16x8(*reinterpret_cast<const u32x4*>(arow + PS * i + 64 * b + koff1));
+      af[i][b][1] = as_bf16x8(*reinterpret_cast<const u32x4*>(arow + PS * i + 64 * b + koff2));
+    }
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+
+  // ---- table (levels as immediates; entry e of copy c at byte 256 e + 4 c),
+  // scales and B into LDS
+  {
+    // thread tid: copy tid % 32, low nibble tid / 32 % 16, the high nibbles
+    // hi with hi % HS == tid / 512 (HS = threads / 512; wave-uniform)
+    constexpr int HS = RW_T / 512;
+    static_assert(HS >= 1 && RW_T % 512 == 0, "table fill");
+    const int hsel = __builtin_amdgcn_readfirstlane(tid >> 9);
+    uint32_t* trow = reinterpret_cast<uint32_t*>(smem + RW_TAB) + ((tid >> 5) & 15) * 64 + (tid & 31);
+#pragma unroll
+    for (int hi = 0; hi < 16; ++hi)
+      if (HS == 1 || hi % HS == hsel) trow[hi * 16 * 64] = pack_bf16x2(lo_level, as_f32(kNF4Bits[hi]));
+  }
+#pragma unroll
+  for (int k = 0; k < PT; ++k) {
+    reinterpret_cast<uint32_t*>(smem + RW_QS)[tid + RW_T * k] = qv[k];
+    reinterpret_cast<uint16_t*>(smem + RW_B)[tid + RW_T * k] = bv[k];
+  }
+  if (tid < 64) reinterpret_cast<float*>(smem + RW_S2)[tid] = s2v;
+  // scale code -> value (a table keeps the main loop free of branches)
+  if (tid < 256) reinterpret_cast<float*>(smem + RW_E4)[tid] = e4m3_to_f32(tid);
+  wait_vm_n(RS + NA);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+
+  const uint8_t* tab = smem + RW_TAB;
+  const uint32_t tbase = 4u * (lane & 31);
+  const float mu = *offset;
+  const int rd = 16 * (4 * l16 + (g4 ^ ((l16 >> 1) & 3)));
+  f32x4 acc[RW_RG];
+#pragma unroll
+  for (int g = 0; g < RW_RG; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int q = 0; q < NU; ++q) {
+    const int g = q / PW, i = q % PW;
+    wait_vm_n(rw_after<NU, RS, NA>(q));  // unit q has landed
+    const u32x4 c = *reinterpret_cast<const u32x4*>(ring + (q % RS) * UB + rd);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (q + RS < NU) dma_unit(q + RS);  // into the slot just read
+    // block scales of row l16 of group g for the pair's two blocks (rows
+    // past the band use its last row: finite, never stored)
+    const int row = min(16 * g + l16, nrows - 1);
+    const int blk = 2 * (wave + NW * i);
+    const uint32_t qs = *reinterpret_cast<const uint16_t*>(smem + RW_QS + row * kb + blk);
+    const float s2 =
+        reinterpret_cast<const float*>(smem + RW_S2)[((n0 + row) * kb + blk) / kGroup - g0];
+    const float* e4 = reinterpret_cast<const float*>(smem + RW_E4);
+    const float sa = __builtin_fmaf(e4[qs & 0xffu], s2, mu);  // = dq_scale
+    const float sb = __builtin_fmaf(e4[(qs >> 8) & 0xffu], s2, mu);
+    const auto h = __builtin_amdgcn_permlane32_swap(c[1], c[2], false, false);
+    const auto l = __builtin_amdgcn_permlane32_swap(c[0], c[3], false, false);
+    f32x4 t = mfma16(xf[i][0][0], tab_pairs4(tab, h[0], tbase), f32x4{0.f, 0.f, 0.f, 0.f});
+    t = mfma16(xf[i][0][1], tab_pairs4(tab, l[0], tbase), t);
+    f32x4 t2 = mfma16(xf[i][1][0], tab_pairs4(tab, h[1], tbase), f32x4{0.f, 0.f, 0.f, 0.f});
+    t2 = mfma16(xf[i][1][1], tab_pairs4(tab, l[1], tbase), t2);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      acc[g][v] = __builtin_fmaf(sa, t[v], acc[g][v]);
+      acc[g][v] = __builtin_fmaf(sb, t2[v], acc[g][v]);
+    }
+    // one unit at a time: later units' table reads are not hoisted into this
+    // one (their registers would be live across it)
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  f32x4 uacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < PW; ++i)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      uacc = mfma16(xf[i][b][0], af[i][b][0], uacc);
+      uacc = mfma16(xf[i][b][1], af[i][b][1], uacc);
+    }
+
+  // ---- the waves' sums: lane (l16, g4) slot v holds row 16 g + l16,
+  // m = 4 g4 + v (and u[m][j = l16])
+  __syncthreads();  // every wave is done with the table and its ring
+  float* s_red = reinterpret_cast<float*>(smem + RW_TAB);   // [wave][g][v][lane]
+  float* s_ured = reinterpret_cast<float*>(smem + RW_RING); // [wave][v][lane]
+  float* s_u = s_ured + RW_W * 4 * 64;                       // [m][17]
+#pragma unroll
+  for (int g = 0; g < RW_RG; ++g)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) s_red[((wave * RW_RG + g) * 4 + v) * 64 + lane] = acc[g][v];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) s_ured[(wave * 4 + v) * 64 + lane] = uacc[v];
+  __syncthreads();
+  if (tid < 256) {
+    const int m = tid >> 4, j = tid & 15;
+    const int slot = ((m & 3) * 64) + j + 16 * (m >> 2);
+    float a = 0.f;
+#pragma unroll
+    for (int w = 0; w < RW_W; ++w) a += s_ured[w * 4 * 64 + slot];
+    s_u[m * 17 + j] = a;
+    if (blockIdx.x == 0 && m < M && j < r) u_out[m * r + j] = a;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < (1024 + RW_T - 1) / RW_T; ++k) {
+    const int o = tid + RW_T * k, om = o >> 6, orow = o & 63;
+    if (om < M && orow < nrows) {
+      const int slot = ((orow >> 4) * 4 + (om & 3)) * 64 + (orow & 15) + 16 * (om >> 2);
+      float a = 0.f;
+#pragma unroll
+      for (int w = 0; w < RW_W; ++w) a += s_red[w * RW_RG * 4 * 64 + slot];
+      const uint16_t* sb = reinterpret_cast<const uint16_t*>(smem + RW_B) + orow * r;
+      float lora = 0.f;
+      for (int j = 0; j < r; ++j) lora = __builtin_fmaf(s_u[om * 17 + j], bf16_lo(sb[j]), lora);
+      Y[om * N + n0 + orow] = (uint16_t)(pack_bf16x2(__builtin_fmaf(s, lora, a), 0.f) & 0xffffu);
+    }
+  }
+}
+
 }  // namespace
 
 int decode_slices(int64_t M, int64_t N, int64_t K) {
@@ -593,6 +847,44 @@ hipError_t launch_decode_tile(const WState& w, const uint16_t* X, int64_t M, con
   hipLaunchKernelGGL(k_decode_tile, dim3((unsigned)(t.bands * t.S)), dim3(TT), 0, st, w.packed,
                      w.qscale, w.scale2, w.offset, X, M, N, K, A, B, r, s, t.rgt, t.S, arrivals,
                      part, upart, Y, u_out);
+  return hipGetLastError();
+}
+
+constexpr int kRowsWaves = 16;  // waves per workgroup of k_decode_rows
+
+int decode_rows_band(int64_t M, int64_t N, int64_t K, int r) {
+  if (M < 1 || M > 16 || r < 1 || r > 16 || N < 1 || (K != 2048 && K != 4096)) return 0;
+  static int cus = [] {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 0;
+    return n;
+  }();
+  if (cus <= 0) return 0;
+  // one band per compute unit, a multiple of 8 rows; below 33 rows a band's
+  // share of A (r x cols, read by every workgroup) outweighs its codes, and
+  // the sliced kernel serves better
+  const int64_t br = 8 * ((N + 8 * (int64_t)cus - 1) / (8 * (int64_t)cus));
+  if (br <= 32) return 0;
+  return (int)min(br, (int64_t)RW_BR);
+}
+
+hipError_t launch_decode_rows(const WState& w, const uint16_t* X, int64_t M, const uint16_t* A,
+                              const uint16_t* B, int r, float s, uint16_t* Y, float* u_out,
+                              int br, hipStream_t st) {
+  const int64_t N = w.rows, K = w.cols;
+  if (br < 8 || br > RW_BR || br % 8 != 0 || M < 1 || M > 16 || r < 1 || r > 16 ||
+      (K != 2048 && K != 4096))
+    return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((N + br - 1) / br));
+  constexpr int NW = kRowsWaves;
+  if (K == 4096)
+    hipLaunchKernelGGL((k_decode_rows<4096 / (128 * NW), NW>), grid, dim3(64 * NW), 0, st,
+                       w.packed, w.qscale, w.scale2, w.offset, X, M, N, A, B, r, s, br, Y, u_out);
+  else
+    hipLaunchKernelGGL((k_decode_rows<2048 / (128 * NW), NW>), grid, dim3(64 * NW), 0, st,
+                       w.packed, w.qscale, w.scale2, w.offset, X, M, N, A, B, r, s, br, Y, u_out);
   return hipGetLastError();
 }
 

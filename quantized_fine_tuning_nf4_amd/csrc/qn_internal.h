@@ -188,6 +188,15 @@ hipError_t launch_decode_tile(const WState& w, const uint16_t* X, int64_t M, con
                               const uint16_t* B, int r, float s, uint16_t* Y, float* u_out,
                               const DecodeTiles& t, float* part, float* upart, hipStream_t st);
 
+// Whole-row decode forward (M <= 16, r <= 16, cols 2048 or 4096): bands of
+// `br` rows (a multiple of 8, at most 64), one workgroup each, every column;
+// writes Y and u_out, no workspace.  decode_rows_band gives br, or 0 when the
+// kernel does not apply (also when bands would be 32 rows or fewer).
+int decode_rows_band(int64_t M, int64_t rows, int64_t cols, int r);
+hipError_t launch_decode_rows(const WState& w, const uint16_t* X, int64_t M, const uint16_t* A,
+                              const uint16_t* B, int r, float s, uint16_t* Y, float* u_out,
+                              int br, hipStream_t st);
+
 // Y[M, N] bf16 = X[M, K] * W'[N, K]^T + s * u[M, r] * B[N, r]^T.
 hipError_t launch_qgemm_fwd(const WState& w, const uint16_t* X, int64_t M, const float* u,
                             const uint16_t* B, int r, float s, uint16_t* Y, hipStream_t st);

@@ -113,14 +113,21 @@ def test_decode_config(qn, M):
 
 
 @pytest.mark.parametrize("rows,cols,M,r", [
-    (4096, 14336, 3, 16),   # one-kernel decode: 14 slices, 240-row bands
-    (8200, 2048, 7, 5),     # one-kernel decode: 2 slices, 80-row bands, ragged last band
-    (16384, 4096, 16, 16),  # one-kernel decode: 4 slices, 256-row bands (the widest)
-    (9000, 4096, 2, 13),    # one-kernel decode: 9 row groups per band, rank 13
-    (1040, 3072, 1, 1),     # one-kernel decode: one row group per band, rank 1
-    (1000, 1024, 5, 7),     # one slice, partial row group, odd rank
+    (4096, 14336, 3, 16),   # sliced decode: 14 slices, 240-row bands
+    (8200, 2048, 7, 5),     # whole-row decode, 2048 columns: 40-row bands
+    (16384, 4096, 16, 16),  # whole-row decode: 64-row bands, M = 16
+    (9000, 4096, 2, 13),    # whole-row decode: 40-row bands (a partial third group), rank 13
+    (20000, 4096, 1, 16),   # whole-row decode: more bands than compute units, ragged last band
+    (10008, 4096, 4, 1),    # whole-row decode: an 8-row last band, rank 1
+    (9000, 2048, 16, 16),   # whole-row decode, 2048 columns, M = 16
+    (1040, 3072, 1, 1),     # sliced decode: one row group per band, rank 1
+    (1000, 1024, 5, 7),     # sliced decode: one slice, partial row group, odd rank
     (2048, 2048, 8, 32),    # rank 32: the two-kernel decode (u by extra workgroups)
     (264, 192, 9, 5),       # cols % 1024 != 0: the 32-row fused GEMM instead
+    (3000, 8192, 1, 16),    # sliced decode: one row, eight column slices
+    (776, 64, 1, 5),        # one row, one block per row, partial row group, rank 5 (fused GEMM)
+    (2056, 4096, 2, 16),    # sliced decode: 16-row bands (too few rows for whole-row bands)
+    (1000, 1536, 2, 3),     # two rows, 24 blocks per row (fused GEMM), rank 3
 ])
 def test_decode_shapes(qn, rows, cols, M, r):
     c = Case(rows, cols, M, r, 2.0 * r, seed=rows + 3 * cols + M)
