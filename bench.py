@@ -448,9 +448,9 @@ def main():
                     help="only the fixed kernel launches used by the rocprofv3 summaries")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only: the hot path is measured "
-                                   "on one MI355X; multi-GPU sharding is a design note, not "
-                                   "built", "n_gpus": args.gpus}))
+        print(json.dumps({"error": "bench.py runs on one GPU only: the hot path is measured "
+                                   "on one MI355X; sharding across GPUs is described in the "
+                                   "design notes, not implemented", "n_gpus": args.gpus}))
         sys.exit(2)
     import torch
     import quantized_fine_tuning_nf4_amd as qn
