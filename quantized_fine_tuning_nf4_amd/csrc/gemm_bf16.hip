@@ -289,13 +289,17 @@ __global__ __launch_bounds__(T, 1) void k_gemm_nt(
     }
   }
   // (a wave's LDS accesses execute in order, so its reads see its writes)
+  // Streaming (non-temporal) stores: the output is written once and never
+  // read here, while the caches still serve other tiles' re-reads of the A
+  // and Bm rows; ordinary stores would displace those lines.
   const int64_t col = c0 + wn * 128 + 8 * (lane & 15);
 #pragma unroll
   for (int q = 0; q < 32; ++q) {
     const int rl = 4 * q + (lane >> 4);
     const int64_t row = m0 + wm * 128 + rl;
     const u32x4 v = *reinterpret_cast<const u32x4*>(stg + rl * OUTP + 16 * (lane & 15));
-    if (row < M && col < Nc) *reinterpret_cast<u32x4*>(C + row * Nc + col) = v;
+    if (row < M && col < Nc)
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(C + row * Nc + col));
   }
 }
 
