@@ -52,57 +52,109 @@ struct BwdAux {
   int r;
   float s;
 };
+// The jobs are rows, one per thread: a row n of B (Bt[j][n] = B[n][j]), a
+// column k of A (At[k][j] = A[j][k]), a column m of su and of sv (all rp
+// ranks of it).  A thread reads its row of B, u or v's slices whole (16-byte
+// loads when r allows), the threads of a wave read neighbouring elements of
+// A's rows, and the transposed writes of neighbouring threads are neighbours.
 __host__ __device__ inline int64_t bwd_aux_count(const BwdAux& a) {
-  const int64_t rp = 16 * ((a.r + 15) / 16);
-  return (a.Bt ? a.N * a.r : 0) + (a.At ? a.K * a.r : 0) + (a.su ? rp * a.Mpu : 0) +
-         (a.sv ? rp * a.Mpv : 0);
+  return (a.Bt ? a.N : 0) + (a.At ? a.K : 0) + (a.su ? a.Mpu : 0) + (a.sv ? a.Mpv : 0);
 }
-// element i of the concatenated jobs (Bt, At, su, sv in that order)
+// x as bf16 at dst[idx] and its remainder as bf16 at dst[half + idx]
+__device__ inline void put_split(uint16_t* dst, int64_t half, int64_t idx, float x) {
+  const uint32_t h = pack_bf16x2(x, 0.f) & 0xffffu;
+  dst[idx] = (uint16_t)h;
+  dst[half + idx] = (uint16_t)(pack_bf16x2(x - bf16_lo(h), 0.f) & 0xffffu);
+}
+// row job i of the concatenated jobs (Bt, At, su, sv in that order)
 __device__ inline void bwd_aux_at(const BwdAux& a, int64_t i) {
-  const int64_t rp = 16 * ((a.r + 15) / 16);
-  const int64_t nb = a.Bt ? a.N * a.r : 0;
-  if (i < nb) {
-    const int64_t j = i / a.N, n = i % a.N;
-    a.Bt[i] = a.B[n * a.r + j];
+  const int r = a.r;
+  const int64_t rp = 16 * ((r + 15) / 16);
+  const int64_t nb = a.Bt ? a.N : 0;
+  if (i < nb) {  // Bt[j][n] = B[n][j]
+    const int64_t n = i;
+    const uint16_t* row = a.B + n * r;
+    if ((r & 7) == 0) {
+      for (int j0 = 0; j0 < r; j0 += 8) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(row + j0);
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          a.Bt[(int64_t)(j0 + q) * a.N + n] = (uint16_t)(v[q >> 1] >> (16 * (q & 1)));
+      }
+    } else {
+      for (int j = 0; j < r; ++j) a.Bt[(int64_t)j * a.N + n] = row[j];
+    }
     return;
   }
   i -= nb;
-  const int64_t na = a.At ? a.K * a.r : 0;
-  if (i < na) {
-    const int64_t k = i / a.r, j = i % a.r;
-    a.At[i] = a.A[j * a.K + k];
+  const int64_t na = a.At ? a.K : 0;
+  if (i < na) {  // At[k][j] = A[j][k]
+    const int64_t k = i;
+    uint16_t* row = a.At + k * r;
+    if ((r & 7) == 0) {
+      for (int j0 = 0; j0 < r; j0 += 8) {
+        uint32_t w[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          w[q] = (uint32_t)a.A[(int64_t)(j0 + 2 * q) * a.K + k] |
+                 ((uint32_t)a.A[(int64_t)(j0 + 2 * q + 1) * a.K + k] << 16);
+        *reinterpret_cast<u32x4*>(row + j0) = u32x4{w[0], w[1], w[2], w[3]};
+      }
+    } else {
+      for (int j = 0; j < r; ++j) row[j] = a.A[(int64_t)j * a.K + k];
+    }
     return;
   }
   i -= na;
-  const int64_t nu = a.su ? rp * a.Mpu : 0;
-  uint16_t* dst;
-  int64_t count;
-  float x = 0.f;
-  if (i < nu) {
-    const int64_t j = i / a.Mpu, m = i % a.Mpu;
-    if (j < a.r && m < a.M) x = a.s * a.u[m * a.r + j];
-    dst = a.su;
-    count = nu;
-  } else {
-    i -= nu;
-    const int64_t j = i / a.Mpv, m = i % a.Mpv;
-    if (j < a.r && m < a.M) {
-      const int64_t e = m * a.r + j;
-      float val;
-      if (a.Sv > 1) {
-        val = slice_sum(a.vpart, a.M * a.r, a.Sv, e);
-        a.v[e] = val;
+  // su: (s u)^T split, column m; sv: v = sum of the slices (written), then
+  // (s v)^T split; ranks j >= r and columns m >= M are zero
+  const int64_t nu = a.su ? a.Mpu : 0;
+  const bool is_u = i < nu;
+  const int64_t m = is_u ? i : i - nu;
+  const int64_t Mp = is_u ? a.Mpu : a.Mpv;
+  uint16_t* dst = is_u ? a.su : a.sv;
+  const int64_t half = rp * Mp;
+  const bool in = m < a.M;
+  const bool vec = (r & 3) == 0;
+  for (int j0 = 0; j0 < rp; j0 += 4) {
+    float x[4] = {0.f, 0.f, 0.f, 0.f};
+    if (in && j0 < r) {
+      const int64_t e = m * r + j0;
+      if (is_u) {
+        if (vec) {
+          const f32x4 v = *reinterpret_cast<const f32x4*>(a.u + e);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) x[q] = v[q];
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) x[q] = j0 + q < r ? a.u[e + q] : 0.f;
+        }
+      } else if (a.Sv > 1) {
+        // slices added in slice order
+        const int64_t cnt = a.M * (int64_t)r;
+        if (vec) {
+          f32x4 acc = *reinterpret_cast<const f32x4*>(a.vpart + e);
+          for (int sl = 1; sl < a.Sv; ++sl)
+            acc += *reinterpret_cast<const f32x4*>(a.vpart + (int64_t)sl * cnt + e);
+          *reinterpret_cast<f32x4*>(a.v + e) = acc;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) x[q] = acc[q];
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (j0 + q < r) {
+              x[q] = slice_sum(a.vpart, cnt, a.Sv, e + q);
+              a.v[e + q] = x[q];
+            }
+        }
       } else {
-        val = a.v[e];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) x[q] = j0 + q < r ? a.v[e + q] : 0.f;
       }
-      x = a.s * val;
     }
-    dst = a.sv;
-    count = rp * a.Mpv;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) put_split(dst, half, (int64_t)(j0 + q) * Mp + m, a.s * x[q]);
   }
-  const uint32_t h = pack_bf16x2(x, 0.f) & 0xffffu;
-  dst[i] = (uint16_t)h;
-  dst[count + i] = (uint16_t)(pack_bf16x2(x - bf16_lo(h), 0.f) & 0xffffu);
 }
 hipError_t launch_bwd_aux(const BwdAux& a, hipStream_t st);
 

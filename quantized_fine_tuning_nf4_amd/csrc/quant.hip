@@ -457,7 +457,7 @@ hipError_t launch_dequant(const uint8_t* packed, const uint8_t* qscale, const fl
 // Transposed dequantization for the dX product: out[k][n] (bf16, row length
 // ldt >= rows, ldt % 8 == 0) = Qhat(W)[n][k], zero for rows <= n < ldt.
 // One-dimensional grid: the first `aux_wgs` workgroups run the small jobs of
-// the same backward (four elements per thread), so they share the machine
+// the same backward (one row job per thread), so they share the machine
 // with the dequantization instead of trailing it; then one workgroup per
 // tile of 128 rows x 128 columns (two blocks; cols % 64 == 0, columns past
 // cols are not stored): wave q takes half q & 1 (32 columns) of block q >> 1,
@@ -474,14 +474,9 @@ __global__ __launch_bounds__(256) void k_dequant_t(const uint8_t* __restrict__ p
   __shared__ float lut[16];
   __shared__ __attribute__((aligned(16))) uint8_t tile[DQT_K * DQT_PITCH];
   const int t = threadIdx.x;
-  if ((int)blockIdx.x < aux_wgs) {
-    const int64_t count = bwd_aux_count(aux), q4 = (count + 3) / 4;
-    const int64_t i0 = (int64_t)blockIdx.x * 256 + t;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int64_t i = i0 + q4 * k;
-      if (i0 < q4 && i < count) bwd_aux_at(aux, i);
-    }
+  if ((int)blockIdx.x < aux_wgs) {  // one row job per thread
+    const int64_t i = (int64_t)blockIdx.x * 256 + t;
+    if (i < bwd_aux_count(aux)) bwd_aux_at(aux, i);
     return;
   }
   if (t < 16) {  // from immediates: no load ahead of the code loads
@@ -537,7 +532,7 @@ hipError_t launch_dequant_t(const uint8_t* packed, const uint8_t* qscale, const 
                             const float* offset, int64_t rows, int64_t cols, uint16_t* out,
                             int64_t ldt, const BwdAux& aux, hipStream_t st) {
   const int64_t gx = (ldt + DQT_N - 1) / DQT_N, gk = (cols + DQT_K - 1) / DQT_K;
-  const int64_t aux_wgs = ((bwd_aux_count(aux) + 3) / 4 + 255) / 256;
+  const int64_t aux_wgs = (bwd_aux_count(aux) + 255) / 256;
   hipLaunchKernelGGL(k_dequant_t, dim3((unsigned)(aux_wgs + gx * gk)), dim3(256), 0, st, packed,
                      qscale, scale2, offset, rows, cols, out, ldt, aux, (int)aux_wgs, (int)gx);
   return hipGetLastError();
