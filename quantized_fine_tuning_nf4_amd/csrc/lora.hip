@@ -10,6 +10,8 @@
 #include <algorithm>
 #include <type_traits>
 
+#include <atomic>
+
 #include "qn_device.h"
 #include "qn_internal.h"
 
@@ -377,10 +379,24 @@ struct TnJob {
   int S;               // slices
   int tiles;           // column tiles of 128
   float* part;         // [S, P, r]
+  float* out;          // [P, r], or [r, P] when transposed
+  int transposed;
 };
 
+// Arrival counters of the column tiles of one launch (both jobs' tiles in
+// grid order), one row per call slot, taken round robin by the launcher and
+// left at zero by the workgroup that finishes a tile.
+constexpr int kTnSlots = 64, kTnMaxTiles = 1024;
+__device__ unsigned g_tn_arrivals[kTnSlots * kTnMaxTiles];
+constexpr int kDeviceScope = 16;  // sc1: the level every XCD shares
+
+// With slot >= 0 the slices are also added here: each workgroup stores its
+// slice with device-coherent stores, and the last of a column tile's S
+// workgroups to arrive (an arrival counter per tile) adds the S slices of
+// the tile in slice order with device-coherent loads and writes the output.
 template <int NJ>
-__global__ __launch_bounds__(kThreads) void k_thin_tn(TnJob j0, TnJob j1, int64_t M, int r) {
+__global__ __launch_bounds__(kThreads) void k_thin_tn(TnJob j0, TnJob j1, int64_t M, int r,
+                                                      int slot) {
   constexpr int ZB = 32 * TN_ROWB;             // Z bytes per stage
   constexpr int VB = 2 * 16 * NJ * 64;         // (sV)^T bytes per stage
   constexpr int SB = ZB + VB;
@@ -518,7 +534,9 @@ __global__ __launch_bounds__(kThreads) void k_thin_tn(TnJob j0, TnJob j1, int64_
   if (st + 2 < steps) body(S2{}, st + 2);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   // lane: column j = 16jt + l%16, rows p = 16pt + 4(l/16) + i of the wave
-  float* dst = part + (int64_t)blockIdx.y * P * r;
+  const int S_ = S;
+  const rsrc_t rp = make_rs(part, (uint32_t)((int64_t)S_ * P * r * 4));
+  const int64_t sl_off = (int64_t)blockIdx.y * P * r;
 #pragma unroll
   for (int jt = 0; jt < NJ; ++jt) {
     const int j = 16 * jt + t;
@@ -528,9 +546,97 @@ __global__ __launch_bounds__(kThreads) void k_thin_tn(TnJob j0, TnJob j1, int64_
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int64_t p = p0 + 32 * wave + 16 * pt + 4 * g + i;
-        if (p < P) dst[p * r + j] = acc[pt][jt][i];
+        if (p < P)
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[pt][jt][i]), rp,
+                                                (uint32_t)((sl_off + p * r + j) * 4), 0,
+                                                kDeviceScope);
       }
   }
+  if (slot < 0) return;
+  // ---- arrival: every wave's stores have completed before the barrier, so
+  // they precede the count; the last workgroup reads them after it
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  __shared__ int s_last;
+  unsigned* ctr = g_tn_arrivals + (int64_t)slot * kTnMaxTiles + blockIdx.x;
+  if (tid == 0)
+    s_last = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+             (unsigned)(S_ - 1);
+  __syncthreads();
+  if (!s_last) return;
+  // ---- the tile's columns p0 .. p0 + np - 1: slice z holds them as np r
+  // contiguous floats at (z P + p0) r; elements e, in chunks of 2048 (eight
+  // per thread, every load of a chunk issued before the first add)
+  const int np = (int)min((int64_t)TN_COLS, P - p0);
+  const int cnt = np * r;
+  const bool tr = second ? j1.transposed : j0.transposed;
+  float* out = second ? j1.out : j0.out;
+  const bool vec = (r % 4) == 0 && (P * r) % 4 == 0;
+  const uint32_t zst = (uint32_t)((int64_t)P * r * 4);  // bytes between slices
+  for (int c0 = 0; c0 < cnt; c0 += 8 * kThreads) {
+    // a[q]: element c0 + 4 ((q / 4) kThreads + tid) + q % 4
+    float a[8];
+    if (vec) {
+      uint32_t o[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        o[h] = (uint32_t)(((int64_t)p0 * r + min(c0 + 4 * (h * kThreads + tid), cnt - 4)) * 4);
+      f32x4 v[2];
+      // one half at a time (registers), sixteen slices' loads in flight
+      // (clamped: the extra ones are not added)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        for (int z0 = 0; z0 < S_; z0 += 16) {
+          f32x4 w[16];
+#pragma unroll
+          for (int k = 0; k < 16; ++k)
+            w[k] = __builtin_bit_cast(
+                f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                           rp, o[h] + (uint32_t)min(z0 + k, S_ - 1) * zst, 0, kDeviceScope));
+          if (z0 == 0) v[h] = w[0];
+#pragma unroll
+          for (int k = 0; k < 16; ++k)
+            if ((z0 > 0 || k > 0) && z0 + k < S_) v[h] += w[k];
+        }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) a[q] = v[q >> 2][q & 3];
+    } else {
+      uint32_t o[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        o[q] = (uint32_t)(((int64_t)p0 * r +
+                           min(c0 + 4 * ((q >> 2) * kThreads + tid) + (q & 3), cnt - 1)) * 4);
+      for (int z0 = 0; z0 < S_; z0 += 8) {
+        float w[8][8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+#pragma unroll
+          for (int q = 0; q < 8; ++q)
+            w[q][k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                rp, o[q] + (uint32_t)min(z0 + k, S_ - 1) * zst, 0, kDeviceScope));
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          if (z0 == 0) a[q] = w[q][0];
+#pragma unroll
+          for (int k = 0; k < 8; ++k)
+            if ((z0 > 0 || k > 0) && z0 + k < S_) a[q] += w[q][k];
+        }
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int e = c0 + 4 * ((q >> 2) * kThreads + tid) + (q & 3);
+      if (e >= cnt) continue;
+      const int64_t p = p0 + e / r;
+      const int j = e % r;
+      if (tr)
+        out[(int64_t)j * P + p] = a[q];
+      else
+        out[p * r + j] = a[q];
+    }
+  }
+  if (tid == 0)  // every slice has arrived: ready for the next call
+    __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // out = sum over slices of part, added in slice order (loads issued eight
@@ -596,18 +702,25 @@ hipError_t launch_thin_tn2(const ThinTn& a, const ThinTn& b, int64_t M, int r,
     j.S = thin_tn_slices(M, x.P, r);
     j.tiles = x.Z ? (int)((x.P + TN_COLS - 1) / TN_COLS) : 0;
     j.part = x.part;
+    j.out = x.out;
+    j.transposed = x.transposed ? 1 : 0;
     if (j.tiles > 0) s_max = std::max(s_max, j.S);
   }
   const int tiles = job[0].tiles + job[1].tiles;
   if (tiles == 0) return hipSuccess;
+  // slices added by the last workgroup of each tile (a call slot of arrival
+  // counters), else by a second launch
+  static std::atomic<unsigned> next_slot{0};
+  const int slot = tiles <= kTnMaxTiles ? (int)(next_slot.fetch_add(1) % kTnSlots) : -1;
   const size_t lds = (size_t)TN_NST * (32 * TN_ROWB + 2 * 16 * nj * 64);
   const dim3 grid((unsigned)tiles, (unsigned)s_max);
   switch (nj) {
-    case 1: hipLaunchKernelGGL(k_thin_tn<1>, grid, dim3(kThreads), lds, st, job[0], job[1], M, r); break;
-    case 2: hipLaunchKernelGGL(k_thin_tn<2>, grid, dim3(kThreads), lds, st, job[0], job[1], M, r); break;
-    case 3: hipLaunchKernelGGL(k_thin_tn<3>, grid, dim3(kThreads), lds, st, job[0], job[1], M, r); break;
-    default: hipLaunchKernelGGL(k_thin_tn<4>, grid, dim3(kThreads), lds, st, job[0], job[1], M, r); break;
+    case 1: hipLaunchKernelGGL(k_thin_tn<1>, grid, dim3(kThreads), lds, st, job[0], job[1], M, r, slot); break;
+    case 2: hipLaunchKernelGGL(k_thin_tn<2>, grid, dim3(kThreads), lds, st, job[0], job[1], M, r, slot); break;
+    case 3: hipLaunchKernelGGL(k_thin_tn<3>, grid, dim3(kThreads), lds, st, job[0], job[1], M, r, slot); break;
+    default: hipLaunchKernelGGL(k_thin_tn<4>, grid, dim3(kThreads), lds, st, job[0], job[1], M, r, slot); break;
   }
+  if (slot >= 0) return hipGetLastError();
   TnSum sum[2];
   int64_t count = 0;
   for (int k = 0; k < 2; ++k) {

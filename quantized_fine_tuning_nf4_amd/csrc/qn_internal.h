@@ -214,8 +214,11 @@ struct ThinTn {
   bool transposed;
   float* part;
 };
-// Two such products (same M and r) in one launch, their slice sums in a
-// second.
+// Two such products (same M and r) in one launch; the slices are added by
+// the last workgroup of each column tile to finish (arrival counters in a
+// per-device table of 64 call slots, taken round robin: more than 64 such
+// calls in flight at once on one device would race), or, past 1024 column
+// tiles, by a second launch.
 hipError_t launch_thin_tn2(const ThinTn& a, const ThinTn& b, int64_t M, int r, hipStream_t st);
 int thin_tn_slices(int64_t M, int64_t P, int r);
 int64_t thin_tn_rows_padded(int64_t M, int64_t P, int r);

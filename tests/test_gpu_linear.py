@@ -249,6 +249,43 @@ def test_adapter_grads_repeat_identical(qn, rows, cols, M, r):
     assert ea <= REL_TOL and eb <= REL_TOL
 
 
+@pytest.mark.parametrize("rows,cols,M,r", [
+    (4096, 4096, 8192, 16),  # the training shape: 16 slices per column tile, vector finish
+    (1024, 1024, 4100, 13),  # scalar finish (r % 4 != 0), 96-row slices
+])
+def test_backward_in_a_graph_replays_exactly(qn, rows, cols, M, r):
+    """The backward captured in a HIP graph: every replay, with eager
+    backward calls between replays (other counter slots), equals the eager
+    result bit for bit: the slices of dA and dB are added in slice order by
+    whichever workgroup of a column tile arrives last, and the arrival
+    counters are back at zero after each call."""
+    c = Case(rows, cols, M, r, 2.0 * r, seed=rows + 5 * r)
+    say(f"[linear] backward graph replays: rows={rows} cols={cols} M={M} r={r}")
+    st, x, A, B, G = c.dev(qn)
+    _, u = qn.qlora_linear_fwd(st, x, A, B, c.alpha)
+    dX_ref, dA_ref, dB_ref = qn.qlora_linear_bwd(st, x, G, A, B, c.alpha, u)
+    dX, dA, dB = torch.empty_like(dX_ref), torch.empty_like(dA_ref), torch.empty_like(dB_ref)
+    L = qn.load_library()
+    ws = torch.empty(L.qlora_linear_workspace(M, rows, cols, r, 1), dtype=torch.uint8,
+                     device="cuda")
+    s = st.c_struct()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        L.qlora_linear_bwd(qn.ctypes.byref(s), x.data_ptr(), G.data_ptr(), M, A.data_ptr(),
+                           B.data_ptr(), r, float(c.alpha), u.data_ptr(), dX.data_ptr(),
+                           dA.data_ptr(), dB.data_ptr(), ws.data_ptr(), ws.numel(),
+                           torch.cuda.current_stream().cuda_stream)
+    for k in range(3):
+        dX.zero_()
+        dA.zero_()
+        dB.zero_()
+        qn.qlora_linear_bwd(st, x, G, A, B, 1.0, u)  # eager work between replays
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(dX, dX_ref) and torch.equal(dA, dA_ref) and torch.equal(dB, dB_ref), k
+
+
 def test_deterministic_repeat(qn):
     c = Case(520, 576, 300, 16, 32.0, seed=15)
     st, x, A, B, G = c.dev(qn)
