@@ -291,9 +291,10 @@ __global__ __launch_bounds__(TT, 1) void k_decode_tile(
     const float* __restrict__ scale2, const float* __restrict__ offset,
     const uint16_t* __restrict__ X, int64_t M, int64_t N, int64_t K,
     const uint16_t* __restrict__ Aad, const uint16_t* __restrict__ Bad, int r, float s, int rgt,
-    int S, unsigned* __restrict__ arrivals, float* __restrict__ part, float* __restrict__ upart,
+    int S, int slot, float* __restrict__ part, float* __restrict__ upart,
     uint16_t* __restrict__ Y, float* __restrict__ u_out) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[L_TOTAL];
+  unsigned* arrivals = g_band_arrivals + (int64_t)slot * kMaxBands;  // this device's table
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int pr = wave & (NPR - 1), par = wave / NPR;
@@ -835,17 +836,10 @@ hipError_t launch_decode_tile(const WState& w, const uint16_t* X, int64_t M, con
   if (t.rgt < 1 || t.rgt > RGM || t.S != K / KSL || t.bands < 1 || t.bands > kMaxBands ||
       (int64_t)t.bands * 16 * t.rgt < N || M < 1 || M > 16 || r < 1 || r > 16)
     return hipErrorInvalidValue;
-  static unsigned* table = [] {
-    void* p = nullptr;
-    return hipGetSymbolAddress(&p, HIP_SYMBOL(g_band_arrivals)) == hipSuccess
-               ? static_cast<unsigned*>(p)
-               : nullptr;
-  }();
-  if (!table) return hipErrorInvalidSymbol;
   static std::atomic<unsigned> next_slot{0};
-  unsigned* arrivals = table + (size_t)(next_slot.fetch_add(1) % kSlots) * kMaxBands;
+  const int slot = (int)(next_slot.fetch_add(1) % kSlots);
   hipLaunchKernelGGL(k_decode_tile, dim3((unsigned)(t.bands * t.S)), dim3(TT), 0, st, w.packed,
-                     w.qscale, w.scale2, w.offset, X, M, N, K, A, B, r, s, t.rgt, t.S, arrivals,
+                     w.qscale, w.scale2, w.offset, X, M, N, K, A, B, r, s, t.rgt, t.S, slot,
                      part, upart, Y, u_out);
   return hipGetLastError();
 }

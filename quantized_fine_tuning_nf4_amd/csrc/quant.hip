@@ -21,7 +21,7 @@
 // numbers is never exactly such a midpoint, so there is no tie to break.
 // x > mu_k is w > mu_k * s; mu_k has 25 significant bits and s 24, so the
 // product is exact in fp64 and the comparison is exact.  Which mu_k to test
-// is found from an approximate quotient q = w * rcp(s) and a table of 65
+// is found from an approximate fp32 quotient q = w * rcp(s) and a table of 65
 // buckets of width 1/32 on [-1, 1]: every bucket holds at most one t_k and
 // every t_k lies at least 1.6e-3 from a bucket edge, far beyond the error of
 // q, so the bucket is right even when q and the true quotient straddle an
@@ -67,23 +67,25 @@ __device__ uint64_t code_lut_entry(int j) {
 }
 
 // Max of v over each row of 16 lanes (DPP: xor 1, xor 2, half-row mirror,
-// row mirror).
+// row mirror; every source lane exists, and 0 is the identity of the
+// unsigned max, so each step can be one max with a DPP operand).
 __device__ __forceinline__ uint32_t row16_max(uint32_t v) {
-  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false));
-  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false));
-  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false));
-  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, true));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, true));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, true));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, true));
   return v;
 }
 
-__device__ __forceinline__ uint32_t nf4_code(float w, double s64, double rs,
+// rs32 = 32 / s (approximate, fp32): the bucket only needs the quotient to
+// well within the 1.6e-3 margin; the comparison that decides is exact (fp64).
+__device__ __forceinline__ uint32_t nf4_code(float w, float rs32, double s64,
                                              const uint64_t* lut_copy) {
-  const double w64 = (double)w;
-  int idx = (int)__builtin_fma(w64 * rs, 32.0, 32.0);
+  int idx = (int)__builtin_fmaf(w, rs32, 32.f);
   idx = min(max(idx, 0), 64);
   const uint64_t e = lut_copy[16 * idx];
   const double mu = __builtin_bit_cast(double, e & ~(uint64_t)15);
-  return (uint32_t)(e & 15u) + (w64 > mu * s64 ? 1u : 0u);
+  return (uint32_t)(e & 15u) + ((double)w > mu * s64 ? 1u : 0u);
 }
 
 // Pass 1.  One workgroup per group of 256 blocks (16384 weights); wave w
@@ -120,30 +122,39 @@ __device__ __forceinline__ void quant_group(const float* __restrict__ W, int64_t
   // code table ready (LDS-only barrier: the loads above stay in flight)
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   const uint64_t* lc = lut + (lane & 15);
+  uint32_t any_bad = 0;
+  float bs[16];  // the block scale of step j (row lane & 15 == 0 stores them)
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     const uint32_t a0 = as_u32(v[j].x) & 0x7fffffffu, a1 = as_u32(v[j].y) & 0x7fffffffu;
     const uint32_t a2 = as_u32(v[j].z) & 0x7fffffffu, a3 = as_u32(v[j].w) & 0x7fffffffu;
     // |w| bit patterns order like the values; NaN/Inf sort above all finite
     const uint32_t m = row16_max(max(max(a0, a1), max(a2, a3)));
-    if (m >= 0x7f800000u) *s_bad = 1;
+    any_bad |= m >= 0x7f800000u ? 1u : 0u;
     const float s = as_f32(m);
+    bs[j] = s;
     const int slot = wave * 64 + 4 * j + (lane >> 4);
     const int64_t b = g * kGroup + slot;
-    if ((lane & 15) == 0) {
-      if (!FULL && b < nb) absmax[b] = s;
-      tree[slot] = (FULL || b < nb) ? (double)s : 0.0;
-    }
     const double s64 = s > 0.f ? (double)s : 1.0;
-    const double rs = __builtin_amdgcn_rcp(s64);
-    const uint32_t c0 = nf4_code(v[j].x, s64, rs, lc), c1 = nf4_code(v[j].y, s64, rs, lc);
-    const uint32_t c2 = nf4_code(v[j].z, s64, rs, lc), c3 = nf4_code(v[j].w, s64, rs, lc);
+    const float rs32 = 32.f * __builtin_amdgcn_rcpf(s > 0.f ? s : 1.f);
+    const uint32_t c0 = nf4_code(v[j].x, rs32, s64, lc), c1 = nf4_code(v[j].y, rs32, s64, lc);
+    const uint32_t c2 = nf4_code(v[j].z, rs32, s64, lc), c3 = nf4_code(v[j].w, rs32, s64, lc);
     const uint16_t c16 = (uint16_t)(c0 | (c1 << 4) | (c2 << 8) | (c3 << 12));
     if (FULL) {
       codes[(wave * 16 + j) * 64 + lane] = c16;
     } else if (b < nb) {
       const int64_t e = e_wave + j * 256 + lane * 4;
       *reinterpret_cast<uint16_t*>(packed + e / 2) = c16;
+    }
+  }
+  if (any_bad) *s_bad = 1;
+  if ((lane & 15) == 0) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int slot = wave * 64 + 4 * j + (lane >> 4);
+      const int64_t b = g * kGroup + slot;
+      if (!FULL && b < nb) absmax[b] = bs[j];
+      tree[slot] = (FULL || b < nb) ? (double)bs[j] : 0.0;
     }
   }
   if (FULL) {
