@@ -21,7 +21,7 @@
 // numbers is never exactly such a midpoint, so there is no tie to break.
 // x > mu_k is w > mu_k * s; mu_k has 25 significant bits and s 24, so the
 // product is exact in fp64 and the comparison is exact.  Which mu_k to test
-// is found from an approximate fp32 quotient q = w * rcp(s) and a table of 65
+// is found from an approximate quotient q = w * rcp(s) and a table of 65
 // buckets of width 1/32 on [-1, 1]: every bucket holds at most one t_k and
 // every t_k lies at least 1.6e-3 from a bucket edge, far beyond the error of
 // q, so the bucket is right even when q and the true quotient straddle an
@@ -77,15 +77,21 @@ __device__ __forceinline__ uint32_t row16_max(uint32_t v) {
   return v;
 }
 
-// rs32 = 32 / s (approximate, fp32): the bucket only needs the quotient to
-// well within the 1.6e-3 margin; the comparison that decides is exact (fp64).
-__device__ __forceinline__ uint32_t nf4_code(float w, float rs32, double s64,
+// rs32 = 32 / s (approximate): the bucket only needs the quotient to well
+// within the 1.6e-3 margin; the comparison that decides is exact.  fp64,
+// because 32 / s overflows fp32 for subnormal block scales.
+__device__ __forceinline__ uint32_t nf4_code(float w, double rs32, double s64,
                                              const uint64_t* lut_copy) {
-  int idx = (int)__builtin_fmaf(w, rs32, 32.f);
+  int idx = (int)__builtin_fma((double)w, rs32, 32.0);
   idx = min(max(idx, 0), 64);
   const uint64_t e = lut_copy[16 * idx];
-  const double mu = __builtin_bit_cast(double, e & ~(uint64_t)15);
-  return (uint32_t)(e & 15u) + ((double)w > mu * s64 ? 1u : 0u);
+  // The threshold keeps c0 in its four low bits: mu' = mu +- c0 ulp(mu).
+  // With mu = m 2^(a-24) (25 bits) and s = n 2^(b-23) (24 bits), w - mu s is
+  // a nonzero multiple of 2^(a+b-47) wherever w is near mu s, while
+  // c0 ulp(mu) s < 15 2^(a+b-51) and the rounding of mu' s is at most
+  // 2^(a+b-51): fl(mu' s) stays within less than 2^(a+b-47) of mu s, so
+  // w > fl(mu' s) decides exactly as w > mu s.
+  return (uint32_t)(e & 15u) + ((double)w > __builtin_bit_cast(double, e) * s64 ? 1u : 0u);
 }
 
 // Pass 1.  One workgroup per group of 256 blocks (16384 weights); wave w
@@ -136,7 +142,7 @@ __device__ __forceinline__ void quant_group(const float* __restrict__ W, int64_t
     const int slot = wave * 64 + 4 * j + (lane >> 4);
     const int64_t b = g * kGroup + slot;
     const double s64 = s > 0.f ? (double)s : 1.0;
-    const float rs32 = 32.f * __builtin_amdgcn_rcpf(s > 0.f ? s : 1.f);
+    const double rs32 = 32.0 * __builtin_amdgcn_rcp(s64);
     const uint32_t c0 = nf4_code(v[j].x, rs32, s64, lc), c1 = nf4_code(v[j].y, rs32, s64, lc);
     const uint32_t c2 = nf4_code(v[j].z, rs32, s64, lc), c3 = nf4_code(v[j].w, rs32, s64, lc);
     const uint16_t c16 = (uint16_t)(c0 | (c1 << 4) | (c2 << 8) | (c3 << 12));

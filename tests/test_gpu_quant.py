@@ -101,6 +101,26 @@ def test_quant_near_thresholds_many_scales(qn):
     check_quant(qn, W, "near thresholds")
 
 
+def test_quant_near_thresholds_subnormal_scales(qn):
+    """As above with subnormal block scales (absmax below 2^-126): the
+    weights near each boundary sit on the subnormal grid."""
+    rng = np.random.default_rng(321)
+    nblk = 2048
+    t = _round_down_thresholds()
+    scales = (rng.uniform(0.5, 1.0, nblk) * 2.0 ** rng.integers(-140, -126, nblk)).astype(np.float32)
+    assert (scales < np.float32(2.0 ** -126)).all() and (scales > 0).all()
+    W = np.zeros((nblk, 64), np.float32)
+    W[:, 0] = scales
+    W[1::2, 0] *= -1
+    ks = rng.integers(0, 15, (nblk, 63))
+    base = (t[ks].astype(np.float64) * scales[:, None].astype(np.float64)).astype(np.float32)
+    d = rng.integers(-3, 4, (nblk, 63)).astype(np.int32)
+    bits = base.view(np.int32)
+    bits = np.where(base >= 0, bits + d, bits - d).astype(np.int32)
+    W[:, 1:] = np.clip(bits.view(np.float32), -np.abs(W[:, :1]), np.abs(W[:, :1]))
+    check_quant(qn, W, "near thresholds, subnormal scales")
+
+
 def test_quant_unit_scale_sweep(qn):
     """Every 97th fp32 in [-1, 1] (about 22 M values) in blocks whose absmax
     is 1 (one element per block is +-1)."""
