@@ -37,8 +37,15 @@ constexpr int OPB = 256 * ROWB;         // bytes per operand per stage (32 KB)
 constexpr int STB = 2 * OPB;            // bytes per stage (64 KB)
 constexpr int OUTP = 128 * 2 + 16;      // epilogue staging row pitch (bytes)
 constexpr int OUTW = 128 * OUTP;        // staging bytes per wave
-constexpr size_t LDS_BYTES = (size_t)NST * STB > (size_t)4 * OUTW ? (size_t)NST * STB
-                                                                   : (size_t)4 * OUTW;
+constexpr size_t LDS_MAIN = (size_t)NST * STB > (size_t)4 * OUTW ? (size_t)NST * STB
+                                                                  : (size_t)4 * OUTW;
+// the LoRA operands of a tile for r == 16, above the stages and the staging
+// tiles: V rows m0 .. m0 + 255 (fp32, 64 B each), then L rows c0 .. c0 + 255
+// (bf16, 32 B each)
+constexpr int LORA_R = 16;
+constexpr size_t LDS_V = LDS_MAIN, LDS_L = LDS_V + 256 * LORA_R * 4;
+constexpr size_t LDS_BYTES = LDS_L + 256 * LORA_R * 2;
+static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
@@ -68,6 +75,10 @@ __device__ __forceinline__ void barrier_lds() {
 }
 __device__ __forceinline__ void wait_all_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// LORA16: r == 16, the LoRA operands prefetched into LDS; otherwise read in
+// the tail from global memory (one tail per instance keeps the registers of
+// the other out of the kernel).
+template <bool LORA16>
 __global__ __launch_bounds__(T, 1) void k_gemm_nt(
     const uint16_t* __restrict__ A, int64_t lda, int64_t R, const uint16_t* __restrict__ Bm,
     int64_t ldb, int steps, int64_t M, int64_t Nc, const float* __restrict__ V,
@@ -156,6 +167,23 @@ __global__ __launch_bounds__(T, 1) void k_gemm_nt(
   // B fragments come in two sets (first and second half of a stage)
   bf16x8 fa[8], fb[2][8];
 
+  // ---- the LoRA operands (r == 16) go first, straight into LDS: they land
+  // before step 0's loads (loads complete in order), long before the tail
+  // reads them; rows past M or Nc read zeros.
+  constexpr bool lora16 = LORA16;
+  if constexpr (LORA16) {
+    const rsrc_t rsV = make_rs(V + m0 * r, (uint32_t)(mrows * LORA_R * 4));
+    const rsrc_t rsL = make_rs(L + c0 * r, (uint32_t)(ncols * LORA_R * 2));
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      dma16(rsV, (uint32_t)(1024 * (4 * wave + k) + 16 * lane), 0,
+            smem + LDS_V + 1024 * (4 * wave + k));
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+      dma16(rsL, (uint32_t)(1024 * (2 * wave + k) + 16 * lane), 0,
+            smem + LDS_L + 1024 * (2 * wave + k));
+  }
+
   // ---- prologue: steps 0 and 1 in flight, 0 landed
 #pragma unroll
   for (int k = 0; k < 2; ++k)
@@ -224,7 +252,34 @@ __global__ __launch_bounds__(T, 1) void k_gemm_nt(
   // both against the same eight ranks 8(g4 & 1) .. +7 of L.
   const bool vec = (r % 8) == 0;
   const bool lo_part = g4 >= 2;
-  for (int j0 = 0; j0 < r; j0 += 16) {
+  if constexpr (LORA16) {
+    // from LDS: L row (tile column) wn 128 + 16 j + l16, ranks 8 (g4 & 1) ..;
+    // V row (tile row) wm 128 + 16 i + l16, the same ranks
+    const int jb = 8 * (g4 & 1);
+    bf16x8 lh[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      lh[j] = as_bf16x8(*reinterpret_cast<const u32x4*>(
+          smem + LDS_L + (wn * 128 + 16 * j + l16) * (LORA_R * 2) + 2 * jb));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint8_t* vp = smem + LDS_V + (wm * 128 + 16 * i + l16) * (LORA_R * 4) + 4 * jb;
+      const f32x4 v0 = *reinterpret_cast<const f32x4*>(vp);
+      const f32x4 v1 = *reinterpret_cast<const f32x4*>(vp + 16);
+      const float vr[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+      uint32_t w[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float x0 = s * vr[2 * q], x1 = s * vr[2 * q + 1];
+        const uint32_t h = pack_bf16x2(x0, x1);
+        w[q] = lo_part ? pack_bf16x2(x0 - bf16_lo(h), x1 - bf16_hi(h)) : h;
+      }
+      const bf16x8 av = as_bf16x8(u32x4{w[0], w[1], w[2], w[3]});
+#pragma unroll
+      for (int j = 0; j < 8; ++j) mfma16_acc(lh[j], av, acc[i][j]);
+    }
+  }
+  for (int j0 = 0; j0 < (LORA16 ? 0 : r); j0 += 16) {
     const int jl = j0 + 8 * (g4 & 1);
     bf16x8 lh[8];
 #pragma unroll
@@ -310,16 +365,24 @@ size_t gemm_nt_lds_bytes() { return LDS_BYTES; }
 hipError_t launch_gemm_nt(const uint16_t* A, int64_t lda, int64_t R, const uint16_t* Bm,
                           int64_t ldb, int64_t M, int64_t Nc, const float* V, const uint16_t* L,
                           int r, float s, uint16_t* C, hipStream_t st) {
-  static hipError_t attr =
-      hipFuncSetAttribute(reinterpret_cast<const void*>(k_gemm_nt),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS_BYTES);
+  static hipError_t attr = [] {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_gemm_nt<true>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS_BYTES);
+    if (e != hipSuccess) return e;
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(k_gemm_nt<false>),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS_MAIN);
+  }();
   if (attr != hipSuccess) return attr;
   if (M <= 0) return hipSuccess;
   if (ldb % BK != 0 || R < 8 || R > ldb) return hipErrorInvalidValue;
   const int64_t tm = (M + BM - 1) / BM, tc = (Nc + BN - 1) / BN;
   const int steps = (int)(ldb / BK);
-  hipLaunchKernelGGL(k_gemm_nt, dim3((unsigned)(tm * tc)), dim3(T), LDS_BYTES, st, A, lda, R, Bm,
-                     ldb, steps, M, Nc, V, L, r, s, C, (int)tm, (int)tc);
+  if (r == LORA_R)
+    hipLaunchKernelGGL(k_gemm_nt<true>, dim3((unsigned)(tm * tc)), dim3(T), LDS_BYTES, st, A, lda,
+                       R, Bm, ldb, steps, M, Nc, V, L, r, s, C, (int)tm, (int)tc);
+  else
+    hipLaunchKernelGGL(k_gemm_nt<false>, dim3((unsigned)(tm * tc)), dim3(T), LDS_MAIN, st, A, lda,
+                       R, Bm, ldb, steps, M, Nc, V, L, r, s, C, (int)tm, (int)tc);
   return hipGetLastError();
 }
 
