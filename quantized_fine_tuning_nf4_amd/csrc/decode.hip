@@ -558,10 +558,11 @@ __global__ __launch_bounds__(TT, 1) void k_decode_tile(
 //     above (same lane mapping, table and MFMA form);
 //   - order of issue, which is the order of completion: the band's scale
 //     codes, second-level scales and B rows (plain loads, written to LDS
-//     before the first barrier), X fragments, the first RS code units, A
-//     fragments; the remaining units refill the ring slot of the unit
-//     consumed RS steps earlier.  The wait for unit q counts the operations
-//     issued after it, a compile-time number;
+//     before the first barrier), X fragments, the first RS code units; the
+//     remaining units refill the ring slot of the unit consumed RS steps
+//     earlier.  The wait for unit q counts the operations issued after it, a
+//     compile-time number.  The A fragments (for u) go out after the last
+//     unit has landed;
 //   - after the main loop the waves' sums meet in LDS (sum over waves in wave
 //     order), u likewise; thread (m, row) adds s sum_j u[m][j] B[row][j] and
 //     stores bf16 y.  Workgroup 0 writes u.
@@ -609,7 +610,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_decode_rows(
     float* __restrict__ u_out) {
   constexpr int RW_T = 64 * NW, RW_W = NW;
   constexpr int64_t K = 128 * NW * PW, kb = K / 64;
-  constexpr int NU = RW_RG * PW, RS = NU < RW_RING_KB / NW ? NU : RW_RING_KB / NW, NA = 4 * PW;
+  constexpr int NU = RW_RG * PW, RS = NU < RW_RING_KB / NW ? NU : RW_RING_KB / NW, NA = 0;
   constexpr int PT = (RW_BR * 16 + RW_T - 1) / RW_T;  // small-load elements per thread
   static_assert(rw_after<NU, RS, NA>(0) <= 39, "wait counts");
   __shared__ __attribute__((aligned(16))) uint8_t smem[RW_TOTAL];
@@ -673,20 +674,6 @@ __global__ __launch_bounds__(64 * NW, 1) void k_decode_rows(
   };
 #pragma unroll
   for (int q = 0; q < RS; ++q) dma_unit(q);
-  // the A fragments go out after the first units and before any wait for
-  // them: the wait counts below rely on that order
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("" ::: "memory");
-#pragma unroll
-  for (int i = 0; i < PW; ++i)
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      af[i][b][0] = as_bf16x8(*reinterpret_cast<const u32x4*>(arow + PS * i + 64 * b + koff1));
-      af[i][b][1] = as_bf16x8(*reinterpret_cast<const u32x4*>(arow + PS * i + 64 * b + koff2));
-    }
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("" ::: "memory");
-
   // ---- table (levels as immediates; entry e of copy c at byte 256 e + 4 c),
   // scales and B into LDS
   {
@@ -750,6 +737,15 @@ __global__ __launch_bounds__(64 * NW, 1) void k_decode_rows(
     // one (their registers would be live across it)
     __builtin_amdgcn_sched_barrier(0);
   }
+  // u = X A^T: the A fragments are loaded only now (earlier, their 128 KB per
+  // workgroup from L2 held back the code stream: 1.2-1.8 us per call)
+#pragma unroll
+  for (int i = 0; i < PW; ++i)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      af[i][b][0] = as_bf16x8(*reinterpret_cast<const u32x4*>(arow + PS * i + 64 * b + koff1));
+      af[i][b][1] = as_bf16x8(*reinterpret_cast<const u32x4*>(arow + PS * i + 64 * b + koff2));
+    }
   f32x4 uacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < PW; ++i)
