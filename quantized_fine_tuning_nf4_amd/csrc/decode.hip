@@ -568,7 +568,10 @@ __global__ __launch_bounds__(TT, 1) void k_decode_tile(
 //     stores bf16 y.  Workgroup 0 writes u.
 constexpr int RW_RG = 4;           // row groups per band
 constexpr int RW_BR = 16 * RW_RG;  // rows per band, at most
-constexpr int RW_RING_KB = 80;     // ring: 80 units of 1 KB, split among the waves
+// ring: 64 units of 1 KB split among the waves (16 waves: 4 in flight each of
+// 8; 5 measured 0.2-1 us slower per call, 3 the same, 2 slower: more requests
+// at once delay the first data)
+constexpr int RW_RING_KB = 64;
 constexpr int RW_TAB = 0, RW_RING = 65536, RW_QS = RW_RING + RW_RING_KB * UB;
 constexpr int RW_S2 = RW_QS + RW_BR * 64, RW_B = RW_S2 + 64 * 4, RW_E4 = RW_B + RW_BR * 16 * 2;
 constexpr int RW_TOTAL = RW_E4 + 256 * 4;
