@@ -97,13 +97,18 @@ __device__ __forceinline__ uint32_t nf4_code(float w, double rs32, double s64,
 // Pass 1.  One workgroup per group of 256 blocks (16384 weights); wave w
 // owns blocks 64w..64w+63 of the group, and at step j its 64 lanes read
 // 1 KB: four blocks, 16 lanes x float4 per block.  The body is instantiated
-// for whole groups (every load unconditional, all 16 in flight at once) and
+// for whole groups (every load unconditional, QD in flight at a time) and
 // for the tail group (element-wise bounds); the kernel branches once, around
 // the whole body, so no loaded value meets a branch join (which would make
 // the compiler wait for every load there).  In whole groups the codes gather
 // in LDS and leave as 16-byte pieces, and the 256 block scales leave in one
 // coalesced store at the end (2-byte and 4-lane stores per step cost more
 // than the code search).
+// loads in flight per thread in the block pass: all sixteen at once put the
+// whole 64 MB in the memory queues together and delay the first data; three
+// measured best (21.7-22.0 us at 4096x4096 against 22.6-23.5 for sixteen,
+// 22.5-23.2 for four, 22.6 for two)
+constexpr int QD = 3;
 template <bool FULL>
 __device__ __forceinline__ void quant_group(const float* __restrict__ W, int64_t n, int64_t nb,
                                             uint8_t* __restrict__ packed,
@@ -113,8 +118,7 @@ __device__ __forceinline__ void quant_group(const float* __restrict__ W, int64_t
   const int64_t g = blockIdx.x;
   const int64_t e_wave = (g * kGroup + wave * 64) * kBlock;
   float4 v[16];
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
+  auto load_j = [&](int j) {
     const int64_t e = e_wave + j * 256 + lane * 4;
     if (FULL) {
       v[j] = *reinterpret_cast<const float4*>(W + e);
@@ -124,7 +128,9 @@ __device__ __forceinline__ void quant_group(const float* __restrict__ W, int64_t
       v[j].z = e + 2 < n ? W[e + 2] : 0.f;
       v[j].w = e + 3 < n ? W[e + 3] : 0.f;
     }
-  }
+  };
+#pragma unroll
+  for (int j = 0; j < QD; ++j) load_j(j);
   // code table ready (LDS-only barrier: the loads above stay in flight)
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   const uint64_t* lc = lut + (lane & 15);
@@ -132,6 +138,8 @@ __device__ __forceinline__ void quant_group(const float* __restrict__ W, int64_t
   float bs[16];  // the block scale of step j (row lane & 15 == 0 stores them)
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
+    if (j + QD < 16) load_j(j + QD);  // QD loads stay in flight
+    __builtin_amdgcn_sched_barrier(0);  // (not hoisted: that would issue all sixteen at once)
     const uint32_t a0 = as_u32(v[j].x) & 0x7fffffffu, a1 = as_u32(v[j].y) & 0x7fffffffu;
     const uint32_t a2 = as_u32(v[j].z) & 0x7fffffffu, a3 = as_u32(v[j].w) & 0x7fffffffu;
     // |w| bit patterns order like the values; NaN/Inf sort above all finite
