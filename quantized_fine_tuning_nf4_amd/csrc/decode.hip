@@ -561,8 +561,9 @@ __global__ __launch_bounds__(TT, 1) void k_decode_tile(
 //     before the first barrier), X fragments, the first RS code units; the
 //     remaining units refill the ring slot of the unit consumed RS steps
 //     earlier.  The wait for unit q counts the operations issued after it, a
-//     compile-time number.  The A fragments (for u) go out after the last
-//     unit has landed;
+//     compile-time number.  The A fragments (for u) go out right after the
+//     last refill, so that they neither hold the code stream back nor add
+//     their latency after the last unit;
 //   - after the main loop the waves' sums meet in LDS (sum over waves in wave
 //     order), u likewise; thread (m, row) adds s sum_j u[m][j] B[row][j] and
 //     stores bf16 y.  Workgroup 0 writes u.
@@ -711,10 +712,27 @@ __global__ __launch_bounds__(64 * NW, 1) void k_decode_rows(
 #pragma unroll
   for (int q = 0; q < NU; ++q) {
     const int g = q / PW, i = q % PW;
-    wait_vm_n(rw_after<NU, RS, NA>(q));  // unit q has landed
+    // unit q has landed (units after the last refill also count the A loads)
+    wait_vm_n(rw_after<NU, RS, NA>(q) + (NU > RS && q > NU - RS - 1 ? 4 * PW : 0));
     const u32x4 c = *reinterpret_cast<const u32x4*>(ring + (q % RS) * UB + rd);
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     if (q + RS < NU) dma_unit(q + RS);  // into the slot just read
+    if (NU > RS && q == NU - RS - 1) {
+      // after the last refill: the A fragments (for u; issued before the
+      // refills, their 128 KB per workgroup from L2 held the code stream
+      // back; after the last unit, their latency came after it)
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int i = 0; i < PW; ++i)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          af[i][b][0] = as_bf16x8(*reinterpret_cast<const u32x4*>(arow + PS * i + 64 * b + koff1));
+          af[i][b][1] = as_bf16x8(*reinterpret_cast<const u32x4*>(arow + PS * i + 64 * b + koff2));
+        }
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("" ::: "memory");
+    }
     // block scales of row l16 of group g for the pair's two blocks (rows
     // past the band use its last row: finite, never stored)
     const int row = min(16 * g + l16, nrows - 1);
@@ -740,15 +758,15 @@ __global__ __launch_bounds__(64 * NW, 1) void k_decode_rows(
     // one (their registers would be live across it)
     __builtin_amdgcn_sched_barrier(0);
   }
-  // u = X A^T: the A fragments are loaded only now (earlier, their 128 KB per
-  // workgroup from L2 held back the code stream: 1.2-1.8 us per call)
+  if constexpr (NU <= RS) {  // no refills: the A fragments after the last unit
 #pragma unroll
-  for (int i = 0; i < PW; ++i)
+    for (int i = 0; i < PW; ++i)
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      af[i][b][0] = as_bf16x8(*reinterpret_cast<const u32x4*>(arow + PS * i + 64 * b + koff1));
-      af[i][b][1] = as_bf16x8(*reinterpret_cast<const u32x4*>(arow + PS * i + 64 * b + koff2));
-    }
+      for (int b = 0; b < 2; ++b) {
+        af[i][b][0] = as_bf16x8(*reinterpret_cast<const u32x4*>(arow + PS * i + 64 * b + koff1));
+        af[i][b][1] = as_bf16x8(*reinterpret_cast<const u32x4*>(arow + PS * i + 64 * b + koff2));
+      }
+  }
   f32x4 uacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < PW; ++i)
