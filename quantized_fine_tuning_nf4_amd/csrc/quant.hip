@@ -282,6 +282,10 @@ __global__ __launch_bounds__(256) void k_quant_dq(const float* __restrict__ absm
   __shared__ double t[128];
   __shared__ int s_any;
   const int tid = threadIdx.x;
+  // this thread's block scale, loaded before the mean's tree (whose barriers
+  // would otherwise keep the load behind it)
+  const int64_t b = (int64_t)blockIdx.x * kGroup + tid;
+  const float sb = b < nb ? absmax[b] : 0.f;
   float mu;
   if constexpr (FUSED) {
     // thread tid holds entries tid + 256 q of the LDS stage (zero past it);
@@ -333,8 +337,7 @@ __global__ __launch_bounds__(256) void k_quant_dq(const float* __restrict__ absm
   } else {
     mu = *offset;
   }
-  const int64_t b = (int64_t)blockIdx.x * kGroup + tid;
-  const float d = (b < nb) ? absmax[b] - mu : 0.f;
+  const float d = (b < nb) ? sb - mu : 0.f;
   float a = __builtin_fabsf(d);
   for (int o = 32; o >= 1; o >>= 1) a = fmaxf(a, __shfl_xor(a, o));
   if ((tid & 63) == 0) red[tid >> 6] = a;
