@@ -133,9 +133,18 @@ __device__ inline void bwd_aux_at(const BwdAux& a, int64_t i) {
         // slices added in slice order
         const int64_t cnt = a.M * (int64_t)r;
         if (vec) {
+          // eight slices' loads in flight at a time (clamped), added in order
           f32x4 acc = *reinterpret_cast<const f32x4*>(a.vpart + e);
-          for (int sl = 1; sl < a.Sv; ++sl)
-            acc += *reinterpret_cast<const f32x4*>(a.vpart + (int64_t)sl * cnt + e);
+          for (int s0 = 1; s0 < a.Sv; s0 += 8) {
+            f32x4 w[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+              w[k] = *reinterpret_cast<const f32x4*>(
+                  a.vpart + (int64_t)min(s0 + k, a.Sv - 1) * cnt + e);
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+              if (s0 + k < a.Sv) acc += w[k];
+          }
           *reinterpret_cast<f32x4*>(a.v + e) = acc;
 #pragma unroll
           for (int q = 0; q < 4; ++q) x[q] = acc[q];

@@ -286,6 +286,16 @@ __global__ __launch_bounds__(256) void k_quant_dq(const float* __restrict__ absm
   // would otherwise keep the load behind it)
   const int64_t b = (int64_t)blockIdx.x * kGroup + tid;
   const float sb = b < nb ? absmax[b] : 0.f;
+  // workgroup 0 also reads the groups' non-finite flags up front (ng <= 2048
+  // when FUSED: at most eight per thread)
+  int any_bad = 0;
+  if (FUSED && blockIdx.x == 0) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int64_t j = tid + 256 * q;
+      if (j < ng) any_bad |= bad[j];
+    }
+  }
   float mu;
   if constexpr (FUSED) {
     // thread tid holds entries tid + 256 q of the LDS stage (zero past it);
@@ -323,11 +333,9 @@ __global__ __launch_bounds__(256) void k_quant_dq(const float* __restrict__ absm
     __syncthreads();
     mu = (float)(t[0] / (double)nb);
     if (blockIdx.x == 0) {  // workgroup 0: offset and the non-finite flag
-      int any = 0;
-      for (int64_t j = tid; j < ng; j += 256) any |= bad[j];
       if (tid == 0) s_any = 0;
       __syncthreads();
-      if (any) s_any = 1;
+      if (any_bad) s_any = 1;
       __syncthreads();
       if (tid == 0) {
         *offset = mu;
