@@ -353,7 +353,7 @@ __device__ __forceinline__ void dma16(rsrc_t rs, uint32_t voff, uint32_t soff, u
 
 constexpr int TN_COLS = 128;             // columns of Z per workgroup
 constexpr int TN_ROWB = TN_COLS * 2;     // 256 B per staged Z row
-constexpr int TN_NST = 4;
+constexpr int TN_NST = 3;  // stages (two steps in flight; three: 1.5 us slower per backward)
 
 }  // namespace
 
@@ -364,7 +364,7 @@ constexpr int TN_NST = 4;
 // (pt, z): columns 128 pt .. +127, wave w: 32w .. 32w+31 (two 16-column MFMA
 // tiles).  A step is 32 rows: their Z (8 KB) and their (s V)^T high and
 // remainder parts (2 x 16 NJ rows of 64 B) go global -> LDS by buffer loads
-// into one stage, four stages deep, every wave issuing 2 + 2 NJ loads per
+// into one stage, three stages deep, every wave issuing 2 + 2 NJ loads per
 // step.
 // Z row y's 16-byte chunk c sits at unit c ^ 2(y & 3); the A operand (16
 // columns x 32 rows) is read transposed with ds_read_b64_tr_b16, lane t of a
@@ -452,15 +452,16 @@ __global__ __launch_bounds__(kThreads) void k_thin_tn(TnJob j0, TnJob j1, int64_
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(base + ZB + 256 * (2 * NJ * wave + k)),
                                                4, voff[k] + (uint32_t)(64 * st), 0, 0, 0);
   };
-  // all but the two newest steps' loads have landed
-  auto wait_two = [&]() {
-    if constexpr (NJ == 1) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-    else if constexpr (NJ == 2) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
-    else if constexpr (NJ == 3) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(20)" ::: "memory");
+  // all but the newest step's loads (2 + 2 NJ per wave) have landed
+  auto wait_step = [&]() {
+    static_assert(TN_NST == 3, "one step in flight beyond the next");
+    if constexpr (NJ == 1) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    else if constexpr (NJ == 2) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+    else if constexpr (NJ == 3) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
   };
   for (int k = 0; k < TN_NST - 1; ++k) load_step(min(k, steps - 1), k);
-  wait_two();
+  wait_step();
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
   // transposed-read addresses: lane l, group g = l/16, t = l%16; p-tile pt,
@@ -477,7 +478,7 @@ __global__ __launch_bounds__(kThreads) void k_thin_tn(TnJob j0, TnJob j1, int64_
     }
   f32x4 acc[2][NJ] = {};
   // one step on stage P (a constant, so that the compiler sees the loads of
-  // step st+3 and this step's LDS reads touch different stages)
+  // step st+2 and this step's LDS reads touch different stages)
   auto body = [&](auto p_t, int st) {
     constexpr int P = decltype(p_t)::value;
     load_step(min(st + TN_NST - 1, steps - 1), (P + TN_NST - 1) % TN_NST);
@@ -513,25 +514,22 @@ __global__ __launch_bounds__(kThreads) void k_thin_tn(TnJob j0, TnJob j1, int64_
         acc[pt][jt] = mfma16(a[pt], bl, acc[pt][jt]);
       }
     }
-    // step st+1's loads (issued 3 steps ago) have landed everywhere before
+    // step st+1's loads (issued 2 steps ago) have landed everywhere before
     // anyone reads them or overwrites this stage
-    wait_two();
+    wait_step();
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   };
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
   using S2 = std::integral_constant<int, 2>;
-  using S3 = std::integral_constant<int, 3>;
   int st = 0;
-  for (; st + 4 <= steps; st += 4) {
+  for (; st + 3 <= steps; st += 3) {
     body(S0{}, st);
     body(S1{}, st + 1);
     body(S2{}, st + 2);
-    body(S3{}, st + 3);
   }
   if (st < steps) body(S0{}, st);
   if (st + 1 < steps) body(S1{}, st + 1);
-  if (st + 2 < steps) body(S2{}, st + 2);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   // lane: column j = 16jt + l%16, rows p = 16pt + 4(l/16) + i of the wave
   const int S_ = S;
