@@ -135,3 +135,16 @@ def test_binding_rejects_cpu_tensors(qn):
     import torch
     with pytest.raises(ValueError):
         qn.nf4_quantize_dq(torch.zeros(4, 64))
+
+
+def test_bench_refuses_more_than_one_gpu():
+    # the measured path runs on one GPU; asking for more ends with a message
+    # and a usage error before anything touches a device
+    import json
+    import subprocess
+    import sys
+    p = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300)
+    assert p.returncode == 2
+    msg = json.loads(p.stdout.strip().splitlines()[-1])
+    assert msg["n_gpus"] == 2 and "one GPU" in msg["error"]
