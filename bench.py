@@ -132,9 +132,9 @@ def _median_min(xs):
 
 
 def bench_train(torch, qn, wl, steps, warmup):
-    cfg = wl.CONFIGS[4]
+    cfg = wl.TRAIN
     N, K, M, r, alpha = cfg["rows"], cfg["cols"], cfg["M"], cfg["r"], cfg["alpha"]
-    W, x, A, B, dY = wl.linear_inputs(N, K, M, r, cfg=4)
+    W, x, A, B, dY = wl.linear_inputs(N, K, M, r, seed=cfg["seed"])
     Wd = torch.from_numpy(W).cuda()
     xd, Ad, Bd, Gd = (_bf16(torch, a) for a in (x, A, B, dY))
     st = qn.empty_state(N, K, "cuda")
@@ -264,7 +264,7 @@ def bench_extras(torch, qn, wl):
     torch.cuda.empty_cache()
 
     # decode forward 14336x4096, M = 1, 4, 16, rotated weight copies
-    cfg = wl.CONFIGS[3]
+    cfg = wl.DECODE
     N, K, r, alpha = cfg["rows"], cfg["cols"], cfg["r"], cfg["alpha"]
     Wq = torch.from_numpy(wl.weight(N, K, wl.SEED_W + 3)).cuda()
     base = qn.nf4_quantize_dq(Wq)
@@ -314,11 +314,11 @@ def bench_extras(torch, qn, wl):
     torch.cuda.empty_cache()
 
     # one decoder layer's seven linears, M = 4096, fwd + bwd
-    cfg = wl.CONFIGS[5]
+    cfg = wl.DECODER_LAYER
     M, r, alpha = cfg["M"], cfg["r"], cfg["alpha"]
     layers = []
     for idx, (name, N, K) in enumerate(wl.DECODER_LINEARS):
-        W, x, A, B, G = wl.linear_inputs(N, K, M, r, cfg=5, index=idx)
+        W, x, A, B, G = wl.linear_inputs(N, K, M, r, seed=cfg["seed"], index=idx)
         st = qn.nf4_quantize_dq(torch.from_numpy(W).cuda())
         layers.append(dict(st=st, x=_bf16(torch, x), A=_bf16(torch, A), B=_bf16(torch, B),
                            G=_bf16(torch, G), N=N, K=K,
@@ -355,9 +355,9 @@ def cpu_baseline(wl, target_s=15.0):
     the sample size so that the timed part takes about target_s seconds."""
     import numpy as np
     import oracle
-    cfg = wl.CONFIGS[4]
+    cfg = wl.TRAIN
     N, K, M, r, alpha = cfg["rows"], cfg["cols"], cfg["M"], cfg["r"], cfg["alpha"]
-    W, x, A, B, dY = wl.linear_inputs(N, K, M, r, cfg=4)
+    W, x, A, B, dY = wl.linear_inputs(N, K, M, r, seed=cfg["seed"])
     s = alpha / r
     t0 = time.perf_counter()
     st = oracle.quantize(W)
@@ -404,9 +404,9 @@ def kernels_workload(torch, qn, wl, launches=5):
         dst.copy_(src)
     torch.cuda.synchronize()
     print(f"[kernels] copy {n_copy * 4} bytes x {launches}", file=sys.stderr, flush=True)
-    cfg = wl.CONFIGS[4]
+    cfg = wl.TRAIN
     N, K, M, r, alpha = cfg["rows"], cfg["cols"], cfg["M"], cfg["r"], cfg["alpha"]
-    W, x, A, B, _ = wl.linear_inputs(N, K, M, r, cfg=4)
+    W, x, A, B, _ = wl.linear_inputs(N, K, M, r, seed=cfg["seed"])
     st = qn.nf4_quantize_dq(torch.from_numpy(W).cuda())
     xd, Bd = _bf16(torch, x), _bf16(torch, B)
     u = torch.randn(M, r, device="cuda", dtype=torch.float32) * 0.01
@@ -426,7 +426,7 @@ def kernels_workload(torch, qn, wl, launches=5):
         qn.nf4_dequantize(st, torch.bfloat16, out=wbf)
     torch.cuda.synchronize()
     print(f"[kernels] dequant bf16 {N}x{K} x {launches}", file=sys.stderr, flush=True)
-    dcfg = wl.CONFIGS[3]
+    dcfg = wl.DECODE
     Nd, Kd = dcfg["rows"], dcfg["cols"]
     std = qn.nf4_quantize_dq(torch.from_numpy(wl.weight(Nd, Kd, wl.SEED_W + 3)).cuda())
     Ad = _bf16(torch, wl.normal_bf16((r, Kd), wl.SEED_A + 3, 0.01))

@@ -85,8 +85,8 @@ def check_fwd_bwd(qn, c: Case, label: str, rows=None, bwd=True):
 
 
 def test_tiny_config(qn):
-    cfg = wl.CONFIGS[1]
-    c = Case(cfg["rows"], cfg["cols"], cfg["M"], cfg["r"], cfg["alpha"], wl.SEED_W + 1)
+    cfg = wl.TINY
+    c = Case(cfg["rows"], cfg["cols"], cfg["M"], cfg["r"], cfg["alpha"], wl.SEED_W + cfg["seed"])
     check_fwd_bwd(qn, c, "tiny")
 
 
@@ -107,8 +107,8 @@ def test_ragged_shapes(qn, rows, cols, M, r):
 
 @pytest.mark.parametrize("M", [1, 4, 16])
 def test_decode_config(qn, M):
-    cfg = wl.CONFIGS[3]
-    c = Case(cfg["rows"], cfg["cols"], M, cfg["r"], cfg["alpha"], wl.SEED_W + 3)
+    cfg = wl.DECODE
+    c = Case(cfg["rows"], cfg["cols"], M, cfg["r"], cfg["alpha"], wl.SEED_W + cfg["seed"])
     check_fwd_bwd(qn, c, f"decode M={M}", bwd=(M == 16))
 
 
@@ -135,8 +135,8 @@ def test_decode_shapes(qn, rows, cols, M, r):
 
 
 def test_train_config_full_size(qn):
-    cfg = wl.CONFIGS[4]
-    c = Case(cfg["rows"], cfg["cols"], cfg["M"], cfg["r"], cfg["alpha"], wl.SEED_W + 4)
+    cfg = wl.TRAIN
+    c = Case(cfg["rows"], cfg["cols"], cfg["M"], cfg["r"], cfg["alpha"], wl.SEED_W + cfg["seed"])
     check_fwd_bwd(qn, c, "train 8192x4096x4096", rows=sample_rows(cfg["M"], 48, seed=4))
 
 

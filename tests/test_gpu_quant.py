@@ -48,8 +48,8 @@ def test_quant_parity_ragged(qn, rows, cols):
 
 
 def test_quant_parity_tiny_config(qn):
-    c = wl.CONFIGS[1]
-    W = wl.weight(c["rows"], c["cols"], wl.SEED_W + 1)
+    c = wl.TINY
+    W = wl.weight(c["rows"], c["cols"], wl.SEED_W + c["seed"])
     check_quant(qn, W, "tiny 256x256")
 
 
@@ -69,7 +69,7 @@ def test_quant_parity_long_mean_tree(qn):
 
 
 def test_quant_parity_decode_weight(qn):
-    W = wl.weight(wl.FFN, wl.HIDDEN, wl.SEED_W + 3)
+    W = wl.weight(wl.FFN, wl.HIDDEN, wl.SEED_W + wl.DECODE["seed"])
     check_quant(qn, W, "14336x4096")
 
 

@@ -32,13 +32,15 @@ DECODER_LINEARS = [
     ("down_proj", HIDDEN, FFN),
 ]
 
-CONFIGS = {
-    1: dict(name="tiny", rows=256, cols=256, M=8, r=8, alpha=16.0),
-    2: dict(name="quant_roundtrip_4096x4096_outliers", rows=4096, cols=4096),
-    3: dict(name="decode_fwd_14336x4096", rows=FFN, cols=HIDDEN, Ms=(1, 4, 16), r=16, alpha=32.0),
-    4: dict(name="train_fwd_bwd_4096x4096_M8192", rows=4096, cols=4096, M=8192, r=16, alpha=32.0),
-    5: dict(name="decoder_layer_7_linears_M4096", M=4096, r=16, alpha=32.0),
-}
+# The synthetic workloads, by name; ``seed`` offsets the input seeds.
+TINY = dict(name="tiny", seed=1, rows=256, cols=256, M=8, r=8, alpha=16.0)
+QUANT_OUTLIERS = dict(name="quant_roundtrip_4096x4096_outliers", seed=2, rows=4096, cols=4096)
+DECODE = dict(name="decode_fwd_14336x4096", seed=3, rows=FFN, cols=HIDDEN, Ms=(1, 4, 16), r=16,
+              alpha=32.0)
+TRAIN = dict(name="train_fwd_bwd_4096x4096_M8192", seed=4, rows=4096, cols=4096, M=8192, r=16,
+             alpha=32.0)
+DECODER_LAYER = dict(name="decoder_layer_7_linears_M4096", seed=5, M=4096, r=16, alpha=32.0)
+WORKLOADS = {w["name"]: w for w in (TINY, QUANT_OUTLIERS, DECODE, TRAIN, DECODER_LAYER)}
 
 
 def normal_f32(shape, seed: int, std: float) -> np.ndarray:
@@ -83,11 +85,12 @@ def outlier_weight(rows: int = 4096, cols: int = 4096, seed: int = SEED_W + 2) -
     return W
 
 
-def linear_inputs(rows: int, cols: int, M: int, r: int, cfg: int, index: int = 0,
+def linear_inputs(rows: int, cols: int, M: int, r: int, seed: int, index: int = 0,
                   with_grad: bool = True, adapter_std: float = 0.01):
     """W fp32 [rows, cols]; x [M, cols], A [r, cols], B [rows, r], dY [M, rows]
-    as bf16 bit patterns.  ``cfg`` and ``index`` offset the seeds."""
-    off = cfg + 10 * index
+    as bf16 bit patterns.  ``seed`` (a workload's) and ``index`` offset the
+    seeds."""
+    off = seed + 10 * index
     W = weight(rows, cols, SEED_W + off)
     x = normal_bf16((M, cols), SEED_X + off, 1.0)
     A = normal_bf16((r, cols), SEED_A + off, adapter_std)
