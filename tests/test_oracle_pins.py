@@ -330,6 +330,102 @@ def test_dq_scale_error_bound(orc):
         assert abs(sp - float(st.absmax[b])) <= bound
 
 
+def _dq_from_numpy(W):
+    """The double-quantisation inputs recomputed from W with numpy alone
+    (no oracle code): block absmax s_b of the flattened, zero-padded weight;
+    the mean of the scales as the fp32 nearest the exact rational mean
+    (math.fsum is exact before its one fp64 rounding, far below an fp32 half
+    ulp); d_b = RN32(s_b - mu), C2_g = max |d_b| per 256 blocks,
+    s2_g = RN32(C2_g / 448) (page "QLoRA Deep Dive: 4-bit NormalFloat &
+    Double Quantization Internals", section "2. Squeezing More Memory:
+    Double Quantization (DQ)": normalise the constants by their group
+    absmax, then an 8-bit float code)."""
+    flat = np.asarray(W, np.float32).ravel()
+    pad = (-flat.size) % 64
+    s = np.abs(np.concatenate([flat, np.zeros(pad, np.float32)]).reshape(-1, 64)).max(axis=1)
+    nb = s.size
+    mu = np.float32(math.fsum(s.astype(np.float64).tolist()) / nb)
+    d = (s - mu).astype(np.float32)
+    ng = (nb + 255) // 256
+    dpad = np.concatenate([np.abs(d), np.zeros(ng * 256 - nb, np.float32)]).reshape(ng, 256)
+    s2 = (dpad.max(axis=1) / np.float32(448.0)).astype(np.float32)
+    return s, mu, d, s2
+
+
+def _observed_block_scales(orc, st):
+    """s'_b as the oracle's dequantize writes it: the value at the element of
+    block b whose code is 15 (level +1) or 0 (level -1); NaN for blocks with
+    neither (all-zero blocks)."""
+    f32, _ = orc.dequantize(st, want_bf16=False)
+    nb = st.absmax.size
+    flat = np.concatenate([f32.ravel(), np.zeros(64 * nb - f32.size, np.float32)]).reshape(nb, 64)
+    codes = orc.codes_of(st)[:64 * nb].reshape(nb, 64)
+    sp = np.full(nb, np.nan, np.float64)
+    for level_code, sign in ((15, 1.0), (0, -1.0)):
+        has = (codes == level_code).any(axis=1) & np.isnan(sp)
+        idx = np.argmax(codes == level_code, axis=1)
+        sp[has] = sign * flat[np.nonzero(has)[0], idx[has]].astype(np.float64)
+    return sp
+
+
+def _dq_scale_bound(s, d, s2, sp):
+    """|s'_b - s_b| bound: half an E4M3 step at x_b = d_b/s2_g (step 2^(e-3)
+    in the binade [2^e, 2^(e+1)), 2^-9 below 2^-6) times s2_g, plus the fp32
+    roundings of d_b, of x_b and of s' itself."""
+    s2b = np.repeat(s2.astype(np.float64), 256)[:s.size]
+    x = np.divide(d.astype(np.float64), s2b, out=np.zeros_like(s2b), where=s2b > 0)
+    e = np.where(x != 0, np.floor(np.log2(np.abs(x), where=x != 0, out=np.zeros_like(x))), -6)
+    e = np.maximum(e, -6)
+    return s2b * 2.0 ** (e - 3) / 2 * (1 + 1e-6) + 2.0 ** -23 * (np.abs(d) + np.abs(sp))
+
+
+def _check_dq_dequant_scale(orc, W):
+    st = orc.quantize(W)
+    s, mu, d, s2 = _dq_from_numpy(W)
+    # the state's second level agrees with the independent recomputation
+    assert st.offset == mu
+    assert np.array_equal(st.scale2, s2)
+    # the 8-bit scale codes are torch's E4M3FN rounding of RN32(d_b / s2_g)
+    s2b = np.repeat(s2, 256)[:s.size]
+    x = np.where(s2b > 0, d / np.where(s2b > 0, s2b, 1), 0).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(st.qscale, ref)
+    # s'_b read back from the dequantized weight stays within the DQ error
+    # of the exact block scale s_b, block by block
+    sp = _observed_block_scales(orc, st)
+    seen = ~np.isnan(sp)
+    assert seen[s > 0].all()
+    bound = _dq_scale_bound(s, d, s2, sp)
+    err = np.abs(sp - s.astype(np.float64))
+    bad = np.nonzero(seen & (err > bound))[0]
+    assert bad.size == 0, (bad[:8], err[bad[:8]], bound[bad[:8]])
+    return st, sp, s
+
+
+def test_dq_dequant_scale_outlier_workload(orc):
+    """Every block of the 4096x4096 quantize workload (N(0, 0.02), 1% of the
+    columns x20, zero and constant blocks): the dequant scale s'_b that the
+    oracle's dequantize applies is within the DQ error bound of s_b."""
+    import workloads as wl
+    _check_dq_dequant_scale(orc, wl.outlier_weight())
+
+
+def test_dq_dequant_scale_groups_differ_tenfold(orc):
+    """Groups of 256 blocks whose absmax differ 10x in turn (and a mean far
+    from every group's scales): a dequant that took another group's s2, or
+    left out the mean offset on some blocks, lands far outside the bound."""
+    rng = np.random.default_rng(15)
+    W = rng.standard_normal((16, 8 * 16384 // 16)).astype(np.float32) * np.float32(0.02)
+    W = W.reshape(8, 16384)
+    W *= np.float32(10.0) ** (np.arange(8) % 2).astype(np.float32)[:, None]
+    W = W.reshape(64, -1)
+    st, sp, s = _check_dq_dequant_scale(orc, W)
+    # the construction really separates the groups and the mean
+    g = s.reshape(8, 256)
+    assert g[1].min() > 2 * g[0].max() and abs(float(st.offset) - g[0].mean()) > 10 * g[0].std()
+    assert np.all(np.diff(st.scale2[:2]) > 0)
+
+
 def test_storage_closed_form(orc):
     g = _golden.table("storage_bits.txt")
     for rows, cols in [(4096, 4096), (1024, 4096), (14336, 4096), (128, 128)]:
