@@ -83,30 +83,89 @@ def decode_bytes(rows, cols, M, r):
     return state_bytes(rows, cols) + 2 * M * cols + 2 * r * cols + 2 * rows * r + 2 * M * rows
 
 
-def throughput(work, seconds):
-    if not (math.isfinite(seconds) and seconds > 0):
-        raise ValueError("invalid elapsed time")
-    return work / seconds
+class Window:
+    """What one timed window of repeated steps measured: its length in
+    seconds, the steps and work units inside it, and the memory gauge at the
+    window's start and its highest value during the window (bytes; None when
+    the probe has no gauge)."""
+
+    def __init__(self, seconds, steps, units, start_bytes=None, peak_bytes=None):
+        if not (isinstance(seconds, (int, float)) and math.isfinite(seconds) and seconds > 0):
+            raise ValueError(f"a timed window must last a positive finite time, got {seconds!r}")
+        self.seconds, self.steps, self.units = float(seconds), steps, units
+        self.start_bytes, self.peak_bytes = start_bytes, peak_bytes
+
+    @property
+    def rate(self):
+        return self.units / self.seconds
+
+    @property
+    def peak_above_start(self):
+        if self.start_bytes is None or self.peak_bytes is None:
+            return None
+        return self.peak_bytes - self.start_bytes
 
 
-def measure(step, batches, tokens, clock, sync, warmup):
-    """Warmup excluded, synchronize, clock, run the measured batches,
-    synchronize, clock; returns (seconds, work units).  (The measurement
-    order of the page-2 measurement reference, without its allocator
-    counters.)"""
-    if type(warmup) is not int or warmup < 0 or len(batches) <= warmup:
-        raise ValueError("warmup and a non-empty measured suffix are required")
-    for b in batches[:warmup]:
-        step(b)
-    sync()
-    t0 = clock()
-    for b in batches[warmup:]:
-        step(b)
-    sync()
-    elapsed = clock() - t0
-    if not (math.isfinite(elapsed) and elapsed > 0):
-        raise ValueError("invalid elapsed time")
-    return elapsed, sum(tokens(b) for b in batches[warmup:])
+def time_window(run, items, units_of, untimed, probe):
+    """Runs run(item) for every item; the first `untimed` items are warmup
+    (outside the window and its work count), the rest are timed as one
+    window.  probe.begin() is called once the warmup has been issued and
+    must wait for it to finish before it stamps the start (and resets its
+    peak gauge); probe.end() must wait for the timed steps before it stamps
+    the stop; probe.seconds(start, stop) converts the two stamps.  A probe
+    may also offer memory() -> (bytes at the start, peak bytes since).
+    Returns a Window."""
+    if isinstance(untimed, bool) or not isinstance(untimed, int) or untimed < 0:
+        raise ValueError(f"the number of untimed steps must be an int >= 0, got {untimed!r}")
+    items = list(items)
+    if len(items) <= untimed:
+        raise ValueError(f"{len(items)} steps leave none to time after {untimed} untimed ones")
+    for item in items[:untimed]:
+        run(item)
+    start = probe.begin()
+    units = 0
+    for item in items[untimed:]:
+        run(item)
+        units += units_of(item)
+    stop = probe.end()
+    gauge = probe.memory() if hasattr(probe, "memory") else (None, None)
+    return Window(probe.seconds(start, stop), len(items) - untimed, units, *gauge)
+
+
+class DeviceProbe:
+    """Window probe for the GPU: synchronizes the device at both ends and
+    stamps the host clock there (the step's wall time, launches included);
+    HIP events recorded on torch's current stream at the same two points
+    give the device's own view of the window (device_seconds).  The memory
+    gauge is torch's allocator (allocated bytes at the start, peak since)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.device_seconds = None
+
+    def begin(self):
+        t = self.torch
+        t.cuda.synchronize()
+        t.cuda.reset_peak_memory_stats()
+        self._start_bytes = t.cuda.memory_allocated()
+        self._e0 = t.cuda.Event(enable_timing=True)
+        self._e1 = t.cuda.Event(enable_timing=True)
+        self._e0.record(t.cuda.current_stream())
+        return time.perf_counter()
+
+    def end(self):
+        t = self.torch
+        self._e1.record(t.cuda.current_stream())
+        t.cuda.synchronize()
+        stamp = time.perf_counter()
+        self.device_seconds = self._e0.elapsed_time(self._e1) / 1e3
+        return stamp
+
+    def seconds(self, start, stop):
+        return stop - start
+
+    def memory(self):
+        return self._start_bytes, self.torch.cuda.max_memory_allocated()
 
 
 # ----------------------------------------------------------------- GPU helpers
@@ -154,14 +213,16 @@ def bench_train(torch, qn, wl, steps, warmup):
         _, u = qn.qlora_linear_fwd(st, xd, Ad, Bd, alpha, y=y, workspace=fws)
         qn.qlora_linear_bwd(st, xd, Gd, Ad, Bd, alpha, u, workspace=bws)
 
-    batches = list(range(warmup + steps))
-    secs, nsteps = measure(step, batches, lambda b: 1, time.perf_counter,
-                           torch.cuda.synchronize, warmup)
+    probe = DeviceProbe(torch)
+    win = time_window(step, range(warmup + steps), lambda _: 1, warmup, probe)
     if int(flag.item()) != 0:
         raise RuntimeError("quantizer reported non-finite input")
     flops = fwd_flops(M, N, K, r) + bwd_flops(M, N, K, r)
+    secs, nsteps = win.seconds, win.steps
     res = dict(seconds=secs, steps=nsteps, ms_per_step=1e3 * secs / nsteps,
-               tflops=flops * nsteps / secs / 1e12, flops_per_step=flops)
+               tflops=flops * nsteps / secs / 1e12, flops_per_step=flops,
+               device_ms_per_step=1e3 * probe.device_seconds / nsteps,
+               peak_bytes_above_start=win.peak_above_start)
 
     # dominant kernels: time the forward and backward calls with HIP events on
     # the stream the library launches on (torch's current stream)
