@@ -199,8 +199,8 @@ def bench_train(torch, qn, wl, steps, warmup):
     st = qn.empty_state(N, K, "cuda")
     L = qn.load_library()
     qws = torch.empty(L.nf4_quantize_dq_workspace(N, K), dtype=torch.uint8, device="cuda")
-    fws = torch.empty(L.qlora_linear_workspace(M, N, K, r, 0), dtype=torch.uint8, device="cuda")
-    bws = torch.empty(L.qlora_linear_workspace(M, N, K, r, 1), dtype=torch.uint8, device="cuda")
+    fws = qn.linear_workspace(L.qlora_linear_workspace(M, N, K, r, 0))
+    bws = qn.linear_workspace(L.qlora_linear_workspace(M, N, K, r, 1))
     wbf = torch.empty((N, K), dtype=torch.bfloat16, device="cuda")
     y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
 
@@ -338,7 +338,7 @@ def bench_extras(torch, qn, wl):
     dec = {}
     for M in cfg["Ms"]:
         x = _bf16(torch, wl.normal_bf16((M, K), wl.SEED_X + 3, 1.0))
-        ws = torch.empty(L.qlora_linear_workspace(M, N, K, r, 0), dtype=torch.uint8, device="cuda")
+        ws = qn.linear_workspace(L.qlora_linear_workspace(M, N, K, r, 0))
         ys = [torch.empty((M, N), dtype=torch.bfloat16, device="cuda") for _ in range(R)]
         us = [torch.empty((M, r), dtype=torch.float32, device="cuda") for _ in range(R)]
         stream = torch.cuda.current_stream().cuda_stream
@@ -383,10 +383,8 @@ def bench_extras(torch, qn, wl):
         st = qn.nf4_quantize_dq(torch.from_numpy(W).cuda())
         layers.append(dict(st=st, x=_bf16(torch, x), A=_bf16(torch, A), B=_bf16(torch, B),
                            G=_bf16(torch, G), N=N, K=K,
-                           fws=torch.empty(L.qlora_linear_workspace(M, N, K, r, 0),
-                                           dtype=torch.uint8, device="cuda"),
-                           bws=torch.empty(L.qlora_linear_workspace(M, N, K, r, 1),
-                                           dtype=torch.uint8, device="cuda"),
+                           fws=qn.linear_workspace(L.qlora_linear_workspace(M, N, K, r, 0)),
+                           bws=qn.linear_workspace(L.qlora_linear_workspace(M, N, K, r, 1)),
                            y=torch.empty((M, N), dtype=torch.bfloat16, device="cuda")))
 
     def layer_step(_):

@@ -59,12 +59,19 @@
  *     QN_EALIGN: misaligned pointer; QN_EWORKSPACE: workspace too small;
  *     QN_EDEVICE: a HIP runtime call failed (no device, launch failure).
  *   - Calls that overlap on one stream are ordered; calls on different
- *     streams that share a workspace race.
- *   - Decode-sized forwards (1 <= M <= 16, r <= 16, cols % 1024 == 0) run as
- *     one kernel whose column slices meet through arrival counters in the
- *     library's static device memory: 64 slots per device, one per call,
- *     taken round robin and left at zero when the call ends.  More than 64
- *     such calls executing at the same time on one device would race.
+ *     streams that share a workspace race.  Calls on different streams with
+ *     their own workspaces are independent: the library keeps no mutable
+ *     state of its own.
+ *   - Linear workspaces (qlora_linear_workspace) begin with QN_ARRIVAL_BYTES
+ *     of arrival counters, through which the workgroups of one launch learn
+ *     which of them finishes a reduction.  They must be zero before the
+ *     workspace is first used (allocate it zeroed, or clear it once); every
+ *     call leaves them at zero when it completes, so a workspace may then
+ *     serve any number of calls, of any shape, on one stream.  The backward
+ *     also clears them in its first kernel.  nf4_quantize_dq leaves the same
+ *     bytes of its workspace untouched, so one buffer may serve all calls.
+ *   - Sizes the linear calls accept: M <= 2^23 rows, rows and cols <= 2^20
+ *     (QN_EINVAL beyond).
  */
 #ifndef QLORA_NF4_H
 #define QLORA_NF4_H
@@ -76,7 +83,10 @@
 extern "C" {
 #endif
 
-#define QN_ABI_VERSION 2
+#define QN_ABI_VERSION 3
+
+/* Bytes of arrival counters at the start of a linear workspace. */
+#define QN_ARRIVAL_BYTES 4096
 
 typedef enum {
   QN_OK = 0,
@@ -130,7 +140,9 @@ qn_status nf4_quantize_dq(const float* W, int64_t rows, int64_t cols, uint8_t* p
 qn_status nf4_dequantize(const qn_nf4dq* w, qn_dtype out_dtype, void* out, void* stream);
 
 /* Workspace bytes needed by qlora_linear_fwd (backward == 0) or
- * qlora_linear_bwd (backward != 0) for M rows of activations. */
+ * qlora_linear_bwd (backward != 0) for M rows of activations (at least
+ * QN_ARRIVAL_BYTES; the first QN_ARRIVAL_BYTES must be zero before first
+ * use, see the conventions above). */
 size_t qlora_linear_workspace(int64_t M, int64_t rows, int64_t cols, int r, int backward);
 
 /* Forward: y [M, rows] bf16 = X Qhat(W)^T + (alpha/r) (X A^T) B^T.
@@ -153,6 +165,22 @@ qn_status qlora_linear_bwd(const qn_nf4dq* w, const uint16_t* x, const uint16_t*
                            const uint16_t* A, const uint16_t* B, int r, float alpha,
                            const float* u_saved, uint16_t* dX, float* dA, float* dB,
                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* Kernel routes of the linear calls (qlora_linear_route). */
+enum {
+  QN_ROUTE_DECODE_ROWS = 1,  /* M <= 16: one kernel over bands of whole rows */
+  QN_ROUTE_DECODE_TILES = 2, /* M <= 16: one kernel over column slices of row bands */
+  QN_ROUTE_DECODE_SPLIT = 3, /* M <= 16, r > 16: partial sums, then a finishing kernel */
+  QN_ROUTE_FUSED_SMALL = 4,  /* M <= 32: dequantization inside 32-row GEMM tiles */
+  QN_ROUTE_FUSED = 5,        /* dequantization inside 128 x 128 GEMM tiles */
+  QN_ROUTE_DENSE = 6         /* bf16 copy of Qhat(W) in the workspace + dense GEMM */
+};
+
+/* Which route qlora_linear_fwd (backward == 0) or the dX product of
+ * qlora_linear_bwd (backward != 0) takes for these sizes on the current
+ * device; -1 for sizes the calls reject.  For tests and profiling: every
+ * route computes the same function. */
+int qlora_linear_route(int64_t M, int64_t rows, int64_t cols, int r, int backward);
 
 /* Dense LoRA linear on an already dequantized weight -- the forward's product
  * once Qhat(W) is held in bf16 (page 2, paragraph after the listing):

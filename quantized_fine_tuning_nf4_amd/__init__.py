@@ -28,7 +28,9 @@ QN_F32, QN_BF16 = 0, 1
 
 EXPORTS = ["qn_abi_version", "qn_status_str", "qn_nf4_codebook", "nf4_quantize_dq_workspace",
            "nf4_quantize_dq", "nf4_dequantize", "qlora_linear_workspace", "qlora_linear_fwd",
-           "qlora_linear_bwd", "lora_linear_bf16"]
+           "qlora_linear_bwd", "lora_linear_bf16", "qlora_linear_route"]
+ROUTES = {1: "decode_rows", 2: "decode_tiles", 3: "decode_split", 4: "fused_small", 5: "fused",
+          6: "dense"}
 
 
 class QNError(RuntimeError):
@@ -76,6 +78,8 @@ def load_library(path: str = LIB_PATH):
     L.qlora_linear_bwd.restype = ctypes.c_int
     L.lora_linear_bf16.argtypes = [P, I64, P, I64, I64, P, P, ctypes.c_int, ctypes.c_float, P, P]
     L.lora_linear_bf16.restype = ctypes.c_int
+    L.qlora_linear_route.argtypes = [I64, I64, I64, ctypes.c_int, ctypes.c_int]
+    L.qlora_linear_route.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -186,6 +190,23 @@ def nf4_dequantize(st: NF4State, dtype=torch.bfloat16, out: torch.Tensor | None 
     return out
 
 
+def route(M: int, rows: int, cols: int, r: int, backward: bool = False) -> str:
+    """Name of the kernel route of the forward (or of the backward's dX) for
+    these sizes on the current device."""
+    code = load_library().qlora_linear_route(M, rows, cols, r, int(bool(backward)))
+    if code < 0:
+        raise ValueError("sizes the linear calls reject")
+    return ROUTES[code]
+
+
+def linear_workspace(nbytes: int, device="cuda") -> torch.Tensor:
+    """A workspace for the linear calls: zeroed, because its first 4 KB are
+    arrival counters that must be zero before first use (every call leaves
+    them at zero).  One workspace may serve calls of any shape on one
+    stream, sized for the largest."""
+    return torch.zeros(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
 def _linear_args(st, x, A, B):
     M = x.shape[0]
     r = A.shape[0]
@@ -217,7 +238,7 @@ def qlora_linear_fwd(st: NF4State, x: torch.Tensor, A: torch.Tensor, B: torch.Te
     u = torch.empty((M, r), dtype=torch.float32, device=x.device) if save_u else None
     ws_bytes = L.qlora_linear_workspace(M, st.rows, st.cols, r, 0)
     if workspace is None or workspace.numel() < ws_bytes:
-        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=x.device)
+        workspace = linear_workspace(ws_bytes, x.device)
     s = st.c_struct()
     _check(L.qlora_linear_fwd(ctypes.byref(s), x.data_ptr(), M, A.data_ptr(), B.data_ptr(), r,
                               float(alpha), y.data_ptr(), _ptr(u), workspace.data_ptr(),
@@ -246,7 +267,7 @@ def qlora_linear_bwd(st: NF4State, x: torch.Tensor, dY: torch.Tensor, A: torch.T
     dB = torch.empty((st.rows, r), dtype=torch.float32, device=x.device)
     ws_bytes = L.qlora_linear_workspace(M, st.rows, st.cols, r, 1)
     if workspace is None or workspace.numel() < ws_bytes:
-        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=x.device)
+        workspace = linear_workspace(ws_bytes, x.device)
     s = st.c_struct()
     _check(L.qlora_linear_bwd(ctypes.byref(s), x.data_ptr(), dY.data_ptr(), M, A.data_ptr(),
                               B.data_ptr(), r, float(alpha), _ptr(u), _ptr(dX), dA.data_ptr(),

@@ -51,6 +51,7 @@ struct QuantWs {
 QuantWs carve_quant(Carver& c, int64_t n) {
   const int64_t nb = blocks_of(n), ng = groups_of(nb);
   QuantWs w;
+  c.take<unsigned>(kArrivalWords);  // left alone: a workspace may be shared with linear calls
   w.absmax = c.take<float>(nb);
   w.part_len = pow2_at_least(ng);
   w.part = c.take<double>(w.part_len);
@@ -69,12 +70,19 @@ qn_status check_state(const qn_nf4dq* w) {
   return QN_OK;
 }
 
+// Largest M and weight dimension the linear calls take: the kernels address
+// buffers through 32-bit offsets from a row or slice base, which these
+// bounds keep below 2^31 bytes.
+constexpr int64_t kMaxRowsM = (int64_t)1 << 23;
+constexpr int64_t kMaxDim = (int64_t)1 << 20;
+
 qn_status check_linear(const qn_nf4dq* w, int64_t M, int r) {
   qn_status s = check_state(w);
   if (s != QN_OK) return s;
   if (w->cols % kBlock != 0 || w->rows % 8 != 0) return QN_EINVAL;
+  if (w->rows > kMaxDim || w->cols > kMaxDim) return QN_EINVAL;
   if (r < 1 || r > 64) return QN_EINVAL;
-  if (M < 0) return QN_EINVAL;
+  if (M < 0 || M > kMaxRowsM) return QN_EINVAL;
   return QN_OK;
 }
 
@@ -91,6 +99,7 @@ bool dense_path(int64_t M, int64_t out_cols) {
 int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 
 struct FwdWs {
+  unsigned* arrivals;  // [kArrivalWords] arrival counters (zero between calls)
   float* u;      // [M, r] when the caller gives no u_out
   float* upart;  // [S, M, r] when S > 1
   int S;
@@ -104,8 +113,10 @@ struct FwdWs {
   int dbr;         // rows per band of the whole-row decode kernel (0: not used)
 };
 
-FwdWs carve_fwd(Carver& c, int64_t M, int64_t rows, int64_t cols, int r, bool need_u) {
+FwdWs carve_fwd(Carver& c, int64_t M, int64_t rows, int64_t cols, int r, bool need_u,
+                bool counters = true) {
   FwdWs f;
+  f.arrivals = counters ? c.take<unsigned>(kArrivalWords) : nullptr;
   f.dbr = rows > 0 ? decode_rows_band(M, rows, cols, r) : 0;
   f.dt = rows > 0 && f.dbr == 0 ? decode_tiles(M, rows, cols, r) : DecodeTiles{0, 0, 0};
   f.dS = rows > 0 && f.dbr == 0 && f.dt.rgt == 0 ? decode_slices(M, rows, cols) : 0;
@@ -122,6 +133,7 @@ FwdWs carve_fwd(Carver& c, int64_t M, int64_t rows, int64_t cols, int r, bool ne
 }
 
 struct BwdWs {
+  unsigned* arrivals;  // [kArrivalWords] arrival counters
   FwdWs fu;      // recomputed u (if not saved)
   uint16_t* Bt;  // [r, rows]
   float* v;      // [M, r]
@@ -140,10 +152,12 @@ struct BwdWs {
 
 BwdWs carve_bwd(Carver& c, int64_t M, int64_t rows, int64_t cols, int r, bool need_u) {
   BwdWs b;
+  b.arrivals = c.take<unsigned>(kArrivalWords);
   if (need_u) {
-    b.fu = carve_fwd(c, M, 0, cols, r, true);
+    b.fu = carve_fwd(c, M, 0, cols, r, true, false);
   } else {
-    b.fu = FwdWs{nullptr, nullptr, 1, nullptr, nullptr, nullptr, 0};
+    b.fu = FwdWs{};
+    b.fu.S = 1;
   }
   b.Bt = c.take<uint16_t>((size_t)r * rows);
   b.Sv = thin_nt_slices(M, rows);
@@ -166,6 +180,8 @@ BwdWs carve_bwd(Carver& c, int64_t M, int64_t rows, int64_t cols, int r, bool ne
 }  // namespace
 
 extern "C" {
+
+static_assert(QN_ARRIVAL_BYTES == 4 * kArrivalWords, "arrival counter page");
 
 int qn_abi_version(void) { return QN_ABI_VERSION; }
 
@@ -266,8 +282,8 @@ qn_status qlora_linear_fwd(const qn_nf4dq* w, const uint16_t* x, int64_t M, cons
   if (f.dbr > 0)  // decode-sized batch, whole rows per workgroup
     return from_hip(launch_decode_rows(to_state(w), x, M, A, B, r, scale, y, u, f.dbr, st));
   if (f.dt.rgt > 0)  // decode-sized batch, one kernel over column slices
-    return from_hip(launch_decode_tile(to_state(w), x, M, A, B, r, scale, y, u, f.dt, f.tpart,
-                                       f.tupart, st));
+    return from_hip(launch_decode_tile(to_state(w), x, M, A, B, r, scale, y, u, f.dt,
+                                       f.arrivals, f.tpart, f.tupart, st));
   if (f.dpart)  // decode-sized batch: u and the product in two kernels
     return from_hip(launch_decode_fwd(to_state(w), x, M, A, B, r, scale, y, u, f.dpart,
                                       f.dupart, f.dS, st));
@@ -315,14 +331,23 @@ qn_status qlora_linear_bwd(const qn_nf4dq* w, const uint16_t* x, const uint16_t*
   const float scale = alpha / (float)r;
   hipError_t e = hipSuccess;
   const float* u = u_saved;
+  // the first launch of the call zeroes the arrival counters the adapter
+  // gradients' launch counts on, so the backward never depends on what the
+  // workspace held before
+  Clear clr{b.arrivals, kArrivalWords};
   if (!u) {
-    e = launch_thin_nt(x, A, M, K, r, b.fu.u, b.fu.upart, b.fu.S, st);
+    e = launch_thin_nt(x, A, M, K, r, b.fu.u, b.fu.upart, b.fu.S, st, true, false, clr);
+    clr = Clear{nullptr, 0};
     u = b.fu.u;
   }
   // v = G B as slices (added below); the product takes B as stored when it
   // can, else B^T made first
   const bool b_rows = thin_nt_rows_ok(M, N, r);
   if (e == hipSuccess && !b_rows) {
+    if (clr.n) {  // (no earlier launch: a kernel, not a memset, for graph capture)
+      e = launch_fill_zero(reinterpret_cast<float*>(clr.p), clr.n, st);
+      clr = Clear{nullptr, 0};
+    }
     BwdAux t{};
     t.B = B;
     t.Bt = b.Bt;
@@ -331,7 +356,8 @@ qn_status qlora_linear_bwd(const qn_nf4dq* w, const uint16_t* x, const uint16_t*
     e = launch_bwd_aux(t, st);
   }
   if (e == hipSuccess)
-    e = launch_thin_nt(dY, b_rows ? B : b.Bt, M, N, r, b.v, b.vpart, b.Sv, st, false, b_rows);
+    e = launch_thin_nt(dY, b_rows ? B : b.Bt, M, N, r, b.v, b.vpart, b.Sv, st, false, b_rows,
+                       clr);
   // the small jobs: v's slice sum, (s u)^T and (s v)^T split for the
   // transposed products, A^T for the dense dX product; in spare workgroups of
   // the transposed dequantization when there is one
@@ -367,8 +393,22 @@ qn_status qlora_linear_bwd(const qn_nf4dq* w, const uint16_t* x, const uint16_t*
   // dB = s G^T u and dA = s v^T X in one launch (and their slice sums in one)
   if (e == hipSuccess)
     e = launch_thin_tn2(ThinTn{dY, b.su, N, dB, false, b.dBpart},
-                        ThinTn{x, b.sv, K, dA, true, b.dApart}, M, r, st);
+                        ThinTn{x, b.sv, K, dA, true, b.dApart}, M, r, b.arrivals, st);
   return from_hip(e);
+}
+
+int qlora_linear_route(int64_t M, int64_t rows, int64_t cols, int r, int backward) {
+  if (M < 1 || M > kMaxRowsM || rows < 8 || cols < kBlock || rows % 8 != 0 ||
+      cols % kBlock != 0 || rows > kMaxDim || cols > kMaxDim || r < 1 || r > 64)
+    return -1;
+  const int64_t out_cols = backward ? cols : rows;
+  if (!backward) {
+    if (decode_rows_band(M, rows, cols, r) > 0) return QN_ROUTE_DECODE_ROWS;
+    if (decode_tiles(M, rows, cols, r).rgt > 0) return QN_ROUTE_DECODE_TILES;
+    if (decode_slices(M, rows, cols) > 0) return QN_ROUTE_DECODE_SPLIT;
+  }
+  if (dense_path(M, out_cols)) return QN_ROUTE_DENSE;
+  return M <= 32 ? QN_ROUTE_FUSED_SMALL : QN_ROUTE_FUSED;
 }
 
 qn_status lora_linear_bf16(const uint16_t* x, int64_t M, const uint16_t* W, int64_t rows,

@@ -14,8 +14,6 @@
 // 64g + 16w .. +15), blocks z*nbs .. (z+1)*nbs-1 of every row; X's slice is
 // staged in LDS once for the four waves.  Partial sums go to part[z][m][n];
 // a second kernel adds the slices, the LoRA term and rounds to bf16.
-#include <atomic>
-
 #include "qn_device.h"
 #include "qn_internal.h"
 
@@ -231,9 +229,9 @@ __global__ __launch_bounds__(T) void k_decode_finish(const float* __restrict__ p
 //     u = X A^T go to the workspace through device-coherent stores; the last
 //     tile of a band to arrive (an arrival counter per band) adds the slices
 //     in slice order with device-coherent loads, adds s u B^T and writes bf16
-//     y, so the result does not depend on the order of arrival.  Counters
-//     live in a per-device table, one row per call slot, and are returned to
-//     zero by the tile that finishes the band.
+//     y, so the result does not depend on the order of arrival.  The
+//     counters live in the caller's workspace (zero before the call) and
+//     are returned to zero by the tile that finishes the band.
 constexpr int TT = 1024;
 constexpr int NWV = TT / 64;       // waves
 constexpr int NPR = 8;             // block pairs per slice
@@ -246,11 +244,9 @@ constexpr int L_TAB = 0, L_RING = 65536, L_U = L_RING + NWV * NST * UB;
 constexpr int L_URED = L_U + 16 * 17 * 4, L_QS = L_URED + NPR * 4 * 64 * 4;
 constexpr int L_S2 = L_QS + RGM * 16 * 16, L_FLAG = L_S2 + RGM * 16 * 4;
 constexpr int L_TOTAL = L_FLAG + 16;
-constexpr int kSlots = 64, kMaxBands = 1024;
+constexpr int kMaxBands = kArrivalWords;  // one arrival counter per band
 static_assert(NPR * RGM * 4 * 64 * 4 <= L_U, "reduction buffer overlaps");
 static_assert(L_TOTAL <= 160 * 1024, "LDS");
-
-__device__ unsigned g_band_arrivals[kSlots * kMaxBands];
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 __device__ __forceinline__ rsrc_t make_rs(const void* base, uint32_t bytes) {
@@ -291,10 +287,9 @@ __global__ __launch_bounds__(TT, 1) void k_decode_tile(
     const float* __restrict__ scale2, const float* __restrict__ offset,
     const uint16_t* __restrict__ X, int64_t M, int64_t N, int64_t K,
     const uint16_t* __restrict__ Aad, const uint16_t* __restrict__ Bad, int r, float s, int rgt,
-    int S, int slot, float* __restrict__ part, float* __restrict__ upart,
+    int S, unsigned* __restrict__ arrivals, float* __restrict__ part, float* __restrict__ upart,
     uint16_t* __restrict__ Y, float* __restrict__ u_out) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[L_TOTAL];
-  unsigned* arrivals = g_band_arrivals + (int64_t)slot * kMaxBands;  // this device's table
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int pr = wave & (NPR - 1), par = wave / NPR;
@@ -848,15 +843,14 @@ DecodeTiles decode_tiles(int64_t M, int64_t N, int64_t K, int r) {
 
 hipError_t launch_decode_tile(const WState& w, const uint16_t* X, int64_t M, const uint16_t* A,
                               const uint16_t* B, int r, float s, uint16_t* Y, float* u_out,
-                              const DecodeTiles& t, float* part, float* upart, hipStream_t st) {
+                              const DecodeTiles& t, unsigned* arrivals, float* part,
+                              float* upart, hipStream_t st) {
   const int64_t N = w.rows, K = w.cols;
   if (t.rgt < 1 || t.rgt > RGM || t.S != K / KSL || t.bands < 1 || t.bands > kMaxBands ||
-      (int64_t)t.bands * 16 * t.rgt < N || M < 1 || M > 16 || r < 1 || r > 16)
+      (int64_t)t.bands * 16 * t.rgt < N || M < 1 || M > 16 || r < 1 || r > 16 || !arrivals)
     return hipErrorInvalidValue;
-  static std::atomic<unsigned> next_slot{0};
-  const int slot = (int)(next_slot.fetch_add(1) % kSlots);
   hipLaunchKernelGGL(k_decode_tile, dim3((unsigned)(t.bands * t.S)), dim3(TT), 0, st, w.packed,
-                     w.qscale, w.scale2, w.offset, X, M, N, K, A, B, r, s, t.rgt, t.S, slot,
+                     w.qscale, w.scale2, w.offset, X, M, N, K, A, B, r, s, t.rgt, t.S, arrivals,
                      part, upart, Y, u_out);
   return hipGetLastError();
 }

@@ -10,8 +10,6 @@
 #include <algorithm>
 #include <type_traits>
 
-#include <atomic>
-
 #include "qn_device.h"
 #include "qn_internal.h"
 
@@ -39,6 +37,13 @@ __device__ __forceinline__ u32x4 load8(const uint16_t* row, int64_t p, int64_t P
   return u32x4{w[0], w[1], w[2], w[3]};
 }
 
+// The first workgroup of a launch zeroes clr.n words at clr.p (the arrival
+// counters a later kernel of the same call counts on).
+__device__ __forceinline__ void clear_words(const Clear& clr) {
+  if (blockIdx.x == 0 && blockIdx.y == 0)
+    for (int i = threadIdx.x; i < clr.n; i += blockDim.x) clr.p[i] = 0u;
+}
+
 }  // namespace
 
 // out[M, r] = Z[M, P] T[r, P]^T over column slice s.  Workgroup (mt, s):
@@ -51,9 +56,10 @@ template <int NJ>
 __global__ __launch_bounds__(kThreads) void k_thin_nt(const uint16_t* __restrict__ Z,
                                                       const uint16_t* __restrict__ T, int64_t M,
                                                       int64_t P, int r, int64_t slice,
-                                                      float* __restrict__ out) {
+                                                      float* __restrict__ out, Clear clr) {
   constexpr int U = NJ <= 2 ? 8 : 4;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  clear_words(clr);
   const int g = lane >> 4, l16 = lane & 15;
   const int64_t mw = (int64_t)blockIdx.x * 64 + 16 * wave;  // first row of the wave
   const int64_t m = min(mw + l16, M - 1);
@@ -112,9 +118,10 @@ template <int TMODE>
 __global__ __launch_bounds__(kThreads) void k_thin_nt1(const uint16_t* __restrict__ Z,
                                                        const uint16_t* __restrict__ T, int64_t M,
                                                        int64_t P, int r, int64_t slice,
-                                                       float* __restrict__ out) {
+                                                       float* __restrict__ out, Clear clr) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  clear_words(clr);
   const int g = lane >> 4, l16 = lane & 15;
   const int64_t mw = (int64_t)blockIdx.x * 64 + 16 * wave;
   const int64_t m = min(mw + l16, M - 1);
@@ -269,7 +276,8 @@ int thin_nt_slices(int64_t M, int64_t P) {
 }
 
 hipError_t launch_thin_nt(const uint16_t* Z, const uint16_t* T, int64_t M, int64_t P, int r,
-                          float* out, float* part, int S, hipStream_t st, bool sum, bool t_rows) {
+                          float* out, float* part, int S, hipStream_t st, bool sum, bool t_rows,
+                          Clear clr) {
   const int64_t slice = thin_nt_slice(P, S);
   const dim3 grid((unsigned)((M + 63) / 64), (unsigned)S);
   float* dst = S > 1 ? part : out;
@@ -289,18 +297,18 @@ hipError_t launch_thin_nt(const uint16_t* Z, const uint16_t* T, int64_t M, int64
     const int steps = (int)((slice + 31) / 32);
     const size_t lds = (size_t)16 * (steps * 64 + 16);
     if (mode == 0)
-      hipLaunchKernelGGL(k_thin_nt1<0>, grid, dim3(kThreads), lds, st, Z, T, M, P, r, slice, dst);
+      hipLaunchKernelGGL(k_thin_nt1<0>, grid, dim3(kThreads), lds, st, Z, T, M, P, r, slice, dst, clr);
     else if (mode == 1)
-      hipLaunchKernelGGL(k_thin_nt1<1>, grid, dim3(kThreads), lds, st, Z, T, M, P, r, slice, dst);
+      hipLaunchKernelGGL(k_thin_nt1<1>, grid, dim3(kThreads), lds, st, Z, T, M, P, r, slice, dst, clr);
     else
-      hipLaunchKernelGGL(k_thin_nt1<2>, grid, dim3(kThreads), lds, st, Z, T, M, P, r, slice, dst);
+      hipLaunchKernelGGL(k_thin_nt1<2>, grid, dim3(kThreads), lds, st, Z, T, M, P, r, slice, dst, clr);
   } else {
     if (t_rows) return hipErrorInvalidValue;  // the general kernel takes T as [r, P]
   switch ((r + 15) / 16) {
-    case 1: hipLaunchKernelGGL(k_thin_nt<1>, grid, dim3(kThreads), 0, st, Z, T, M, P, r, slice, dst); break;
-    case 2: hipLaunchKernelGGL(k_thin_nt<2>, grid, dim3(kThreads), 0, st, Z, T, M, P, r, slice, dst); break;
-    case 3: hipLaunchKernelGGL(k_thin_nt<3>, grid, dim3(kThreads), 0, st, Z, T, M, P, r, slice, dst); break;
-    default: hipLaunchKernelGGL(k_thin_nt<4>, grid, dim3(kThreads), 0, st, Z, T, M, P, r, slice, dst); break;
+    case 1: hipLaunchKernelGGL(k_thin_nt<1>, grid, dim3(kThreads), 0, st, Z, T, M, P, r, slice, dst, clr); break;
+    case 2: hipLaunchKernelGGL(k_thin_nt<2>, grid, dim3(kThreads), 0, st, Z, T, M, P, r, slice, dst, clr); break;
+    case 3: hipLaunchKernelGGL(k_thin_nt<3>, grid, dim3(kThreads), 0, st, Z, T, M, P, r, slice, dst, clr); break;
+    default: hipLaunchKernelGGL(k_thin_nt<4>, grid, dim3(kThreads), 0, st, Z, T, M, P, r, slice, dst, clr); break;
   }
   }
   if (S > 1 && sum) {
@@ -384,19 +392,19 @@ struct TnJob {
 };
 
 // Arrival counters of the column tiles of one launch (both jobs' tiles in
-// grid order), one row per call slot, taken round robin by the launcher and
+// grid order) sit in the caller's workspace: zero when the launch starts,
 // left at zero by the workgroup that finishes a tile.
-constexpr int kTnSlots = 64, kTnMaxTiles = 1024;
-__device__ unsigned g_tn_arrivals[kTnSlots * kTnMaxTiles];
+constexpr int kTnMaxTiles = kArrivalWords;
 constexpr int kDeviceScope = 16;  // sc1: the level every XCD shares
 
-// With slot >= 0 the slices are also added here: each workgroup stores its
-// slice with device-coherent stores, and the last of a column tile's S
-// workgroups to arrive (an arrival counter per tile) adds the S slices of
-// the tile in slice order with device-coherent loads and writes the output.
+// With arrivals != null the slices are also added here: each workgroup
+// stores its slice with device-coherent stores, and the last of a column
+// tile's S workgroups to arrive (an arrival counter per tile) adds the S
+// slices of the tile in slice order with device-coherent loads and writes
+// the output.
 template <int NJ>
 __global__ __launch_bounds__(kThreads) void k_thin_tn(TnJob j0, TnJob j1, int64_t M, int r,
-                                                      int slot) {
+                                                      unsigned* __restrict__ arrivals) {
   constexpr int ZB = 32 * TN_ROWB;             // Z bytes per stage
   constexpr int VB = 2 * 16 * NJ * 64;         // (sV)^T bytes per stage
   constexpr int SB = ZB + VB;
@@ -423,8 +431,10 @@ __global__ __launch_bounds__(kThreads) void k_thin_tn(TnJob j0, TnJob j1, int64_
   // (sV)^T loads: 4 of its 64-byte rows per 4-byte-per-lane instruction
   // (lane l: row 4q + l/16, word l%16), instruction q = 2 NJ w + k of the
   // step (all lanes active: no branch around a load into LDS).
-  const rsrc_t rz = make_rs(Z, (uint32_t)(M * P * 2));
-  const rsrc_t rv = make_rs(vt, (uint32_t)(2 * 16 * NJ * Mp * 2));
+  // descriptors start at the slice's first row, so that only one slice's
+  // bytes (below 2^31, thin_tn_slice_rows) are ever addressed by an offset
+  const rsrc_t rz = make_rs(Z + mb * P, (uint32_t)((me - mb) * P * 2));
+  const rsrc_t rv = make_rs(vt + mb, (uint32_t)((2 * 16 * NJ * Mp - mb) * 2));
   uint32_t zoff[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
@@ -437,7 +447,7 @@ __global__ __launch_bounds__(kThreads) void k_thin_tn(TnJob j0, TnJob j1, int64_
 #pragma unroll
   for (int k = 0; k < 2 * NJ; ++k) {
     const int q = 2 * NJ * wave + k, row = 4 * q + (lane >> 4);
-    voff[k] = (uint32_t)((row * Mp + mb) * 2 + 4 * (lane & 15));
+    voff[k] = (uint32_t)(row * Mp * 2 + 4 * (lane & 15));
   }
   auto load_step = [&](int st, int stage) {
     uint8_t* base = smem + stage * SB;
@@ -445,7 +455,7 @@ __global__ __launch_bounds__(kThreads) void k_thin_tn(TnJob j0, TnJob j1, int64_
     for (int h = 0; h < 2; ++h) {
       const int i = 2 * wave + h, row = 4 * i + (lane >> 4);
       const int64_t mm = min(mb + 32 * (int64_t)st + row, M - 1);
-      dma16(rz, zoff[h] + (uint32_t)(mm * P * 2), 0, base + 1024 * i);
+      dma16(rz, zoff[h] + (uint32_t)((mm - mb) * P * 2), 0, base + 1024 * i);
     }
 #pragma unroll
     for (int k = 0; k < 2 * NJ; ++k)
@@ -550,13 +560,13 @@ __global__ __launch_bounds__(kThreads) void k_thin_tn(TnJob j0, TnJob j1, int64_
                                                 kDeviceScope);
       }
   }
-  if (slot < 0) return;
+  if (!arrivals) return;
   // ---- arrival: every wave's stores have completed before the barrier, so
   // they precede the count; the last workgroup reads them after it
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   __shared__ int s_last;
-  unsigned* ctr = g_tn_arrivals + (int64_t)slot * kTnMaxTiles + blockIdx.x;
+  unsigned* ctr = arrivals + blockIdx.x;
   if (tid == 0)
     s_last = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
              (unsigned)(S_ - 1);
@@ -662,13 +672,17 @@ __global__ void k_sum_slices_tn(TnSum a, TnSum b, int r) {
 }
 
 // Slices of the M rows for the transposed products: enough workgroups to
-// fill the chip (about 512 per product), a multiple of 32 rows each.
+// fill the chip (about 512 per product), a multiple of 32 rows each, and
+// small enough that a slice of Z spans less than 2^31 bytes (the kernel
+// addresses one slice through a 32-bit buffer offset).
 int64_t thin_tn_slice_rows(int64_t M, int64_t P, int r) {
   (void)r;
   const int64_t pt = (P + TN_COLS - 1) / TN_COLS;
   const int64_t S = (512 + pt - 1) / pt;
   int64_t slice = (M + S - 1) / S;
   slice = (slice + 31) / 32 * 32;
+  const int64_t cap = ((((int64_t)1 << 31) - 1) / (2 * P)) / 32 * 32;
+  if (slice > cap) slice = cap;
   if (slice < 32) slice = 32;
   return slice;
 }
@@ -684,7 +698,7 @@ int64_t thin_tn_rows_padded(int64_t M, int64_t P, int r) {
 }
 
 hipError_t launch_thin_tn2(const ThinTn& a, const ThinTn& b, int64_t M, int r,
-                           hipStream_t st) {
+                           unsigned* arrivals, hipStream_t st) {
   const int nj = (r + 15) / 16;
   TnJob job[2];
   const ThinTn* in[2] = {&a, &b};
@@ -706,19 +720,18 @@ hipError_t launch_thin_tn2(const ThinTn& a, const ThinTn& b, int64_t M, int r,
   }
   const int tiles = job[0].tiles + job[1].tiles;
   if (tiles == 0) return hipSuccess;
-  // slices added by the last workgroup of each tile (a call slot of arrival
-  // counters), else by a second launch
-  static std::atomic<unsigned> next_slot{0};
-  const int slot = tiles <= kTnMaxTiles ? (int)(next_slot.fetch_add(1) % kTnSlots) : -1;
+  // slices added by the last workgroup of each tile (one arrival counter per
+  // tile), else by a second launch
+  unsigned* ctr = tiles <= kTnMaxTiles ? arrivals : nullptr;
   const size_t lds = (size_t)TN_NST * (32 * TN_ROWB + 2 * 16 * nj * 64);
   const dim3 grid((unsigned)tiles, (unsigned)s_max);
   switch (nj) {
-    case 1: hipLaunchKernelGGL(k_thin_tn<1>, grid, dim3(kThreads), lds, st, job[0], job[1], M, r, slot); break;
-    case 2: hipLaunchKernelGGL(k_thin_tn<2>, grid, dim3(kThreads), lds, st, job[0], job[1], M, r, slot); break;
-    case 3: hipLaunchKernelGGL(k_thin_tn<3>, grid, dim3(kThreads), lds, st, job[0], job[1], M, r, slot); break;
-    default: hipLaunchKernelGGL(k_thin_tn<4>, grid, dim3(kThreads), lds, st, job[0], job[1], M, r, slot); break;
+    case 1: hipLaunchKernelGGL(k_thin_tn<1>, grid, dim3(kThreads), lds, st, job[0], job[1], M, r, ctr); break;
+    case 2: hipLaunchKernelGGL(k_thin_tn<2>, grid, dim3(kThreads), lds, st, job[0], job[1], M, r, ctr); break;
+    case 3: hipLaunchKernelGGL(k_thin_tn<3>, grid, dim3(kThreads), lds, st, job[0], job[1], M, r, ctr); break;
+    default: hipLaunchKernelGGL(k_thin_tn<4>, grid, dim3(kThreads), lds, st, job[0], job[1], M, r, ctr); break;
   }
-  if (slot >= 0) return hipGetLastError();
+  if (ctr) return hipGetLastError();
   TnSum sum[2];
   int64_t count = 0;
   for (int k = 0; k < 2; ++k) {

@@ -7,6 +7,19 @@
 
 namespace qn {
 
+// Arrival counters: the first kArrivalWords 32-bit words of every linear
+// workspace.  They are zero before a call that counts on them (zeroed once
+// when the workspace is allocated, or by an earlier kernel of the same call)
+// and every workgroup that finishes a reduction puts its counter back to
+// zero, so the words are zero again when the call ends.
+constexpr int kArrivalWords = 1024;
+
+// n words at p to clear (by the first workgroup of a launch); n == 0: none.
+struct Clear {
+  unsigned* p;
+  int n;
+};
+
 // ws_bad [ng] per-group non-finite flags; *flag = 1 when any weight is NaN
 // or infinite, else 0 (written by the last kernel; no clearing needed).
 hipError_t launch_quantize(const float* W, int64_t n, uint8_t* packed, uint8_t* qscale,
@@ -199,10 +212,11 @@ struct WState {
 // the slices are written to part[S][M][r] and summed in slice order into
 // out; S == 1 writes out directly.
 // sum == false leaves the slices in part for the caller to add.  t_rows:
-// T is given as its transpose [P, r] (r <= 16 only).
+// T is given as its transpose [P, r] (r <= 16 only).  clr: words the first
+// workgroup zeroes.
 hipError_t launch_thin_nt(const uint16_t* Z, const uint16_t* T, int64_t M, int64_t P, int r,
                           float* out, float* part, int S, hipStream_t st, bool sum = true,
-                          bool t_rows = false);
+                          bool t_rows = false, Clear clr = Clear{nullptr, 0});
 int thin_nt_slices(int64_t M, int64_t P);
 bool thin_nt_rows_ok(int64_t M, int64_t P, int r);
 
@@ -224,11 +238,11 @@ struct ThinTn {
   float* part;
 };
 // Two such products (same M and r) in one launch; the slices are added by
-// the last workgroup of each column tile to finish (arrival counters in a
-// per-device table of 64 call slots, taken round robin: more than 64 such
-// calls in flight at once on one device would race), or, past 1024 column
-// tiles, by a second launch.
-hipError_t launch_thin_tn2(const ThinTn& a, const ThinTn& b, int64_t M, int r, hipStream_t st);
+// the last workgroup of each column tile to finish (arrivals: kArrivalWords
+// counters, zero at the launch and left at zero), or, past kArrivalWords
+// column tiles or with arrivals == null, by a second launch.
+hipError_t launch_thin_tn2(const ThinTn& a, const ThinTn& b, int64_t M, int r,
+                           unsigned* arrivals, hipStream_t st);
 int thin_tn_slices(int64_t M, int64_t P, int r);
 int64_t thin_tn_rows_padded(int64_t M, int64_t P, int r);
 
@@ -241,16 +255,17 @@ hipError_t launch_decode_fwd(const WState& w, const uint16_t* X, int64_t M, cons
 // One-kernel decode forward (M <= 16, r <= 16, cols % 1024 == 0): tiles of
 // 16 rgt rows x 1024 columns; S = cols / 1024 slices, `bands` row bands.
 // rgt == 0 when it does not apply.  Workspace: part [S, M, rows rounded up
-// to 4] and upart [bands, S, 256] fp32, 16-byte aligned.  Writes Y and u_out.  Calls on one device share
-// a table of 64 call slots of arrival counters (taken round robin): more than
-// 64 such calls in flight at once on one device would race.
+// to 4] and upart [bands, S, 256] fp32, 16-byte aligned; arrivals: one
+// counter per band (bands <= kArrivalWords), zero at the launch and left at
+// zero.  Writes Y and u_out.
 struct DecodeTiles {
   int rgt, S, bands;
 };
 DecodeTiles decode_tiles(int64_t M, int64_t rows, int64_t cols, int r);
 hipError_t launch_decode_tile(const WState& w, const uint16_t* X, int64_t M, const uint16_t* A,
                               const uint16_t* B, int r, float s, uint16_t* Y, float* u_out,
-                              const DecodeTiles& t, float* part, float* upart, hipStream_t st);
+                              const DecodeTiles& t, unsigned* arrivals, float* part,
+                              float* upart, hipStream_t st);
 
 // Whole-row decode forward (M <= 16, r <= 16, cols 2048 or 4096): bands of
 // `br` rows (a multiple of 8, at most 64), one workgroup each, every column;

@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol(qn):
 
 def test_abi_version_and_status_strings(qn):
     L = qn.load_library()
-    assert L.qn_abi_version() == 2
+    assert L.qn_abi_version() == 3
     for s in range(6):
         assert len(L.qn_status_str(s)) > 0
     assert L.qn_status_str(0) == b"ok"
@@ -57,19 +57,22 @@ def test_library_codebook_equals_page_table(qn):
 
 def test_workspace_sizes(qn):
     L = qn.load_library()
-    # absmax fp32 [nb] | fp64 partials [pow2(ng)] | group flags int [ng] | flag,
-    # 256-aligned pieces
+    # arrival-counter page (left alone by the quantizer) | absmax fp32 [nb] |
+    # fp64 partials [pow2(ng)] | group flags int [ng] | flag, 256-aligned pieces
     nb, ng = 262144, 1024
-    want = nb * 4 + ng * 8 + ng * 4 + 4
+    want = 4096 + nb * 4 + ng * 8 + ng * 4 + 4
     assert L.nf4_quantize_dq_workspace(4096, 4096) == want
     assert L.nf4_quantize_dq_workspace(0, 5) == 0
-    assert L.qlora_linear_workspace(8192, 4096, 4096, 16, 0) >= 8192 * 16 * 4
+    assert L.qlora_linear_workspace(8192, 4096, 4096, 16, 0) >= 4096 + 8192 * 16 * 4
     b = L.qlora_linear_workspace(8192, 4096, 4096, 16, 1)
-    assert b >= 8192 * 16 * 4 * 2 + 16 * 4096 * 2
+    assert b >= 4096 + 8192 * 16 * 4 * 2 + 16 * 4096 * 2
     assert L.qlora_linear_workspace(1, 8, 64, 65, 0) == 0
     # an empty batch is legal: its workspace query must not fault on the host
-    assert L.qlora_linear_workspace(0, 4096, 4096, 16, 0) == 0
-    assert L.qlora_linear_workspace(0, 4096, 4096, 16, 1) >= 0
+    # (the counter page is always part of a linear workspace)
+    assert L.qlora_linear_workspace(0, 4096, 4096, 16, 0) == 4096
+    assert L.qlora_linear_workspace(0, 4096, 4096, 16, 1) >= 4096
+    # the largest batch the calls accept still sizes on the host
+    assert L.qlora_linear_workspace(1 << 23, 14336, 4096, 16, 1) > (1 << 23) * 16 * 4
 
 
 FAKE = 1 << 20  # a non-null, 256-aligned address that is never dereferenced
@@ -118,6 +121,13 @@ def test_argument_errors_are_host_side(qn):
                               FAKE, FAKE, FAKE, 10, None) == EWS
     assert L.qlora_linear_bwd(ctypes.byref(s), FAKE, FAKE, 2, FAKE, FAKE, 4, 8.0, None, FAKE,
                               None, FAKE, FAKE, 1 << 20, None) == EINVAL
+    # sizes past what the kernels' 32-bit buffer offsets allow are refused
+    for rows, cols, M in [(8, 64, (1 << 23) + 1), ((1 << 20) + 8, 64, 2), (8, (1 << 20) + 64, 2)]:
+        s2 = _state(rows, cols)
+        assert L.qlora_linear_fwd(ctypes.byref(s2), FAKE, M, FAKE, FAKE, 4, 8.0, FAKE, None, FAKE,
+                                  1 << 40, None) == EINVAL
+        assert L.qlora_linear_bwd(ctypes.byref(s2), FAKE, FAKE, M, FAKE, FAKE, 4, 8.0, None,
+                                  FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == EINVAL
     # M == 0 forward is a no-op that touches nothing
     assert L.qlora_linear_fwd(ctypes.byref(s), None, 0, None, None, 4, 8.0, None, None, None, 0,
                               None) == qn.QN_OK

@@ -255,10 +255,10 @@ def test_adapter_grads_repeat_identical(qn, rows, cols, M, r):
 ])
 def test_backward_in_a_graph_replays_exactly(qn, rows, cols, M, r):
     """The backward captured in a HIP graph: every replay, with eager
-    backward calls between replays (other counter slots), equals the eager
+    backward calls between replays (their own workspaces), equals the eager
     result bit for bit: the slices of dA and dB are added in slice order by
     whichever workgroup of a column tile arrives last, and the arrival
-    counters are back at zero after each call."""
+    counters are cleared by the call's first kernel."""
     c = Case(rows, cols, M, r, 2.0 * r, seed=rows + 5 * r)
     say(f"[linear] backward graph replays: rows={rows} cols={cols} M={M} r={r}")
     st, x, A, B, G = c.dev(qn)
@@ -330,8 +330,7 @@ def test_decode_calls_sharing_a_workspace_see_fresh_inputs(qn, rows, M):
     ref1, _ = qn.qlora_linear_fwd(st, x1, A, B, c.alpha)
     ref2, _ = qn.qlora_linear_fwd(st, x2, A, B, c.alpha)
     L = qn.load_library()
-    ws = torch.zeros(max(L.qlora_linear_workspace(M, rows, 4096, 16, 0), 1), dtype=torch.uint8,
-                     device="cuda")
+    ws = qn.linear_workspace(L.qlora_linear_workspace(M, rows, 4096, 16, 0))
     for xin, ref in ((x1, ref1), (x2, ref2), (x1, ref1), (x2, ref2)):
         y, _ = qn.qlora_linear_fwd(st, xin, A, B, c.alpha, workspace=ws)
         torch.cuda.synchronize()
@@ -349,8 +348,7 @@ def test_decode_forward_in_a_graph_replays_exactly(qn, rows):
     y = torch.empty_like(y_ref)
     u = torch.empty_like(u_ref)
     L = qn.load_library()
-    ws = torch.empty(L.qlora_linear_workspace(4, rows, 4096, 16, 0), dtype=torch.uint8,
-                     device="cuda")
+    ws = qn.linear_workspace(L.qlora_linear_workspace(4, rows, 4096, 16, 0))
     s = st.c_struct()
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()

@@ -1,0 +1,275 @@
+"""GPU parity on every kernel route of the linear calls:
+
+* the adapter term isolated on each route (W = 0: y and dX are the adapter
+  terms alone; B = 0: y is exactly the base output and dA exactly zero), so
+  a fault in the LoRA path cannot hide under the base product's share of the
+  5e-3 budget;
+* exact one-hot pins through the decode kernels (every block's absmax equal,
+  so the dequantization scale is one power of two and each output is one
+  exact product);
+* the decoder layer's seven linears at their own shapes;
+* calls on two streams with their own workspaces, and a graph replay beside
+  them, stay bit-identical (the library keeps no state between calls).
+
+Routes are named by qlora_linear_route; every expected value comes from the
+CPU oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+from tests._gpu import REL_TOL, bf16_dev, bf16_host_f64, f32_dev, needs_gpu, rel_err, say
+
+pytestmark = [pytest.mark.gpu, needs_gpu]
+
+
+@pytest.fixture(scope="module")
+def qn():
+    import quantized_fine_tuning_nf4_amd as qn
+    qn.load_library()
+    return qn
+
+
+# (rows, cols, M, r): one shape per forward route and per dX route
+FWD_ROUTES = {
+    "decode_rows": (14336, 4096, 4, 16),
+    "decode_tiles": (4096, 4096, 4, 16),
+    "decode_split": (2048, 2048, 8, 32),
+    "fused_small": (264, 192, 24, 8),
+    "fused": (520, 576, 300, 16),
+    "dense": (3848, 3840, 4100, 16),
+}
+DX_ROUTES = {
+    "fused_small": (264, 192, 24, 8),
+    "fused": (520, 576, 300, 16),
+    "dense": (3848, 3840, 4100, 16),
+}
+
+
+def test_shapes_take_the_routes_they_are_named_for(qn):
+    for name, (rows, cols, M, r) in FWD_ROUTES.items():
+        assert qn.route(M, rows, cols, r) == name, name
+    for name, (rows, cols, M, r) in DX_ROUTES.items():
+        assert qn.route(M, rows, cols, r, backward=True) == name, name
+
+
+def _sample(M, k=48, seed=0):
+    if M <= k:
+        return np.arange(M)
+    rng = np.random.default_rng(seed)
+    return np.sort(np.concatenate([[0, M - 1], rng.choice(np.arange(1, M - 1), k - 2, False)]))
+
+
+def _inputs(rows, cols, M, r, seed, adapter_std=0.05):
+    W = wl.weight(rows, cols, seed)
+    x = wl.normal_bf16((M, cols), seed + 1, 1.0)
+    A = wl.normal_bf16((r, cols), seed + 2, adapter_std)
+    B = wl.normal_bf16((rows, r), seed + 3, adapter_std)
+    G = wl.normal_bf16((M, rows), seed + 4, 1.0)
+    return W, x, A, B, G
+
+
+ALL_ROUTES = sorted(set(FWD_ROUTES) | {"dx_" + k for k in DX_ROUTES})
+
+
+@pytest.mark.parametrize("route", sorted(FWD_ROUTES))
+def test_zero_weight_isolates_adapter_term(qn, route):
+    """W = 0 (every block all zeros): y = s (x A^T) B^T and dX = s (G B) A
+    alone, within 5e-3 of the fp64 oracle, on each forward route (and the
+    dX route of the same sizes)."""
+    rows, cols, M, r = FWD_ROUTES[route]
+    say(f"[paths] W=0 route={route} rows={rows} cols={cols} M={M} r={r}")
+    W, x, A, B, G = _inputs(rows, cols, M, r, seed=101 + rows)
+    W[:] = 0
+    alpha = 2.0 * r
+    s = float(np.float32(alpha) / np.float32(r))
+    st = qn.nf4_quantize_dq(f32_dev(W))
+    xd, Ad, Bd, Gd = (bf16_dev(a) for a in (x, A, B, G))
+    y, u = qn.qlora_linear_fwd(st, xd, Ad, Bd, alpha)
+    dX, dA, dB = qn.qlora_linear_bwd(st, xd, Gd, Ad, Bd, alpha, u)
+    torch.cuda.synchronize()
+    Wd = np.zeros((rows, cols), np.float32)
+    sel = _sample(M, seed=rows)
+    Y_ref, _ = oracle.qlora_fwd(Wd, x, A, B, s, rows=sel)
+    dX_ref, _ = oracle.qlora_dx(Wd, G, A, B, s, rows=sel)
+    dA_ref, dB_ref = oracle.adapter_grads(x, G, A, B, s)
+    errs = dict(y=rel_err(bf16_host_f64(y)[sel], Y_ref), dX=rel_err(bf16_host_f64(dX)[sel], dX_ref),
+                dA=rel_err(dA.cpu().numpy(), dA_ref), dB=rel_err(dB.cpu().numpy(), dB_ref))
+    say("  rel err", {k: f"{v:.2e}" for k, v in errs.items()},
+        "dX route", qn.route(M, rows, cols, r, backward=True))
+    assert all(e <= REL_TOL for e in errs.values()), errs
+
+
+@pytest.mark.parametrize("route", sorted(FWD_ROUTES))
+def test_adapter_b_zero_leaves_base_exact(qn, route):
+    """B = 0: y equals the alpha = 0 output bit for bit, dA is exactly zero
+    and dB is not, on each forward route (and the dX route of the sizes)."""
+    rows, cols, M, r = FWD_ROUTES[route]
+    say(f"[paths] B=0 route={route} rows={rows} cols={cols} M={M} r={r}")
+    W, x, A, B, G = _inputs(rows, cols, M, r, seed=202 + rows)
+    B[:] = 0
+    st = qn.nf4_quantize_dq(f32_dev(W))
+    xd, Ad, Bd, Gd = (bf16_dev(a) for a in (x, A, B, G))
+    y, u = qn.qlora_linear_fwd(st, xd, Ad, Bd, 2.0 * r)
+    y0, _ = qn.qlora_linear_fwd(st, xd, Ad, Bd, 0.0)
+    dX, dA, dB = qn.qlora_linear_bwd(st, xd, Gd, Ad, Bd, 2.0 * r, u)
+    dX0, _, _ = qn.qlora_linear_bwd(st, xd, Gd, Ad, Bd, 0.0, u)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y0)
+    assert torch.equal(dX, dX0)
+    assert int(torch.count_nonzero(dA)) == 0 and float(dB.abs().sum()) > 0
+
+
+def _equal_absmax_weight(rows, cols, seed):
+    """Every 64-block holds one element of +-0.25 and the rest inside
+    (-0.2, 0.2): all block scales are 0.25, so their mean is 0.25, every
+    group's spread C2 is 0 and the dequantization scale s' is exactly 0.25
+    for every block (a power of two: L[c] s' and bf16(L[c]) s' are exact)."""
+    rng = np.random.default_rng(seed)
+    W = rng.uniform(-0.2, 0.2, (rows, cols)).astype(np.float32)
+    pos = rng.integers(0, 64, size=(rows, cols // 64))
+    sign = np.where(rng.integers(0, 2, size=pos.shape) == 1, 1.0, -1.0).astype(np.float32)
+    W.reshape(rows, cols // 64, 64)[np.arange(rows)[:, None], np.arange(cols // 64)[None, :],
+                                    pos] = 0.25 * sign
+    return W
+
+
+@pytest.mark.parametrize("rows,cols,r,route", [
+    (14336, 4096, 16, "decode_rows"),
+    (4096, 4096, 16, "decode_tiles"),
+    (2048, 2048, 32, "decode_split"),
+])
+def test_decode_one_hot_reads_every_column_exactly(qn, rows, cols, r, route):
+    """x rows = e_k (16 per call, every column k over the calls), B = 0:
+    y[m, :] = bf16(W'[:, k]) exactly through the decode kernels, which scale
+    each block's fp32 partial by s' (exact here: s' = 0.25)."""
+    assert qn.route(16, rows, cols, r) == route
+    say(f"[paths] decode one-hot route={route} rows={rows} cols={cols}")
+    W = _equal_absmax_weight(rows, cols, seed=rows + cols)
+    ref = oracle.quantize(W)
+    assert ref.offset == np.float32(0.25) and not ref.scale2.any() and not ref.qscale.any()
+    _, Wb = oracle.dequantize(ref, want_f32=False)
+    st = qn.nf4_quantize_dq(f32_dev(W))
+    A = bf16_dev(wl.normal_bf16((r, cols), 7, 0.01))
+    B = torch.zeros((rows, r), dtype=torch.bfloat16, device="cuda")
+    eye = torch.zeros((cols, cols), dtype=torch.bfloat16, device="cuda")
+    eye.fill_diagonal_(1.0)
+    got = torch.empty((cols, rows), dtype=torch.bfloat16, device="cuda")
+    ws = qn.linear_workspace(qn.load_library().qlora_linear_workspace(16, rows, cols, r, 0))
+    for k0 in range(0, cols, 16):
+        qn.qlora_linear_fwd(st, eye[k0:k0 + 16], A, B, 2.0 * r, y=got[k0:k0 + 16], workspace=ws)
+    torch.cuda.synchronize()
+    want = wl.bf16_bits_to_f32(np.ascontiguousarray(Wb.T))
+    assert np.array_equal(got.float().cpu().numpy(), want)
+    # M = 1 and M = 4 on a few columns
+    for M in (1, 4):
+        ks = (np.arange(M) * 997 + 13) % cols
+        x = eye[torch.from_numpy(ks).cuda()].contiguous()
+        y, _ = qn.qlora_linear_fwd(st, x, A, B, 2.0 * r)
+        torch.cuda.synchronize()
+        assert np.array_equal(y.float().cpu().numpy(), want[ks])
+
+
+def test_decoder_layer_linears(qn):
+    """The decoder-layer workload's seven linears (q 4096->4096, k/v
+    4096->1024, o 4096->4096, gate/up 4096->14336, down 14336->4096) at
+    M = 4096, rank 16, alpha 32: y and dX on 48 sampled rows and dA, dB in
+    full against the fp64 oracle."""
+    cfg = wl.DECODER_LAYER
+    M, r, alpha = cfg["M"], cfg["r"], cfg["alpha"]
+    s = alpha / r
+    for idx, (name, N, K) in enumerate(wl.DECODER_LINEARS):
+        say(f"[paths] decoder layer {name}: {N}x{K} M={M} routes fwd="
+            f"{qn.route(M, N, K, r)} dX={qn.route(M, N, K, r, backward=True)}")
+        W, x, A, B, G = wl.linear_inputs(N, K, M, r, seed=cfg["seed"], index=idx)
+        st = qn.nf4_quantize_dq(f32_dev(W))
+        xd, Ad, Bd, Gd = (bf16_dev(a) for a in (x, A, B, G))
+        y, u = qn.qlora_linear_fwd(st, xd, Ad, Bd, alpha)
+        dX, dA, dB = qn.qlora_linear_bwd(st, xd, Gd, Ad, Bd, alpha, u)
+        torch.cuda.synchronize()
+        Wd, _ = oracle.dequantize(oracle.quantize(W), want_bf16=False)
+        sel = _sample(M, seed=idx)
+        Y_ref, _ = oracle.qlora_fwd(Wd, x, A, B, s, rows=sel)
+        dX_ref, _ = oracle.qlora_dx(Wd, G, A, B, s, rows=sel)
+        dA_ref, dB_ref = oracle.adapter_grads(x, G, A, B, s)
+        errs = dict(y=rel_err(bf16_host_f64(y)[sel], Y_ref),
+                    dX=rel_err(bf16_host_f64(dX)[sel], dX_ref),
+                    dA=rel_err(dA.cpu().numpy(), dA_ref), dB=rel_err(dB.cpu().numpy(), dB_ref))
+        say("  rel err", {k: f"{v:.2e}" for k, v in errs.items()})
+        assert all(e <= REL_TOL for e in errs.values()), (name, errs)
+        del st, xd, Ad, Bd, Gd, y, u, dX, dA, dB
+
+
+@pytest.mark.parametrize("rows,cols,M,r", [
+    (4096, 4096, 4, 16),     # decode over column slices (arrival counters) + fused dX
+    (1024, 1024, 4100, 13),  # adapter-gradient slices summed by arrival (scalar finish)
+])
+def test_two_streams_with_own_workspaces(qn, rows, cols, M, r):
+    """Forward + backward captured in a HIP graph (one workspace shared by
+    both calls) and replayed on one stream while the same calls run eagerly
+    on a second stream with a workspace of their own: both give the eager
+    single-stream results bit for bit, replay after replay."""
+    say(f"[paths] two streams rows={rows} cols={cols} M={M} r={r}")
+    W, x, A, B, G = _inputs(rows, cols, M, r, seed=303 + rows, adapter_std=0.01)
+    alpha = 2.0 * r
+    st = qn.nf4_quantize_dq(f32_dev(W))
+    xd, Ad, Bd, Gd = (bf16_dev(a) for a in (x, A, B, G))
+    y_ref, u_ref = qn.qlora_linear_fwd(st, xd, Ad, Bd, alpha)
+    dX_ref, dA_ref, dB_ref = qn.qlora_linear_bwd(st, xd, Gd, Ad, Bd, alpha, u_ref)
+    L = qn.load_library()
+    nbytes = max(L.qlora_linear_workspace(M, rows, cols, r, 0),
+                 L.qlora_linear_workspace(M, rows, cols, r, 1))
+    ws1, ws2 = qn.linear_workspace(nbytes), qn.linear_workspace(nbytes)
+    outs = [dict(y=torch.empty_like(y_ref), u=torch.empty_like(u_ref), dX=torch.empty_like(dX_ref),
+                 dA=torch.empty_like(dA_ref), dB=torch.empty_like(dB_ref)) for _ in range(2)]
+    s = st.c_struct()
+
+    def call(o, ws):
+        stream = torch.cuda.current_stream().cuda_stream
+        assert L.qlora_linear_fwd(qn.ctypes.byref(s), xd.data_ptr(), M, Ad.data_ptr(),
+                                  Bd.data_ptr(), r, float(alpha), o["y"].data_ptr(),
+                                  o["u"].data_ptr(), ws.data_ptr(), ws.numel(), stream) == 0
+        assert L.qlora_linear_bwd(qn.ctypes.byref(s), xd.data_ptr(), Gd.data_ptr(), M,
+                                  Ad.data_ptr(), Bd.data_ptr(), r, float(alpha),
+                                  o["u"].data_ptr(), o["dX"].data_ptr(), o["dA"].data_ptr(),
+                                  o["dB"].data_ptr(), ws.data_ptr(), ws.numel(), stream) == 0
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call(outs[0], ws1)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    for k in range(3):
+        for o in outs:
+            for t in o.values():
+                t.zero_()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s1):
+            g.replay()
+        with torch.cuda.stream(s2):
+            call(outs[1], ws2)
+            call(outs[1], ws2)
+        torch.cuda.synchronize()
+        for o in outs:
+            assert torch.equal(o["y"], y_ref) and torch.equal(o["u"], u_ref), k
+            assert torch.equal(o["dX"], dX_ref) and torch.equal(o["dA"], dA_ref), k
+            assert torch.equal(o["dB"], dB_ref), k
+
+
+def test_backward_clears_its_counters(qn):
+    """A backward workspace that holds garbage (all bytes 0xff) gives the
+    same gradients: the backward's first kernel zeroes the arrival counters
+    its adapter-gradient launch counts on."""
+    rows, cols, M, r = 1024, 1024, 4100, 16
+    W, x, A, B, G = _inputs(rows, cols, M, r, seed=404, adapter_std=0.01)
+    st = qn.nf4_quantize_dq(f32_dev(W))
+    xd, Ad, Bd, Gd = (bf16_dev(a) for a in (x, A, B, G))
+    ref = qn.qlora_linear_bwd(st, xd, Gd, Ad, Bd, 32.0, None)
+    ws = torch.full((qn.load_library().qlora_linear_workspace(M, rows, cols, r, 1),), 255,
+                    dtype=torch.uint8, device="cuda")
+    for saved_u in (None, qn.qlora_linear_fwd(st, xd, Ad, Bd, 32.0)[1]):
+        ws.fill_(255)
+        got = qn.qlora_linear_bwd(st, xd, Gd, Ad, Bd, 32.0, saved_u, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(got[0], ref[0]) and torch.equal(got[1], ref[1])
+        assert rel_err(got[2].cpu().numpy(), ref[2].cpu().numpy().astype(np.float64)) <= 1e-5
