@@ -154,6 +154,22 @@ qn_status qlora_linear_fwd(const qn_nf4dq* w, const uint16_t* x, int64_t M, cons
                            const uint16_t* B, int r, float alpha, uint16_t* y, float* u_out,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/* The forward without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  Same arguments, results and
+ * routes as qlora_linear_fwd (bit-identical output), but its scratch memory
+ * is a file-scope device array of QN_STATIC_SCRATCH_BYTES inside the
+ * library, one per GPU, held until the process ends; the call allocates
+ * nothing.  Sizes whose forward needs more scratch than that (the large-
+ * batch route, which keeps a bf16 copy of the weight) return QN_EWORKSPACE.
+ * All calls on one GPU share that GPU's array: calls that overlap in time on
+ * one GPU (other streams, other threads) race.  The array keeps what the
+ * last call left in it; the call clears what must start at zero. */
+#define QN_STATIC_SCRATCH_BYTES (16u << 20)
+qn_status qlora_linear_fwd_noalloc(const qn_nf4dq* w, const uint16_t* x, int64_t M,
+                                   const uint16_t* A, const uint16_t* B, int r, float alpha,
+                                   uint16_t* y, float* u_out, void* stream);
+
 /* Backward: from G = dY [M, rows] bf16 computes
  *   dX [M, cols] bf16 = G Qhat(W) + s (G B) A      (skipped if dX == NULL)
  *   dA [r, cols] fp32 = s (G B)^T X                 (overwritten)

@@ -28,7 +28,8 @@ QN_F32, QN_BF16 = 0, 1
 
 EXPORTS = ["qn_abi_version", "qn_status_str", "qn_nf4_codebook", "nf4_quantize_dq_workspace",
            "nf4_quantize_dq", "nf4_dequantize", "qlora_linear_workspace", "qlora_linear_fwd",
-           "qlora_linear_bwd", "lora_linear_bf16", "qlora_linear_route"]
+           "qlora_linear_bwd", "lora_linear_bf16", "qlora_linear_route",
+           "qlora_linear_fwd_noalloc"]
 ROUTES = {1: "decode_rows", 2: "decode_tiles", 3: "decode_split", 4: "fused_small", 5: "fused",
           6: "dense"}
 
@@ -78,6 +79,9 @@ def load_library(path: str = LIB_PATH):
     L.qlora_linear_bwd.restype = ctypes.c_int
     L.lora_linear_bf16.argtypes = [P, I64, P, I64, I64, P, P, ctypes.c_int, ctypes.c_float, P, P]
     L.lora_linear_bf16.restype = ctypes.c_int
+    L.qlora_linear_fwd_noalloc.argtypes = [ctypes.POINTER(_NF4DQ), P, I64, P, P, ctypes.c_int,
+                                           ctypes.c_float, P, P, P]
+    L.qlora_linear_fwd_noalloc.restype = ctypes.c_int
     L.qlora_linear_route.argtypes = [I64, I64, I64, ctypes.c_int, ctypes.c_int]
     L.qlora_linear_route.restype = ctypes.c_int
     _lib = L

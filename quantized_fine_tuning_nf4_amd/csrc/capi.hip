@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstring>
+#include <mutex>
 
 #include "../../include/qlora_nf4.h"
 #include "qn_device.h"
@@ -177,6 +178,84 @@ BwdWs carve_bwd(Carver& c, int64_t M, int64_t rows, int64_t cols, int r, bool ne
   return b;
 }
 
+// The forward, on a workspace of ws_bytes at ws; clear: zero the arrival
+// counters with a kernel before the launch that counts on them.
+qn_status forward(const qn_nf4dq* w, const uint16_t* x, int64_t M, const uint16_t* A,
+                  const uint16_t* B, int r, float alpha, uint16_t* y, float* u_out,
+                  void* workspace, size_t workspace_bytes, void* stream, bool clear) {
+  qn_status s = check_linear(w, M, r);
+  if (s != QN_OK) return s;
+  if (M == 0) return QN_OK;
+  if (!x || !A || !B || !y) return QN_EINVAL;
+  if (!aligned16(x) || !aligned16(A) || !aligned16(B) || !aligned16(y) ||
+      (u_out && !aligned16(u_out)))
+    return QN_EALIGN;
+  Carver probe(nullptr);
+  carve_fwd(probe, M, w->rows, w->cols, r, u_out == nullptr);
+  if (probe.used > 0) {
+    if (!workspace) return QN_EINVAL;
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u) return QN_EALIGN;
+    if (workspace_bytes < probe.used) return QN_EWORKSPACE;
+  }
+  Carver c(workspace);
+  FwdWs f = carve_fwd(c, M, w->rows, w->cols, r, u_out == nullptr);
+  float* u = u_out ? u_out : f.u;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const float scale = alpha / (float)r;
+  const int64_t N = w->rows, K = w->cols;
+  if (f.dbr > 0)  // decode-sized batch, whole rows per workgroup
+    return from_hip(launch_decode_rows(to_state(w), x, M, A, B, r, scale, y, u, f.dbr, st));
+  if (f.dt.rgt > 0) {  // decode-sized batch, one kernel over column slices
+    hipError_t e = hipSuccess;
+    if (clear) e = launch_fill_zero(reinterpret_cast<float*>(f.arrivals), kArrivalWords, st);
+    if (e == hipSuccess)
+      e = launch_decode_tile(to_state(w), x, M, A, B, r, scale, y, u, f.dt, f.arrivals, f.tpart,
+                             f.tupart, st);
+    return from_hip(e);
+  }
+  if (f.dpart)  // decode-sized batch: u and the product in two kernels
+    return from_hip(launch_decode_fwd(to_state(w), x, M, A, B, r, scale, y, u, f.dpart,
+                                      f.dupart, f.dS, st));
+  // dense path: the slices of u are added by spare workgroups of the
+  // dequantization launch that follows
+  const bool fold = f.wd && f.S > 1;
+  hipError_t e = launch_thin_nt(x, A, M, K, r, u, f.upart, f.S, st, !fold);
+  if (f.wd) {
+    if (e == hipSuccess)
+      e = launch_dequant(w->packed, w->qscale, w->scale2, w->offset, N * K, true, f.wd, st,
+                         fold ? SliceSum{f.upart, M * (int64_t)r, f.S, u} : SliceSum{});
+    if (e == hipSuccess) e = launch_gemm_nt(x, K, K, f.wd, K, M, N, u, B, r, scale, y, st);
+  } else if (e == hipSuccess) {
+    e = launch_qgemm_fwd(to_state(w), x, M, u, B, r, scale, y, st);
+  }
+  return from_hip(e);
+}
+
+// Scratch of qlora_linear_fwd_noalloc: a file-scope device array, one copy
+// per GPU, held until the process ends.  Host code never passes its name to
+// a kernel (on the host it is only a stand-in for the symbol): it uses the
+// device address hipGetSymbolAddress returns for the current device.
+constexpr size_t kStaticScratchBytes = QN_STATIC_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// This device's address of the scratch array (looked up once per device).
+qn_status static_scratch(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return QN_EDEVICE;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return QN_EDEVICE;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return QN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -259,48 +338,27 @@ size_t qlora_linear_workspace(int64_t M, int64_t rows, int64_t cols, int r, int 
 qn_status qlora_linear_fwd(const qn_nf4dq* w, const uint16_t* x, int64_t M, const uint16_t* A,
                            const uint16_t* B, int r, float alpha, uint16_t* y, float* u_out,
                            void* workspace, size_t workspace_bytes, void* stream) {
+  return forward(w, x, M, A, B, r, alpha, y, u_out, workspace, workspace_bytes, stream, false);
+}
+
+qn_status qlora_linear_fwd_noalloc(const qn_nf4dq* w, const uint16_t* x, int64_t M,
+                                   const uint16_t* A, const uint16_t* B, int r, float alpha,
+                                   uint16_t* y, float* u_out, void* stream) {
   qn_status s = check_linear(w, M, r);
   if (s != QN_OK) return s;
   if (M == 0) return QN_OK;
-  if (!x || !A || !B || !y) return QN_EINVAL;
-  if (!aligned16(x) || !aligned16(A) || !aligned16(B) || !aligned16(y) ||
-      (u_out && !aligned16(u_out)))
-    return QN_EALIGN;
   Carver probe(nullptr);
   carve_fwd(probe, M, w->rows, w->cols, r, u_out == nullptr);
-  if (probe.used > 0) {
-    if (!workspace) return QN_EINVAL;
-    if (reinterpret_cast<uintptr_t>(workspace) & 255u) return QN_EALIGN;
-    if (workspace_bytes < probe.used) return QN_EWORKSPACE;
-  }
-  Carver c(workspace);
-  FwdWs f = carve_fwd(c, M, w->rows, w->cols, r, u_out == nullptr);
-  float* u = u_out ? u_out : f.u;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  const float scale = alpha / (float)r;
-  const int64_t N = w->rows, K = w->cols;
-  if (f.dbr > 0)  // decode-sized batch, whole rows per workgroup
-    return from_hip(launch_decode_rows(to_state(w), x, M, A, B, r, scale, y, u, f.dbr, st));
-  if (f.dt.rgt > 0)  // decode-sized batch, one kernel over column slices
-    return from_hip(launch_decode_tile(to_state(w), x, M, A, B, r, scale, y, u, f.dt,
-                                       f.arrivals, f.tpart, f.tupart, st));
-  if (f.dpart)  // decode-sized batch: u and the product in two kernels
-    return from_hip(launch_decode_fwd(to_state(w), x, M, A, B, r, scale, y, u, f.dpart,
-                                      f.dupart, f.dS, st));
-  // dense path: the slices of u are added by spare workgroups of the
-  // dequantization launch that follows
-  const bool fold = f.wd && f.S > 1;
-  hipError_t e = launch_thin_nt(x, A, M, K, r, u, f.upart, f.S, st, !fold);
-  if (f.wd) {
-    if (e == hipSuccess)
-      e = launch_dequant(w->packed, w->qscale, w->scale2, w->offset, N * K, true, f.wd, st,
-                         fold ? SliceSum{f.upart, M * (int64_t)r, f.S, u} : SliceSum{});
-    if (e == hipSuccess) e = launch_gemm_nt(x, K, K, f.wd, K, M, N, u, B, r, scale, y, st);
-  } else if (e == hipSuccess) {
-    e = launch_qgemm_fwd(to_state(w), x, M, u, B, r, scale, y, st);
-  }
-  return from_hip(e);
+  if (probe.used > kStaticScratchBytes) return QN_EWORKSPACE;
+  void* ptr = nullptr;
+  s = static_scratch(&ptr);
+  if (s != QN_OK) return s;
+  // the array keeps what the last call left in it: its counters are cleared
+  // by a kernel before the launch that counts on them
+  return forward(w, x, M, A, B, r, alpha, y, u_out, ptr, kStaticScratchBytes, stream, true);
 }
+
+
 
 qn_status qlora_linear_bwd(const qn_nf4dq* w, const uint16_t* x, const uint16_t* dY, int64_t M,
                            const uint16_t* A, const uint16_t* B, int r, float alpha,
