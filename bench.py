@@ -407,13 +407,27 @@ def bench_extras(torch, qn, wl):
     return out
 
 
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(wl, target_s=15.0):
-    """The oracle, untuned, on a bounded sample of the training workload:
-    forward and input-gradient rows for a row sample, adapter gradients over
-    a row block; reported as sampled FLOPs per second.  A 16-row probe sets
-    the sample size so that the timed part takes about target_s seconds."""
+    """The oracle, untuned, on the host.  Headline: a bounded sample of the
+    training workload (forward and input-gradient rows for a row sample,
+    adapter gradients over a row block) as sampled FLOPs per second; a
+    16-row probe sizes the sample to about target_s seconds.  Beside it, the
+    other workloads' legs (each a few seconds at most): the tiny workload and
+    the 4096x4096 quantize on one thread, the full quantize / dequantize /
+    decode forward on every thread, and a row sample of the decoder layer."""
     import numpy as np
     import oracle
+    threads = oracle.num_threads()
     cfg = wl.TRAIN
     N, K, M, r, alpha = cfg["rows"], cfg["cols"], cfg["M"], cfg["r"], cfg["alpha"]
     W, x, A, B, dY = wl.linear_inputs(N, K, M, r, seed=cfg["seed"])
@@ -441,12 +455,90 @@ def cpu_baseline(wl, target_s=15.0):
     mb = min(M, 16 * nr)
     t_lin = run(nr, mb)
     flops = sample_flops(nr, mb)
-    return dict(value=flops / t_lin / 1e12, unit="TFLOP/s", cores=oracle.num_threads(),
-                kind="oracle",
+    legs = _cpu_legs(wl, oracle, np)
+    return dict(value=flops / t_lin / 1e12, unit="TFLOP/s", cores=threads,
+                kind="oracle", cpu_model=_cpu_model(),
                 sample=(f"fp64 oracle: y and dX rows for {nr} of {M} rows, dA/dB over {mb} "
                         f"rows, at 4096x4096 r=16 ({flops / 1e9:.1f} GFLOP in {t_lin:.1f} s); "
                         f"quantize+dequantize 4096x4096 took {t_q:.2f} s"),
-                seconds=t_lin)
+                seconds=t_lin, legs=legs)
+
+
+def _cpu_legs(wl, oracle, np):
+    """Oracle timings of the other workloads (see cpu_baseline)."""
+    legs = {}
+    threads = oracle.num_threads()
+
+    def timed(f):
+        t = time.perf_counter()
+        out = f()
+        return time.perf_counter() - t, out
+
+    # tiny workload, one thread: quantize, dequantize, forward, backward
+    oracle.set_num_threads(1)
+    try:
+        c = wl.TINY
+        W, x, A, B, G = wl.linear_inputs(c["rows"], c["cols"], c["M"], c["r"], seed=c["seed"])
+        sc = c["alpha"] / c["r"]
+
+        def tiny():
+            st = oracle.quantize(W)
+            Wd, _ = oracle.dequantize(st)
+            oracle.qlora_fwd(Wd, x, A, B, sc)
+            oracle.qlora_dx(Wd, G, A, B, sc)
+            oracle.adapter_grads(x, G, A, B, sc)
+        sec, _ = timed(tiny)
+        legs["tiny_1thread"] = dict(seconds=sec, threads=1)
+        W2 = wl.outlier_weight()
+        sec, _ = timed(lambda: oracle.quantize(W2))
+        nbytes = quant_bytes(4096, 4096)
+        legs["quantize_dq_4096x4096_1thread"] = dict(seconds=sec, threads=1, GBs=nbytes / sec / 1e9)
+    finally:
+        oracle.set_num_threads(threads)
+    sec, st2 = timed(lambda: oracle.quantize(W2))
+    legs["quantize_dq_4096x4096"] = dict(seconds=sec, threads=threads,
+                                         GBs=quant_bytes(4096, 4096) / sec / 1e9)
+    sec, _ = timed(lambda: oracle.dequantize(st2, want_f32=False))
+    legs["dequant_bf16_4096x4096"] = dict(seconds=sec, threads=threads,
+                                          GBs=dequant_bytes(4096, 4096, 2) / sec / 1e9)
+    # decode forward 14336x4096, M = 1 and 16 (all rows)
+    d = wl.DECODE
+    Nd, Kd, rd = d["rows"], d["cols"], d["r"]
+    Wq = wl.weight(Nd, Kd, wl.SEED_W + d["seed"])
+    Wdd, _ = oracle.dequantize(oracle.quantize(Wq), want_bf16=False)
+    Ad = wl.normal_bf16((rd, Kd), wl.SEED_A + d["seed"], 0.01)
+    Bd = wl.normal_bf16((Nd, rd), wl.SEED_B + d["seed"], 0.01)
+    for Mx in (1, 16):
+        xd = wl.normal_bf16((Mx, Kd), wl.SEED_X + d["seed"], 1.0)
+        sec, _ = timed(lambda: oracle.qlora_fwd(Wdd, xd, Ad, Bd, d["alpha"] / rd))
+        nbytes = decode_bytes(Nd, Kd, Mx, rd)
+        legs[f"decode_fwd_14336x4096_M{Mx}"] = dict(seconds=sec, threads=threads,
+                                                    GBs=nbytes / sec / 1e9)
+    del Wq, Wdd
+    # decoder layer: every linear quantized and dequantized, y and dX for 8
+    # sampled rows, dA and dB over the first 256 rows
+    c5 = wl.DECODER_LAYER
+    M5, r5 = c5["M"], c5["r"]
+    s5 = c5["alpha"] / r5
+    rows = np.linspace(0, M5 - 1, 8).astype(np.int64)
+    flops, secs = 0, 0.0
+    for idx, (_, N5, K5) in enumerate(wl.DECODER_LINEARS):
+        W5, x5, A5, B5, G5 = wl.linear_inputs(N5, K5, M5, r5, seed=c5["seed"], index=idx)
+
+        def layer():
+            Wd5, _ = oracle.dequantize(oracle.quantize(W5), want_bf16=False)
+            oracle.qlora_fwd(Wd5, x5, A5, B5, s5, rows=rows)
+            oracle.qlora_dx(Wd5, G5, A5, B5, s5, rows=rows)
+            oracle.adapter_grads(x5[:256], G5[:256], A5, B5, s5)
+        sec, _ = timed(layer)
+        secs += sec
+        flops += (fwd_flops(8, N5, K5, r5) + 2 * 8 * N5 * K5 + 2 * 8 * r5 * (N5 + K5)
+                  + 2 * 256 * r5 * (K5 + N5) + 2 * 256 * N5 * r5 + 2 * 256 * K5 * r5)
+    legs["decoder_layer_7_linears_M4096_sample"] = dict(
+        seconds=secs, threads=threads, TFLOPs=flops / secs / 1e12,
+        sample="each linear: quantize + dequantize, y and dX for 8 of 4096 rows, "
+               "dA and dB over 256 rows")
+    return legs
 
 
 def kernels_workload(torch, qn, wl, launches=5):

@@ -72,6 +72,7 @@ def lib():
         L.orc_adapter_grads.argtypes = [_P, _P, _P, _P, _I64, _I64, _I64,
                                         ctypes.c_int, ctypes.c_double, _P, _P]
         L.orc_num_threads.restype = ctypes.c_int
+        L.orc_set_num_threads.argtypes = [ctypes.c_int]
         _lib = L
     return _lib
 
@@ -95,6 +96,11 @@ def _bf16_bits(a) -> np.ndarray:
 
 def num_threads() -> int:
     return int(lib().orc_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads of the oracle's OpenMP loops from now on."""
+    lib().orc_set_num_threads(int(n))
 
 
 # ---------------------------------------------------------------- codebook

@@ -384,6 +384,16 @@ void orc_adapter_grads(const uint16_t* X, const uint16_t* G, const double* u,
   }
 }
 
+/* Threads the oracle's parallel loops use from now on (n >= 1). */
+void orc_set_num_threads(int n) {
+#ifdef _OPENMP
+  extern void omp_set_num_threads(int);
+  if (n >= 1) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 int orc_num_threads(void) {
 #ifdef _OPENMP
   extern int omp_get_max_threads(void);
