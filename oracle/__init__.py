@@ -71,6 +71,7 @@ def lib():
                                    ctypes.c_double, _P, _I64, _P, _P]
         L.orc_adapter_grads.argtypes = [_P, _P, _P, _P, _I64, _I64, _I64,
                                         ctypes.c_int, ctypes.c_double, _P, _P]
+        L.orc_merge.argtypes = [_P, _I64, _I64, _P, _P, ctypes.c_int, ctypes.c_float, _P]
         L.orc_num_threads.restype = ctypes.c_int
         L.orc_set_num_threads.argtypes = [ctypes.c_int]
         _lib = L
@@ -275,6 +276,19 @@ def adapter_grads(X, G, A, B, s: float):
     lib().orc_adapter_grads(_ptr(Xb), _ptr(Gb), _ptr(u), _ptr(v), M, N, K, r, float(s),
                             _ptr(dA), _ptr(dB))
     return dA, dB
+
+
+def merge(Wd: np.ndarray, A, B, s: float) -> np.ndarray:
+    """Qhat(W) + s B A as fp32 [rows, cols] from the dequantized fp32 weight
+    (fp64 rank sum, one fp32 rounding at the end; see orc_merge)."""
+    Wd = np.ascontiguousarray(Wd, dtype=np.float32)
+    Ab, Bb = _bf16_bits(A), _bf16_bits(B)
+    rows, cols = Wd.shape
+    r = Ab.shape[0]
+    assert Ab.shape == (r, cols) and Bb.shape == (rows, r)
+    out = np.empty((rows, cols), np.float32)
+    lib().orc_merge(_ptr(Wd), rows, cols, _ptr(Ab), _ptr(Bb), r, float(np.float32(s)), _ptr(out))
+    return out
 
 
 def rel_frobenius(out, ref) -> float:

@@ -394,6 +394,30 @@ void orc_set_num_threads(int n) {
 #endif
 }
 
+/* ---------------- merge of the adapter into the weight -------------------- */
+
+/* Page 2, section "Merge changes the operator: test it explicitly": merging
+ * the adapter into the dequantized weight gives the operator
+ * Qhat(W) + s B A; requantizing it is a further, separate step (done by
+ * orc_quantize on the result).  Reading for the rounding: per element
+ * d = sum_j B[n][j] A[j][k] in fp64 with j ascending (each product of two
+ * bf16 values is exact in fp64), then out = RN32(RN64(w' + RN64(s d))).
+ *   Wd [rows, cols] fp32 dequantized weight, A [r, cols] and B [rows, r]
+ *   bf16, s = alpha / r as fp32; out [rows, cols] fp32. */
+void orc_merge(const float* Wd, int64_t rows, int64_t cols, const uint16_t* A,
+               const uint16_t* B, int r, float s, float* out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t n = 0; n < rows; ++n) {
+    for (int64_t k = 0; k < cols; ++k) {
+      double d = 0.0;
+      for (int j = 0; j < r; ++j) d += bf(B, n * r + j) * bf(A, (int64_t)j * cols + k);
+      double t = (double)s * d;
+      double m = (double)Wd[n * cols + k] + t;
+      out[n * cols + k] = (float)m;
+    }
+  }
+}
+
 int orc_num_threads(void) {
 #ifdef _OPENMP
   extern int omp_get_max_threads(void);

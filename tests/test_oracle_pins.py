@@ -586,3 +586,70 @@ def test_merge_identity(orc):
     Ym = _f64(x) @ merged.T
     gap = np.max(np.abs(Y - Ym))
     assert gap <= 1e-12 * np.max(np.abs(Y)) and gap < g["merge_gap_fp32"] * 1e-3
+
+
+# --------------------------------------------------------------- merge and requantize
+# Page "QLoRA: NF4 storage, gradients and local integration", section "Merge
+# changes the operator: test it explicitly", and the merge checks of the
+# teaching listing: the adapter merged into Qhat(W) gives the operator used in
+# training, merged into W it does not, and requantizing the merged weight
+# changes the operator again.
+def _merge_case(rows, cols, r, seed):
+    import workloads as wl
+    W = wl.weight(rows, cols, seed)
+    A = wl.normal_bf16((r, cols), seed + 1, 0.05)
+    B = wl.normal_bf16((rows, r), seed + 2, 0.05)
+    return W, A, B
+
+
+def _bf64(bits):
+    return ((np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32)).astype(np.float64)
+
+
+def test_merge_is_the_nearest_fp32_of_the_exact_sum(orc):
+    """Every merged value lies within half an fp32 ulp (plus the fp64 steps'
+    slack) of the exact rational Qhat(W) + s B A; non-square shapes and
+    several ranks, so a transposed operand or a dropped term fails."""
+    for rows, cols, r, alpha in [(5, 7, 3, 6.0), (3, 64, 8, 16.0), (16, 9, 1, 1.0)]:
+        W, A, B = _merge_case(rows, cols, r, seed=rows * 100 + cols)
+        Wd, _ = orc.dequantize(orc.quantize(W), want_bf16=False)
+        s = np.float32(alpha) / np.float32(r)
+        got = orc.merge(Wd, A, B, s)
+        Af, Bf = _bf64(A), _bf64(B)
+        for n in range(rows):
+            for k in range(cols):
+                exact = Fraction(float(Wd[n, k])) + Fraction(float(s)) * sum(
+                    Fraction(float(Bf[n, j])) * Fraction(float(Af[j, k])) for j in range(r))
+                g = np.float32(got[n, k])
+                ulp = float(np.spacing(np.float32(abs(float(exact)) or 1e-38)))
+                assert abs(Fraction(float(g)) - exact) <= Fraction(ulp) / 2 * Fraction(1 + 2 ** -20)
+
+
+def test_merge_with_zero_adapter_is_the_dequantized_weight(orc):
+    W, A, B = _merge_case(24, 128, 4, seed=31)
+    B[:] = 0
+    Wd, _ = orc.dequantize(orc.quantize(W), want_bf16=False)
+    assert np.array_equal(orc.merge(Wd, A, B, np.float32(8.0)), Wd)
+
+
+def test_merge_distinguishes_the_three_operators(orc):
+    """y of the separate adapter path = y of the merged weight (up to the fp32
+    rounding of the merged weight), but not y of W + s B A (the original
+    weight merged) and not y of the requantized merged weight."""
+    import workloads as wl
+    rows, cols, r = 64, 256, 8
+    W, A, B = _merge_case(rows, cols, r, seed=41)
+    s = np.float32(2.0)
+    Wd, _ = orc.dequantize(orc.quantize(W), want_bf16=False)
+    x = _bf64(wl.normal_bf16((32, cols), 42, 1.0))
+    Af, Bf = _bf64(A), _bf64(B)
+    separate = x @ Wd.astype(np.float64).T + float(s) * (x @ Af.T) @ Bf.T
+    merged = orc.merge(Wd, A, B, s)
+    y_merged = x @ merged.astype(np.float64).T
+    assert np.linalg.norm(y_merged - separate) / np.linalg.norm(separate) < 1e-6
+    original = W.astype(np.float64) + float(s) * Bf @ Af
+    assert not np.allclose(original, merged.astype(np.float64))
+    requant, _ = orc.dequantize(orc.quantize(merged), want_bf16=False)
+    y_requant = x @ requant.astype(np.float64).T
+    err = np.linalg.norm(y_requant - separate) / np.linalg.norm(separate)
+    assert not np.allclose(y_requant, separate) and err > 1e-3
