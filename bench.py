@@ -78,6 +78,11 @@ def quant_bytes(rows, cols):
     return 4 * rows * cols + state_bytes(rows, cols)
 
 
+def merge_bytes(rows, cols, r):
+    """Algorithmic HBM bytes of one merge: the NF4 state, A, B and the fp32 output."""
+    return state_bytes(rows, cols) + 2 * r * (rows + cols) + 4 * rows * cols
+
+
 def decode_bytes(rows, cols, M, r):
     """Algorithmic HBM bytes of one decode forward: the NF4 state, x, A, B, y."""
     return state_bytes(rows, cols) + 2 * M * cols + 2 * r * cols + 2 * rows * r + 2 * M * rows
@@ -321,7 +326,20 @@ def bench_extras(torch, qn, wl):
     out["quantize_dq_4096x4096"] = dict(ms=med, ms_min=mn, bytes=nbytes, GBs=nbytes / med / 1e6,
                                         hbm_frac=nbytes / med / 1e6 / HBM_PEAK_GBS,
                                         sync_call_wall_ms=q_wall)
-    del Ws, states, W2
+    # adapter merge Qhat(W) + s B A into fp32 (rank 16), rotated states
+    Am = _bf16(torch, wl.normal_bf16((16, 4096), wl.SEED_A + 2, 0.01))
+    Bm = _bf16(torch, wl.normal_bf16((4096, 16), wl.SEED_B + 2, 0.01))
+    outs_m = [torch.empty((4096, 4096), dtype=torch.float32, device="cuda") for _ in range(6)]
+    qn.nf4_merge_lora(states[0], Am, Bm, 32.0, out=outs_m[0])
+    torch.cuda.synchronize()
+    ms = [_event_time_ms(torch, lambda i: qn.nf4_merge_lora(states[i % R], Am, Bm, 32.0,
+                                                             out=outs_m[i % 6]), 24)
+          for _ in range(5)]
+    med, mn = _median_min(ms)
+    nbytes = merge_bytes(4096, 4096, 16)
+    out["merge_lora_4096x4096_r16"] = dict(ms=med, ms_min=mn, bytes=nbytes, GBs=nbytes / med / 1e6,
+                                           hbm_frac=nbytes / med / 1e6 / HBM_PEAK_GBS)
+    del Ws, states, W2, outs_m
     torch.cuda.empty_cache()
 
     # decode forward 14336x4096, M = 1, 4, 16, rotated weight copies

@@ -182,6 +182,19 @@ qn_status qlora_linear_bwd(const qn_nf4dq* w, const uint16_t* x, const uint16_t*
                            const float* u_saved, uint16_t* dX, float* dA, float* dB,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/* Adapter merged into the dequantized weight (page "QLoRA: NF4 storage,
+ * gradients and local integration", section "Merge changes the operator:
+ * test it explicitly"):
+ *   out [rows, cols] fp32 = Qhat(W) + (alpha/r) B A
+ * with A [r, cols] and B [rows, r] bf16, 1 <= r <= 64.  Rounding: per
+ * element, d = sum_j B[n][j] A[j][k] in fp64 in rank order, then
+ * out = RN32(RN64(w' + RN64(s d))), w' the fp32 dequantized weight and
+ * s = alpha / r in fp32.  This is the operator the separate adapter path
+ * computes, up to the final fp32 rounding; requantizing it (nf4_quantize_dq
+ * on out) is a different operator again.  Stream-ordered, no workspace. */
+qn_status nf4_merge_lora(const qn_nf4dq* w, const uint16_t* A, const uint16_t* B, int r,
+                         float alpha, float* out, void* stream);
+
 /* Kernel routes of the linear calls (qlora_linear_route). */
 enum {
   QN_ROUTE_DECODE_ROWS = 1,  /* M <= 16: one kernel over bands of whole rows */

@@ -29,7 +29,7 @@ QN_F32, QN_BF16 = 0, 1
 EXPORTS = ["qn_abi_version", "qn_status_str", "qn_nf4_codebook", "nf4_quantize_dq_workspace",
            "nf4_quantize_dq", "nf4_dequantize", "qlora_linear_workspace", "qlora_linear_fwd",
            "qlora_linear_bwd", "lora_linear_bf16", "qlora_linear_route",
-           "qlora_linear_fwd_noalloc"]
+           "qlora_linear_fwd_noalloc", "nf4_merge_lora"]
 ROUTES = {1: "decode_rows", 2: "decode_tiles", 3: "decode_split", 4: "fused_small", 5: "fused",
           6: "dense"}
 
@@ -82,6 +82,8 @@ def load_library(path: str = LIB_PATH):
     L.qlora_linear_fwd_noalloc.argtypes = [ctypes.POINTER(_NF4DQ), P, I64, P, P, ctypes.c_int,
                                            ctypes.c_float, P, P, P]
     L.qlora_linear_fwd_noalloc.restype = ctypes.c_int
+    L.nf4_merge_lora.argtypes = [ctypes.POINTER(_NF4DQ), P, P, ctypes.c_int, ctypes.c_float, P, P]
+    L.nf4_merge_lora.restype = ctypes.c_int
     L.qlora_linear_route.argtypes = [I64, I64, I64, ctypes.c_int, ctypes.c_int]
     L.qlora_linear_route.restype = ctypes.c_int
     _lib = L
@@ -192,6 +194,31 @@ def nf4_dequantize(st: NF4State, dtype=torch.bfloat16, out: torch.Tensor | None 
     s = st.c_struct()
     _check(L.nf4_dequantize(ctypes.byref(s), code, out.data_ptr(), _stream(st.device)))
     return out
+
+
+def nf4_merge_lora(st: NF4State, A: torch.Tensor, B: torch.Tensor, alpha: float,
+                   out: torch.Tensor | None = None) -> torch.Tensor:
+    """Qhat(W) + (alpha/r) B A as an fp32 [d_out, d_in] tensor (the merged
+    weight; requantize it with nf4_quantize_dq)."""
+    L = load_library()
+    A = _dev(A, torch.bfloat16, "A")
+    B = _dev(B, torch.bfloat16, "B")
+    r = A.shape[0]
+    if A.dim() != 2 or A.shape[1] != st.cols or B.shape != (st.rows, r):
+        raise ValueError(f"A must be [r, {st.cols}] and B [{st.rows}, r]")
+    if out is None:
+        out = torch.empty((st.rows, st.cols), dtype=torch.float32, device=st.device)
+    _dev(out, torch.float32, "out")
+    s = st.c_struct()
+    _check(L.nf4_merge_lora(ctypes.byref(s), A.data_ptr(), B.data_ptr(), r, float(alpha),
+                            out.data_ptr(), _stream(st.device)))
+    return out
+
+
+def nf4_merge_requantize(st: NF4State, A: torch.Tensor, B: torch.Tensor,
+                         alpha: float) -> NF4State:
+    """The merged weight quantized again: the state of Qhat(Qhat(W) + s B A)."""
+    return nf4_quantize_dq(nf4_merge_lora(st, A, B, alpha))
 
 
 def route(M: int, rows: int, cols: int, r: int, backward: bool = False) -> str:

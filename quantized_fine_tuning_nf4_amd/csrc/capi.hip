@@ -455,6 +455,17 @@ qn_status qlora_linear_bwd(const qn_nf4dq* w, const uint16_t* x, const uint16_t*
   return from_hip(e);
 }
 
+qn_status nf4_merge_lora(const qn_nf4dq* w, const uint16_t* A, const uint16_t* B, int r,
+                         float alpha, float* out, void* stream) {
+  qn_status s = check_state(w);
+  if (s != QN_OK) return s;
+  if (r < 1 || r > 64 || w->rows > kMaxDim * 64 || w->cols > kMaxDim * 64) return QN_EINVAL;
+  if (!A || !B || !out) return QN_EINVAL;
+  if (!aligned16(A) || !aligned16(B) || !aligned16(out)) return QN_EALIGN;
+  return from_hip(launch_merge(to_state(w), A, B, r, alpha / (float)r, out,
+                               static_cast<hipStream_t>(stream)));
+}
+
 int qlora_linear_route(int64_t M, int64_t rows, int64_t cols, int r, int backward) {
   if (M < 1 || M > kMaxRowsM || rows < 8 || cols < kBlock || rows % 8 != 0 ||
       cols % kBlock != 0 || rows > kMaxDim || cols > kMaxDim || r < 1 || r > 64)

@@ -276,6 +276,11 @@ hipError_t launch_decode_rows(const WState& w, const uint16_t* X, int64_t M, con
                               const uint16_t* B, int r, float s, uint16_t* Y, float* u_out,
                               int br, hipStream_t st);
 
+// out [rows, cols] fp32 = Qhat(W) + s B A (fp64 rank sum in rank order, one
+// fp32 rounding at the end); A [r, cols], B [rows, r] bf16, 1 <= r <= 64.
+hipError_t launch_merge(const WState& w, const uint16_t* A, const uint16_t* B, int r, float s,
+                        float* out, hipStream_t st);
+
 // Y[M, N] bf16 = X[M, K] * W'[N, K]^T + s * u[M, r] * B[N, r]^T.
 hipError_t launch_qgemm_fwd(const WState& w, const uint16_t* X, int64_t M, const float* u,
                             const uint16_t* B, int r, float s, uint16_t* Y, hipStream_t st);

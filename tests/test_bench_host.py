@@ -111,3 +111,5 @@ def test_flop_accounting_closed_forms():
     assert bench.quant_bytes(4096, 4096) == 75763716
     assert bench.dequant_bytes(4096, 4096, 2) == 42209284
     assert bench.decode_bytes(14336, 4096, 16, 16) == 31471620
+    # merge: the state, A and B (bf16, rank 16), the fp32 merged weight
+    assert bench.merge_bytes(4096, 4096, 16) == bench.state_bytes(4096, 4096) + 2 * 16 * 8192 + 4 * 4096 * 4096
