@@ -4,6 +4,8 @@ One step = one pass of the whole hot path over one synthetic batch of the
 training-shaped workload (W 4096x4096 fp32 ~ N(0, 0.02), x and dY bf16
 [8192, 4096] ~ N(0, 1), rank-16 bf16 adapters ~ N(0, 0.01), alpha 32):
     nf4_quantize_dq -> nf4_dequantize (bf16) -> qlora_linear_fwd -> qlora_linear_bwd
+captured once in a HIP graph and replayed once per timed step (the same step
+issued call by call from Python is timed too and reported beside it).
 The headline value is the fwd+bwd algorithmic FLOPs of the step divided by
 the wall time of the whole step (quantize and dequantize included).
 Also printed in the same JSON line: the roofline of the dominant kernel,
@@ -216,18 +218,35 @@ def bench_train(torch, qn, wl, steps, warmup):
         qn.nf4_quantize_dq(Wd, out=st, workspace=qws, nonfinite=flag)
         qn.nf4_dequantize(st, torch.bfloat16, out=wbf)
         _, u = qn.qlora_linear_fwd(st, xd, Ad, Bd, alpha, y=y, workspace=fws)
-        qn.qlora_linear_bwd(st, xd, Gd, Ad, Bd, alpha, u, workspace=bws)
+        return (u,) + qn.qlora_linear_bwd(st, xd, Gd, Ad, Bd, alpha, u, workspace=bws)
 
+    # the step as issued from Python, call by call
     probe = DeviceProbe(torch)
-    win = time_window(step, range(warmup + steps), lambda _: 1, warmup, probe)
+    eager = time_window(step, range(warmup + steps), lambda _: 1, warmup, probe)
+    eager_device_s = probe.device_seconds
+    # the same step captured once in a HIP graph and replayed: one replay is
+    # one step (every kernel of the eager step, no host work between them)
+    ref = [t.clone() for t in step(0)] + [y.clone()]
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        outs = step(0)
+    probe = DeviceProbe(torch)
+    win = time_window(lambda _: graph.replay(), range(warmup + steps), lambda _: 1, warmup, probe)
     if int(flag.item()) != 0:
         raise RuntimeError("quantizer reported non-finite input")
+    # the replays computed what the eager step computes, bit for bit
+    if not all(torch.equal(a, b) for a, b in zip(list(outs) + [y], ref)):
+        raise RuntimeError("graph replay of the step differs from the eager step")
     flops = fwd_flops(M, N, K, r) + bwd_flops(M, N, K, r)
     secs, nsteps = win.seconds, win.steps
     res = dict(seconds=secs, steps=nsteps, ms_per_step=1e3 * secs / nsteps,
                tflops=flops * nsteps / secs / 1e12, flops_per_step=flops,
                device_ms_per_step=1e3 * probe.device_seconds / nsteps,
+               eager_ms_per_step=1e3 * eager.seconds / eager.steps,
+               eager_device_ms_per_step=1e3 * eager_device_s / eager.steps,
                peak_bytes_above_start=win.peak_above_start)
+    del graph
 
     # dominant kernels: time the forward and backward calls with HIP events on
     # the stream the library launches on (torch's current stream)
@@ -672,7 +691,9 @@ def main():
         "config": {"workload": "train_fwd_bwd_4096x4096_M8192", "rows": 4096, "cols": 4096,
                    "M": 8192, "r": 16, "alpha": 32,
                    "step": "nf4_quantize_dq (device non-finite flag) + nf4_dequantize(bf16) + "
-                           "qlora_linear_fwd + qlora_linear_bwd", "flops_per_step": tr["flops_per_step"]},
+                           "qlora_linear_fwd + qlora_linear_bwd, captured once in a HIP graph "
+                           "and replayed once per step", "flops_per_step": tr["flops_per_step"],
+                   "eager_ms_per_step": tr["eager_ms_per_step"]},
         "roofline": roof,
         "cpu_baseline": cpu,
         "extras": extras,

@@ -20,7 +20,9 @@
 // were read during its first half; the end of the first half of step s+1
 // waits for them.  Chunk c (16 bytes) of LDS row y sits at unit
 // c ^ ((y >> 1) & 7), which keeps the sixteen rows of one fragment read on
-// distinct banks.  Rows of A past its length R are moved back onto its last
+// distinct banks.  The next half's B fragments are read during the first
+// row of a half's MFMAs (its first row uses all eight), its A fragments one
+// per row.  Rows of A past its length R are moved back onto its last
 // chunk; Bm is zero there (its rows are padded to a multiple of 64 with
 // zeros).
 #include <type_traits>
@@ -214,7 +216,9 @@ __global__ __launch_bounds__(T, 1) void k_gemm_nt(
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         mfma16_acc(fb[H][j], fa[i], acc[i][j]);
-        if (j == 1) fb[RH][i] = frag(RS, bbase, i, RH);
+        // the next half's B fragments are all read during the first row of
+        // MFMAs: its first row needs every one of them
+        if (i == 0) fb[RH][j] = frag(RS, bbase, j, RH);
         if (H == 1 && (j == 3 || j == 6)) load_one(2 * i + (j == 6), lst, P);
       }
       fa[i] = frag(RS, abase, i, RH);
