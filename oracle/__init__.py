@@ -72,6 +72,9 @@ def lib():
         L.orc_adapter_grads.argtypes = [_P, _P, _P, _P, _I64, _I64, _I64,
                                         ctypes.c_int, ctypes.c_double, _P, _P]
         L.orc_merge.argtypes = [_P, _I64, _I64, _P, _P, ctypes.c_int, ctypes.c_float, _P]
+        L.orc_dropout_apply.argtypes = [_P, _P, _I64, _I64, _P]
+        L.orc_qlora_dx_dropout.argtypes = [_P, _I64, _I64, _P, _P, _P, ctypes.c_int,
+                                           ctypes.c_double, _P, _P, _I64, _P, _P]
         L.orc_num_threads.restype = ctypes.c_int
         L.orc_set_num_threads.argtypes = [ctypes.c_int]
         _lib = L
@@ -276,6 +279,69 @@ def adapter_grads(X, G, A, B, s: float):
     lib().orc_adapter_grads(_ptr(Xb), _ptr(Gb), _ptr(u), _ptr(v), M, N, K, r, float(s),
                             _ptr(dA), _ptr(dB))
     return dA, dB
+
+
+# ---------------------------------------------------------------- adapter variants
+def lora_scale(alpha: float, r: int, rslora: bool = False, dropout_p: float = 0.0) -> float:
+    """The adapter branch's scale in fp32: alpha / r, or alpha / sqrt(r) for
+    rsLoRA (course notebook FT-02, "Exercise 4: alpha/r vs alpha/sqrt(r)
+    scaling (rsLoRA)"), divided by 1 - p when dropout with probability p acts
+    on the branch's input (inverted dropout, folded into the scale)."""
+    a, rf = np.float32(alpha), np.float32(r)
+    s = a / np.sqrt(rf, dtype=np.float32) if rslora else a / rf
+    if dropout_p:
+        s = np.float32(s) / (np.float32(1.0) - np.float32(dropout_p))
+    return float(np.float32(s))
+
+
+def dropout_apply(X, mask: np.ndarray) -> np.ndarray:
+    """The adapter branch's input: X with dropped elements zeroed (mask
+    bit-packed over the row-major elements, bit e % 8 of byte e / 8)."""
+    Xb = _bf16_bits(X)
+    M, K = Xb.shape
+    mask = np.ascontiguousarray(mask, dtype=np.uint8)
+    assert mask.size * 8 >= M * K
+    out = np.empty_like(Xb)
+    lib().orc_dropout_apply(_ptr(Xb), _ptr(mask), M, K, _ptr(out))
+    return out
+
+
+def qlora_dx_dropout(Wd: np.ndarray, G, A, B, s: float, mask: np.ndarray, rows=None):
+    """dX = G W' + s ((G B) A) (.) mask in fp64 for the listed rows.  Returns (dX, v)."""
+    Wd = np.ascontiguousarray(Wd, dtype=np.float32)
+    Gb, Ab, Bb = _bf16_bits(G), _bf16_bits(A), _bf16_bits(B)
+    N, K = Wd.shape
+    M = Gb.shape[0]
+    r = Ab.shape[0]
+    mask = np.ascontiguousarray(mask, dtype=np.uint8)
+    assert mask.size * 8 >= M * K
+    rr = _rows_arg(rows)
+    nrows = M if rr is None else rr.size
+    dX = np.empty((nrows, K), np.float64)
+    v = np.empty((nrows, r), np.float64)
+    lib().orc_qlora_dx_dropout(_ptr(Wd), N, K, _ptr(Gb), _ptr(Ab), _ptr(Bb), r, float(s),
+                               _ptr(mask), _ptr(rr), nrows, _ptr(dX), _ptr(v))
+    return dX, v
+
+
+def qlora_fwd_dropout(Wd: np.ndarray, X, A, B, s: float, mask: np.ndarray, rows=None):
+    """y = X W'^T + s ((mask (.) X) A^T) B^T for the listed rows; returns (y, u)
+    with u = (mask (.) X) A^T."""
+    Xb = _bf16_bits(X)
+    Xd = dropout_apply(Xb, mask)
+    base, _ = qlora_fwd(Wd, Xb, A, np.zeros_like(_bf16_bits(B)), 0.0, rows=rows)
+    u = lora_down(Xd, A, rows=rows)
+    return base + s * (u @ _bf16_f64(B).T), u
+
+
+def adapter_grads_dropout(X, G, A, B, s: float, mask: np.ndarray):
+    """dA = s (G B)^T (mask (.) X), dB = s G^T ((mask (.) X) A^T), over all rows."""
+    return adapter_grads(dropout_apply(X, mask), G, A, B, s)
+
+
+def _bf16_f64(a) -> np.ndarray:
+    b = _bf16_bits(a)
+    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
 def merge(Wd: np.ndarray, A, B, s: float) -> np.ndarray:

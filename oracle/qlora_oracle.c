@@ -394,6 +394,50 @@ void orc_set_num_threads(int n) {
 #endif
 }
 
+/* ---------------- dropout on the adapter branch ---------------------------- */
+
+/* Course notebook FT-02, the LoraConfig of the QLoRA setup (lora_dropout
+ * 0.05): dropout acts on the adapter branch's input only.  Reading: a kept
+ * element passes unchanged, a dropped one is zero, and the 1/(1-p) of
+ * inverted dropout is folded into the branch's scale s (the caller passes
+ * s / (1 - p)).  mask is bit-packed row-major over [M, K]: element e is kept
+ * when bit e % 8 of byte e / 8 is set.
+ *   X [M, K] bf16 -> Xd [M, K] bf16 (the masked input). */
+void orc_dropout_apply(const uint16_t* X, const uint8_t* mask, int64_t M, int64_t K,
+                       uint16_t* Xd) {
+#pragma omp parallel for schedule(static)
+  for (int64_t m = 0; m < M; ++m)
+    for (int64_t k = 0; k < K; ++k) {
+      int64_t e = m * K + k;
+      int kept = (mask[e / 8] >> (e % 8)) & 1;
+      Xd[e] = kept ? X[e] : (uint16_t)0;
+    }
+}
+
+/* Input gradient with dropout on the adapter branch, for the listed rows:
+ * dX = G W' + s ((G B) A) (.) mask, the mask applied elementwise to the
+ * branch's contribution (its input was masked in the forward).
+ *   dX [nrows, K] fp64, v [nrows, r] fp64 (output, G B). */
+void orc_qlora_dx_dropout(const float* Wd, int64_t N, int64_t K, const uint16_t* G,
+                          const uint16_t* A, const uint16_t* B, int r, double s,
+                          const uint8_t* mask, const int64_t* rows, int64_t nrows,
+                          double* dX, double* v) {
+  orc_lora_up_grad(G, B, N, r, rows, nrows, v);
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < nrows; ++i) {
+    int64_t m = rows ? rows[i] : i;
+    for (int64_t k = 0; k < K; ++k) {
+      double base = 0.0;
+      for (int64_t n = 0; n < N; ++n) base += bf(G, m * N + n) * (double)Wd[n * K + k];
+      double lora = 0.0;
+      for (int j = 0; j < r; ++j) lora += v[i * r + j] * bf(A, (int64_t)j * K + k);
+      int64_t e = m * K + k;
+      int kept = (mask[e / 8] >> (e % 8)) & 1;
+      dX[i * K + k] = base + (kept ? s * lora : 0.0);
+    }
+  }
+}
+
 /* ---------------- merge of the adapter into the weight -------------------- */
 
 /* Page 2, section "Merge changes the operator: test it explicitly": merging

@@ -653,3 +653,75 @@ def test_merge_distinguishes_the_three_operators(orc):
     y_requant = x @ requant.astype(np.float64).T
     err = np.linalg.norm(y_requant - separate) / np.linalg.norm(separate)
     assert not np.allclose(y_requant, separate) and err > 1e-3
+
+
+# --------------------------------------------------------------- adapter variants
+# Course notebook FT-02: "Exercise 4: alpha/r vs alpha/sqrt(r) scaling
+# (rsLoRA)", and the LoraConfig of the QLoRA setup (lora_dropout=0.05).
+def test_rslora_scale(orc):
+    # alpha fixed at 16, the exercise's ranks: alpha/sqrt(r) = 8, 4, 2 exactly
+    assert [orc.lora_scale(16.0, r, rslora=True) for r in (4, 16, 64)] == [8.0, 4.0, 2.0]
+    assert [orc.lora_scale(16.0, r) for r in (4, 16, 64)] == [4.0, 1.0, 0.25]
+    # doubling the rank halves alpha/r but divides alpha/sqrt(r) by sqrt(2)
+    for r in (4, 16):
+        a, b = orc.lora_scale(16.0, r), orc.lora_scale(16.0, 2 * r)
+        ra, rb = orc.lora_scale(16.0, r, True), orc.lora_scale(16.0, 2 * r, True)
+        assert a / b == 2.0 and abs(ra / rb - math.sqrt(2)) < 1e-6
+    # inverted dropout folds 1/(1-p) into the scale
+    assert orc.lora_scale(32.0, 16, dropout_p=0.5) == 4.0
+
+
+def _packed_mask(M, K, keep, seed):
+    bits = np.random.default_rng(seed).random(M * K) < keep
+    return np.packbits(bits, bitorder="little"), bits.reshape(M, K)
+
+
+def test_dropout_gradients_match_autograd(orc):
+    """The dropout variant against torch autograd in fp64 on
+    y = x W'^T + s ((m (.) x) A^T) B^T with L = sum(y * G)."""
+    import workloads as wl
+    M, N, K, r = 6, 24, 64, 4
+    W = wl.weight(N, K, 71)
+    x, A, B, G = (wl.normal_bf16(sh, 72 + i, sd) for i, (sh, sd) in
+                  enumerate([((M, K), 1.0), ((r, K), 0.1), ((N, r), 0.1), ((M, N), 1.0)]))
+    mask, bits = _packed_mask(M, K, 0.7, 73)
+    s = orc.lora_scale(8.0, r, dropout_p=0.3)
+    Wd, _ = orc.dequantize(orc.quantize(W), want_bf16=False)
+    y, _ = orc.qlora_fwd_dropout(Wd, x, A, B, s, mask)
+    dX, _ = orc.qlora_dx_dropout(Wd, G, A, B, s, mask)
+    dA, dB = orc.adapter_grads_dropout(x, G, A, B, s, mask)
+    t = lambda a: torch.tensor(_bf64(a), dtype=torch.float64)
+    xt = t(x).requires_grad_(True)
+    At, Bt = t(A).requires_grad_(True), t(B).requires_grad_(True)
+    mt = torch.tensor(bits, dtype=torch.float64)
+    yt = xt @ torch.tensor(Wd, dtype=torch.float64).T + s * ((mt * xt) @ At.T) @ Bt.T
+    (yt * t(G)).sum().backward()
+    assert np.allclose(y, yt.detach().numpy(), rtol=1e-12, atol=1e-12)
+    assert np.allclose(dX, xt.grad.numpy(), rtol=1e-12, atol=1e-12)
+    assert np.allclose(dA, At.grad.numpy(), rtol=1e-12, atol=1e-12)
+    assert np.allclose(dB, Bt.grad.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_dropout_special_masks(orc):
+    """All kept: the plain linear at the same scale.  All dropped: the base
+    product alone, zero adapter gradients, dX = G W'."""
+    import workloads as wl
+    M, N, K, r = 5, 16, 128, 3
+    W, x, A, B, G = (wl.weight(N, K, 81), wl.normal_bf16((M, K), 82, 1.0),
+                     wl.normal_bf16((r, K), 83, 0.1), wl.normal_bf16((N, r), 84, 0.1),
+                     wl.normal_bf16((M, N), 85, 1.0))
+    Wd, _ = orc.dequantize(orc.quantize(W), want_bf16=False)
+    s = 2.0
+    ones = np.full(M * K // 8, 0xFF, np.uint8)
+    zeros = np.zeros(M * K // 8, np.uint8)
+    y1, _ = orc.qlora_fwd_dropout(Wd, x, A, B, s, ones)
+    y_ref, _ = orc.qlora_fwd(Wd, x, A, B, s)
+    assert np.allclose(y1, y_ref, rtol=1e-13, atol=1e-13)
+    dX1, _ = orc.qlora_dx_dropout(Wd, G, A, B, s, ones)
+    assert np.array_equal(dX1, orc.qlora_dx(Wd, G, A, B, s)[0])
+    y0, _ = orc.qlora_fwd_dropout(Wd, x, A, B, s, zeros)
+    assert np.allclose(y0, orc.qlora_fwd(Wd, x, A, B, 0.0)[0], rtol=1e-13, atol=1e-13)
+    dX0, _ = orc.qlora_dx_dropout(Wd, G, A, B, s, zeros)
+    assert np.array_equal(dX0, orc.qlora_dx(Wd, G, A, B, 0.0)[0])
+    dA0, dB0 = orc.adapter_grads_dropout(x, G, A, B, s, zeros)
+    assert not dA0.any() and not dB0.any()
