@@ -287,6 +287,24 @@ def bench_train(torch, qn, wl, steps, warmup):
     res["fwd_call_ms"] = _median_min(fwd_ms)
     res["bwd_call_ms"] = _median_min(bwd_ms)
     res["gemm_ms"] = _median_min(gemm_ms)
+    # the adapter-branch variants on the same workload: rsLoRA's scale (no
+    # extra work) and dropout p = 0.05 on the branch's input (a keep mask in,
+    # the masked x for dA, the branch's dX share added after the base product)
+    mask = qn.dropout_mask(M, K, 0.05, generator=torch.Generator(device="cuda").manual_seed(7))
+    dws = qn.linear_workspace(max(L.qlora_linear_workspace_ex(M, N, K, r, 1, None),
+                                  L.qlora_linear_workspace_ex(
+                                      M, N, K, r, 1, qn.ctypes.byref(qn._LoraOpts(0, 1, 0.05)))))
+
+    def fwd_bwd_dropout(_):
+        _, ud = qn.qlora_linear_fwd(st, xd, Ad, Bd, alpha, y=y, workspace=dws, dropout_mask=mask,
+                                    dropout_p=0.05)
+        qn.qlora_linear_bwd(st, xd, Gd, Ad, Bd, alpha, ud, workspace=dws, dropout_mask=mask,
+                            dropout_p=0.05)
+
+    fwd_bwd_dropout(0)
+    torch.cuda.synchronize()
+    res["fwd_bwd_dropout_ms"] = _median_min([_event_time_ms(torch, fwd_bwd_dropout, 10)
+                                             for _ in range(5)])
     res["fwd_flops"] = fwd_flops(M, N, K, r)
     res["bwd_flops"] = bwd_flops(M, N, K, r)
     res["gemm_flops"] = gemm_flops(M, N, K, r)
@@ -676,6 +694,11 @@ def main():
                 bwd_call=dict(ms=bwd_med, TFLOPs=tr["bwd_flops"] / bwd_med / 1e9,
                               frac=tr["bwd_flops"] / bwd_med / 1e9 / BF16_PEAK_TFLOPS))
     extras = {}
+    dms = tr["fwd_bwd_dropout_ms"][0]
+    extras["train_fwd_bwd_dropout_p0.05_4096x4096_M8192"] = dict(
+        ms=dms, ms_min=tr["fwd_bwd_dropout_ms"][1], TFLOPs=(tr["fwd_flops"] + tr["bwd_flops"]) / dms / 1e9,
+        mfma_frac=(tr["fwd_flops"] + tr["bwd_flops"]) / dms / 1e9 / BF16_PEAK_TFLOPS,
+        without_dropout_ms=fwd_med + bwd_med)
     if not args.no_extras:
         print("[bench] extras", file=sys.stderr, flush=True)
         extras = bench_extras(torch, qn, wl)

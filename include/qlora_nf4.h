@@ -170,6 +170,36 @@ qn_status qlora_linear_fwd_noalloc(const qn_nf4dq* w, const uint16_t* x, int64_t
                                    const uint16_t* A, const uint16_t* B, int r, float alpha,
                                    uint16_t* y, float* u_out, void* stream);
 
+/* Options of the adapter branch for the _ex calls (a NULL pointer means
+ * alpha / r and no dropout).
+ *   rslora: 0 -> s = alpha / r; 1 -> s = alpha / sqrt(r) (rsLoRA; course
+ *     notebook FT-02, "Exercise 4: alpha/r vs alpha/sqrt(r) scaling").
+ *   dropout_mask (nullable): dropout on the adapter branch's input (FT-02,
+ *     the LoraConfig's lora_dropout): a keep mask over x [M, cols],
+ *     bit-packed row-major (element e kept when bit e % 8 of byte e / 8 is
+ *     set), device memory; the caller draws it.  Kept elements pass
+ *     unchanged and the branch's scale becomes s / (1 - dropout_p); the
+ *     backward takes the same mask (dA reads the masked x, the branch's
+ *     share of dX is masked).  Forwards with dropout take the GEMM routes,
+ *     never the decode kernels.
+ *   dropout_p: in [0, 1) with a mask; 0 without one. */
+typedef struct {
+  int rslora;
+  const uint8_t* dropout_mask;
+  float dropout_p;
+} qn_lora_opts;
+
+/* Workspace bytes for the _ex calls with these options (dropout needs room
+ * for the masked x in the backward). */
+size_t qlora_linear_workspace_ex(int64_t M, int64_t rows, int64_t cols, int r, int backward,
+                                 const qn_lora_opts* opts);
+
+/* qlora_linear_fwd with adapter options (opts nullable). */
+qn_status qlora_linear_fwd_ex(const qn_nf4dq* w, const uint16_t* x, int64_t M, const uint16_t* A,
+                              const uint16_t* B, int r, float alpha, const qn_lora_opts* opts,
+                              uint16_t* y, float* u_out, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
 /* Backward: from G = dY [M, rows] bf16 computes
  *   dX [M, cols] bf16 = G Qhat(W) + s (G B) A      (skipped if dX == NULL)
  *   dA [r, cols] fp32 = s (G B)^T X                 (overwritten)
@@ -210,6 +240,14 @@ enum {
  * device; -1 for sizes the calls reject.  For tests and profiling: every
  * route computes the same function. */
 int qlora_linear_route(int64_t M, int64_t rows, int64_t cols, int r, int backward);
+
+/* qlora_linear_bwd with adapter options (opts nullable; the same options as
+ * the forward whose u_saved is passed). */
+qn_status qlora_linear_bwd_ex(const qn_nf4dq* w, const uint16_t* x, const uint16_t* dY,
+                              int64_t M, const uint16_t* A, const uint16_t* B, int r, float alpha,
+                              const qn_lora_opts* opts, const float* u_saved, uint16_t* dX,
+                              float* dA, float* dB, void* workspace, size_t workspace_bytes,
+                              void* stream);
 
 /* Dense LoRA linear on an already dequantized weight -- the forward's product
  * once Qhat(W) is held in bf16 (page 2, paragraph after the listing):

@@ -29,7 +29,8 @@ QN_F32, QN_BF16 = 0, 1
 EXPORTS = ["qn_abi_version", "qn_status_str", "qn_nf4_codebook", "nf4_quantize_dq_workspace",
            "nf4_quantize_dq", "nf4_dequantize", "qlora_linear_workspace", "qlora_linear_fwd",
            "qlora_linear_bwd", "lora_linear_bf16", "qlora_linear_route",
-           "qlora_linear_fwd_noalloc", "nf4_merge_lora"]
+           "qlora_linear_fwd_noalloc", "nf4_merge_lora", "qlora_linear_workspace_ex",
+           "qlora_linear_fwd_ex", "qlora_linear_bwd_ex"]
 ROUTES = {1: "decode_rows", 2: "decode_tiles", 3: "decode_split", 4: "fused_small", 5: "fused",
           6: "dense"}
 
@@ -38,6 +39,11 @@ class QNError(RuntimeError):
     def __init__(self, status: int, msg: str):
         super().__init__(f"{msg} (status {status})")
         self.status = status
+
+
+class _LoraOpts(ctypes.Structure):
+    _fields_ = [("rslora", ctypes.c_int), ("dropout_mask", ctypes.c_void_p),
+                ("dropout_p", ctypes.c_float)]
 
 
 class _NF4DQ(ctypes.Structure):
@@ -82,6 +88,15 @@ def load_library(path: str = LIB_PATH):
     L.qlora_linear_fwd_noalloc.argtypes = [ctypes.POINTER(_NF4DQ), P, I64, P, P, ctypes.c_int,
                                            ctypes.c_float, P, P, P]
     L.qlora_linear_fwd_noalloc.restype = ctypes.c_int
+    OP = ctypes.POINTER(_LoraOpts)
+    L.qlora_linear_workspace_ex.argtypes = [I64, I64, I64, ctypes.c_int, ctypes.c_int, OP]
+    L.qlora_linear_workspace_ex.restype = SZ
+    L.qlora_linear_fwd_ex.argtypes = [ctypes.POINTER(_NF4DQ), P, I64, P, P, ctypes.c_int,
+                                      ctypes.c_float, OP, P, P, P, SZ, P]
+    L.qlora_linear_fwd_ex.restype = ctypes.c_int
+    L.qlora_linear_bwd_ex.argtypes = [ctypes.POINTER(_NF4DQ), P, P, I64, P, P, ctypes.c_int,
+                                      ctypes.c_float, OP, P, P, P, P, P, SZ, P]
+    L.qlora_linear_bwd_ex.restype = ctypes.c_int
     L.nf4_merge_lora.argtypes = [ctypes.POINTER(_NF4DQ), P, P, ctypes.c_int, ctypes.c_float, P, P]
     L.nf4_merge_lora.restype = ctypes.c_int
     L.qlora_linear_route.argtypes = [I64, I64, I64, ctypes.c_int, ctypes.c_int]
@@ -254,11 +269,34 @@ def _bits(t):
     return t.data_ptr()
 
 
+def dropout_mask(M: int, cols: int, p: float, device="cuda", generator=None) -> torch.Tensor:
+    """A keep mask for dropout with probability p on the adapter branch's
+    input x [M, cols], bit-packed as the library takes it (element e kept
+    when bit e % 8 of byte e / 8 is set): uint8 [M * cols / 8].  The random
+    draw itself is torch's."""
+    if (M * cols) % 8:
+        raise ValueError("M * cols must be a multiple of 8")
+    keep = torch.rand(M * cols, device=device, generator=generator) >= p
+    w = torch.tensor([1, 2, 4, 8, 16, 32, 64, 128], dtype=torch.int32, device=device)
+    return (keep.view(-1, 8).to(torch.int32) * w).sum(dim=1).to(torch.uint8)
+
+
+def _opts(rslora, mask, p):
+    if not rslora and mask is None and not p:
+        return None
+    if mask is not None:
+        _dev(mask, torch.uint8, "dropout_mask")
+    return _LoraOpts(int(bool(rslora)), _ptr(mask), float(p))
+
+
 def qlora_linear_fwd(st: NF4State, x: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
                      alpha: float, save_u: bool = True, y: torch.Tensor | None = None,
-                     workspace: torch.Tensor | None = None):
-    """y = x Qhat(W)^T + (alpha/r) (x A^T) B^T; returns (y bf16 [M, d_out],
-    u fp32 [M, r] or None)."""
+                     workspace: torch.Tensor | None = None, rslora: bool = False,
+                     dropout_mask: torch.Tensor | None = None, dropout_p: float = 0.0):
+    """y = x Qhat(W)^T + s (x A^T) B^T with s = alpha / r (alpha / sqrt(r)
+    with rslora); dropout_mask / dropout_p: dropout on the adapter branch's
+    input (see dropout_mask()).  Returns (y bf16 [M, d_out], u fp32 [M, r] or
+    None; u is the branch's x A^T, masked under dropout)."""
     L = load_library()
     x = _dev(x, torch.bfloat16, "x")
     A = _dev(A, torch.bfloat16, "A")
@@ -267,19 +305,23 @@ def qlora_linear_fwd(st: NF4State, x: torch.Tensor, A: torch.Tensor, B: torch.Te
     if y is None:
         y = torch.empty((M, st.rows), dtype=torch.bfloat16, device=x.device)
     u = torch.empty((M, r), dtype=torch.float32, device=x.device) if save_u else None
-    ws_bytes = L.qlora_linear_workspace(M, st.rows, st.cols, r, 0)
+    o = _opts(rslora, dropout_mask, dropout_p)
+    op = ctypes.byref(o) if o is not None else None
+    ws_bytes = L.qlora_linear_workspace_ex(M, st.rows, st.cols, r, 0, op)
     if workspace is None or workspace.numel() < ws_bytes:
         workspace = linear_workspace(ws_bytes, x.device)
     s = st.c_struct()
-    _check(L.qlora_linear_fwd(ctypes.byref(s), x.data_ptr(), M, A.data_ptr(), B.data_ptr(), r,
-                              float(alpha), y.data_ptr(), _ptr(u), workspace.data_ptr(),
-                              workspace.numel(), _stream(x.device)))
+    _check(L.qlora_linear_fwd_ex(ctypes.byref(s), x.data_ptr(), M, A.data_ptr(), B.data_ptr(), r,
+                                 float(alpha), op, y.data_ptr(), _ptr(u), workspace.data_ptr(),
+                                 workspace.numel(), _stream(x.device)))
     return y, u
 
 
 def qlora_linear_bwd(st: NF4State, x: torch.Tensor, dY: torch.Tensor, A: torch.Tensor,
                      B: torch.Tensor, alpha: float, u: torch.Tensor | None = None,
-                     need_dx: bool = True, workspace: torch.Tensor | None = None):
+                     need_dx: bool = True, workspace: torch.Tensor | None = None,
+                     rslora: bool = False, dropout_mask: torch.Tensor | None = None,
+                     dropout_p: float = 0.0):
     """Returns (dX bf16 [M, d_in] or None, dA fp32 [r, d_in], dB fp32 [d_out, r])."""
     L = load_library()
     x = _dev(x, torch.bfloat16, "x")
@@ -296,14 +338,16 @@ def qlora_linear_bwd(st: NF4State, x: torch.Tensor, dY: torch.Tensor, A: torch.T
     dX = torch.empty((M, st.cols), dtype=torch.bfloat16, device=x.device) if need_dx else None
     dA = torch.empty((r, st.cols), dtype=torch.float32, device=x.device)
     dB = torch.empty((st.rows, r), dtype=torch.float32, device=x.device)
-    ws_bytes = L.qlora_linear_workspace(M, st.rows, st.cols, r, 1)
+    o = _opts(rslora, dropout_mask, dropout_p)
+    op = ctypes.byref(o) if o is not None else None
+    ws_bytes = L.qlora_linear_workspace_ex(M, st.rows, st.cols, r, 1, op)
     if workspace is None or workspace.numel() < ws_bytes:
         workspace = linear_workspace(ws_bytes, x.device)
     s = st.c_struct()
-    _check(L.qlora_linear_bwd(ctypes.byref(s), x.data_ptr(), dY.data_ptr(), M, A.data_ptr(),
-                              B.data_ptr(), r, float(alpha), _ptr(u), _ptr(dX), dA.data_ptr(),
-                              dB.data_ptr(), workspace.data_ptr(), workspace.numel(),
-                              _stream(x.device)))
+    _check(L.qlora_linear_bwd_ex(ctypes.byref(s), x.data_ptr(), dY.data_ptr(), M, A.data_ptr(),
+                                 B.data_ptr(), r, float(alpha), op, _ptr(u), _ptr(dX),
+                                 dA.data_ptr(), dB.data_ptr(), workspace.data_ptr(),
+                                 workspace.numel(), _stream(x.device)))
     return dX, dA, dB
 
 
@@ -331,30 +375,35 @@ def lora_linear_bf16(x: torch.Tensor, W: torch.Tensor, V: torch.Tensor, L_: torc
 
 class _QLoRAFn(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, x, A, B, st, alpha):
-        y, u = qlora_linear_fwd(st, x, A, B, alpha)
-        ctx.save_for_backward(x, A, B, u)
-        ctx.st, ctx.alpha = st, alpha
+    def forward(ctx, x, A, B, st, alpha, rslora, mask, p):
+        y, u = qlora_linear_fwd(st, x, A, B, alpha, rslora=rslora, dropout_mask=mask,
+                                dropout_p=p)
+        ctx.save_for_backward(x, A, B, u, mask)
+        ctx.st, ctx.alpha, ctx.rslora, ctx.p = st, alpha, rslora, p
         return y
 
     @staticmethod
     def backward(ctx, dY):
-        x, A, B, u = ctx.saved_tensors
+        x, A, B, u, mask = ctx.saved_tensors
         dX, dA, dB = qlora_linear_bwd(ctx.st, x, dY.contiguous(), A, B, ctx.alpha, u,
-                                      need_dx=ctx.needs_input_grad[0])
-        return dX, dA.to(A.dtype), dB.to(B.dtype), None, None
+                                      need_dx=ctx.needs_input_grad[0], rslora=ctx.rslora,
+                                      dropout_mask=mask, dropout_p=ctx.p)
+        return dX, dA.to(A.dtype), dB.to(B.dtype), None, None, None, None, None
 
 
 class QLoRALinear(torch.nn.Module):
     """Frozen NF4+DQ base weight with a rank-r adapter: y = x Qhat(W)^T +
-    (alpha/r) x A^T B^T.  A: (r, d_in), B: (d_out, r), bf16 (B starts at
-    zero, A Kaiming-uniform, as in the course notebook's LoRALinear)."""
+    s x A^T B^T, s = alpha/r (alpha/sqrt(r) with rslora), and dropout with
+    probability `dropout` on the adapter branch's input in training mode.
+    A: (r, d_in), B: (d_out, r), bf16 (B starts at zero, A Kaiming-uniform,
+    as in the course notebook's LoRALinear)."""
 
-    def __init__(self, weight: torch.Tensor, r: int = 16, alpha: float = 32.0):
+    def __init__(self, weight: torch.Tensor, r: int = 16, alpha: float = 32.0,
+                 dropout: float = 0.0, rslora: bool = False):
         super().__init__()
         d_out, d_in = weight.shape
         self.st = nf4_quantize_dq(weight.detach().float().contiguous())
-        self.r, self.alpha = r, alpha
+        self.r, self.alpha, self.dropout, self.rslora = r, alpha, float(dropout), bool(rslora)
         A = torch.empty(r, d_in, dtype=torch.float32, device=weight.device)
         torch.nn.init.kaiming_uniform_(A, a=5 ** 0.5)
         self.lora_A = torch.nn.Parameter(A.to(torch.bfloat16))
@@ -363,6 +412,9 @@ class QLoRALinear(torch.nn.Module):
 
     def forward(self, x):
         shp = x.shape
-        y = _QLoRAFn.apply(x.reshape(-1, shp[-1]).contiguous(), self.lora_A, self.lora_B,
-                           self.st, self.alpha)
+        x2 = x.reshape(-1, shp[-1]).contiguous()
+        p = self.dropout if self.training else 0.0
+        mask = dropout_mask(x2.shape[0], x2.shape[1], p, x2.device) if p > 0 else None
+        y = _QLoRAFn.apply(x2, self.lora_A, self.lora_B, self.st, self.alpha, self.rslora, mask,
+                           p)
         return y.reshape(*shp[:-1], y.shape[-1])

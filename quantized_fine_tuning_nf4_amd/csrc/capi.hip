@@ -3,6 +3,7 @@
 // launches nothing on error.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstring>
 #include <mutex>
 
@@ -114,13 +115,17 @@ struct FwdWs {
   int dbr;         // rows per band of the whole-row decode kernel (0: not used)
 };
 
+// dropout: the adapter branch reads a masked x, which the decode kernels
+// (one set of x fragments for both products) do not take; such forwards use
+// the GEMM routes.
 FwdWs carve_fwd(Carver& c, int64_t M, int64_t rows, int64_t cols, int r, bool need_u,
-                bool counters = true) {
+                bool counters = true, bool dropout = false) {
   FwdWs f;
   f.arrivals = counters ? c.take<unsigned>(kArrivalWords) : nullptr;
-  f.dbr = rows > 0 ? decode_rows_band(M, rows, cols, r) : 0;
-  f.dt = rows > 0 && f.dbr == 0 ? decode_tiles(M, rows, cols, r) : DecodeTiles{0, 0, 0};
-  f.dS = rows > 0 && f.dbr == 0 && f.dt.rgt == 0 ? decode_slices(M, rows, cols) : 0;
+  const bool dec = rows > 0 && !dropout;
+  f.dbr = dec ? decode_rows_band(M, rows, cols, r) : 0;
+  f.dt = dec && f.dbr == 0 ? decode_tiles(M, rows, cols, r) : DecodeTiles{0, 0, 0};
+  f.dS = dec && f.dbr == 0 && f.dt.rgt == 0 ? decode_slices(M, rows, cols) : 0;
   const bool decode = f.dbr > 0 || f.dt.rgt > 0 || f.dS > 0;  // u from the decode kernels
   f.S = thin_nt_slices(M, cols);
   f.u = need_u ? c.take<float>((size_t)M * r) : nullptr;
@@ -149,9 +154,11 @@ struct BwdWs {
   uint16_t* wt;   // [cols, ldt] bf16 Qhat(W)^T (dense path)
   int64_t ldt;
   uint16_t* At;   // [cols, r] A^T (dense path)
+  uint16_t* xd;   // [M, cols] the adapter branch's masked input (dropout)
 };
 
-BwdWs carve_bwd(Carver& c, int64_t M, int64_t rows, int64_t cols, int r, bool need_u) {
+BwdWs carve_bwd(Carver& c, int64_t M, int64_t rows, int64_t cols, int r, bool need_u,
+                bool dropout = false) {
   BwdWs b;
   b.arrivals = c.take<unsigned>(kArrivalWords);
   if (need_u) {
@@ -175,13 +182,38 @@ BwdWs carve_bwd(Carver& c, int64_t M, int64_t rows, int64_t cols, int r, bool ne
   const bool dense = dense_path(M, cols);
   b.wt = dense ? c.take<uint16_t>((size_t)cols * b.ldt) : nullptr;
   b.At = dense ? c.take<uint16_t>((size_t)cols * r) : nullptr;
+  b.xd = dropout ? c.take<uint16_t>((size_t)M * cols) : nullptr;
   return b;
+}
+
+// The adapter branch's options (nullable: alpha / r, no dropout).
+struct Lora {
+  float s;               // branch scale
+  const uint8_t* mask;   // dropout keep mask (nullable)
+};
+
+qn_status lora_options(const qn_lora_opts* o, float alpha, int r, Lora* out) {
+  out->s = alpha / (float)r;
+  out->mask = nullptr;
+  if (!o) return QN_OK;
+  if (o->rslora != 0 && o->rslora != 1) return QN_EINVAL;
+  // rsLoRA: alpha / sqrt(r) (sqrtf is correctly rounded)
+  if (o->rslora) out->s = alpha / sqrtf((float)r);
+  if (o->dropout_mask) {
+    const float p = o->dropout_p;
+    if (!(p >= 0.f && p < 1.f)) return QN_EINVAL;
+    out->mask = o->dropout_mask;
+    out->s = out->s / (1.f - p);  // inverted dropout, folded into the scale
+  } else if (o->dropout_p != 0.f) {
+    return QN_EINVAL;
+  }
+  return QN_OK;
 }
 
 // The forward, on a workspace of ws_bytes at ws; clear: zero the arrival
 // counters with a kernel before the launch that counts on them.
 qn_status forward(const qn_nf4dq* w, const uint16_t* x, int64_t M, const uint16_t* A,
-                  const uint16_t* B, int r, float alpha, uint16_t* y, float* u_out,
+                  const uint16_t* B, int r, const Lora& lo, uint16_t* y, float* u_out,
                   void* workspace, size_t workspace_bytes, void* stream, bool clear) {
   qn_status s = check_linear(w, M, r);
   if (s != QN_OK) return s;
@@ -191,17 +223,18 @@ qn_status forward(const qn_nf4dq* w, const uint16_t* x, int64_t M, const uint16_
       (u_out && !aligned16(u_out)))
     return QN_EALIGN;
   Carver probe(nullptr);
-  carve_fwd(probe, M, w->rows, w->cols, r, u_out == nullptr);
+  const bool drop = lo.mask != nullptr;
+  carve_fwd(probe, M, w->rows, w->cols, r, u_out == nullptr, true, drop);
   if (probe.used > 0) {
     if (!workspace) return QN_EINVAL;
     if (reinterpret_cast<uintptr_t>(workspace) & 255u) return QN_EALIGN;
     if (workspace_bytes < probe.used) return QN_EWORKSPACE;
   }
   Carver c(workspace);
-  FwdWs f = carve_fwd(c, M, w->rows, w->cols, r, u_out == nullptr);
+  FwdWs f = carve_fwd(c, M, w->rows, w->cols, r, u_out == nullptr, true, drop);
   float* u = u_out ? u_out : f.u;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const float scale = alpha / (float)r;
+  const float scale = lo.s;
   const int64_t N = w->rows, K = w->cols;
   if (f.dbr > 0)  // decode-sized batch, whole rows per workgroup
     return from_hip(launch_decode_rows(to_state(w), x, M, A, B, r, scale, y, u, f.dbr, st));
@@ -219,7 +252,8 @@ qn_status forward(const qn_nf4dq* w, const uint16_t* x, int64_t M, const uint16_
   // dense path: the slices of u are added by spare workgroups of the
   // dequantization launch that follows
   const bool fold = f.wd && f.S > 1;
-  hipError_t e = launch_thin_nt(x, A, M, K, r, u, f.upart, f.S, st, !fold);
+  hipError_t e = launch_thin_nt(x, A, M, K, r, u, f.upart, f.S, st, !fold, false,
+                                Clear{nullptr, 0}, lo.mask);
   if (f.wd) {
     if (e == hipSuccess)
       e = launch_dequant(w->packed, w->qscale, w->scale2, w->offset, N * K, true, f.wd, st,
@@ -325,20 +359,38 @@ qn_status nf4_dequantize(const qn_nf4dq* w, qn_dtype out_dtype, void* out, void*
                                  out_dtype == QN_BF16, out, static_cast<hipStream_t>(stream)));
 }
 
-size_t qlora_linear_workspace(int64_t M, int64_t rows, int64_t cols, int r, int backward) {
+size_t qlora_linear_workspace_ex(int64_t M, int64_t rows, int64_t cols, int r, int backward,
+                                 const qn_lora_opts* opts) {
   if (M < 0 || rows < 1 || cols < 1 || r < 1 || r > 64) return 0;
+  const bool drop = opts && opts->dropout_mask;
   Carver c(nullptr);
   if (backward)
-    carve_bwd(c, M, rows, cols, r, true);
+    carve_bwd(c, M, rows, cols, r, true, drop);
   else
-    carve_fwd(c, M, rows, cols, r, true);
+    carve_fwd(c, M, rows, cols, r, true, true, drop);
   return c.used;
+}
+
+size_t qlora_linear_workspace(int64_t M, int64_t rows, int64_t cols, int r, int backward) {
+  return qlora_linear_workspace_ex(M, rows, cols, r, backward, nullptr);
 }
 
 qn_status qlora_linear_fwd(const qn_nf4dq* w, const uint16_t* x, int64_t M, const uint16_t* A,
                            const uint16_t* B, int r, float alpha, uint16_t* y, float* u_out,
                            void* workspace, size_t workspace_bytes, void* stream) {
-  return forward(w, x, M, A, B, r, alpha, y, u_out, workspace, workspace_bytes, stream, false);
+  return qlora_linear_fwd_ex(w, x, M, A, B, r, alpha, nullptr, y, u_out, workspace,
+                             workspace_bytes, stream);
+}
+
+qn_status qlora_linear_fwd_ex(const qn_nf4dq* w, const uint16_t* x, int64_t M, const uint16_t* A,
+                              const uint16_t* B, int r, float alpha, const qn_lora_opts* opts,
+                              uint16_t* y, float* u_out, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  if (r < 1 || r > 64) return QN_EINVAL;
+  Lora lo;
+  qn_status s = lora_options(opts, alpha, r, &lo);
+  if (s != QN_OK) return s;
+  return forward(w, x, M, A, B, r, lo, y, u_out, workspace, workspace_bytes, stream, false);
 }
 
 qn_status qlora_linear_fwd_noalloc(const qn_nf4dq* w, const uint16_t* x, int64_t M,
@@ -355,7 +407,8 @@ qn_status qlora_linear_fwd_noalloc(const qn_nf4dq* w, const uint16_t* x, int64_t
   if (s != QN_OK) return s;
   // the array keeps what the last call left in it: its counters are cleared
   // by a kernel before the launch that counts on them
-  return forward(w, x, M, A, B, r, alpha, y, u_out, ptr, kStaticScratchBytes, stream, true);
+  return forward(w, x, M, A, B, r, Lora{alpha / (float)r, nullptr}, y, u_out, ptr,
+                 kStaticScratchBytes, stream, true);
 }
 
 
@@ -364,8 +417,21 @@ qn_status qlora_linear_bwd(const qn_nf4dq* w, const uint16_t* x, const uint16_t*
                            const uint16_t* A, const uint16_t* B, int r, float alpha,
                            const float* u_saved, uint16_t* dX, float* dA, float* dB,
                            void* workspace, size_t workspace_bytes, void* stream) {
+  return qlora_linear_bwd_ex(w, x, dY, M, A, B, r, alpha, nullptr, u_saved, dX, dA, dB,
+                             workspace, workspace_bytes, stream);
+}
+
+qn_status qlora_linear_bwd_ex(const qn_nf4dq* w, const uint16_t* x, const uint16_t* dY,
+                              int64_t M, const uint16_t* A, const uint16_t* B, int r, float alpha,
+                              const qn_lora_opts* opts, const float* u_saved, uint16_t* dX,
+                              float* dA, float* dB, void* workspace, size_t workspace_bytes,
+                              void* stream) {
   qn_status s = check_linear(w, M, r);
   if (s != QN_OK) return s;
+  Lora lo;
+  s = lora_options(opts, alpha, r, &lo);
+  if (s != QN_OK) return s;
+  const bool drop = lo.mask != nullptr;
   if (!A || !B || !dA || !dB) return QN_EINVAL;
   if (M > 0 && (!x || !dY)) return QN_EINVAL;
   if (!aligned16(x) || !aligned16(dY) || !aligned16(A) || !aligned16(B) || !aligned16(dA) ||
@@ -380,21 +446,24 @@ qn_status qlora_linear_bwd(const qn_nf4dq* w, const uint16_t* x, const uint16_t*
     return from_hip(e);
   }
   Carver probe(nullptr);
-  carve_bwd(probe, M, N, K, r, u_saved == nullptr);
+  carve_bwd(probe, M, N, K, r, u_saved == nullptr, drop);
   if (!workspace) return QN_EINVAL;
   if (reinterpret_cast<uintptr_t>(workspace) & 255u) return QN_EALIGN;
   if (workspace_bytes < probe.used) return QN_EWORKSPACE;
   Carver c(workspace);
-  BwdWs b = carve_bwd(c, M, N, K, r, u_saved == nullptr);
-  const float scale = alpha / (float)r;
+  BwdWs b = carve_bwd(c, M, N, K, r, u_saved == nullptr, drop);
+  const float scale = lo.s;
   hipError_t e = hipSuccess;
+  // dropout: the adapter branch's masked input, for dA (u takes the mask on
+  // the fly)
+  if (drop) e = launch_dropout_apply(x, lo.mask, M, K, b.xd, st);
   const float* u = u_saved;
-  // the first launch of the call zeroes the arrival counters the adapter
+  // an early launch of the call zeroes the arrival counters the adapter
   // gradients' launch counts on, so the backward never depends on what the
   // workspace held before
   Clear clr{b.arrivals, kArrivalWords};
-  if (!u) {
-    e = launch_thin_nt(x, A, M, K, r, b.fu.u, b.fu.upart, b.fu.S, st, true, false, clr);
+  if (!u && e == hipSuccess) {
+    e = launch_thin_nt(x, A, M, K, r, b.fu.u, b.fu.upart, b.fu.S, st, true, false, clr, lo.mask);
     clr = Clear{nullptr, 0};
     u = b.fu.u;
   }
@@ -443,15 +512,19 @@ qn_status qlora_linear_bwd(const qn_nf4dq* w, const uint16_t* x, const uint16_t*
       e = launch_bwd_aux(aux, st);
   }
   if (e == hipSuccess && dX) {
+    // under dropout the branch's share is added masked after the base product
+    const float sx = drop ? 0.f : scale;
     if (dense_dx)
-      e = launch_gemm_nt(dY, N, N, b.wt, b.ldt, M, K, b.v, b.At, r, scale, dX, st);
+      e = launch_gemm_nt(dY, N, N, b.wt, b.ldt, M, K, b.v, b.At, r, sx, dX, st);
     else
-      e = launch_qgemm_dx(to_state(w), dY, M, b.v, A, r, scale, dX, st);
+      e = launch_qgemm_dx(to_state(w), dY, M, b.v, A, r, sx, dX, st);
+    if (e == hipSuccess && drop) e = launch_lora_masked_add(dX, b.v, A, lo.mask, M, K, r, scale, st);
   }
   // dB = s G^T u and dA = s v^T X in one launch (and their slice sums in one)
   if (e == hipSuccess)
     e = launch_thin_tn2(ThinTn{dY, b.su, N, dB, false, b.dBpart},
-                        ThinTn{x, b.sv, K, dA, true, b.dApart}, M, r, b.arrivals, st);
+                        ThinTn{drop ? b.xd : x, b.sv, K, dA, true, b.dApart}, M, r, b.arrivals,
+                        st);
   return from_hip(e);
 }
 

@@ -37,6 +37,16 @@ __device__ __forceinline__ u32x4 load8(const uint16_t* row, int64_t p, int64_t P
   return u32x4{w[0], w[1], w[2], w[3]};
 }
 
+// 8 bf16 values with the dropped ones zeroed: mb holds their 8 mask bits
+// (the masks are bit-packed over the elements, bit e % 8 of byte e / 8 set:
+// kept, so 8 elements starting at a multiple of 8 share one byte).
+__device__ __forceinline__ u32x4 keep8(u32x4 v, uint32_t mb) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    v[q] &= (((mb >> (2 * q)) & 1u) * 0xffffu) | (((mb >> (2 * q + 1)) & 1u) * 0xffff0000u);
+  return v;
+}
+
 // The first workgroup of a launch zeroes clr.n words at clr.p (the arrival
 // counters a later kernel of the same call counts on).
 __device__ __forceinline__ void clear_words(const Clear& clr) {
@@ -56,7 +66,8 @@ template <int NJ>
 __global__ __launch_bounds__(kThreads) void k_thin_nt(const uint16_t* __restrict__ Z,
                                                       const uint16_t* __restrict__ T, int64_t M,
                                                       int64_t P, int r, int64_t slice,
-                                                      float* __restrict__ out, Clear clr) {
+                                                      float* __restrict__ out, Clear clr,
+                                                      const uint8_t* __restrict__ zmask) {
   constexpr int U = NJ <= 2 ? 8 : 4;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   clear_words(clr);
@@ -81,6 +92,7 @@ __global__ __launch_bounds__(kThreads) void k_thin_nt(const uint16_t* __restrict
       za[u] = *reinterpret_cast<const u32x4*>(zp + o);
 #pragma unroll
       for (int jt = 0; jt < NJ; ++jt) tb[u][jt] = *reinterpret_cast<const u32x4*>(tp[jt] + o);
+      if (zmask) za[u] = keep8(za[u], zmask[(m * P + pb + 8 * g + o) >> 3]);
       if (!ok) za[u] = u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
@@ -118,7 +130,8 @@ template <int TMODE>
 __global__ __launch_bounds__(kThreads) void k_thin_nt1(const uint16_t* __restrict__ Z,
                                                        const uint16_t* __restrict__ T, int64_t M,
                                                        int64_t P, int r, int64_t slice,
-                                                       float* __restrict__ out, Clear clr) {
+                                                       float* __restrict__ out, Clear clr,
+                                                       const uint8_t* __restrict__ zmask) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   clear_words(clr);
@@ -133,11 +146,13 @@ __global__ __launch_bounds__(kThreads) void k_thin_nt1(const uint16_t* __restric
   const uint16_t* zp = Z + m * P + pb + 8 * g;
   const int64_t lim = width - 8 * g;  // in-slice columns left for this lane's chunk
   u32x4 za[2][TN1_U];
+  uint32_t zm[2][TN1_U];  // their mask bytes (dropout on Z), loaded beside them
   auto load_batch = [&](int buf, int b) {
 #pragma unroll
     for (int u = 0; u < TN1_U; ++u) {
       const int64_t off = 32 * (int64_t)(TN1_U * b + u);
       za[buf][u] = *reinterpret_cast<const u32x4*>(zp + (off < lim ? off : 0));
+      if (zmask) zm[buf][u] = zmask[(m * P + pb + 8 * g + (off < lim ? off : 0)) >> 3];
     }
   };
   if constexpr (TMODE == 0) {
@@ -222,7 +237,8 @@ __global__ __launch_bounds__(kThreads) void k_thin_nt1(const uint16_t* __restric
     for (int u = 0; u < TN1_U; ++u) {
       const int st = TN1_U * b + u;
       if (st < steps) {
-        const u32x4 z = 32 * (int64_t)st < lim ? za[buf][u] : u32x4{0u, 0u, 0u, 0u};
+        u32x4 z = 32 * (int64_t)st < lim ? za[buf][u] : u32x4{0u, 0u, 0u, 0u};
+        if (zmask) z = keep8(z, zm[buf][u]);
         const u32x4 t = *reinterpret_cast<const u32x4*>(trow + 64 * st);
         acc = mfma16(as_bf16x8(z), as_bf16x8(t), acc);
       }
@@ -277,7 +293,7 @@ int thin_nt_slices(int64_t M, int64_t P) {
 
 hipError_t launch_thin_nt(const uint16_t* Z, const uint16_t* T, int64_t M, int64_t P, int r,
                           float* out, float* part, int S, hipStream_t st, bool sum, bool t_rows,
-                          Clear clr) {
+                          Clear clr, const uint8_t* zmask) {
   const int64_t slice = thin_nt_slice(P, S);
   const dim3 grid((unsigned)((M + 63) / 64), (unsigned)S);
   float* dst = S > 1 ? part : out;
@@ -297,18 +313,18 @@ hipError_t launch_thin_nt(const uint16_t* Z, const uint16_t* T, int64_t M, int64
     const int steps = (int)((slice + 31) / 32);
     const size_t lds = (size_t)16 * (steps * 64 + 16);
     if (mode == 0)
-      hipLaunchKernelGGL(k_thin_nt1<0>, grid, dim3(kThreads), lds, st, Z, T, M, P, r, slice, dst, clr);
+      hipLaunchKernelGGL(k_thin_nt1<0>, grid, dim3(kThreads), lds, st, Z, T, M, P, r, slice, dst, clr, zmask);
     else if (mode == 1)
-      hipLaunchKernelGGL(k_thin_nt1<1>, grid, dim3(kThreads), lds, st, Z, T, M, P, r, slice, dst, clr);
+      hipLaunchKernelGGL(k_thin_nt1<1>, grid, dim3(kThreads), lds, st, Z, T, M, P, r, slice, dst, clr, zmask);
     else
-      hipLaunchKernelGGL(k_thin_nt1<2>, grid, dim3(kThreads), lds, st, Z, T, M, P, r, slice, dst, clr);
+      hipLaunchKernelGGL(k_thin_nt1<2>, grid, dim3(kThreads), lds, st, Z, T, M, P, r, slice, dst, clr, zmask);
   } else {
     if (t_rows) return hipErrorInvalidValue;  // the general kernel takes T as [r, P]
   switch ((r + 15) / 16) {
-    case 1: hipLaunchKernelGGL(k_thin_nt<1>, grid, dim3(kThreads), 0, st, Z, T, M, P, r, slice, dst, clr); break;
-    case 2: hipLaunchKernelGGL(k_thin_nt<2>, grid, dim3(kThreads), 0, st, Z, T, M, P, r, slice, dst, clr); break;
-    case 3: hipLaunchKernelGGL(k_thin_nt<3>, grid, dim3(kThreads), 0, st, Z, T, M, P, r, slice, dst, clr); break;
-    default: hipLaunchKernelGGL(k_thin_nt<4>, grid, dim3(kThreads), 0, st, Z, T, M, P, r, slice, dst, clr); break;
+    case 1: hipLaunchKernelGGL(k_thin_nt<1>, grid, dim3(kThreads), 0, st, Z, T, M, P, r, slice, dst, clr, zmask); break;
+    case 2: hipLaunchKernelGGL(k_thin_nt<2>, grid, dim3(kThreads), 0, st, Z, T, M, P, r, slice, dst, clr, zmask); break;
+    case 3: hipLaunchKernelGGL(k_thin_nt<3>, grid, dim3(kThreads), 0, st, Z, T, M, P, r, slice, dst, clr, zmask); break;
+    default: hipLaunchKernelGGL(k_thin_nt<4>, grid, dim3(kThreads), 0, st, Z, T, M, P, r, slice, dst, clr, zmask); break;
   }
   }
   if (S > 1 && sum) {

@@ -213,10 +213,24 @@ struct WState {
 // out; S == 1 writes out directly.
 // sum == false leaves the slices in part for the caller to add.  t_rows:
 // T is given as its transpose [P, r] (r <= 16 only).  clr: words the first
-// workgroup zeroes.
+// workgroup zeroes.  zmask (nullable): Z's elements whose bit is clear read
+// as zero (bit-packed over the row-major elements, bit e % 8 of byte e / 8;
+// P % 8 == 0).
 hipError_t launch_thin_nt(const uint16_t* Z, const uint16_t* T, int64_t M, int64_t P, int r,
                           float* out, float* part, int S, hipStream_t st, bool sum = true,
-                          bool t_rows = false, Clear clr = Clear{nullptr, 0});
+                          bool t_rows = false, Clear clr = Clear{nullptr, 0},
+                          const uint8_t* zmask = nullptr);
+
+// Xd [M, K] = X with the elements whose mask bit is clear zeroed (K % 8 == 0).
+hipError_t launch_dropout_apply(const uint16_t* X, const uint8_t* mask, int64_t M, int64_t K,
+                                uint16_t* Xd, hipStream_t st);
+
+// dX[m][k] (bf16) += s (v A)[m][k] where mask bit (m, k) is set: the
+// adapter branch's input gradient under dropout.  v fp32 [M, r], A bf16
+// [r, K], K % 8 == 0, 1 <= r <= 64.
+hipError_t launch_lora_masked_add(uint16_t* dX, const float* v, const uint16_t* A,
+                                  const uint8_t* mask, int64_t M, int64_t K, int r, float s,
+                                  hipStream_t st);
 int thin_nt_slices(int64_t M, int64_t P);
 bool thin_nt_rows_ok(int64_t M, int64_t P, int r);
 
