@@ -62,7 +62,14 @@ def lib():
         L.orc_scale_mean.restype = ctypes.c_float
         L.orc_quantize.argtypes = [_P, _I64, ctypes.c_int, _P, _P, _P, _P, _P]
         L.orc_quantize.restype = ctypes.c_int
+        L.orc_quantize_cb.argtypes = [_P, _I64, ctypes.c_int, ctypes.c_int, _P, _P, _P, _P, _P]
+        L.orc_quantize_cb.restype = ctypes.c_int
         L.orc_dequantize.argtypes = [_P, _I64, ctypes.c_int, _P, _P, _P, _P, _P, _P]
+        L.orc_dequantize_cb.argtypes = [_P, _I64, ctypes.c_int, ctypes.c_int, _P, _P, _P, _P,
+                                        _P, _P]
+        L.orc_fp4_codebook.argtypes = [_P]
+        L.orc_fp4_code.argtypes = [ctypes.c_float]
+        L.orc_fp4_code.restype = ctypes.c_int
         L.orc_lora_down.argtypes = [_P, _P, _I64, ctypes.c_int, _P, _I64, _P]
         L.orc_qlora_fwd.argtypes = [_P, _I64, _I64, _P, _P, _P, ctypes.c_int,
                                     ctypes.c_double, _P, _I64, _P, _P]
@@ -114,6 +121,18 @@ def codebook() -> np.ndarray:
     return out
 
 
+def fp4_codebook() -> np.ndarray:
+    """The 16 FP4 code values (code c: sign bit 3, magnitude index c & 7)."""
+    out = np.zeros(16, np.float32)
+    lib().orc_fp4_codebook(_ptr(out))
+    return out
+
+
+def fp4_codes(n: np.ndarray) -> np.ndarray:
+    n = np.ascontiguousarray(n, dtype=np.float32).ravel()
+    return np.array([lib().orc_fp4_code(float(v)) for v in n], np.uint8)
+
+
 def nf4_codes(n: np.ndarray) -> np.ndarray:
     n = np.ascontiguousarray(n, dtype=np.float32)
     out = np.empty(n.size, np.uint8)
@@ -149,14 +168,19 @@ class State:
     rows: int
     cols: int
     double_quant: bool
+    codebook: int = 0    # 0 NF4, 1 FP4
 
     @property
     def n(self) -> int:
         return self.rows * self.cols
 
 
-def quantize(W: np.ndarray, double_quant: bool = True) -> State:
-    """NF4 block-64 quantisation (+ double quantisation) of an fp32 array.
+CODEBOOKS = {"nf4": 0, "fp4": 1}
+
+
+def quantize(W: np.ndarray, double_quant: bool = True, codebook: str = "nf4") -> State:
+    """Block-64 4-bit quantisation (NF4 or FP4 codes, + double quantisation)
+    of an fp32 array.
 
     Raises ValueError on empty or non-finite input, like the page's listing.
     """
@@ -170,13 +194,14 @@ def quantize(W: np.ndarray, double_quant: bool = True) -> State:
     qscale = np.zeros(nb, np.uint8)
     scale2 = np.zeros(ng, np.float32)
     offset = np.zeros(1, np.float32)
-    st = lib().orc_quantize(_ptr(W), n, int(bool(double_quant)), _ptr(packed), _ptr(absmax),
-                            _ptr(qscale), _ptr(scale2), _ptr(offset))
+    cb = CODEBOOKS[codebook]
+    st = lib().orc_quantize_cb(_ptr(W), n, cb, int(bool(double_quant)), _ptr(packed),
+                               _ptr(absmax), _ptr(qscale), _ptr(scale2), _ptr(offset))
     if st == EINVAL:
         raise ValueError("quantizer input: empty")
     if st == ENONFINITE:
         raise ValueError("quantizer input: non-finite")
-    return State(packed, absmax, qscale, scale2, offset[0], rows, cols, bool(double_quant))
+    return State(packed, absmax, qscale, scale2, offset[0], rows, cols, bool(double_quant), cb)
 
 
 def dequantize(s: State, want_f32: bool = True, want_bf16: bool = True):
@@ -185,8 +210,8 @@ def dequantize(s: State, want_f32: bool = True, want_bf16: bool = True):
     f32 = np.empty(n, np.float32) if want_f32 else None
     b16 = np.empty(n, np.uint16) if want_bf16 else None
     off = np.array([s.offset], np.float32)
-    lib().orc_dequantize(_ptr(s.packed), n, int(s.double_quant), _ptr(s.absmax), _ptr(s.qscale),
-                         _ptr(s.scale2), _ptr(off), _ptr(f32), _ptr(b16))
+    lib().orc_dequantize_cb(_ptr(s.packed), n, s.codebook, int(s.double_quant), _ptr(s.absmax),
+                            _ptr(s.qscale), _ptr(s.scale2), _ptr(off), _ptr(f32), _ptr(b16))
     shape = (s.rows, s.cols)
     return (f32.reshape(shape) if f32 is not None else None,
             b16.reshape(shape) if b16 is not None else None)

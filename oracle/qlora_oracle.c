@@ -65,6 +65,38 @@ static const double NF4_PAGE_LITERALS[16] = {
 
 static float level(int k) { return (float)NF4_PAGE_LITERALS[k]; }
 
+/* FP4 (course notebook FT-02, "Exercise 3: NF4 vs FP4 at equal memory"): an
+ * E2M1 float format whose normalized positive levels, as the notebook
+ * prints them from bitsandbytes, are 0, 0.0052, 0.1667, 0.25, 0.3333, 0.5,
+ * 0.6667, 1.  Reading: the exact levels are {0, 0.0625, 2, 3, 4, 6, 8, 12}
+ * / 12 (each rounds to the printed value at four decimals), stored as fp32;
+ * a code is sign (bit 3) and magnitude index (bits 0..2), code c meaning
+ * (c & 8 ? -1 : +1) * FP4_MAG[c & 7]. */
+static const double FP4_MAG[8] = {0.0,       0.0625 / 12, 2.0 / 12, 3.0 / 12,
+                                  4.0 / 12, 6.0 / 12,    8.0 / 12, 1.0};
+
+static float fp4_level(int c) {
+  float m = (float)FP4_MAG[c & 7];
+  return (c & 8) ? -m : m;
+}
+
+void orc_fp4_codebook(float out[16]) {
+  for (int c = 0; c < 16; ++c) out[c] = fp4_level(c);
+}
+
+/* FP4 code of a normalised value n: the sign of n, and the nearest
+ * magnitude of |n| (exact fp64 midpoints of adjacent fp32 magnitudes; a
+ * value exactly on a midpoint takes the lower magnitude). */
+int orc_fp4_code(float n) {
+  float a = fabsf(n);
+  int m = 0;
+  for (int k = 0; k < 7; ++k) {
+    double mid = ((double)(float)FP4_MAG[k] + (double)(float)FP4_MAG[k + 1]) / 2.0;
+    if ((double)a > mid) m = k + 1;
+  }
+  return (signbit(n) ? 8 : 0) | m;
+}
+
 void orc_codebook(float out[16]) {
   for (int k = 0; k < 16; ++k) out[k] = level(k);
 }
@@ -219,6 +251,13 @@ static void double_quantize(const float* absmax, int64_t nb, uint8_t* qscale,
   }
 }
 
+/* Blockwise 4-bit quantisation with the NF4 (codebook 0) or FP4 (codebook
+ * 1) codes; the same blocks, scales, packing and double quantisation as
+ * orc_quantize below, which is codebook 0. */
+int orc_quantize_cb(const float* w, int64_t n, int codebook, int double_quant,
+                    uint8_t* packed, float* absmax, uint8_t* qscale, float* scale2,
+                    float* offset);
+
 /* Blockwise NF4 quantisation of n fp32 values.
  *   packed [32*nb]  two codes per byte, element 2j low nibble
  *   absmax [nb]     fp32 first-level scales (kept: the DQ-off state)
@@ -228,7 +267,13 @@ static void double_quantize(const float* absmax, int64_t nb, uint8_t* qscale,
 int orc_quantize(const float* w, int64_t n, int double_quant, uint8_t* packed,
                  float* absmax, uint8_t* qscale, float* scale2,
                  float* offset) {
-  if (n < 1) return ORC_EINVAL;
+  return orc_quantize_cb(w, n, 0, double_quant, packed, absmax, qscale, scale2, offset);
+}
+
+int orc_quantize_cb(const float* w, int64_t n, int codebook, int double_quant,
+                    uint8_t* packed, float* absmax, uint8_t* qscale, float* scale2,
+                    float* offset) {
+  if (n < 1 || codebook < 0 || codebook > 1) return ORC_EINVAL;
   for (int64_t i = 0; i < n; ++i)
     if (!isfinite(w[i])) return ORC_ENONFINITE;
   int64_t nb = (n + 63) / 64;
@@ -246,7 +291,7 @@ int orc_quantize(const float* w, int64_t n, int double_quant, uint8_t* packed,
     uint8_t code[64];
     for (int i = 0; i < 64; ++i) {
       float nv = (s > 0.0f) ? blk[i] / s : blk[i] / 1.0f;
-      code[i] = (uint8_t)orc_nf4_code(nv);
+      code[i] = (uint8_t)(codebook ? orc_fp4_code(nv) : orc_nf4_code(nv));
     }
     for (int j = 0; j < 32; ++j)
       packed[b * 32 + j] = (uint8_t)(code[2 * j] | (code[2 * j + 1] << 4));
@@ -265,10 +310,22 @@ static float block_scale(int64_t b, int double_quant, const float* absmax,
 
 /* w'_i = RN32(L[c_i] * s'_b); fp32 and/or bf16 (RNE of w') outputs, n
  * elements (padding is not written).  Either output may be NULL. */
+void orc_dequantize_cb(const uint8_t* packed, int64_t n, int codebook, int double_quant,
+                       const float* absmax, const uint8_t* qscale, const float* scale2,
+                       const float* offset, float* out_f32, uint16_t* out_bf16);
+
 void orc_dequantize(const uint8_t* packed, int64_t n, int double_quant,
                     const float* absmax, const uint8_t* qscale,
                     const float* scale2, const float* offset, float* out_f32,
                     uint16_t* out_bf16) {
+  orc_dequantize_cb(packed, n, 0, double_quant, absmax, qscale, scale2, offset, out_f32,
+                    out_bf16);
+}
+
+/* orc_dequantize with the codes of either codebook (0 NF4, 1 FP4). */
+void orc_dequantize_cb(const uint8_t* packed, int64_t n, int codebook, int double_quant,
+                       const float* absmax, const uint8_t* qscale, const float* scale2,
+                       const float* offset, float* out_f32, uint16_t* out_bf16) {
   int64_t nb = (n + 63) / 64;
 #pragma omp parallel for schedule(static)
   for (int64_t b = 0; b < nb; ++b) {
@@ -278,7 +335,7 @@ void orc_dequantize(const uint8_t* packed, int64_t n, int double_quant,
       if (idx >= n) break;
       uint8_t byte = packed[idx / 2];
       int c = (idx % 2 == 0) ? (byte & 15) : (byte >> 4);
-      float v = level(c) * sp;
+      float v = (codebook ? fp4_level(c) : level(c)) * sp;
       if (out_f32) out_f32[idx] = v;
       if (out_bf16) out_bf16[idx] = orc_bf16_rne(v);
     }

@@ -725,3 +725,81 @@ def test_dropout_special_masks(orc):
     assert np.array_equal(dX0, orc.qlora_dx(Wd, G, A, B, 0.0)[0])
     dA0, dB0 = orc.adapter_grads_dropout(x, G, A, B, s, zeros)
     assert not dA0.any() and not dB0.any()
+
+
+# --------------------------------------------------------------- FP4 codes and DQ off
+# Course notebook FT-02: "Exercise 3: NF4 vs FP4 at equal memory" (FP4
+# levels) and "Guided example 3: double quantization" (DQ on/off, 4.5 vs
+# 4.127 bits per weight).
+def test_fp4_levels_round_to_the_printed_table(orc):
+    printed = np.array(_golden.values("fp4_levels_page1.txt"))
+    cb = orc.fp4_codebook().astype(np.float64)
+    assert np.array_equal(np.round(cb[:8], 4), printed)
+    assert np.array_equal(cb[8:], -cb[:8])
+    assert np.signbit(cb[8]) and cb[8] == 0.0 and cb[0] == 0.0 and not np.signbit(cb[0])
+    # E2M1: sign, two exponent bits, one mantissa bit; with the subnormal
+    # level 0.0625 (bitsandbytes' table), over the largest value 12
+    e2m1 = np.array([0, 0.0625, 2, 3, 4, 6, 8, 12]) / 12
+    assert np.array_equal(cb[:8], e2m1.astype(np.float32).astype(np.float64))
+    assert np.all(np.diff(cb[:8]) > 0)
+
+
+def _fp4_exact(n):
+    """Sign of n and the nearest magnitude by exact rational distances,
+    ties to the lower magnitude."""
+    mags = [Fraction(float(np.float32(v))) for v in np.array([0, 0.0625, 2, 3, 4, 6, 8, 12]) / 12]
+    out = []
+    for v in np.asarray(n, np.float32):
+        a = Fraction(abs(float(v)))
+        d = [abs(a - m) for m in mags]
+        k = min(range(8), key=lambda i: (d[i], i))
+        out.append((8 if np.signbit(v) else 0) | k)
+    return np.array(out, np.uint8)
+
+
+def test_fp4_codes_brute_force(orc):
+    cb = orc.fp4_codebook()
+    mids = [(float(cb[k]) + float(cb[k + 1])) / 2 for k in range(7)]
+    vals = np.concatenate([fp32_window(m, 200) for m in mids] +
+                          [-fp32_window(m, 200) for m in mids] +
+                          [np.random.default_rng(3).uniform(-1, 1, 20000).astype(np.float32),
+                           np.array([0.0, -0.0, 1.0, -1.0, 1e-45, -1e-45], np.float32)])
+    assert np.array_equal(orc.fp4_codes(vals), _fp4_exact(vals))
+
+
+def test_fp4_quantize_against_brute_force(orc):
+    rng = np.random.default_rng(4)
+    W = (rng.standard_normal((7, 100)) * 0.02).astype(np.float32)
+    W[2, :64] = 0.0
+    st = orc.quantize(W, codebook="fp4")
+    flat = np.concatenate([W.ravel(), np.zeros((-W.size) % 64, np.float32)]).reshape(-1, 64)
+    s = np.abs(flat).max(axis=1)
+    n = np.where(s[:, None] > 0, flat / np.where(s > 0, s, 1)[:, None], flat).astype(np.float32)
+    assert np.array_equal(orc.codes_of(st)[:flat.size], _fp4_exact(n.ravel()))
+    # every nonzero block holds its absmax at magnitude index 7 (+-1)
+    codes = orc.codes_of(st)[:flat.size].reshape(-1, 64)
+    assert all(((codes[b] & 7) == 7).any() for b in range(codes.shape[0]) if s[b] > 0)
+    # dequantization: level times the block scale
+    f32, _ = orc.dequantize(st, want_bf16=False)
+    cbv = orc.fp4_codebook()
+    assert f32.shape == W.shape
+    ref = (cbv[codes.ravel()].reshape(codes.shape) *
+           np.array([orc.e4m3_decode(q) * st.scale2[b // 256] + st.offset
+                     for b, q in enumerate(st.qscale)], np.float32)[:, None])
+    assert np.allclose(f32.ravel(), ref.ravel()[:W.size], rtol=1e-6, atol=0)
+
+
+def test_dq_off_state_and_storage(orc):
+    """DQ off: the state keeps the fp32 block scales and dequantization uses
+    them as they are; 4 + 32/64 = 4.5 bits per weight against 4.127 with DQ."""
+    g = _golden.table("storage_bits.txt")
+    W = np.random.default_rng(5).standard_normal((64, 1024)).astype(np.float32) * 0.02
+    for cb in ("nf4", "fp4"):
+        st = orc.quantize(W, double_quant=False, codebook=cb)
+        f32, _ = orc.dequantize(st, want_bf16=False)
+        levels = orc.codebook() if cb == "nf4" else orc.fp4_codebook()
+        codes = orc.codes_of(st)[:W.size].reshape(-1, 64)
+        ref = (levels[codes] * st.absmax[:, None]).astype(np.float32)
+        assert np.array_equal(f32.ravel().view(np.uint32), ref.ravel().view(np.uint32))
+        bits = 8 * st.packed.size + 32 * st.absmax.size
+        assert bits / W.size == g["bits_no_dq"]
