@@ -363,6 +363,30 @@ def bench_extras(torch, qn, wl):
     out["quantize_dq_4096x4096"] = dict(ms=med, ms_min=mn, bytes=nbytes, GBs=nbytes / med / 1e6,
                                         hbm_frac=nbytes / med / 1e6 / HBM_PEAK_GBS,
                                         sync_call_wall_ms=q_wall)
+    # the format variants on the same weight: FP4 codes, double quantization
+    # off (fp32 block scales): quantize and dequantize to bf16
+    fmt = {}
+    for cb, dq in (("fp4", True), ("nf4", False), ("fp4", False)):
+        sts = [qn.qn_quantize(Ws[i % 6], codebook=cb, double_quant=dq) for i in range(6)]
+        torch.cuda.synchronize()
+        qms = [_event_time_ms(torch, lambda i: qn.qn_quantize(
+            Ws[i % 6], codebook=cb, double_quant=dq, workspace=qws, nonfinite=flag), 24)
+            for _ in range(5)]
+        outs_fmt = [torch.empty((4096, 4096), dtype=torch.bfloat16, device="cuda")
+                    for _ in range(6)]
+        dms = [_event_time_ms(torch, lambda i: qn.nf4_dequantize(sts[i % 6], torch.bfloat16,
+                                                                  out=outs_fmt[i % 6]), 24)
+               for _ in range(5)]
+        sb = sts[0].nbytes()
+        qb, db = 4 * 4096 * 4096 + sb, sb + 2 * 4096 * 4096
+        qmed, dmed = _median_min(qms)[0], _median_min(dms)[0]
+        fmt[f"{cb}_{'dq' if dq else 'nodq'}"] = dict(
+            quantize_ms=qmed, quantize_hbm_frac=qb / qmed / 1e6 / HBM_PEAK_GBS,
+            dequant_bf16_ms=dmed, dequant_hbm_frac=db / dmed / 1e6 / HBM_PEAK_GBS,
+            state_bytes=sb, bits_per_weight=8 * sb / (4096 * 4096))
+        del sts, outs_fmt
+    out["formats_4096x4096"] = fmt
+
     # adapter merge Qhat(W) + s B A into fp32 (rank 16), rotated states
     Am = _bf16(torch, wl.normal_bf16((16, 4096), wl.SEED_A + 2, 0.01))
     Bm = _bf16(torch, wl.normal_bf16((4096, 16), wl.SEED_B + 2, 0.01))

@@ -83,7 +83,7 @@
 extern "C" {
 #endif
 
-#define QN_ABI_VERSION 3
+#define QN_ABI_VERSION 4
 
 /* Bytes of arrival counters at the start of a linear workspace. */
 #define QN_ARRIVAL_BYTES 4096
@@ -99,7 +99,23 @@ typedef enum {
 
 typedef enum { QN_F32 = 0, QN_BF16 = 1 } qn_dtype;
 
-/* A quantized weight in format v1 (device pointers, host struct). */
+/* Codebooks of the 4-bit codes (qn_nf4dq.codebook). */
+#define QN_CODE_NF4 0 /* the NF4 table above                                  */
+#define QN_CODE_FP4 1 /* FP4 (course notebook FT-02, "Exercise 3: NF4 vs FP4 at
+                         equal memory"): E2M1 levels {0, 0.0625, 2, 3, 4, 6, 8,
+                         12} / 12 in fp32; code = sign (bit 3) | magnitude index;
+                         nearest magnitude, ties to the lower                 */
+
+/* A quantized weight (device pointers, host struct).  With absmax == NULL
+ * the block scales are double quantized (qscale, scale2, offset: format v1
+ * above); with absmax != NULL double quantization is off (course notebook
+ * FT-02, "Guided example 3: double quantization"): absmax [nb] holds the
+ * fp32 block scales and qscale, scale2, offset are ignored (4.5 bits per
+ * weight against 4.127).  codebook: QN_CODE_NF4 (zero-initialised structs
+ * are NF4) or QN_CODE_FP4.  Calls other than quantize, dequantize, merge and
+ * the linear calls' large-batch route take NF4 with double quantization; the
+ * linear calls route other states through the large-batch route (a bf16
+ * copy of the weight in the workspace) at every batch size. */
 typedef struct {
   const uint8_t* packed; /* [32*nb] */
   const uint8_t* qscale; /* [nb]    */
@@ -107,6 +123,8 @@ typedef struct {
   const float* offset;   /* [1]     */
   int64_t rows;          /* d_out   */
   int64_t cols;          /* d_in    */
+  const float* absmax;   /* [nb] fp32 block scales (double quantization off), or NULL */
+  int32_t codebook;      /* QN_CODE_NF4 or QN_CODE_FP4 */
 } qn_nf4dq;
 
 /* ABI version of the loaded library (QN_ABI_VERSION). */
@@ -117,6 +135,10 @@ const char* qn_status_str(qn_status s);
 
 /* The 16 NF4 levels the library uses, as fp32, into host memory. */
 void qn_nf4_codebook(float out[16]);
+
+/* The 16 FP4 code values the library uses (QN_CODE_FP4), as fp32, into host
+ * memory. */
+void qn_fp4_codebook(float out[16]);
 
 /* Workspace bytes needed by nf4_quantize_dq for a rows x cols weight. */
 size_t nf4_quantize_dq_workspace(int64_t rows, int64_t cols);
@@ -134,6 +156,17 @@ size_t nf4_quantize_dq_workspace(int64_t rows, int64_t cols);
 qn_status nf4_quantize_dq(const float* W, int64_t rows, int64_t cols, uint8_t* packed,
                           uint8_t* qscale, float* scale2, float* offset, int* nonfinite,
                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Blockwise 4-bit quantization with a choice of codebook and of double
+ * quantization: nf4_quantize_dq is (QN_CODE_NF4, double_quant = 1).  With
+ * double_quant != 0 writes packed, qscale, scale2, offset (absmax may be
+ * NULL); with double_quant == 0 writes packed and absmax [nb] fp32 (qscale,
+ * scale2, offset may be NULL).  Same blocks, codes search rule, workspace
+ * (nf4_quantize_dq_workspace) and non-finite reporting as nf4_quantize_dq. */
+qn_status qn_quantize(const float* W, int64_t rows, int64_t cols, int codebook,
+                      int double_quant, uint8_t* packed, uint8_t* qscale, float* scale2,
+                      float* offset, float* absmax, int* nonfinite, void* workspace,
+                      size_t workspace_bytes, void* stream);
 
 /* Dequantize w into out [rows, cols]: fp32 (QN_F32) or bf16 bit patterns
  * (QN_BF16, round to nearest even of the fp32 value). */
@@ -189,8 +222,14 @@ typedef struct {
   float dropout_p;
 } qn_lora_opts;
 
+/* Workspace bytes for a linear call on this state (its format decides the
+ * route) with these options (nullable). */
+size_t qlora_linear_workspace_state(const qn_nf4dq* w, int64_t M, int r, int backward,
+                                    const qn_lora_opts* opts);
+
 /* Workspace bytes for the _ex calls with these options (dropout needs room
- * for the masked x in the backward). */
+ * for the masked x in the backward), for an NF4 state with double
+ * quantization. */
 size_t qlora_linear_workspace_ex(int64_t M, int64_t rows, int64_t cols, int r, int backward,
                                  const qn_lora_opts* opts);
 

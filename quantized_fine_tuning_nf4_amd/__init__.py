@@ -30,7 +30,8 @@ EXPORTS = ["qn_abi_version", "qn_status_str", "qn_nf4_codebook", "nf4_quantize_d
            "nf4_quantize_dq", "nf4_dequantize", "qlora_linear_workspace", "qlora_linear_fwd",
            "qlora_linear_bwd", "lora_linear_bf16", "qlora_linear_route",
            "qlora_linear_fwd_noalloc", "nf4_merge_lora", "qlora_linear_workspace_ex",
-           "qlora_linear_fwd_ex", "qlora_linear_bwd_ex"]
+           "qlora_linear_fwd_ex", "qlora_linear_bwd_ex", "qn_quantize",
+           "qlora_linear_workspace_state", "qn_fp4_codebook"]
 ROUTES = {1: "decode_rows", 2: "decode_tiles", 3: "decode_split", 4: "fused_small", 5: "fused",
           6: "dense"}
 
@@ -49,7 +50,11 @@ class _LoraOpts(ctypes.Structure):
 class _NF4DQ(ctypes.Structure):
     _fields_ = [("packed", ctypes.c_void_p), ("qscale", ctypes.c_void_p),
                 ("scale2", ctypes.c_void_p), ("offset", ctypes.c_void_p),
-                ("rows", ctypes.c_int64), ("cols", ctypes.c_int64)]
+                ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
+                ("absmax", ctypes.c_void_p), ("codebook", ctypes.c_int32)]
+
+
+CODEBOOKS = {"nf4": 0, "fp4": 1}
 
 
 _lib = None
@@ -69,10 +74,14 @@ def load_library(path: str = LIB_PATH):
     L.qn_status_str.argtypes = [ctypes.c_int]
     L.qn_status_str.restype = ctypes.c_char_p
     L.qn_nf4_codebook.argtypes = [P]
+    L.qn_fp4_codebook.argtypes = [P]
     L.nf4_quantize_dq_workspace.argtypes = [I64, I64]
     L.nf4_quantize_dq_workspace.restype = SZ
     L.nf4_quantize_dq.argtypes = [P, I64, I64, P, P, P, P, P, P, SZ, P]
     L.nf4_quantize_dq.restype = ctypes.c_int
+    L.qn_quantize.argtypes = [P, I64, I64, ctypes.c_int, ctypes.c_int, P, P, P, P, P, P, P, SZ,
+                              P]
+    L.qn_quantize.restype = ctypes.c_int
     L.nf4_dequantize.argtypes = [ctypes.POINTER(_NF4DQ), ctypes.c_int, P, P]
     L.nf4_dequantize.restype = ctypes.c_int
     L.qlora_linear_workspace.argtypes = [I64, I64, I64, ctypes.c_int, ctypes.c_int]
@@ -91,6 +100,9 @@ def load_library(path: str = LIB_PATH):
     OP = ctypes.POINTER(_LoraOpts)
     L.qlora_linear_workspace_ex.argtypes = [I64, I64, I64, ctypes.c_int, ctypes.c_int, OP]
     L.qlora_linear_workspace_ex.restype = SZ
+    L.qlora_linear_workspace_state.argtypes = [ctypes.POINTER(_NF4DQ), I64, ctypes.c_int,
+                                               ctypes.c_int, OP]
+    L.qlora_linear_workspace_state.restype = SZ
     L.qlora_linear_fwd_ex.argtypes = [ctypes.POINTER(_NF4DQ), P, I64, P, P, ctypes.c_int,
                                       ctypes.c_float, OP, P, P, P, SZ, P]
     L.qlora_linear_fwd_ex.restype = ctypes.c_int
@@ -131,31 +143,38 @@ def _ptr(t):
 
 @dataclass
 class NF4State:
-    """Quantized weight, format v1: packed codes, E4M3 scale codes, second-
-    level scales and the mean offset, all on the device."""
-    packed: torch.Tensor  # uint8 [32*nb]
-    qscale: torch.Tensor  # uint8 [nb]
-    scale2: torch.Tensor  # float32 [ng]
-    offset: torch.Tensor  # float32 [1]
+    """Quantized weight on the device: packed 4-bit codes and either the
+    double-quantized block scales (E4M3 scale codes, second-level scales and
+    the mean offset) or, with double quantization off, the fp32 block scales
+    (absmax).  codebook: 0 NF4, 1 FP4."""
+    packed: torch.Tensor                  # uint8 [32*nb]
+    qscale: torch.Tensor | None           # uint8 [nb]
+    scale2: torch.Tensor | None           # float32 [ng]
+    offset: torch.Tensor | None           # float32 [1]
     rows: int
     cols: int
+    absmax: torch.Tensor | None = None    # float32 [nb] (double quantization off)
+    codebook: int = 0
 
     def c_struct(self) -> _NF4DQ:
-        return _NF4DQ(self.packed.data_ptr(), self.qscale.data_ptr(), self.scale2.data_ptr(),
-                      self.offset.data_ptr(), self.rows, self.cols)
+        return _NF4DQ(self.packed.data_ptr(), _ptr(self.qscale), _ptr(self.scale2),
+                      _ptr(self.offset), self.rows, self.cols, _ptr(self.absmax), self.codebook)
 
     @property
     def device(self):
         return self.packed.device
 
     def nbytes(self) -> int:
+        if self.absmax is not None:
+            return self.packed.numel() + 4 * self.absmax.numel()
         return (self.packed.numel() + self.qscale.numel() + 4 * self.scale2.numel()
                 + 4 * self.offset.numel())
 
 
-def codebook() -> list:
+def codebook(name: str = "nf4") -> list:
     out = (ctypes.c_float * 16)()
-    load_library().qn_nf4_codebook(out)
+    L = load_library()
+    (L.qn_fp4_codebook if name == "fp4" else L.qn_nf4_codebook)(out)
     return list(out)
 
 
@@ -197,6 +216,40 @@ def nf4_quantize_dq(W: torch.Tensor, out: NF4State | None = None,
     _check(L.nf4_quantize_dq(W.data_ptr(), rows, cols, st.packed.data_ptr(),
                              st.qscale.data_ptr(), st.scale2.data_ptr(), st.offset.data_ptr(),
                              _ptr(nonfinite), ws.data_ptr(), ws.numel(), _stream(W.device)))
+    return st
+
+
+def qn_quantize(W: torch.Tensor, codebook: str = "nf4", double_quant: bool = True,
+                workspace: torch.Tensor | None = None,
+                nonfinite: torch.Tensor | None = None) -> NF4State:
+    """Block-64 4-bit quantisation with NF4 or FP4 codes, with or without
+    double quantisation of the block scales (see nf4_quantize_dq for the
+    rest)."""
+    L = load_library()
+    W = _dev(W, torch.float32, "W")
+    if W.dim() not in (1, 2):
+        raise ValueError("W must be 1-D or 2-D")
+    rows, cols = (W.shape[0], W.shape[1]) if W.dim() == 2 else (1, W.numel())
+    cb = CODEBOOKS[codebook]
+    nb, ng = state_sizes(rows, cols)
+    dev = W.device
+    if double_quant:
+        st = NF4State(torch.empty(32 * nb, dtype=torch.uint8, device=dev),
+                      torch.empty(nb, dtype=torch.uint8, device=dev),
+                      torch.empty(ng, dtype=torch.float32, device=dev),
+                      torch.empty(1, dtype=torch.float32, device=dev), rows, cols, None, cb)
+    else:
+        st = NF4State(torch.empty(32 * nb, dtype=torch.uint8, device=dev), None, None, None,
+                      rows, cols, torch.empty(nb, dtype=torch.float32, device=dev), cb)
+    ws_bytes = L.nf4_quantize_dq_workspace(rows, cols)
+    ws = workspace if workspace is not None else torch.empty(max(ws_bytes, 1), dtype=torch.uint8,
+                                                             device=dev)
+    if nonfinite is not None:
+        _dev(nonfinite, torch.int32, "nonfinite")
+    _check(L.qn_quantize(W.data_ptr(), rows, cols, cb, int(bool(double_quant)),
+                         st.packed.data_ptr(), _ptr(st.qscale), _ptr(st.scale2), _ptr(st.offset),
+                         _ptr(st.absmax), _ptr(nonfinite), ws.data_ptr(), ws.numel(),
+                         _stream(dev)))
     return st
 
 
@@ -307,7 +360,8 @@ def qlora_linear_fwd(st: NF4State, x: torch.Tensor, A: torch.Tensor, B: torch.Te
     u = torch.empty((M, r), dtype=torch.float32, device=x.device) if save_u else None
     o = _opts(rslora, dropout_mask, dropout_p)
     op = ctypes.byref(o) if o is not None else None
-    ws_bytes = L.qlora_linear_workspace_ex(M, st.rows, st.cols, r, 0, op)
+    sc = st.c_struct()
+    ws_bytes = L.qlora_linear_workspace_state(ctypes.byref(sc), M, r, 0, op)
     if workspace is None or workspace.numel() < ws_bytes:
         workspace = linear_workspace(ws_bytes, x.device)
     s = st.c_struct()
@@ -340,7 +394,8 @@ def qlora_linear_bwd(st: NF4State, x: torch.Tensor, dY: torch.Tensor, A: torch.T
     dB = torch.empty((st.rows, r), dtype=torch.float32, device=x.device)
     o = _opts(rslora, dropout_mask, dropout_p)
     op = ctypes.byref(o) if o is not None else None
-    ws_bytes = L.qlora_linear_workspace_ex(M, st.rows, st.cols, r, 1, op)
+    sc = st.c_struct()
+    ws_bytes = L.qlora_linear_workspace_state(ctypes.byref(sc), M, r, 1, op)
     if workspace is None or workspace.numel() < ws_bytes:
         workspace = linear_workspace(ws_bytes, x.device)
     s = st.c_struct()

@@ -48,6 +48,7 @@ struct QuantWs {
   int64_t part_len;
   int* bad;   // [ng] per-group flags
   int* flag;  // the synchronous call's flag
+  float* mean;  // the mean of a call without double quantization (unused)
 };
 
 QuantWs carve_quant(Carver& c, int64_t n) {
@@ -59,18 +60,27 @@ QuantWs carve_quant(Carver& c, int64_t n) {
   w.part = c.take<double>(w.part_len);
   w.bad = c.take<int>(ng);
   w.flag = c.take<int>(1);
+  w.mean = c.take<float>(1);
   return w;
 }
 
 qn_status check_state(const qn_nf4dq* w) {
-  if (!w || !w->packed || !w->qscale || !w->scale2 || !w->offset) return QN_EINVAL;
+  if (!w || !w->packed) return QN_EINVAL;
+  if (w->codebook != QN_CODE_NF4 && w->codebook != QN_CODE_FP4) return QN_EINVAL;
+  if (!w->absmax && (!w->qscale || !w->scale2 || !w->offset)) return QN_EINVAL;
   if (w->rows < 1 || w->cols < 1) return QN_EINVAL;
   if (w->rows > (INT64_MAX / 2) / w->cols) return QN_EINVAL;
-  if (!aligned16(w->packed) || !aligned16(w->qscale) || !aligned16(w->scale2) ||
-      !aligned16(w->offset))
+  if (!aligned16(w->packed)) return QN_EALIGN;
+  if (w->absmax ? !aligned16(w->absmax)
+                : (!aligned16(w->qscale) || !aligned16(w->scale2) || !aligned16(w->offset)))
     return QN_EALIGN;
   return QN_OK;
 }
+
+// NF4 codes with double-quantized scales: the format every route takes;
+// other states go through the large-batch route (dequantization kernels
+// that take every format, then the dense GEMM).
+bool default_format(const qn_nf4dq* w) { return !w->absmax && w->codebook == QN_CODE_NF4; }
 
 // Largest M and weight dimension the linear calls take: the kernels address
 // buffers through 32-bit offsets from a row or slice base, which these
@@ -119,10 +129,10 @@ struct FwdWs {
 // (one set of x fragments for both products) do not take; such forwards use
 // the GEMM routes.
 FwdWs carve_fwd(Carver& c, int64_t M, int64_t rows, int64_t cols, int r, bool need_u,
-                bool counters = true, bool dropout = false) {
+                bool counters = true, bool dropout = false, bool dense_only = false) {
   FwdWs f;
   f.arrivals = counters ? c.take<unsigned>(kArrivalWords) : nullptr;
-  const bool dec = rows > 0 && !dropout;
+  const bool dec = rows > 0 && !dropout && !dense_only;
   f.dbr = dec ? decode_rows_band(M, rows, cols, r) : 0;
   f.dt = dec && f.dbr == 0 ? decode_tiles(M, rows, cols, r) : DecodeTiles{0, 0, 0};
   f.dS = dec && f.dbr == 0 && f.dt.rgt == 0 ? decode_slices(M, rows, cols) : 0;
@@ -130,7 +140,9 @@ FwdWs carve_fwd(Carver& c, int64_t M, int64_t rows, int64_t cols, int r, bool ne
   f.S = thin_nt_slices(M, cols);
   f.u = need_u ? c.take<float>((size_t)M * r) : nullptr;
   f.upart = f.S > 1 && !decode ? c.take<float>((size_t)f.S * M * r) : nullptr;
-  f.wd = dense_path(M, rows) ? c.take<uint16_t>((size_t)rows * cols) : nullptr;
+  f.wd = rows > 0 && M > 0 && (dense_only || dense_path(M, rows))
+             ? c.take<uint16_t>((size_t)rows * cols)
+             : nullptr;
   f.dpart = f.dS > 0 ? c.take<float>((size_t)f.dS * M * rows) : nullptr;
   f.dupart = f.dS > 0 ? c.take<float>((size_t)f.dS * M * r) : nullptr;
   f.tpart = f.dt.rgt > 0 ? c.take<float>((size_t)f.dt.S * M * round_up(rows, 4)) : nullptr;
@@ -158,7 +170,7 @@ struct BwdWs {
 };
 
 BwdWs carve_bwd(Carver& c, int64_t M, int64_t rows, int64_t cols, int r, bool need_u,
-                bool dropout = false) {
+                bool dropout = false, bool dense_only = false) {
   BwdWs b;
   b.arrivals = c.take<unsigned>(kArrivalWords);
   if (need_u) {
@@ -179,7 +191,7 @@ BwdWs carve_bwd(Carver& c, int64_t M, int64_t rows, int64_t cols, int r, bool ne
   b.dApart = c.take<float>((size_t)b.Sa * cols * r);
   b.sv = c.take<uint16_t>((size_t)2 * rp * thin_tn_rows_padded(M, cols, r));
   b.ldt = round_up(rows, 64);
-  const bool dense = dense_path(M, cols);
+  const bool dense = M > 0 && (dense_only || dense_path(M, cols));
   b.wt = dense ? c.take<uint16_t>((size_t)cols * b.ldt) : nullptr;
   b.At = dense ? c.take<uint16_t>((size_t)cols * r) : nullptr;
   b.xd = dropout ? c.take<uint16_t>((size_t)M * cols) : nullptr;
@@ -223,15 +235,15 @@ qn_status forward(const qn_nf4dq* w, const uint16_t* x, int64_t M, const uint16_
       (u_out && !aligned16(u_out)))
     return QN_EALIGN;
   Carver probe(nullptr);
-  const bool drop = lo.mask != nullptr;
-  carve_fwd(probe, M, w->rows, w->cols, r, u_out == nullptr, true, drop);
+  const bool drop = lo.mask != nullptr, plain = !default_format(w);
+  carve_fwd(probe, M, w->rows, w->cols, r, u_out == nullptr, true, drop, plain);
   if (probe.used > 0) {
     if (!workspace) return QN_EINVAL;
     if (reinterpret_cast<uintptr_t>(workspace) & 255u) return QN_EALIGN;
     if (workspace_bytes < probe.used) return QN_EWORKSPACE;
   }
   Carver c(workspace);
-  FwdWs f = carve_fwd(c, M, w->rows, w->cols, r, u_out == nullptr, true, drop);
+  FwdWs f = carve_fwd(c, M, w->rows, w->cols, r, u_out == nullptr, true, drop, plain);
   float* u = u_out ? u_out : f.u;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const float scale = lo.s;
@@ -257,7 +269,8 @@ qn_status forward(const qn_nf4dq* w, const uint16_t* x, int64_t M, const uint16_
   if (f.wd) {
     if (e == hipSuccess)
       e = launch_dequant(w->packed, w->qscale, w->scale2, w->offset, N * K, true, f.wd, st,
-                         fold ? SliceSum{f.upart, M * (int64_t)r, f.S, u} : SliceSum{});
+                         fold ? SliceSum{f.upart, M * (int64_t)r, f.S, u} : SliceSum{},
+                         w->codebook, w->absmax);
     if (e == hipSuccess) e = launch_gemm_nt(x, K, K, f.wd, K, M, N, u, B, r, scale, y, st);
   } else if (e == hipSuccess) {
     e = launch_qgemm_fwd(to_state(w), x, M, u, B, r, scale, y, st);
@@ -317,6 +330,13 @@ void qn_nf4_codebook(float out[16]) {
   }
 }
 
+void qn_fp4_codebook(float out[16]) {
+  for (int k = 0; k < 16; ++k) {
+    uint32_t b = kFP4Bits[k];
+    std::memcpy(&out[k], &b, 4);
+  }
+}
+
 size_t nf4_quantize_dq_workspace(int64_t rows, int64_t cols) {
   if (rows < 1 || cols < 1 || rows > INT64_MAX / 2 / cols) return 0;
   Carver c(nullptr);
@@ -327,11 +347,23 @@ size_t nf4_quantize_dq_workspace(int64_t rows, int64_t cols) {
 qn_status nf4_quantize_dq(const float* W, int64_t rows, int64_t cols, uint8_t* packed,
                           uint8_t* qscale, float* scale2, float* offset, int* nonfinite,
                           void* workspace, size_t workspace_bytes, void* stream) {
-  if (!W || !packed || !qscale || !scale2 || !offset || !workspace) return QN_EINVAL;
+  return qn_quantize(W, rows, cols, QN_CODE_NF4, 1, packed, qscale, scale2, offset, nullptr,
+                     nonfinite, workspace, workspace_bytes, stream);
+}
+
+qn_status qn_quantize(const float* W, int64_t rows, int64_t cols, int codebook,
+                      int double_quant, uint8_t* packed, uint8_t* qscale, float* scale2,
+                      float* offset, float* absmax, int* nonfinite, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  if (codebook != QN_CODE_NF4 && codebook != QN_CODE_FP4) return QN_EINVAL;
+  if (!W || !packed || !workspace) return QN_EINVAL;
+  if (double_quant ? (!qscale || !scale2 || !offset) : !absmax) return QN_EINVAL;
   if (rows < 1 || cols < 1 || rows > INT64_MAX / 2 / cols) return QN_EINVAL;
-  if (!aligned16(W) || !aligned16(packed) || !aligned16(qscale) || !aligned16(scale2) ||
-      !aligned16(offset) || (reinterpret_cast<uintptr_t>(workspace) & 255u) ||
+  if (!aligned16(W) || !aligned16(packed) || (reinterpret_cast<uintptr_t>(workspace) & 255u) ||
       (reinterpret_cast<uintptr_t>(nonfinite) & 3u))
+    return QN_EALIGN;
+  if (double_quant ? (!aligned16(qscale) || !aligned16(scale2) || !aligned16(offset))
+                   : !aligned16(absmax))
     return QN_EALIGN;
   const int64_t n = rows * cols;
   if (workspace_bytes < nf4_quantize_dq_workspace(rows, cols)) return QN_EWORKSPACE;
@@ -339,7 +371,8 @@ qn_status nf4_quantize_dq(const float* W, int64_t rows, int64_t cols, uint8_t* p
   QuantWs ws = carve_quant(c, n);
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = launch_quantize(W, n, packed, qscale, scale2, offset, ws.absmax, ws.part,
-                                 ws.part_len, ws.bad, nonfinite ? nonfinite : ws.flag, st);
+                                 ws.part_len, ws.bad, nonfinite ? nonfinite : ws.flag, st,
+                                 codebook, double_quant ? nullptr : absmax, ws.mean);
   if (e != hipSuccess) return QN_EDEVICE;
   if (nonfinite) return QN_OK;  // asynchronous: the caller reads the flag
   int bad = 0;
@@ -356,7 +389,8 @@ qn_status nf4_dequantize(const qn_nf4dq* w, qn_dtype out_dtype, void* out, void*
   if (!out || (out_dtype != QN_F32 && out_dtype != QN_BF16)) return QN_EINVAL;
   if (!aligned16(out)) return QN_EALIGN;
   return from_hip(launch_dequant(w->packed, w->qscale, w->scale2, w->offset, w->rows * w->cols,
-                                 out_dtype == QN_BF16, out, static_cast<hipStream_t>(stream)));
+                                 out_dtype == QN_BF16, out, static_cast<hipStream_t>(stream),
+                                 SliceSum{}, w->codebook, w->absmax));
 }
 
 size_t qlora_linear_workspace_ex(int64_t M, int64_t rows, int64_t cols, int r, int backward,
@@ -373,6 +407,18 @@ size_t qlora_linear_workspace_ex(int64_t M, int64_t rows, int64_t cols, int r, i
 
 size_t qlora_linear_workspace(int64_t M, int64_t rows, int64_t cols, int r, int backward) {
   return qlora_linear_workspace_ex(M, rows, cols, r, backward, nullptr);
+}
+
+size_t qlora_linear_workspace_state(const qn_nf4dq* w, int64_t M, int r, int backward,
+                                    const qn_lora_opts* opts) {
+  if (!w || M < 0 || w->rows < 1 || w->cols < 1 || r < 1 || r > 64) return 0;
+  const bool drop = opts && opts->dropout_mask, plain = !default_format(w);
+  Carver c(nullptr);
+  if (backward)
+    carve_bwd(c, M, w->rows, w->cols, r, true, drop, plain);
+  else
+    carve_fwd(c, M, w->rows, w->cols, r, true, true, drop, plain);
+  return c.used;
 }
 
 qn_status qlora_linear_fwd(const qn_nf4dq* w, const uint16_t* x, int64_t M, const uint16_t* A,
@@ -445,13 +491,14 @@ qn_status qlora_linear_bwd_ex(const qn_nf4dq* w, const uint16_t* x, const uint16
     if (e == hipSuccess) e = launch_fill_zero(dB, N * (int64_t)r, st);
     return from_hip(e);
   }
+  const bool plain = !default_format(w);
   Carver probe(nullptr);
-  carve_bwd(probe, M, N, K, r, u_saved == nullptr, drop);
+  carve_bwd(probe, M, N, K, r, u_saved == nullptr, drop, plain);
   if (!workspace) return QN_EINVAL;
   if (reinterpret_cast<uintptr_t>(workspace) & 255u) return QN_EALIGN;
   if (workspace_bytes < probe.used) return QN_EWORKSPACE;
   Carver c(workspace);
-  BwdWs b = carve_bwd(c, M, N, K, r, u_saved == nullptr, drop);
+  BwdWs b = carve_bwd(c, M, N, K, r, u_saved == nullptr, drop, plain);
   const float scale = lo.s;
   hipError_t e = hipSuccess;
   // dropout: the adapter branch's masked input, for dA (u takes the mask on
@@ -507,7 +554,7 @@ qn_status qlora_linear_bwd_ex(const qn_nf4dq* w, const uint16_t* x, const uint16
   if (e == hipSuccess) {
     if (dense_dx)
       e = launch_dequant_t(w->packed, w->qscale, w->scale2, w->offset, N, K, b.wt, b.ldt, aux,
-                           st);
+                           st, w->codebook, w->absmax);
     else
       e = launch_bwd_aux(aux, st);
   }
@@ -536,7 +583,7 @@ qn_status nf4_merge_lora(const qn_nf4dq* w, const uint16_t* A, const uint16_t* B
   if (!A || !B || !out) return QN_EINVAL;
   if (!aligned16(A) || !aligned16(B) || !aligned16(out)) return QN_EALIGN;
   return from_hip(launch_merge(to_state(w), A, B, r, alpha / (float)r, out,
-                               static_cast<hipStream_t>(stream)));
+                               static_cast<hipStream_t>(stream), w->codebook, w->absmax));
 }
 
 int qlora_linear_route(int64_t M, int64_t rows, int64_t cols, int r, int backward) {

@@ -22,10 +22,12 @@ namespace {
 constexpr int MB = 16;   // rows per workgroup
 constexpr int RC = 16;   // ranks per chunk
 
+template <int CB, bool ABS>
 __global__ __launch_bounds__(256) void k_merge(const uint8_t* __restrict__ packed,
                                                const uint8_t* __restrict__ qscale,
                                                const float* __restrict__ scale2,
-                                               const float* __restrict__ offset, int64_t rows,
+                                               const float* __restrict__ offset,
+                                               const float* __restrict__ absmax, int64_t rows,
                                                int64_t cols, const uint16_t* __restrict__ A,
                                                const uint16_t* __restrict__ B, int r, float s,
                                                float* __restrict__ out) {
@@ -33,9 +35,9 @@ __global__ __launch_bounds__(256) void k_merge(const uint8_t* __restrict__ packe
   __shared__ double sb[MB][64];  // the band's B rows as fp64 (read as broadcasts)
   const int tid = threadIdx.x;
   if (tid < 16) {  // levels from immediates
-    uint32_t v = kNF4Bits[0];
+    uint32_t v = level_bits(CB, 0);
 #pragma unroll
-    for (int k = 1; k < 16; ++k) v = tid == k ? kNF4Bits[k] : v;
+    for (int k = 1; k < 16; ++k) v = tid == k ? level_bits(CB, k) : v;
     lut[tid] = as_f32(v);
   }
   const int64_t n0 = (int64_t)blockIdx.y * MB;
@@ -68,7 +70,7 @@ __global__ __launch_bounds__(256) void k_merge(const uint8_t* __restrict__ packe
     }
   }
   if (k >= cols) return;
-  const float mu = *offset;
+  const float mu = ABS ? 0.f : *offset;
   const double s64 = (double)s;
 #pragma unroll
   for (int i = 0; i < MB; ++i) {
@@ -76,7 +78,7 @@ __global__ __launch_bounds__(256) void k_merge(const uint8_t* __restrict__ packe
     const int64_t e = (n0 + i) * cols + k;
     const uint32_t c = (packed[e >> 1] >> (4 * (uint32_t)(e & 1))) & 15u;
     const int64_t b = e / kBlock;
-    const float w = lut[c] * dq_scale(qscale[b], scale2[b / kGroup], mu);
+    const float w = lut[c] * (ABS ? absmax[b] : dq_scale(qscale[b], scale2[b / kGroup], mu));
     const double t = s64 * acc[i];
     out[e] = (float)((double)w + t);
   }
@@ -85,10 +87,17 @@ __global__ __launch_bounds__(256) void k_merge(const uint8_t* __restrict__ packe
 }  // namespace
 
 hipError_t launch_merge(const WState& w, const uint16_t* A, const uint16_t* B, int r, float s,
-                        float* out, hipStream_t st) {
+                        float* out, hipStream_t st, int codebook, const float* absmax) {
   const dim3 grid((unsigned)((w.cols + 255) / 256), (unsigned)((w.rows + MB - 1) / MB));
-  hipLaunchKernelGGL(k_merge, grid, dim3(256), 0, st, w.packed, w.qscale, w.scale2, w.offset,
-                     w.rows, w.cols, A, B, r, s, out);
+#define QN_MERGE(CB, ABS)                                                                  \
+  hipLaunchKernelGGL((k_merge<CB, ABS>), grid, dim3(256), 0, st, w.packed, w.qscale, w.scale2, \
+                     w.offset, absmax, w.rows, w.cols, A, B, r, s, out)
+  if (codebook == kCodeFP4) {
+    if (absmax) QN_MERGE(kCodeFP4, true); else QN_MERGE(kCodeFP4, false);
+  } else {
+    if (absmax) QN_MERGE(kCodeNF4, true); else QN_MERGE(kCodeNF4, false);
+  }
+#undef QN_MERGE
   return hipGetLastError();
 }
 

@@ -14,6 +14,25 @@ constexpr uint32_t kNF4Bits[16] = {
     0xbdba7871u, 0x00000000u, 0x3da2faffu, 0x3e24cae3u,
     0x3e7c04ddu, 0x3ead033au, 0x3ee1a4b8u, 0x3f1007abu, 0x3f3913b3u, 0x3f800000u};
 
+// FP4 code values, codes 0..15 (code c: sign bit 3, magnitude index c & 7),
+// as binary32 bit patterns: the E2M1 levels {0, 0.0625, 2, 3, 4, 6, 8, 12}
+// / 12 (course notebook FT-02, "Exercise 3: NF4 vs FP4 at equal memory",
+// prints them to four decimals: 0, 0.0052, 0.1667, 0.25, 0.3333, 0.5,
+// 0.6667, 1), each rounded to fp32.
+constexpr uint32_t kFP4Bits[16] = {
+    0x00000000u, 0x3baaaaabu, 0x3e2aaaabu, 0x3e800000u, 0x3eaaaaabu, 0x3f000000u,
+    0x3f2aaaabu, 0x3f800000u, 0x80000000u, 0xbbaaaaabu, 0xbe2aaaabu, 0xbe800000u,
+    0xbeaaaaabu, 0xbf000000u, 0xbf2aaaabu, 0xbf800000u};
+
+// Codebooks of the 4-bit codes.
+constexpr int kCodeNF4 = 0, kCodeFP4 = 1;
+
+// Level k of codebook cb, as a bit pattern (cb and k known at compile time
+// give an immediate).
+__host__ __device__ constexpr uint32_t level_bits(int cb, int k) {
+  return cb == kCodeFP4 ? kFP4Bits[k] : kNF4Bits[k];
+}
+
 constexpr int kBlock = 64;        // first-level block (weights per absmax scale)
 constexpr int kGroup = 256;       // second-level block (scales per fp32 scale2)
 constexpr float kE4M3Max = 448.f; // largest finite OCP FP8 E4M3FN value
@@ -87,5 +106,15 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
 __device__ __forceinline__ float dq_scale(uint32_t q, float s2, float mu) {
   return __builtin_fmaf(e4m3_to_f32(q), s2, mu);
 }
+
+// Where a state's block scales come from: the double-quantized codes
+// (absmax == null) or fp32 block scales as they are (double quantization
+// off).
+struct ScaleSrc {
+  const uint8_t* qscale;
+  const float* scale2;
+  const float* offset;
+  const float* absmax;
+};
 
 }  // namespace qn

@@ -22,9 +22,14 @@ struct Clear {
 
 // ws_bad [ng] per-group non-finite flags; *flag = 1 when any weight is NaN
 // or infinite, else 0 (written by the last kernel; no clearing needed).
+// codebook: kCodeNF4 or kCodeFP4.  absmax_out (nullable): double
+// quantization off, the fp32 block scales are written there (qscale,
+// scale2, offset unused; ws_offset receives a mean nobody reads).
 hipError_t launch_quantize(const float* W, int64_t n, uint8_t* packed, uint8_t* qscale,
                            float* scale2, float* offset, float* ws_absmax, double* ws_part,
-                           int64_t part_len, int* ws_bad, int* flag, hipStream_t st);
+                           int64_t part_len, int* ws_bad, int* flag, hipStream_t st,
+                           int codebook = kCodeNF4, float* absmax_out = nullptr,
+                           float* ws_offset = nullptr);
 
 // out = sum over S slices of part[S][count] (slice order); count == 0: none.
 struct SliceSum {
@@ -36,9 +41,12 @@ struct SliceSum {
 
 // n weights -> bf16 or fp32 out; the slice sum ss (independent of the
 // weight) runs in spare workgroups of the same launch.
+// codebook and absmax (nullable: double quantized scales) as the state has
+// them.
 hipError_t launch_dequant(const uint8_t* packed, const uint8_t* qscale, const float* scale2,
                           const float* offset, int64_t n, bool bf16, void* out, hipStream_t st,
-                          const SliceSum& ss = SliceSum{nullptr, 0, 0, nullptr});
+                          const SliceSum& ss = SliceSum{nullptr, 0, 0, nullptr},
+                          int codebook = kCodeNF4, const float* absmax = nullptr);
 
 // Small backward jobs, run by spare workgroups of another launch or alone:
 //   Bt [r, N] = B[N, r]^T and At [K, r] = A[r, K]^T (bf16);
@@ -185,7 +193,8 @@ hipError_t launch_bwd_aux(const BwdAux& a, hipStream_t st);
 // aux run in extra workgroups of the same launch.
 hipError_t launch_dequant_t(const uint8_t* packed, const uint8_t* qscale, const float* scale2,
                             const float* offset, int64_t rows, int64_t cols, uint16_t* out,
-                            int64_t ldt, const BwdAux& aux, hipStream_t st);
+                            int64_t ldt, const BwdAux& aux, hipStream_t st,
+                            int codebook = kCodeNF4, const float* absmax = nullptr);
 
 // C[M, Nc] bf16 = A[M, R] (row stride lda) * Bm[Nc, :R]^T (row stride ldb,
 // ldb % 64 == 0, zero in columns R..ldb) + s * V[M, r] * L[Nc, r]^T.
@@ -293,7 +302,8 @@ hipError_t launch_decode_rows(const WState& w, const uint16_t* X, int64_t M, con
 // out [rows, cols] fp32 = Qhat(W) + s B A (fp64 rank sum in rank order, one
 // fp32 rounding at the end); A [r, cols], B [rows, r] bf16, 1 <= r <= 64.
 hipError_t launch_merge(const WState& w, const uint16_t* A, const uint16_t* B, int r, float s,
-                        float* out, hipStream_t st);
+                        float* out, hipStream_t st, int codebook = kCodeNF4,
+                        const float* absmax = nullptr);
 
 // Y[M, N] bf16 = X[M, K] * W'[N, K]^T + s * u[M, r] * B[N, r]^T.
 hipError_t launch_qgemm_fwd(const WState& w, const uint16_t* X, int64_t M, const float* u,

@@ -48,13 +48,17 @@ __device__ __forceinline__ float f32_next_down(float t) {
 // Entry j covers quotients in [(j-32)/32, (j-31)/32): mu (4.0: the bucket
 // holds no threshold) with c0, the code of the bucket's lower part, in its
 // four low bits.
+// NF4: the sixteen levels over [-1, 1].  FP4: the eight magnitudes over
+// [0, 1] (entries j >= 32; the sign is taken apart).
+template <int CB>
 __device__ uint64_t code_lut_entry(int j) {
   const double lo = (double)(j - 32) * 0.03125, hi = (double)(j - 31) * 0.03125;
   int c0 = 0;
   double mu = 4.0;
-  for (int k = 0; k < 15; ++k) {
+  constexpr int NT = CB == kCodeFP4 ? 7 : 15;  // thresholds between adjacent levels
+  for (int k = 0; k < NT; ++k) {
     // exact midpoint of two adjacent levels, then its round-down to fp32
-    double m = ((double)as_f32(kNF4Bits[k]) + (double)as_f32(kNF4Bits[k + 1])) * 0.5;
+    double m = ((double)as_f32(level_bits(CB, k)) + (double)as_f32(level_bits(CB, k + 1))) * 0.5;
     float t = (float)m;
     if ((double)t > m) t = f32_next_down(t);
     if ((double)t < lo) {
@@ -94,6 +98,27 @@ __device__ __forceinline__ uint32_t nf4_code(float w, double rs32, double s64,
   return (uint32_t)(e & 15u) + ((double)w > __builtin_bit_cast(double, e) * s64 ? 1u : 0u);
 }
 
+// FP4: the sign of w, and the magnitude code of |w| by the same exact
+// search over the magnitudes' buckets (entries 32..64).
+__device__ __forceinline__ uint32_t fp4_code(float w, double rs32, double s64,
+                                             const uint64_t* lut_copy) {
+  const float a = __builtin_fabsf(w);
+  int idx = (int)__builtin_fma((double)a, rs32, 32.0);
+  idx = min(max(idx, 32), 64);
+  const uint64_t e = lut_copy[16 * idx];
+  const uint32_t m =
+      (uint32_t)(e & 15u) + ((double)a > __builtin_bit_cast(double, e) * s64 ? 1u : 0u);
+  return (as_u32(w) >> 28 & 8u) | m;
+}
+
+template <int CB>
+__device__ __forceinline__ uint32_t code_of(float w, double rs32, double s64, const uint64_t* lc) {
+  if constexpr (CB == kCodeFP4)
+    return fp4_code(w, rs32, s64, lc);
+  else
+    return nf4_code(w, rs32, s64, lc);
+}
+
 // Pass 1.  One workgroup per group of 256 blocks (16384 weights); wave w
 // owns blocks 64w..64w+63 of the group, and at step j its 64 lanes read
 // 1 KB: four blocks, 16 lanes x float4 per block.  The body is instantiated
@@ -109,7 +134,7 @@ __device__ __forceinline__ uint32_t nf4_code(float w, double rs32, double s64,
 // measured best (21.7-22.0 us at 4096x4096 against 22.6-23.5 for sixteen,
 // 22.5-23.2 for four, 22.6 for two)
 constexpr int QD = 3;
-template <bool FULL>
+template <bool FULL, int CB>
 __device__ __forceinline__ void quant_group(const float* __restrict__ W, int64_t n, int64_t nb,
                                             uint8_t* __restrict__ packed,
                                             float* __restrict__ absmax, double* tree,
@@ -151,8 +176,8 @@ __device__ __forceinline__ void quant_group(const float* __restrict__ W, int64_t
     const int64_t b = g * kGroup + slot;
     const double s64 = s > 0.f ? (double)s : 1.0;
     const double rs32 = 32.0 * __builtin_amdgcn_rcp(s64);
-    const uint32_t c0 = nf4_code(v[j].x, rs32, s64, lc), c1 = nf4_code(v[j].y, rs32, s64, lc);
-    const uint32_t c2 = nf4_code(v[j].z, rs32, s64, lc), c3 = nf4_code(v[j].w, rs32, s64, lc);
+    const uint32_t c0 = code_of<CB>(v[j].x, rs32, s64, lc), c1 = code_of<CB>(v[j].y, rs32, s64, lc);
+    const uint32_t c2 = code_of<CB>(v[j].z, rs32, s64, lc), c3 = code_of<CB>(v[j].w, rs32, s64, lc);
     const uint16_t c16 = (uint16_t)(c0 | (c1 << 4) | (c2 << 8) | (c3 << 12));
     if (FULL) {
       codes[(wave * 16 + j) * 64 + lane] = c16;
@@ -186,6 +211,7 @@ __device__ __forceinline__ void quant_group(const float* __restrict__ W, int64_t
   }
 }
 
+template <int CB>
 __global__ __launch_bounds__(256) void k_quant_blocks(
     const float* __restrict__ W, int64_t n, int64_t nb, uint8_t* __restrict__ packed,
     float* __restrict__ absmax, double* __restrict__ part, int* __restrict__ bad) {
@@ -195,7 +221,7 @@ __global__ __launch_bounds__(256) void k_quant_blocks(
   __shared__ int s_bad;
   const int tid = threadIdx.x;
   if (tid < 65) {
-    const uint64_t e = code_lut_entry(tid);
+    const uint64_t e = code_lut_entry<CB>(tid);
 #pragma unroll
     for (int c = 0; c < 16; ++c) lut[16 * tid + c] = e;
   }
@@ -203,9 +229,9 @@ __global__ __launch_bounds__(256) void k_quant_blocks(
   const int64_t g = blockIdx.x;
   const bool full = (g + 1) * (int64_t)(kGroup * kBlock) <= n;
   if (full)
-    quant_group<true>(W, n, nb, packed, absmax, tree, lut, &s_bad, codes);
+    quant_group<true, CB>(W, n, nb, packed, absmax, tree, lut, &s_bad, codes);
   else
-    quant_group<false>(W, n, nb, packed, absmax, tree, lut, &s_bad, codes);
+    quant_group<false, CB>(W, n, nb, packed, absmax, tree, lut, &s_bad, codes);
   // (LDS-only barriers from here: the code stores stay in flight)
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   // a whole group's 256 block scales leave in one coalesced store
@@ -359,11 +385,25 @@ __global__ __launch_bounds__(256) void k_quant_dq(const float* __restrict__ absm
 
 hipError_t launch_quantize(const float* W, int64_t n, uint8_t* packed, uint8_t* qscale,
                            float* scale2, float* offset, float* ws_absmax, double* ws_part,
-                           int64_t part_len, int* ws_bad, int* flag, hipStream_t st) {
+                           int64_t part_len, int* ws_bad, int* flag, hipStream_t st, int codebook,
+                           float* absmax_out, float* ws_offset) {
   const int64_t nb = (n + kBlock - 1) / kBlock;
   const int64_t ng = (nb + kGroup - 1) / kGroup;
-  hipLaunchKernelGGL(k_quant_blocks, dim3((unsigned)ng), dim3(256), 0, st, W, n, nb, packed,
-                     ws_absmax, ws_part, ws_bad);
+  float* am = absmax_out ? absmax_out : ws_absmax;
+  if (codebook == kCodeFP4)
+    hipLaunchKernelGGL(k_quant_blocks<kCodeFP4>, dim3((unsigned)ng), dim3(256), 0, st, W, n, nb,
+                       packed, am, ws_part, ws_bad);
+  else
+    hipLaunchKernelGGL(k_quant_blocks<kCodeNF4>, dim3((unsigned)ng), dim3(256), 0, st, W, n, nb,
+                       packed, am, ws_part, ws_bad);
+  if (absmax_out) {
+    // double quantization off: the block scales are the state; one small
+    // launch reduces the groups' non-finite flags (the mean it also forms
+    // goes to the workspace)
+    hipLaunchKernelGGL(k_quant_mean, dim3(1), dim3(1024), 0, st, ws_part, ng, part_len, nb,
+                       ws_offset, ws_bad, flag);
+    return hipGetLastError();
+  }
   if (part_len <= 2048) {
     // the mean inside the scale pass: one launch fewer
     hipLaunchKernelGGL(k_quant_dq<true>, dim3((unsigned)ng), dim3(256), 0, st, ws_absmax, nb,
@@ -386,11 +426,12 @@ hipError_t launch_quantize(const float* W, int64_t n, uint8_t* packed, uint8_t* 
 // is used.  Whole workgroups (every chunk in range) take unconditional
 // loads; only the last workgroup checks bounds, and the kernel branches once
 // around the whole body, so no loaded value meets a branch join.
-template <bool BF16, bool FULL>
+template <bool BF16, bool FULL, bool ABS>
 __device__ __forceinline__ void dequant_chunks(const uint8_t* __restrict__ packed,
                                                const uint8_t* __restrict__ qscale,
                                                const float* __restrict__ scale2,
-                                               const float* __restrict__ offset, int64_t n,
+                                               const float* __restrict__ offset,
+                                               const float* __restrict__ absmax, int64_t n,
                                                void* __restrict__ out, const float* lut) {
   constexpr int CH = BF16 ? 8 : 4;
   constexpr int UNROLL = 4;
@@ -406,10 +447,14 @@ __device__ __forceinline__ void dequant_chunks(const uint8_t* __restrict__ packe
     else
       p[i] = *reinterpret_cast<const uint16_t*>(packed + c * 2);
     const int64_t b = c * CH / kBlock;
-    qb[i] = qscale[b];
-    s2[i] = scale2[b / kGroup];
+    if (ABS) {
+      s2[i] = absmax[b];  // double quantization off: the block scale itself
+    } else {
+      qb[i] = qscale[b];
+      s2[i] = scale2[b / kGroup];
+    }
   }
-  const float mu = *offset;
+  const float mu = ABS ? 0.f : *offset;
   __builtin_amdgcn_sched_barrier(0);  // every load issues before the first use
   // the level table is ready (LDS-only barrier: the loads stay in flight)
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -417,7 +462,7 @@ __device__ __forceinline__ void dequant_chunks(const uint8_t* __restrict__ packe
   for (int i = 0; i < UNROLL; ++i) {
     const int64_t c = c_first + i * 256;
     if (!FULL && c >= nchunk) continue;
-    const float sc = dq_scale(qb[i], s2[i], mu);
+    const float sc = ABS ? s2[i] : dq_scale(qb[i], s2[i], mu);
     float w[CH];
 #pragma unroll
     for (int k = 0; k < CH; ++k) w[k] = lut[(p[i] >> (4 * k)) & 15u] * sc;
@@ -443,11 +488,12 @@ __device__ __forceinline__ void dequant_chunks(const uint8_t* __restrict__ packe
   }
 }
 
-template <bool BF16>
+template <bool BF16, int CB, bool ABS>
 __global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ packed,
                                                  const uint8_t* __restrict__ qscale,
                                                  const float* __restrict__ scale2,
-                                                 const float* __restrict__ offset, int64_t n,
+                                                 const float* __restrict__ offset,
+                                                 const float* __restrict__ absmax, int64_t n,
                                                  void* __restrict__ out, SliceSum ss,
                                                  unsigned dq_blocks) {
   constexpr int CH = BF16 ? 8 : 4;
@@ -460,32 +506,51 @@ __global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ pac
   }
   __shared__ float lut[16];
   if (threadIdx.x < 16) {  // from immediates: no load that the first weight loads would queue behind
-    uint32_t v = kNF4Bits[0];
+    uint32_t v = level_bits(CB, 0);
 #pragma unroll
-    for (int k = 1; k < 16; ++k) v = threadIdx.x == k ? kNF4Bits[k] : v;
+    for (int k = 1; k < 16; ++k) v = threadIdx.x == k ? level_bits(CB, k) : v;
     lut[threadIdx.x] = as_f32(v);
   }
   const int64_t last_elem = ((int64_t)blockIdx.x + 1) * 256 * UNROLL * CH;  // one past
   if (last_elem <= n)
-    dequant_chunks<BF16, true>(packed, qscale, scale2, offset, n, out, lut);
+    dequant_chunks<BF16, true, ABS>(packed, qscale, scale2, offset, absmax, n, out, lut);
   else
-    dequant_chunks<BF16, false>(packed, qscale, scale2, offset, n, out, lut);
+    dequant_chunks<BF16, false, ABS>(packed, qscale, scale2, offset, absmax, n, out, lut);
+}
+
+template <bool BF16, int CB, bool ABS>
+void launch_dq(dim3 grid, hipStream_t st, const uint8_t* packed, const ScaleSrc& sc,
+                      int64_t n, void* out, const SliceSum& ss, unsigned dq_blocks) {
+  hipLaunchKernelGGL((k_dequant<BF16, CB, ABS>), grid, dim3(256), 0, st, packed, sc.qscale,
+                     sc.scale2, sc.offset, sc.absmax, n, out, ss, dq_blocks);
 }
 
 hipError_t launch_dequant(const uint8_t* packed, const uint8_t* qscale, const float* scale2,
                           const float* offset, int64_t n, bool bf16, void* out, hipStream_t st,
-                          const SliceSum& ss) {
+                          const SliceSum& ss, int codebook, const float* absmax) {
   const int CH = bf16 ? 8 : 4;
   const int64_t nchunk = (n + CH - 1) / CH;
   const int64_t per_wg = 256 * 4;
   const unsigned grid = (unsigned)((nchunk + per_wg - 1) / per_wg);
   const unsigned extra = ss.count > 0 ? (unsigned)((ss.count + 255) / 256) : 0u;
-  if (bf16)
-    hipLaunchKernelGGL(k_dequant<true>, dim3(grid + extra), dim3(256), 0, st, packed, qscale,
-                       scale2, offset, n, out, ss, grid);
-  else
-    hipLaunchKernelGGL(k_dequant<false>, dim3(grid + extra), dim3(256), 0, st, packed, qscale,
-                       scale2, offset, n, out, ss, grid);
+  const dim3 g(grid + extra);
+  const ScaleSrc sc{qscale, scale2, offset, absmax};
+  const bool fp4 = codebook == kCodeFP4, abs = absmax != nullptr;
+  if (bf16) {
+    if (fp4)
+      abs ? launch_dq<true, kCodeFP4, true>(g, st, packed, sc, n, out, ss, grid)
+          : launch_dq<true, kCodeFP4, false>(g, st, packed, sc, n, out, ss, grid);
+    else
+      abs ? launch_dq<true, kCodeNF4, true>(g, st, packed, sc, n, out, ss, grid)
+          : launch_dq<true, kCodeNF4, false>(g, st, packed, sc, n, out, ss, grid);
+  } else {
+    if (fp4)
+      abs ? launch_dq<false, kCodeFP4, true>(g, st, packed, sc, n, out, ss, grid)
+          : launch_dq<false, kCodeFP4, false>(g, st, packed, sc, n, out, ss, grid);
+    else
+      abs ? launch_dq<false, kCodeNF4, true>(g, st, packed, sc, n, out, ss, grid)
+          : launch_dq<false, kCodeNF4, false>(g, st, packed, sc, n, out, ss, grid);
+  }
   return hipGetLastError();
 }
 
@@ -500,10 +565,12 @@ hipError_t launch_dequant(const uint8_t* packed, const uint8_t* qscale, const fl
 // lane l rows n0 + 2l and n0 + 2l + 1, whose two values per column go to the
 // LDS tile [k][n] as one word; the tile leaves as 256-byte row pieces.
 constexpr int DQT_N = 128, DQT_K = 128, DQT_PITCH = DQT_N * 2 + 16;
+template <int CB, bool ABS>
 __global__ __launch_bounds__(256) void k_dequant_t(const uint8_t* __restrict__ packed,
                                                    const uint8_t* __restrict__ qscale,
                                                    const float* __restrict__ scale2,
-                                                   const float* __restrict__ offset, int64_t rows,
+                                                   const float* __restrict__ offset,
+                                                   const float* __restrict__ absmax, int64_t rows,
                                                    int64_t cols, uint16_t* __restrict__ out,
                                                    int64_t ldt, BwdAux aux, int aux_wgs,
                                                    int gx) {
@@ -516,9 +583,9 @@ __global__ __launch_bounds__(256) void k_dequant_t(const uint8_t* __restrict__ p
     return;
   }
   if (t < 16) {  // from immediates: no load ahead of the code loads
-    uint32_t v = kNF4Bits[0];
+    uint32_t v = level_bits(CB, 0);
 #pragma unroll
-    for (int k = 1; k < 16; ++k) v = t == k ? kNF4Bits[k] : v;
+    for (int k = 1; k < 16; ++k) v = t == k ? level_bits(CB, k) : v;
     lut[t] = as_f32(v);
   }
   const int d = (int)blockIdx.x - aux_wgs;
@@ -536,10 +603,16 @@ __global__ __launch_bounds__(256) void k_dequant_t(const uint8_t* __restrict__ p
   const u32x4 a = *reinterpret_cast<const u32x4*>(packed + ra * (cols / 2) + kb * 32 + 16 * kh);
   const u32x4 b = *reinterpret_cast<const u32x4*>(packed + rb * (cols / 2) + kb * 32 + 16 * kh);
   const int64_t ba = ra * kblocks + kb, bb = rb * kblocks + kb;
-  const uint32_t qa = qscale[ba], qb = qscale[bb];
-  const float s2a = scale2[ba / kGroup], s2b = scale2[bb / kGroup], mu = *offset;
-  const float sa = na < rows ? dq_scale(qa, s2a, mu) : 0.f;
-  const float sb = nb < rows ? dq_scale(qb, s2b, mu) : 0.f;
+  float sa, sb;
+  if (ABS) {  // double quantization off: the block scales themselves
+    sa = na < rows ? absmax[ba] : 0.f;
+    sb = nb < rows ? absmax[bb] : 0.f;
+  } else {
+    const uint32_t qa = qscale[ba], qb = qscale[bb];
+    const float s2a = scale2[ba / kGroup], s2b = scale2[bb / kGroup], mu = *offset;
+    sa = na < rows ? dq_scale(qa, s2a, mu) : 0.f;
+    sb = nb < rows ? dq_scale(qb, s2b, mu) : 0.f;
+  }
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // lut ready
   uint8_t* trow = tile + (int64_t)(64 * (q >> 1) + 32 * kh) * DQT_PITCH + 4 * l;
 #pragma unroll
@@ -566,11 +639,20 @@ __global__ __launch_bounds__(256) void k_dequant_t(const uint8_t* __restrict__ p
 
 hipError_t launch_dequant_t(const uint8_t* packed, const uint8_t* qscale, const float* scale2,
                             const float* offset, int64_t rows, int64_t cols, uint16_t* out,
-                            int64_t ldt, const BwdAux& aux, hipStream_t st) {
+                            int64_t ldt, const BwdAux& aux, hipStream_t st, int codebook,
+                            const float* absmax) {
   const int64_t gx = (ldt + DQT_N - 1) / DQT_N, gk = (cols + DQT_K - 1) / DQT_K;
   const int64_t aux_wgs = (bwd_aux_count(aux) + 255) / 256;
-  hipLaunchKernelGGL(k_dequant_t, dim3((unsigned)(aux_wgs + gx * gk)), dim3(256), 0, st, packed,
-                     qscale, scale2, offset, rows, cols, out, ldt, aux, (int)aux_wgs, (int)gx);
+  const dim3 g((unsigned)(aux_wgs + gx * gk));
+#define QN_DQT(CB, ABS)                                                                         \
+  hipLaunchKernelGGL((k_dequant_t<CB, ABS>), g, dim3(256), 0, st, packed, qscale, scale2, offset, \
+                     absmax, rows, cols, out, ldt, aux, (int)aux_wgs, (int)gx)
+  if (codebook == kCodeFP4) {
+    if (absmax) QN_DQT(kCodeFP4, true); else QN_DQT(kCodeFP4, false);
+  } else {
+    if (absmax) QN_DQT(kCodeNF4, true); else QN_DQT(kCodeNF4, false);
+  }
+#undef QN_DQT
   return hipGetLastError();
 }
 

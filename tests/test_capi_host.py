@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol(qn):
 
 def test_abi_version_and_status_strings(qn):
     L = qn.load_library()
-    assert L.qn_abi_version() == 3
+    assert L.qn_abi_version() == 4
     for s in range(6):
         assert len(L.qn_status_str(s)) > 0
     assert L.qn_status_str(0) == b"ok"
@@ -55,12 +55,21 @@ def test_library_codebook_equals_page_table(qn):
     assert np.array_equal(np.array(qn.codebook(), np.float32), lit)
 
 
+def test_library_fp4_table_equals_the_oracles(qn):
+    import oracle
+    lib_t = np.array(qn.codebook("fp4"), np.float32)
+    assert np.array_equal(lib_t.view(np.uint32), oracle.fp4_codebook().view(np.uint32))
+    printed = np.array(_golden.values("fp4_levels_page1.txt"))
+    assert np.array_equal(np.round(lib_t[:8].astype(np.float64), 4), printed)
+
+
 def test_workspace_sizes(qn):
     L = qn.load_library()
     # arrival-counter page (left alone by the quantizer) | absmax fp32 [nb] |
-    # fp64 partials [pow2(ng)] | group flags int [ng] | flag, 256-aligned pieces
+    # fp64 partials [pow2(ng)] | group flags int [ng] | flag | the unused
+    # mean of a call without double quantization, 256-aligned pieces
     nb, ng = 262144, 1024
-    want = 4096 + nb * 4 + ng * 8 + ng * 4 + 4
+    want = 4096 + nb * 4 + ng * 8 + ng * 4 + 256 + 4
     assert L.nf4_quantize_dq_workspace(4096, 4096) == want
     assert L.nf4_quantize_dq_workspace(0, 5) == 0
     assert L.qlora_linear_workspace(8192, 4096, 4096, 16, 0) >= 4096 + 8192 * 16 * 4

@@ -1,0 +1,121 @@
+"""GPU parity of the format variants with the CPU oracle (course notebook
+FT-02: "Guided example 3: double quantization" on/off and "Exercise 3: NF4
+vs FP4 at equal memory"): quantize and dequantize bit-exact for NF4 and FP4
+codes with and without double quantization; merge bit-exact; the linear
+calls (which route these states through the large-batch route) within
+5e-3 of fp64."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+from tests._gpu import REL_TOL, bf16_dev, bf16_host_f64, f32_dev, needs_gpu, rel_err, say
+
+pytestmark = [pytest.mark.gpu, needs_gpu]
+
+FORMATS = [("nf4", False), ("fp4", True), ("fp4", False)]
+
+
+@pytest.fixture(scope="module")
+def qn():
+    import quantized_fine_tuning_nf4_amd as qn
+    qn.load_library()
+    return qn
+
+
+def _check_state(qn, st, ref):
+    torch.cuda.synchronize()
+    assert np.array_equal(st.packed.cpu().numpy(), ref.packed)
+    if ref.double_quant:
+        assert np.array_equal(st.qscale.cpu().numpy(), ref.qscale)
+        assert np.array_equal(st.scale2.cpu().numpy().view(np.uint32), ref.scale2.view(np.uint32))
+        assert st.offset.cpu().numpy()[0] == ref.offset
+    else:
+        assert np.array_equal(st.absmax.cpu().numpy().view(np.uint32), ref.absmax.view(np.uint32))
+    f32 = qn.nf4_dequantize(st, torch.float32).cpu().numpy()
+    b16 = qn.nf4_dequantize(st, torch.bfloat16).cpu().contiguous().view(torch.int16).numpy()
+    rf32, rb16 = oracle.dequantize(ref)
+    assert np.array_equal(f32.view(np.uint32), rf32.view(np.uint32))
+    assert np.array_equal(b16.view(np.uint16), rb16)
+
+
+@pytest.mark.parametrize("codebook,dq", FORMATS)
+@pytest.mark.parametrize("rows,cols", [(256, 256), (37, 16448), (1, 1), (1000, 1000)])
+def test_quantize_formats_bit_exact(qn, codebook, dq, rows, cols):
+    say(f"[formats] quantize {codebook} dq={dq} {rows}x{cols}")
+    W = wl.weight(rows, cols, 1100 + rows)
+    if W.size >= 192:  # a zero block and a constant block
+        W.ravel()[64:128] = 0.0
+        W.ravel()[128:192] = -0.03
+    st = qn.qn_quantize(f32_dev(W), codebook=codebook, double_quant=dq)
+    _check_state(qn, st, oracle.quantize(W, double_quant=dq, codebook=codebook))
+
+
+@pytest.mark.parametrize("codebook,dq", FORMATS)
+def test_quantize_formats_outlier_workload(qn, codebook, dq):
+    W = wl.outlier_weight()
+    st = qn.qn_quantize(f32_dev(W), codebook=codebook, double_quant=dq)
+    _check_state(qn, st, oracle.quantize(W, double_quant=dq, codebook=codebook))
+
+
+def test_fp4_codes_near_every_threshold(qn):
+    """Unit-scale blocks of weights within a few ulps of every FP4 midpoint
+    (both signs): the codes are the exact nearest magnitude, ties lower."""
+    cb = oracle.fp4_codebook()
+    vals = []
+    for k in range(7):
+        m = np.float32((float(cb[k]) + float(cb[k + 1])) / 2)
+        for d in range(-20, 21):
+            v = m
+            for _ in range(abs(d)):
+                v = np.nextafter(v, np.float32(np.inf if d > 0 else -np.inf))
+            vals += [v, -v]
+    vals = np.array(vals, np.float32)
+    pad = (-vals.size) % 63
+    vals = np.concatenate([vals, np.zeros(pad, np.float32)]).reshape(-1, 63)
+    W = np.concatenate([np.ones((vals.shape[0], 1), np.float32), vals], axis=1)  # absmax 1
+    st = qn.qn_quantize(f32_dev(W), codebook="fp4", double_quant=False)
+    _check_state(qn, st, oracle.quantize(W, double_quant=False, codebook="fp4"))
+
+
+@pytest.mark.parametrize("codebook,dq", FORMATS)
+@pytest.mark.parametrize("rows,cols,M,r", [(264, 192, 4, 8), (520, 576, 300, 16),
+                                           (3848, 3840, 4100, 16)])
+def test_linear_formats(qn, codebook, dq, rows, cols, M, r):
+    say(f"[formats] linear {codebook} dq={dq} rows={rows} cols={cols} M={M} r={r}")
+    W, x, A, B, G = (wl.weight(rows, cols, 1200 + rows), wl.normal_bf16((M, cols), 1201, 1.0),
+                     wl.normal_bf16((r, cols), 1202, 0.05), wl.normal_bf16((rows, r), 1203, 0.05),
+                     wl.normal_bf16((M, rows), 1204, 1.0))
+    alpha = 2.0 * r
+    st = qn.qn_quantize(f32_dev(W), codebook=codebook, double_quant=dq)
+    xd, Ad, Bd, Gd = (bf16_dev(a) for a in (x, A, B, G))
+    y, u = qn.qlora_linear_fwd(st, xd, Ad, Bd, alpha)
+    dX, dA, dB = qn.qlora_linear_bwd(st, xd, Gd, Ad, Bd, alpha, u)
+    torch.cuda.synchronize()
+    s = float(np.float32(alpha) / np.float32(r))
+    Wd, _ = oracle.dequantize(oracle.quantize(W, double_quant=dq, codebook=codebook),
+                              want_bf16=False)
+    rng = np.random.default_rng(M)
+    sel = np.arange(M) if M <= 48 else np.sort(rng.choice(M, 48, replace=False))
+    Y_ref, _ = oracle.qlora_fwd(Wd, x, A, B, s, rows=sel)
+    dX_ref, _ = oracle.qlora_dx(Wd, G, A, B, s, rows=sel)
+    dA_ref, dB_ref = oracle.adapter_grads(x, G, A, B, s)
+    errs = dict(y=rel_err(bf16_host_f64(y)[sel], Y_ref), dX=rel_err(bf16_host_f64(dX)[sel], dX_ref),
+                dA=rel_err(dA.cpu().numpy(), dA_ref), dB=rel_err(dB.cpu().numpy(), dB_ref))
+    say("  rel err", {k: f"{v:.2e}" for k, v in errs.items()})
+    assert all(e <= REL_TOL for e in errs.values()), errs
+
+
+@pytest.mark.parametrize("codebook,dq", FORMATS)
+def test_merge_formats_bit_exact(qn, codebook, dq):
+    rows, cols, r = 520, 576, 16
+    W = wl.weight(rows, cols, 1300)
+    A = wl.normal_bf16((r, cols), 1301, 0.05)
+    B = wl.normal_bf16((rows, r), 1302, 0.05)
+    st = qn.qn_quantize(f32_dev(W), codebook=codebook, double_quant=dq)
+    merged = qn.nf4_merge_lora(st, bf16_dev(A), bf16_dev(B), 32.0).cpu().numpy()
+    Wd, _ = oracle.dequantize(oracle.quantize(W, double_quant=dq, codebook=codebook),
+                              want_bf16=False)
+    ref = oracle.merge(Wd, A, B, np.float32(2.0))
+    assert np.array_equal(merged.view(np.uint32), ref.view(np.uint32))
