@@ -79,6 +79,8 @@ def lib():
         L.orc_adapter_grads.argtypes = [_P, _P, _P, _P, _I64, _I64, _I64,
                                         ctypes.c_int, ctypes.c_double, _P, _P]
         L.orc_merge.argtypes = [_P, _I64, _I64, _P, _P, ctypes.c_int, ctypes.c_float, _P]
+        F = ctypes.c_float
+        L.orc_adamw8_step.argtypes = [_P, _P, _I64, _P, _P, _P, _P, _P] + [F] * 9
         L.orc_dropout_apply.argtypes = [_P, _P, _I64, _I64, _P]
         L.orc_qlora_dx_dropout.argtypes = [_P, _I64, _I64, _P, _P, _P, ctypes.c_int,
                                            ctypes.c_double, _P, _P, _I64, _P, _P]
@@ -362,6 +364,44 @@ def qlora_fwd_dropout(Wd: np.ndarray, X, A, B, s: float, mask: np.ndarray, rows=
 def adapter_grads_dropout(X, G, A, B, s: float, mask: np.ndarray):
     """dA = s (G B)^T (mask (.) X), dB = s G^T ((mask (.) X) A^T), over all rows."""
     return adapter_grads(dropout_apply(X, mask), G, A, B, s)
+
+
+@dataclass
+class Adam8State:
+    """8-bit AdamW state of one parameter tensor: E4M3 codes and fp32 block
+    scales (256 elements per block) of the two moments."""
+    mq: np.ndarray
+    ms: np.ndarray
+    vq: np.ndarray
+    vs: np.ndarray
+
+    @staticmethod
+    def zeros(n: int) -> "Adam8State":
+        nb = (n + 255) // 256
+        return Adam8State(np.zeros(n, np.uint8), np.zeros(nb, np.float32),
+                          np.zeros(n, np.uint8), np.zeros(nb, np.float32))
+
+
+def adamw_scalars(lr, beta1, beta2, eps, weight_decay, step):
+    """The fp32 scalars of AdamW step `step` (>= 1): lr, b1, b2, 1 - b1,
+    1 - b2, eps, the bias corrections 1 - b^t (fp64, rounded once) and the
+    decoupled decay 1 - lr wd."""
+    f = lambda x: float(np.float32(x))
+    return (f(lr), f(beta1), f(beta2), f(1.0 - beta1), f(1.0 - beta2), f(eps),
+            f(1.0 - beta1 ** step), f(1.0 - beta2 ** step), f(1.0 - lr * weight_decay))
+
+
+def adamw8_step(p: np.ndarray, g: np.ndarray, st: Adam8State, lr=2e-4, beta1=0.9,
+                beta2=0.999, eps=1e-8, weight_decay=0.0, step=1, want_bf16=False):
+    """One 8-bit AdamW step in place on p (fp32) and st; returns bf16(p)
+    bits when want_bf16."""
+    assert p.dtype == np.float32 and g.dtype == np.float32 and p.flags["C_CONTIGUOUS"]
+    g = np.ascontiguousarray(g)
+    pb = np.empty(p.size, np.uint16) if want_bf16 else None
+    lib().orc_adamw8_step(_ptr(p), _ptr(g), p.size, _ptr(st.mq), _ptr(st.ms), _ptr(st.vq),
+                          _ptr(st.vs), _ptr(pb),
+                          *adamw_scalars(lr, beta1, beta2, eps, weight_decay, step))
+    return pb
 
 
 def _bf16_f64(a) -> np.ndarray:

@@ -495,6 +495,61 @@ void orc_qlora_dx_dropout(const float* Wd, int64_t N, int64_t K, const uint16_t*
   }
 }
 
+/* ---------------- 8-bit AdamW step for the adapters ------------------------ */
+
+/* The adapters' optimizer (course notebook FT-02, the training arguments'
+ * optim="paged_adamw_8bit": AdamW whose two moment states are stored in 8
+ * bits).  The pages fix no 8-bit state format; reading: each state tensor
+ * is stored blockwise, 256 elements per block, as OCP E4M3FN codes of
+ * x / s_b with one fp32 block scale s_b = RN32(max|x| / 448) (s_b = 0: all
+ * codes 0).  The update follows AdamW with decoupled weight decay, in fp32,
+ * one rounding per operation in this order:
+ *   m = RN(RN(b1 m_old) + RN(omb1 g)),  v = RN(RN(b2 v_old) + RN(RN(omb2 g) g))
+ *   p = RN(p decay),  denom = RN(sqrt(RN(v / c2)) + eps)
+ *   p = RN(p - RN(lr RN(RN(m / c1) / denom)))
+ * with m_old = RN(e4m3(code) s_b) (likewise v_old), omb1 = 1 - b1 and
+ * omb2 = 1 - b2, c1 = 1 - b1^t and c2 = 1 - b2^t (bias corrections of step
+ * t >= 1) and decay = 1 - lr wd, all given as fp32; then both states are
+ * quantized again with new block scales.
+ *   p [n] fp32 (updated), g [n] fp32, mq/vq [n] codes, ms/vs [ceil(n/256)]
+ *   fp32 block scales (updated); pb (nullable) receives bf16(p). */
+static void state_requant(const float* x, int64_t b0, int64_t b1, uint8_t* q, float* sc,
+                          int64_t blk) {
+  float amax = 0.0f;
+  for (int64_t i = b0; i < b1; ++i)
+    if (fabsf(x[i - b0]) > amax) amax = fabsf(x[i - b0]);
+  float s = amax / 448.0f;
+  sc[blk] = s;
+  for (int64_t i = b0; i < b1; ++i) q[i] = s > 0.0f ? orc_e4m3_encode(x[i - b0] / s) : 0;
+}
+
+void orc_adamw8_step(float* p, const float* g, int64_t n, uint8_t* mq, float* ms, uint8_t* vq,
+                     float* vs, uint16_t* pb, float lr, float b1, float b2, float omb1,
+                     float omb2, float eps, float c1, float c2, float decay) {
+  int64_t nb = (n + 255) / 256;
+#pragma omp parallel for schedule(static)
+  for (int64_t blk = 0; blk < nb; ++blk) {
+    int64_t i0 = blk * 256, i1 = i0 + 256 < n ? i0 + 256 : n;
+    float m[256], v[256];
+    for (int64_t i = i0; i < i1; ++i) {
+      float mo = orc_e4m3_decode(mq[i]) * ms[blk];
+      float vo = orc_e4m3_decode(vq[i]) * vs[blk];
+      float mi = b1 * mo + omb1 * g[i];
+      float vi = b2 * vo + (omb2 * g[i]) * g[i];
+      float pi = p[i] * decay;
+      float denom = sqrtf(vi / c2) + eps;
+      float upd = (mi / c1) / denom;
+      pi = pi - lr * upd;
+      p[i] = pi;
+      if (pb) pb[i] = orc_bf16_rne(pi);
+      m[i - i0] = mi;
+      v[i - i0] = vi;
+    }
+    state_requant(m, i0, i1, mq, ms, blk);
+    state_requant(v, i0, i1, vq, vs, blk);
+  }
+}
+
 /* ---------------- merge of the adapter into the weight -------------------- */
 
 /* Page 2, section "Merge changes the operator: test it explicitly": merging

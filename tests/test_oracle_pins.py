@@ -803,3 +803,86 @@ def test_dq_off_state_and_storage(orc):
         assert np.array_equal(f32.ravel().view(np.uint32), ref.ravel().view(np.uint32))
         bits = 8 * st.packed.size + 32 * st.absmax.size
         assert bits / W.size == g["bits_no_dq"]
+
+
+# --------------------------------------------------------------- 8-bit AdamW
+# Course notebook FT-02: the training arguments' optim="paged_adamw_8bit"
+# (the Adam states kept in 8 bits) and the memory table's "Optimizer states
+# (AdamW) 8 bytes/param (m + v)".
+def _torch_adamw(p0, grads, lr, b1, b2, eps, wd):
+    pt = torch.nn.Parameter(torch.tensor(p0, dtype=torch.float32))
+    opt = torch.optim.AdamW([pt], lr=lr, betas=(b1, b2), eps=eps, weight_decay=wd,
+                            foreach=False)
+    for g in grads:
+        pt.grad = torch.tensor(g, dtype=torch.float32)
+        opt.step()
+    return pt.detach().numpy().astype(np.float64)
+
+
+def test_adamw8_first_step_is_adamw(orc):
+    """From zero states the first update uses the fp32 moments before they
+    are stored, so it is AdamW's (torch.optim.AdamW), up to rounding order."""
+    rng = np.random.default_rng(21)
+    n = 1000
+    p0 = rng.standard_normal(n).astype(np.float32) * 0.05
+    g = rng.standard_normal(n).astype(np.float32) * 1e-3
+    hp = dict(lr=2e-4, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
+    p = p0.copy()
+    orc.adamw8_step(p, g, orc.Adam8State.zeros(n), step=1, **hp)
+    ref = _torch_adamw(p0, [g], hp["lr"], hp["beta1"], hp["beta2"], hp["eps"], hp["weight_decay"])
+    # within two fp32 ulps of the parameter (the two round in another order)
+    assert np.all(np.abs(p.astype(np.float64) - ref) <= 2 * np.spacing(np.abs(p)))
+    assert np.abs(ref - p0).max() > 1e4 * np.spacing(np.float32(0.05))  # a real step
+
+
+def test_adamw8_tracks_adamw_over_steps(orc):
+    """Twenty steps on random gradients: the 8-bit states move the parameters
+    as fp32 AdamW does, within the states' 3-bit-mantissa precision."""
+    rng = np.random.default_rng(22)
+    n = 4096
+    p0 = rng.standard_normal(n).astype(np.float32) * 0.05
+    grads = [(rng.standard_normal(n) * 1e-3 + 5e-4).astype(np.float32) for _ in range(20)]
+    hp = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0)
+    p, st = p0.copy(), orc.Adam8State.zeros(n)
+    for t, g in enumerate(grads, 1):
+        orc.adamw8_step(p, g, st, step=t, **hp)
+    ref = _torch_adamw(p0, grads, hp["lr"], hp["beta1"], hp["beta2"], hp["eps"], 0.0)
+    d, dref = p.astype(np.float64) - p0, ref - p0
+    rel = np.linalg.norm(d - dref) / np.linalg.norm(dref)
+    assert rel < 0.03, rel
+
+
+def test_adamw8_states_hold_the_moments(orc):
+    """After a step each stored moment decodes to within half an E4M3 step
+    (at its magnitude relative to the block scale) of the fp32 moment, and
+    every nonzero block holds a code of magnitude 448."""
+    rng = np.random.default_rng(23)
+    n = 700  # a partial last block
+    g = rng.standard_normal(n).astype(np.float32) * 1e-2
+    p, st = np.zeros(n, np.float32), orc.Adam8State.zeros(n)
+    orc.adamw8_step(p, g, st, lr=1e-3, step=1)
+    m = (np.float32(0.1) * g).astype(np.float64)        # (1 - b1) g
+    v = ((np.float32(0.001) * g) * g).astype(np.float64)  # (1 - b2) g g
+    for q, sc, x in ((st.mq, st.ms, m), (st.vq, st.vs, v)):
+        dec = np.array([orc.e4m3_decode(c) for c in q], np.float64) * np.repeat(sc, 256)[:n]
+        s = np.repeat(sc.astype(np.float64), 256)[:n]
+        xs = np.abs(x) / s
+        e = np.maximum(np.floor(np.log2(np.maximum(xs, 2.0 ** -9))), -6)
+        assert np.all(np.abs(dec - x) <= s * 2.0 ** (e - 3) / 2 * (1 + 1e-6) + 1e-30)
+        for b in range(sc.size):
+            blk = q[256 * b:256 * b + 256]
+            assert (blk & 0x7F).max() == 0x7E  # 448
+    assert np.all(st.vq < 0x80)  # the second moment is never negative
+
+
+def test_adamw8_decay_and_state_bytes(orc):
+    """No gradient: the decoupled decay alone, p (1 - lr wd); the states take
+    2 (1 + 4/256) bytes per parameter against the table's 8 for fp32 m and v."""
+    p = np.linspace(-1, 1, 512).astype(np.float32)
+    p0 = p.copy()
+    orc.adamw8_step(p, np.zeros(512, np.float32), orc.Adam8State.zeros(512), lr=0.1,
+                    weight_decay=0.5, step=3)
+    assert np.array_equal(p, p0 * np.float32(1 - 0.1 * 0.5))
+    st = orc.Adam8State.zeros(256 * 1000)
+    per_param = (st.mq.nbytes + st.vq.nbytes + st.ms.nbytes + st.vs.nbytes) / st.mq.size
+    assert per_param == 2 * (1 + 4 / 256) and per_param < 8
