@@ -383,12 +383,14 @@ class Adam8State:
 
 
 def adamw_scalars(lr, beta1, beta2, eps, weight_decay, step):
-    """The fp32 scalars of AdamW step `step` (>= 1): lr, b1, b2, 1 - b1,
-    1 - b2, eps, the bias corrections 1 - b^t (fp64, rounded once) and the
+    """The fp32 scalars of AdamW step `step` (>= 1).  The hyperparameters are
+    fp32 values (rounded from what is given); from them, in fp64 and rounded
+    once to fp32: 1 - b1, 1 - b2, the bias corrections 1 - b^t and the
     decoupled decay 1 - lr wd."""
     f = lambda x: float(np.float32(x))
-    return (f(lr), f(beta1), f(beta2), f(1.0 - beta1), f(1.0 - beta2), f(eps),
-            f(1.0 - beta1 ** step), f(1.0 - beta2 ** step), f(1.0 - lr * weight_decay))
+    lr, b1, b2, eps, wd = f(lr), f(beta1), f(beta2), f(eps), f(weight_decay)
+    return (lr, b1, b2, f(1.0 - b1), f(1.0 - b2), eps, f(1.0 - b1 ** int(step)),
+            f(1.0 - b2 ** int(step)), f(1.0 - lr * wd))
 
 
 def adamw8_step(p: np.ndarray, g: np.ndarray, st: Adam8State, lr=2e-4, beta1=0.9,
