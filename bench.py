@@ -367,15 +367,17 @@ def bench_extras(torch, qn, wl):
     # off (fp32 block scales): quantize and dequantize to bf16
     fmt = {}
     for cb, dq in (("fp4", True), ("nf4", False), ("fp4", False)):
-        sts = [qn.qn_quantize(Ws[i % 6], codebook=cb, double_quant=dq) for i in range(6)]
+        # 12 rotated states and outputs (> 2x the 256 MB memory-side cache),
+        # as for the NF4 figures above
+        sts = [qn.qn_quantize(Ws[i % 6], codebook=cb, double_quant=dq) for i in range(12)]
         torch.cuda.synchronize()
         qms = [_event_time_ms(torch, lambda i: qn.qn_quantize(
             Ws[i % 6], codebook=cb, double_quant=dq, workspace=qws, nonfinite=flag), 24)
             for _ in range(5)]
         outs_fmt = [torch.empty((4096, 4096), dtype=torch.bfloat16, device="cuda")
-                    for _ in range(6)]
-        dms = [_event_time_ms(torch, lambda i: qn.nf4_dequantize(sts[i % 6], torch.bfloat16,
-                                                                  out=outs_fmt[i % 6]), 24)
+                    for _ in range(12)]
+        dms = [_event_time_ms(torch, lambda i: qn.nf4_dequantize(sts[i % 12], torch.bfloat16,
+                                                                  out=outs_fmt[i % 12]), 48)
                for _ in range(5)]
         sb = sts[0].nbytes()
         qb, db = 4 * 4096 * 4096 + sb, sb + 2 * 4096 * 4096
@@ -452,6 +454,23 @@ def bench_extras(torch, qn, wl):
     out["decode_fwd_14336x4096"] = dec
     del copies, base
     torch.cuda.empty_cache()
+
+    # 8-bit AdamW step over the decoder layer's adapters (1,310,720
+    # parameters: A and B of the seven rank-16 targets), fp32 gradients
+    n_ad = wl.adapter_params(r=16)
+    pa = torch.randn(n_ad, device="cuda") * 0.01
+    ga = torch.randn(n_ad, device="cuda") * 1e-3
+    pab = torch.empty(n_ad, dtype=torch.bfloat16, device="cuda")
+    opt = qn.Adam8(pa, lr=2e-4)
+    opt.step(ga, pab)
+    torch.cuda.synchronize()
+    ms = [_event_time_ms(torch, lambda i: opt.step(ga, pab), 50) for _ in range(5)]
+    med, mn = _median_min(ms)
+    nbytes = n_ad * (4 + 4 + 4 + 2 + 2 + 2) + 4 * 4 * ((n_ad + 255) // 256)
+    out["adamw8_step_decoder_layer_adapters"] = dict(
+        ms=med, ms_min=mn, params=n_ad, bytes=nbytes, GBs=nbytes / med / 1e6,
+        hbm_frac=nbytes / med / 1e6 / HBM_PEAK_GBS)
+    del pa, ga, pab, opt
 
     # one decoder layer's seven linears, M = 4096, fwd + bwd
     cfg = wl.DECODER_LAYER

@@ -264,6 +264,29 @@ qn_status qlora_linear_bwd(const qn_nf4dq* w, const uint16_t* x, const uint16_t*
 qn_status nf4_merge_lora(const qn_nf4dq* w, const uint16_t* A, const uint16_t* B, int r,
                          float alpha, float* out, void* stream);
 
+/* Hyperparameters of one AdamW step (fp32 values; step >= 1). */
+typedef struct {
+  float lr, beta1, beta2, eps, weight_decay;
+  int64_t step;
+} qn_adamw_hparams;
+
+/* One AdamW step with 8-bit moment states, for the adapters (course notebook
+ * FT-02, the training arguments' optim="paged_adamw_8bit").  State format (a
+ * reading: the pages name the optimizer but not its format): each moment in
+ * blocks of 256 elements, OCP E4M3FN codes m_codes/v_codes [n] of x / s_b
+ * with fp32 block scales m_scales/v_scales [ceil(n/256)], s_b = max|x| / 448
+ * (all zero to start).  Update in fp32, one rounding per operation:
+ *   m = b1 m + (1-b1) g,  v = b2 v + ((1-b2) g) g,  p = p (1 - lr wd),
+ *   p = p - lr ((m / (1 - b1^t)) / (sqrt(v / (1 - b2^t)) + eps))
+ * (1-b, 1 - b^t and 1 - lr wd formed in fp64 from the fp32 values and
+ * rounded once), then both moments are stored again with new block scales.
+ * p [n] fp32 is updated in place from g [n] fp32 (for instance dA or dB);
+ * p_bf16 (nullable) receives bf16(p) for the next forward.  Device pointers
+ * 16-byte aligned; stream-ordered. */
+qn_status adamw8_step(float* p, const float* g, int64_t n, uint8_t* m_codes, float* m_scales,
+                      uint8_t* v_codes, float* v_scales, uint16_t* p_bf16,
+                      const qn_adamw_hparams* h, void* stream);
+
 /* Kernel routes of the linear calls (qlora_linear_route). */
 enum {
   QN_ROUTE_DECODE_ROWS = 1,  /* M <= 16: one kernel over bands of whole rows */

@@ -31,7 +31,7 @@ EXPORTS = ["qn_abi_version", "qn_status_str", "qn_nf4_codebook", "nf4_quantize_d
            "qlora_linear_bwd", "lora_linear_bf16", "qlora_linear_route",
            "qlora_linear_fwd_noalloc", "nf4_merge_lora", "qlora_linear_workspace_ex",
            "qlora_linear_fwd_ex", "qlora_linear_bwd_ex", "qn_quantize",
-           "qlora_linear_workspace_state", "qn_fp4_codebook"]
+           "qlora_linear_workspace_state", "qn_fp4_codebook", "adamw8_step"]
 ROUTES = {1: "decode_rows", 2: "decode_tiles", 3: "decode_split", 4: "fused_small", 5: "fused",
           6: "dense"}
 
@@ -45,6 +45,12 @@ class QNError(RuntimeError):
 class _LoraOpts(ctypes.Structure):
     _fields_ = [("rslora", ctypes.c_int), ("dropout_mask", ctypes.c_void_p),
                 ("dropout_p", ctypes.c_float)]
+
+
+class _AdamHP(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
+                ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float),
+                ("step", ctypes.c_int64)]
 
 
 class _NF4DQ(ctypes.Structure):
@@ -110,6 +116,8 @@ def load_library(path: str = LIB_PATH):
                                       ctypes.c_float, OP, P, P, P, P, P, SZ, P]
     L.qlora_linear_bwd_ex.restype = ctypes.c_int
     L.nf4_merge_lora.argtypes = [ctypes.POINTER(_NF4DQ), P, P, ctypes.c_int, ctypes.c_float, P, P]
+    L.adamw8_step.argtypes = [P, P, I64, P, P, P, P, P, ctypes.POINTER(_AdamHP), P]
+    L.adamw8_step.restype = ctypes.c_int
     L.nf4_merge_lora.restype = ctypes.c_int
     L.qlora_linear_route.argtypes = [I64, I64, I64, ctypes.c_int, ctypes.c_int]
     L.qlora_linear_route.restype = ctypes.c_int
@@ -287,6 +295,37 @@ def nf4_merge_requantize(st: NF4State, A: torch.Tensor, B: torch.Tensor,
                          alpha: float) -> NF4State:
     """The merged weight quantized again: the state of Qhat(Qhat(W) + s B A)."""
     return nf4_quantize_dq(nf4_merge_lora(st, A, B, alpha))
+
+
+class Adam8:
+    """8-bit AdamW state for one fp32 parameter tensor (moments as E4M3
+    codes with one fp32 scale per 256 elements) and its step."""
+
+    def __init__(self, param: torch.Tensor, lr=2e-4, betas=(0.9, 0.999), eps=1e-8,
+                 weight_decay=0.0):
+        p = _dev(param, torch.float32, "param")
+        n, nb = p.numel(), (p.numel() + 255) // 256
+        dev = p.device
+        self.p = p
+        self.mq = torch.zeros(max(n, 16), dtype=torch.uint8, device=dev)
+        self.vq = torch.zeros(max(n, 16), dtype=torch.uint8, device=dev)
+        self.ms = torch.zeros(max(nb, 4), dtype=torch.float32, device=dev)
+        self.vs = torch.zeros(max(nb, 4), dtype=torch.float32, device=dev)
+        self.lr, self.betas, self.eps, self.wd = lr, betas, eps, weight_decay
+        self.t = 0
+
+    def step(self, grad: torch.Tensor, p_bf16: torch.Tensor | None = None):
+        g = _dev(grad, torch.float32, "grad")
+        if g.numel() != self.p.numel():
+            raise ValueError("grad must have the parameter's size")
+        if p_bf16 is not None:
+            _dev(p_bf16, torch.bfloat16, "p_bf16")
+        self.t += 1
+        h = _AdamHP(self.lr, self.betas[0], self.betas[1], self.eps, self.wd, self.t)
+        _check(load_library().adamw8_step(self.p.data_ptr(), g.data_ptr(), self.p.numel(),
+                                          self.mq.data_ptr(), self.ms.data_ptr(),
+                                          self.vq.data_ptr(), self.vs.data_ptr(), _ptr(p_bf16),
+                                          ctypes.byref(h), _stream(self.p.device)))
 
 
 def route(M: int, rows: int, cols: int, r: int, backward: bool = False) -> str:

@@ -11,7 +11,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libqlora_nf4.so")
 SOURCES = ["quant.hip", "lora.hip", "qgemm.hip", "gemm_bf16.hip", "decode.hip", "merge.hip",
-           "dropout.hip",
+           "dropout.hip", "adamw8.hip",
            "capi.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

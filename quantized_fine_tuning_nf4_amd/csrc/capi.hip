@@ -586,6 +586,32 @@ qn_status nf4_merge_lora(const qn_nf4dq* w, const uint16_t* A, const uint16_t* B
                                static_cast<hipStream_t>(stream), w->codebook, w->absmax));
 }
 
+qn_status adamw8_step(float* p, const float* g, int64_t n, uint8_t* m_codes, float* m_scales,
+                      uint8_t* v_codes, float* v_scales, uint16_t* p_bf16,
+                      const qn_adamw_hparams* h, void* stream) {
+  if (n < 0 || !h || h->step < 1) return QN_EINVAL;
+  if (n == 0) return QN_OK;
+  if (!p || !g || !m_codes || !m_scales || !v_codes || !v_scales) return QN_EINVAL;
+  if (!aligned16(p) || !aligned16(g) || !aligned16(m_codes) || !aligned16(v_codes) ||
+      !aligned16(m_scales) || !aligned16(v_scales) || (p_bf16 && !aligned16(p_bf16)))
+    return QN_EALIGN;
+  if (!(h->beta1 >= 0.f && h->beta1 < 1.f && h->beta2 >= 0.f && h->beta2 < 1.f)) return QN_EINVAL;
+  // the derived scalars in fp64 from the fp32 hyperparameters, rounded once
+  const double b1 = h->beta1, b2 = h->beta2, t = (double)h->step;
+  AdamScalars s;
+  s.lr = h->lr;
+  s.b1 = h->beta1;
+  s.b2 = h->beta2;
+  s.omb1 = (float)(1.0 - b1);
+  s.omb2 = (float)(1.0 - b2);
+  s.eps = h->eps;
+  s.c1 = (float)(1.0 - std::pow(b1, t));
+  s.c2 = (float)(1.0 - std::pow(b2, t));
+  s.decay = (float)(1.0 - (double)h->lr * (double)h->weight_decay);
+  return from_hip(launch_adamw8(p, g, n, m_codes, m_scales, v_codes, v_scales, p_bf16, s,
+                                static_cast<hipStream_t>(stream)));
+}
+
 int qlora_linear_route(int64_t M, int64_t rows, int64_t cols, int r, int backward) {
   if (M < 1 || M > kMaxRowsM || rows < 8 || cols < kBlock || rows % 8 != 0 ||
       cols % kBlock != 0 || rows > kMaxDim || cols > kMaxDim || r < 1 || r > 64)

@@ -230,6 +230,17 @@ hipError_t launch_thin_nt(const uint16_t* Z, const uint16_t* T, int64_t M, int64
                           bool t_rows = false, Clear clr = Clear{nullptr, 0},
                           const uint8_t* zmask = nullptr);
 
+// fp32 scalars of one 8-bit AdamW step (the 1 - b, bias corrections and
+// decay formed on the host).
+struct AdamScalars {
+  float lr, b1, b2, omb1, omb2, eps, c1, c2, decay;
+};
+// One 8-bit AdamW step over n parameters (p, g fp32; moments as E4M3 codes
+// with fp32 scales per 256; pb nullable: bf16 copy of the new p).  p, g
+// 16-byte aligned, mq, vq 4-byte aligned.
+hipError_t launch_adamw8(float* p, const float* g, int64_t n, uint8_t* mq, float* ms, uint8_t* vq,
+                         float* vs, uint16_t* pb, const AdamScalars& h, hipStream_t st);
+
 // Xd [M, K] = X with the elements whose mask bit is clear zeroed (K % 8 == 0).
 hipError_t launch_dropout_apply(const uint16_t* X, const uint8_t* mask, int64_t M, int64_t K,
                                 uint16_t* Xd, hipStream_t st);
