@@ -79,6 +79,43 @@ def test_fp4_codes_near_every_threshold(qn):
     _check_state(qn, st, oracle.quantize(W, double_quant=False, codebook="fp4"))
 
 
+def _thresholds(cb):
+    """The decision thresholds in quotient space: the largest fp32 not above
+    each midpoint of adjacent levels (NF4: all sixteen levels; FP4: the
+    eight magnitudes)."""
+    L = (oracle.codebook() if cb == "nf4" else oracle.fp4_codebook()[:8]).astype(np.float64)
+    m = (L[:-1] + L[1:]) / 2
+    t = m.astype(np.float32)
+    return np.where(t.astype(np.float64) > m, np.nextafter(t, np.float32(-np.inf)), t)
+
+
+@pytest.mark.parametrize("codebook", ["nf4", "fp4"])
+@pytest.mark.parametrize("lo,hi", [(-100, -80), (100, 127)])
+def test_codes_near_thresholds_at_extreme_scales(qn, codebook, lo, hi):
+    """Weights within a few ulps of every threshold times the block scale, at
+    block scales from 2^lo to 2^hi: tiny scales on both sides of 2^-90 (the
+    waves mix the code search's fp32 and fp64 forms) and scales up to the top
+    of the fp32 range.  Both signs; the codes are the oracle's."""
+    rng = np.random.default_rng(500 + lo)
+    nblk = 4096
+    t = _thresholds(codebook)
+    scales = (rng.uniform(0.5, 1.0, nblk) * 2.0 ** rng.integers(lo, hi, nblk)).astype(np.float32)
+    W = np.zeros((nblk, 64), np.float32)
+    W[:, 0] = scales
+    W[1::3, 0] *= -1
+    ks = rng.integers(0, t.size, (nblk, 63))
+    base = (t[ks].astype(np.float64) * scales[:, None].astype(np.float64)).astype(np.float32)
+    d = rng.integers(-4, 5, (nblk, 63)).astype(np.int32)
+    bits = base.view(np.int32)
+    bits = np.where(base >= 0, bits + d, bits - d).astype(np.int32)
+    v = bits.view(np.float32)
+    v = np.where(rng.random((nblk, 63)) < 0.5, -v, v)
+    W[:, 1:] = np.clip(v, -np.abs(W[:, :1]), np.abs(W[:, :1]))
+    say(f"[formats] {codebook} near thresholds, scales 2^{lo}..2^{hi}")
+    st = qn.qn_quantize(f32_dev(W), codebook=codebook, double_quant=False)
+    _check_state(qn, st, oracle.quantize(W, double_quant=False, codebook=codebook))
+
+
 @pytest.mark.parametrize("codebook,dq", FORMATS)
 @pytest.mark.parametrize("rows,cols,M,r", [(264, 192, 4, 8), (520, 576, 300, 16),
                                            (3848, 3840, 4100, 16)])
