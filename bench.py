@@ -496,10 +496,32 @@ def bench_extras(torch, qn, wl):
     ms = [_event_time_ms(torch, layer_step, 3) for _ in range(5)]
     med, mn = _median_min(ms)
     flops = sum(fwd_flops(M, d["N"], d["K"], r) + bwd_flops(M, d["N"], d["K"], r) for d in layers)
+    # each linear's forward and backward on its own (same inputs, eager calls)
+    per = {}
+    for (name, N, K), d in zip(wl.DECODER_LINEARS, layers):
+        def f_call(_, d=d):
+            qn.qlora_linear_fwd(d["st"], d["x"], d["A"], d["B"], alpha, y=d["y"],
+                                workspace=d["fws"])
+        _, u = qn.qlora_linear_fwd(d["st"], d["x"], d["A"], d["B"], alpha, y=d["y"],
+                                   workspace=d["fws"])
+
+        def b_call(_, d=d, u=u):
+            qn.qlora_linear_bwd(d["st"], d["x"], d["G"], d["A"], d["B"], alpha, u,
+                                workspace=d["bws"])
+        b_call(0)
+        torch.cuda.synchronize()
+        fm, _ = _median_min([_event_time_ms(torch, f_call, 5) for _ in range(3)])
+        bm, _ = _median_min([_event_time_ms(torch, b_call, 5) for _ in range(3)])
+        ff, bf = fwd_flops(M, N, K, r), bwd_flops(M, N, K, r)
+        per[name] = dict(rows=N, cols=K, fwd_route=qn.route(M, N, K, r, False),
+                         bwd_route=qn.route(M, N, K, r, True), fwd_ms=fm, bwd_ms=bm,
+                         fwd_mfma_frac=ff / fm / 1e9 / BF16_PEAK_TFLOPS,
+                         bwd_mfma_frac=bf / bm / 1e9 / BF16_PEAK_TFLOPS)
     out["decoder_layer_7_linears_M4096"] = dict(ms=med, ms_min=mn, flops=flops,
                                                 TFLOPs=flops / med / 1e9,
                                                 mfma_frac=flops / med / 1e9 / BF16_PEAK_TFLOPS,
-                                                adapter_params=wl.adapter_params(r=r))
+                                                adapter_params=wl.adapter_params(r=r),
+                                                per_linear=per)
     del layers
     torch.cuda.empty_cache()
     return out
@@ -685,6 +707,22 @@ def kernels_workload(torch, qn, wl, launches=5):
         qn.qlora_linear_fwd(std, xdec, Ad, Bdd, alpha)
     torch.cuda.synchronize()
     print(f"[kernels] decode forward M=16 {Nd}x{Kd} x {launches}", file=sys.stderr, flush=True)
+    x1 = xdec[:1].contiguous()
+    for _ in range(launches):
+        qn.qlora_linear_fwd(std, x1, Ad, Bdd, alpha)
+    torch.cuda.synchronize()
+    print(f"[kernels] decode forward M=1 {Nd}x{Kd} x {launches}", file=sys.stderr, flush=True)
+    # the decoder layer's k_proj shape (1024 x 4096, M = 4096): the forward
+    # with the dequantization inside 128 x 128 GEMM tiles
+    lc = wl.DECODER_LAYER
+    Wk, xk, Ak, Bk, _ = wl.linear_inputs(1024, 4096, lc["M"], r, seed=lc["seed"], index=1)
+    stk = qn.nf4_quantize_dq(torch.from_numpy(Wk).cuda())
+    xk, Ak, Bk = _bf16(torch, xk), _bf16(torch, Ak), _bf16(torch, Bk)
+    for _ in range(launches):
+        qn.qlora_linear_fwd(stk, xk, Ak, Bk, alpha)
+    torch.cuda.synchronize()
+    print(f"[kernels] fused forward M={lc['M']} 1024x4096 ({qn.route(lc['M'], 1024, 4096, r)}) "
+          f"x {launches}", file=sys.stderr, flush=True)
     Wq = torch.from_numpy(wl.weight(N, K, wl.SEED_W + 90)).cuda()
     for _ in range(launches):
         qn.nf4_quantize_dq(Wq, out=st)
