@@ -8,7 +8,10 @@
 // listing), once the weight has been dequantized to bf16 in a workspace.
 //
 // Workgroup tile 256 x 256, four waves (2 x 2), each wave 128 x 128 as 8 x 8
-// tiles of v_mfma_f32_16x16x32_bf16 (256 accumulators, pinned in AGPRs).  On
+// tiles of v_mfma_f32_16x16x32_bf16 (256 accumulators, pinned in AGPRs); for
+// outputs with too few such tiles to fill the chip, the same kernel with
+// 128 x 128 tiles (each wave 64 x 64 as 4 x 4 tiles, half the LDS, two
+// workgroups per compute unit).  On
 // gfx950 this shape keeps a higher shader clock under load than the 32x32x16
 // one at the same issue rate.  A step covers 64 reduction elements: both
 // operands go from global memory straight into LDS by buffer loads, each
@@ -33,21 +36,37 @@
 namespace qn {
 namespace {
 
-constexpr int BM = 256, BN = 256, BK = 64, NST = 2, T = 256;
-constexpr int ROWB = BK * 2;            // bytes per tile row per stage (one cache line)
-constexpr int OPB = 256 * ROWB;         // bytes per operand per stage (32 KB)
-constexpr int STB = 2 * OPB;            // bytes per stage (64 KB)
-constexpr int OUTP = 128 * 2 + 16;      // epilogue staging row pitch (bytes)
-constexpr int OUTW = 128 * OUTP;        // staging bytes per wave
-constexpr size_t LDS_MAIN = (size_t)NST * STB > (size_t)4 * OUTW ? (size_t)NST * STB
-                                                                  : (size_t)4 * OUTW;
-// the LoRA operands of a tile for r == 16, above the stages and the staging
-// tiles: V rows m0 .. m0 + 255 (fp32, 64 B each), then L rows c0 .. c0 + 255
-// (bf16, 32 B each)
+constexpr int BK = 64, T = 256;
+constexpr int ROWB = BK * 2;  // bytes per tile row per stage (one cache line)
 constexpr int LORA_R = 16;
-constexpr size_t LDS_V = LDS_MAIN, LDS_L = LDS_V + 256 * LORA_R * 4;
-constexpr size_t LDS_BYTES = LDS_L + 256 * LORA_R * 2;
-static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+// Tile geometry for a wave tile of WT x WT MFMA tiles (16 x 16 each): the
+// workgroup tile is BM x BM, BM = 32 WT.
+template <int WT>
+struct Geo {
+  static constexpr int WR = 16 * WT;                 // rows (and columns) per wave
+  static constexpr int BM = 2 * WR;                  // workgroup tile rows and columns
+  static constexpr int OPB = BM * ROWB;              // bytes per operand per stage
+  static constexpr int STB = 2 * OPB;                // bytes per stage
+  static constexpr int OUTP = WR * 2 + 16;           // epilogue staging row pitch (bytes)
+  static constexpr int OUTW = WR * OUTP;             // staging bytes per wave
+  // LDS stages: a 128 x 128 tile's step is a quarter of a 256 x 256 one's
+  // MFMA time, so its loads go out three steps ahead instead of one
+  static constexpr int NST = WT == 8 ? 2 : 4;
+  static constexpr size_t LDS_MAIN = (size_t)NST * STB > (size_t)4 * OUTW ? (size_t)NST * STB
+                                                                         : (size_t)4 * OUTW;
+  // the LoRA operands of a tile for r == 16, above the stages and the
+  // staging tiles: V rows m0 .. m0 + BM - 1 (fp32, 64 B each), then L rows
+  // c0 .. c0 + BM - 1 (bf16, 32 B each)
+  static constexpr size_t LDS_V = LDS_MAIN, LDS_L = LDS_V + BM * LORA_R * 4;
+  static constexpr size_t LDS_BYTES = LDS_L + BM * LORA_R * 2;
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+  static_assert(NST == 2 || NST == 4, "stages");
+  // the loads of one operand and step: WT instructions per wave, each eight
+  // whole rows; the load slots of a step's second half where they go out
+  static constexpr int J1 = WT == 8 ? 3 : 1, J2 = WT == 8 ? 6 : 3;
+  // workgroups per compute unit the launch bounds ask for
+  static constexpr int OCC = 1;
+};
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
@@ -80,12 +99,16 @@ __device__ __forceinline__ void wait_all_loads() { asm volatile("s_waitcnt vmcnt
 // LORA16: r == 16, the LoRA operands prefetched into LDS; otherwise read in
 // the tail from global memory (one tail per instance keeps the registers of
 // the other out of the kernel).
-template <bool LORA16>
-__global__ __launch_bounds__(T, 1) void k_gemm_nt(
+template <bool LORA16, int WT>
+__global__ __launch_bounds__(T, Geo<WT>::OCC) void k_gemm_nt(
     const uint16_t* __restrict__ A, int64_t lda, int64_t R, const uint16_t* __restrict__ Bm,
     int64_t ldb, int steps, int64_t M, int64_t Nc, const float* __restrict__ V,
     const uint16_t* __restrict__ L, int r, float s, uint16_t* __restrict__ C, int tiles_m,
     int tiles_c) {
+  using G = Geo<WT>;
+  constexpr int BM = G::BM, BN = G::BM, WR = G::WR, OPB = G::OPB, STB = G::STB;
+  constexpr int OUTP = G::OUTP, OUTW = G::OUTW, NST = G::NST;
+  constexpr size_t LDS_V = G::LDS_V, LDS_L = G::LDS_L;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -113,18 +136,18 @@ __global__ __launch_bounds__(T, 1) void k_gemm_nt(
   const int64_t mrows = min((int64_t)BM, M - m0), ncols = min((int64_t)BN, Nc - c0);
 
   // ---- loads: a stage holds 64 reduction elements (128-byte rows, one
-  // cache line per row and step).  Load instruction i (0..7) of wave w covers
-  // rows 64w + 8i + l/8 of an operand; lane l fills unit l%8 of its row with
+  // cache line per row and step).  Load instruction i (0..WT-1) of wave w
+  // covers rows 8 WT w + 8i + l/8 of an operand; lane l fills unit l%8 of its row with
   // source chunk (l%8) ^ ((row >> 1) & 7), so the 1 KB it writes is
   // contiguous and the sixteen rows a fragment read touches sit on distinct
   // banks.
   const rsrc_t rsA = make_rs(A + m0 * lda, (uint32_t)(mrows * lda * 2));
   const rsrc_t rsB = make_rs(Bm + c0 * ldb, (uint32_t)(ncols * ldb * 2));
-  uint32_t aoff[8], boff[8];
-  int achunk[8];
+  uint32_t aoff[WT], boff[WT];
+  int achunk[WT];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int64_t row = 64 * wave + 8 * i + (lane >> 3);
+  for (int i = 0; i < WT; ++i) {
+    const int64_t row = 8 * WT * wave + 8 * i + (lane >> 3);
     const int chunk = (lane & 7) ^ (int)((row >> 1) & 7);
     achunk[i] = chunk;
     aoff[i] = (uint32_t)((min(row, mrows - 1) * lda + 8 * chunk) * 2);
@@ -136,38 +159,38 @@ __global__ __launch_bounds__(T, 1) void k_gemm_nt(
     const int64_t k = (int64_t)st * BK + 8 * achunk[i];
     return (uint32_t)(2 * (k - min(k, R - 8)));
   };
-  // load q (0..15) of step st: q < 8 A rows, else B rows
+  // load q (0 .. 2 WT - 1) of step st: q < WT A rows, else B rows
   auto load_one = [&](int q, int st, int stage) {
-    uint8_t* d = smem + stage * STB + (q >= 8 ? OPB : 0) + wave * 8192 + 1024 * (q & 7);
+    uint8_t* d = smem + stage * STB + (q >= WT ? OPB : 0) + wave * (1024 * WT) + 1024 * (q % WT);
     const uint32_t so = (uint32_t)st * (BK * 2);
-    if (q < 8)
+    if (q < WT)
       dma16(rsA, aoff[q] - a_back(st, q), so, d);
     else
-      dma16(rsB, boff[q - 8], so, d);
+      dma16(rsB, boff[q - WT], so, d);
   };
 
-  // ---- fragment reads (v_mfma_f32_16x16x32_bf16): tile t of the wave's 128
+  // ---- fragment reads (v_mfma_f32_16x16x32_bf16): tile t of the wave's WR
   // rows, half h of the stage: lane l reads row 16t + l%16 at chunk
   // 4h + l/16 (eight consecutive reduction elements)
   const int l16 = lane & 15, g4 = lane >> 4;
   int roff[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) roff[h] = l16 * ROWB + 16 * ((4 * h + g4) ^ ((l16 >> 1) & 7));
-  const int abase = wm * 128 * ROWB, bbase = OPB + wn * 128 * ROWB;
+  const int abase = wm * WR * ROWB, bbase = OPB + wn * WR * ROWB;
   auto frag = [&](int stage, int opbase, int t, int h) {
     return as_bf16x8(*reinterpret_cast<const u32x4*>(smem + stage * STB + opbase + t * 16 * ROWB +
                                                      roff[h]));
   };
 
-  f32x4 acc[8][8];
+  f32x4 acc[WT][WT];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < WT; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{};
+    for (int j = 0; j < WT; ++j) acc[i][j] = f32x4{};
 
   // A fragments are replaced in place once their row of MFMAs has issued;
   // B fragments come in two sets (first and second half of a stage)
-  bf16x8 fa[8], fb[2][8];
+  bf16x8 fa[WT], fb[2][WT];
 
   // ---- the LoRA operands (r == 16) go first, straight into LDS: they land
   // before step 0's loads (loads complete in order), long before the tail
@@ -176,78 +199,106 @@ __global__ __launch_bounds__(T, 1) void k_gemm_nt(
   if constexpr (LORA16) {
     const rsrc_t rsV = make_rs(V + m0 * r, (uint32_t)(mrows * LORA_R * 4));
     const rsrc_t rsL = make_rs(L + c0 * r, (uint32_t)(ncols * LORA_R * 2));
+    // V: BM rows x 64 B = WT / 2 KB per wave; L: BM rows x 32 B = WT / 4 KB
+    constexpr int KV = WT / 2, KL = WT / 4;
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
-      dma16(rsV, (uint32_t)(1024 * (4 * wave + k) + 16 * lane), 0,
-            smem + LDS_V + 1024 * (4 * wave + k));
+    for (int k = 0; k < KV; ++k)
+      dma16(rsV, (uint32_t)(1024 * (KV * wave + k) + 16 * lane), 0,
+            smem + LDS_V + 1024 * (KV * wave + k));
 #pragma unroll
-    for (int k = 0; k < 2; ++k)
-      dma16(rsL, (uint32_t)(1024 * (2 * wave + k) + 16 * lane), 0,
-            smem + LDS_L + 1024 * (2 * wave + k));
+    for (int k = 0; k < KL; ++k)
+      dma16(rsL, (uint32_t)(1024 * (KL * wave + k) + 16 * lane), 0,
+            smem + LDS_L + 1024 * (KL * wave + k));
   }
 
-  // ---- prologue: steps 0 and 1 in flight, 0 landed
+  // ---- prologue: steps 0 .. NST-1 in flight, 0 landed (all but the later
+  // steps' 2 WT loads each)
 #pragma unroll
-  for (int k = 0; k < 2; ++k)
+  for (int k = 0; k < NST; ++k)
 #pragma unroll
-    for (int q = 0; q < 16; ++q) load_one(q, min(k, steps - 1), k);
-  asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    for (int q = 0; q < 2 * WT; ++q) load_one(q, min(k, steps - 1), k);
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * WT * (NST - 1)) : "memory");
   barrier_lds();
 #pragma unroll
-  for (int t = 0; t < 8; ++t) {
+  for (int t = 0; t < WT; ++t) {
     fa[t] = frag(0, abase, t, 0);
     fb[0][t] = frag(0, bbase, t, 0);
   }
 
-  // ---- half h of step st on stage P: 64 MFMAs.  Half 0 reads half 1's
-  // fragments from the same stage, then waits for step st+1 (sent during
-  // half 1 of step st-1) and meets the other waves: after that barrier no
-  // wave reads stage P again.  Half 1 reads the next step's first half from
-  // the other stage and sends the sixteen loads of step st+2 into stage P.
-  // Half 1 needs no barrier of its own: the next half 0 reads only data that
-  // every wave waited for before the barrier above, and writes none.
+  // ---- half h of step st on stage P = st % NST: WT x WT MFMAs.  Half 0
+  // reads half 1's fragments from the same stage, then waits for step st+1
+  // (sent during half 1 of step st+1-NST; the later steps' loads stay in
+  // flight) and meets the other waves: after that barrier no wave reads
+  // stage P again.  Half 1 reads the next step's first half from the next
+  // stage and sends the 2 WT loads of step st+NST into stage P.  Half 1
+  // needs no barrier of its own: the next half 0 reads only data that every
+  // wave waited for before the barrier above, and writes none.
   auto half = [&](auto p_t, auto h_t, int st) {
     constexpr int P = decltype(p_t)::value, H = decltype(h_t)::value;
     constexpr int RS = H == 0 ? P : (P + 1) % NST;  // stage of the fragments read ahead
     constexpr int RH = H ^ 1;                       // their half
-    const int lst = min(st + 2, steps - 1);
+    const int lst = min(st + NST, steps - 1);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < WT; ++i) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
+      for (int j = 0; j < WT; ++j) {
         mfma16_acc(fb[H][j], fa[i], acc[i][j]);
         // the next half's B fragments are all read during the first row of
         // MFMAs: its first row needs every one of them
         if (i == 0) fb[RH][j] = frag(RS, bbase, j, RH);
-        if (H == 1 && (j == 3 || j == 6)) load_one(2 * i + (j == 6), lst, P);
+        if (H == 1 && (j == G::J1 || j == G::J2)) load_one(2 * i + (j == G::J2), lst, P);
       }
       fa[i] = frag(RS, abase, i, RH);
       __builtin_amdgcn_sched_barrier(0);
     }
     if (H == 0) {
-      wait_all_loads();
+      if constexpr (NST == 2)
+        wait_all_loads();
+      else
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * WT * (NST - 2)) : "memory");
       barrier_lds();
     }
   };
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+  using S3 = std::integral_constant<int, 3>;
+  auto step = [&](auto p_t, int st) {
+    half(p_t, S0{}, st);
+    half(p_t, S1{}, st);
+  };
   int st = 0;
-  for (; st + 2 <= steps; st += 2) {
-    half(S0{}, S0{}, st);
-    half(S0{}, S1{}, st);
-    half(S1{}, S0{}, st + 1);
-    half(S1{}, S1{}, st + 1);
+  for (; st + NST <= steps; st += NST) {
+    step(S0{}, st);
+    step(S1{}, st + 1);
+    if constexpr (NST == 4) {
+      step(S2{}, st + 2);
+      step(S3{}, st + 3);
+    }
   }
-  if (st < steps) {
-    half(S0{}, S0{}, st);
-    half(S0{}, S1{}, st);
+  // the last steps % NST steps, on stages 0, 1, 2 in turn
+  if (st < steps) step(S0{}, st++);
+  if constexpr (NST == 4) {
+    if (st < steps) step(S1{}, st++);
+    if (st < steps) step(S2{}, st++);
   }
+  // The compiler cannot see that the asm MFMAs write the accumulators some
+  // cycles after they issue, so nothing it places may read one before the
+  // last products are complete: 32 wait states, then an empty asm that
+  // "rewrites" every accumulator, which no read of it can move above (a
+  // register copy is not ordered by a memory clobber alone; without the ties
+  // the compiler hoisted the output conversion's AGPR reads above the wait
+  // states and read partial sums).
+  auto settle = [&]() {
+    asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < WT; ++i)
+#pragma unroll
+      for (int j = 0; j < WT; ++j) asm volatile("" : "+a"(acc[i][j]));
+  };
   // every wave's loads have landed and all reads are done before the stages
-  // are reused for the output staging below; the last products' results are
-  // complete before any instruction the compiler places here (a register
-  // spill, say) reads an accumulator: it cannot see that the asm MFMAs write
-  // them
-  asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");
+  // are reused for the output staging below
+  settle();
   wait_all_loads();
   barrier_lds();
 
@@ -257,17 +308,17 @@ __global__ __launch_bounds__(T, 1) void k_gemm_nt(
   const bool vec = (r % 8) == 0;
   const bool lo_part = g4 >= 2;
   if constexpr (LORA16) {
-    // from LDS: L row (tile column) wn 128 + 16 j + l16, ranks 8 (g4 & 1) ..;
-    // V row (tile row) wm 128 + 16 i + l16, the same ranks
+    // from LDS: L row (tile column) wn WR + 16 j + l16, ranks 8 (g4 & 1) ..;
+    // V row (tile row) wm WR + 16 i + l16, the same ranks
     const int jb = 8 * (g4 & 1);
-    bf16x8 lh[8];
+    bf16x8 lh[WT];
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
+    for (int j = 0; j < WT; ++j)
       lh[j] = as_bf16x8(*reinterpret_cast<const u32x4*>(
-          smem + LDS_L + (wn * 128 + 16 * j + l16) * (LORA_R * 2) + 2 * jb));
+          smem + LDS_L + (wn * WR + 16 * j + l16) * (LORA_R * 2) + 2 * jb));
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint8_t* vp = smem + LDS_V + (wm * 128 + 16 * i + l16) * (LORA_R * 4) + 4 * jb;
+    for (int i = 0; i < WT; ++i) {
+      const uint8_t* vp = smem + LDS_V + (wm * WR + 16 * i + l16) * (LORA_R * 4) + 4 * jb;
       const f32x4 v0 = *reinterpret_cast<const f32x4*>(vp);
       const f32x4 v1 = *reinterpret_cast<const f32x4*>(vp + 16);
       const float vr[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
@@ -280,15 +331,15 @@ __global__ __launch_bounds__(T, 1) void k_gemm_nt(
       }
       const bf16x8 av = as_bf16x8(u32x4{w[0], w[1], w[2], w[3]});
 #pragma unroll
-      for (int j = 0; j < 8; ++j) mfma16_acc(lh[j], av, acc[i][j]);
+      for (int j = 0; j < WT; ++j) mfma16_acc(lh[j], av, acc[i][j]);
     }
   }
   for (int j0 = 0; j0 < (LORA16 ? 0 : r); j0 += 16) {
     const int jl = j0 + 8 * (g4 & 1);
-    bf16x8 lh[8];
+    bf16x8 lh[WT];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int64_t col = min(c0 + wn * 128 + 16 * j + l16, Nc - 1);
+    for (int j = 0; j < WT; ++j) {
+      const int64_t col = min(c0 + wn * WR + 16 * j + l16, Nc - 1);
       const uint16_t* lp = L + col * r;
       if (vec) {
         lh[j] = jl < r ? as_bf16x8(*reinterpret_cast<const u32x4*>(lp + jl)) : bf16x8{};
@@ -301,8 +352,8 @@ __global__ __launch_bounds__(T, 1) void k_gemm_nt(
       }
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int64_t m = min(m0 + wm * 128 + 16 * i + l16, M - 1);
+    for (int i = 0; i < WT; ++i) {
+      const int64_t m = min(m0 + wm * WR + 16 * i + l16, M - 1);
       const float* vp = V + m * r;
       float vr[8];
       if (vec && jl < r) {
@@ -326,22 +377,22 @@ __global__ __launch_bounds__(T, 1) void k_gemm_nt(
       }
       const bf16x8 av = as_bf16x8(u32x4{w[0], w[1], w[2], w[3]});
 #pragma unroll
-      for (int j = 0; j < 8; ++j) mfma16_acc(lh[j], av, acc[i][j]);
+      for (int j = 0; j < WT; ++j) mfma16_acc(lh[j], av, acc[i][j]);
     }
   }
 
   // ---- store.  Tile (i, j) is held transposed: lane l has row 16i + l%16
   // and columns 16j + 4(l/16) .. +3 in its four registers; they go to the
   // wave's LDS staging tile as 8 bytes, and the tile then leaves as rows of
-  // 256 contiguous bytes, four rows per store.  The staging tiles overlap the
-  // stages, freed by the barrier above.
+  // 2 WR contiguous bytes (2 WT lanes of 16 bytes per row).  The staging
+  // tiles overlap the stages, freed by the barrier above.
   uint8_t* stg = smem + wave * OUTW;
   // the last products' results are complete before they are read
-  asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");
+  settle();
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < WT; ++i) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < WT; ++j) {
       const f32x4& c = acc[i][j];
       *reinterpret_cast<u32x2*>(stg + (16 * i + l16) * OUTP + 2 * (16 * j + 4 * g4)) =
           u32x2{pack_bf16x2(c[0], c[1]), pack_bf16x2(c[2], c[3])};
@@ -351,12 +402,14 @@ __global__ __launch_bounds__(T, 1) void k_gemm_nt(
   // Streaming (non-temporal) stores: the output is written once and never
   // read here, while the caches still serve other tiles' re-reads of the A
   // and Bm rows; ordinary stores would displace those lines.
-  const int64_t col = c0 + wn * 128 + 8 * (lane & 15);
+  constexpr int LR = 2 * WT, RPS = 64 / LR;  // lanes per row, rows per store
+  const int lc = lane % LR;
+  const int64_t col = c0 + wn * WR + 8 * lc;
 #pragma unroll
-  for (int q = 0; q < 32; ++q) {
-    const int rl = 4 * q + (lane >> 4);
-    const int64_t row = m0 + wm * 128 + rl;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(stg + rl * OUTP + 16 * (lane & 15));
+  for (int q = 0; q < WR / RPS; ++q) {
+    const int rl = RPS * q + lane / LR;
+    const int64_t row = m0 + wm * WR + rl;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(stg + rl * OUTP + 16 * lc);
     if (row < M && col < Nc)
       __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(C + row * Nc + col));
   }
@@ -364,30 +417,49 @@ __global__ __launch_bounds__(T, 1) void k_gemm_nt(
 
 }  // namespace
 
-size_t gemm_nt_lds_bytes() { return LDS_BYTES; }
+size_t gemm_nt_lds_bytes() { return Geo<8>::LDS_BYTES; }
+
+namespace {
+template <int WT>
+hipError_t launch_wt(const uint16_t* A, int64_t lda, int64_t R, const uint16_t* Bm, int64_t ldb,
+                     int64_t M, int64_t Nc, const float* V, const uint16_t* L, int r, float s,
+                     uint16_t* C, hipStream_t st) {
+  using G = Geo<WT>;
+  static hipError_t attr = [] {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_gemm_nt<true, WT>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)G::LDS_BYTES);
+    if (e != hipSuccess) return e;
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(k_gemm_nt<false, WT>),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)G::LDS_MAIN);
+  }();
+  if (attr != hipSuccess) return attr;
+  const int64_t tm = (M + G::BM - 1) / G::BM, tc = (Nc + G::BM - 1) / G::BM;
+  const int steps = (int)(ldb / BK);
+  if (r == LORA_R)
+    hipLaunchKernelGGL((k_gemm_nt<true, WT>), dim3((unsigned)(tm * tc)), dim3(T), G::LDS_BYTES, st,
+                       A, lda, R, Bm, ldb, steps, M, Nc, V, L, r, s, C, (int)tm, (int)tc);
+  else
+    hipLaunchKernelGGL((k_gemm_nt<false, WT>), dim3((unsigned)(tm * tc)), dim3(T), G::LDS_MAIN,
+                       st, A, lda, R, Bm, ldb, steps, M, Nc, V, L, r, s, C, (int)tm, (int)tc);
+  return hipGetLastError();
+}
+}  // namespace
+
+bool gemm_nt_small_tiles(int64_t M, int64_t Nc) {
+  return ((M + 255) / 256) * ((Nc + 255) / 256) < 240;
+}
 
 hipError_t launch_gemm_nt(const uint16_t* A, int64_t lda, int64_t R, const uint16_t* Bm,
                           int64_t ldb, int64_t M, int64_t Nc, const float* V, const uint16_t* L,
                           int r, float s, uint16_t* C, hipStream_t st) {
-  static hipError_t attr = [] {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_gemm_nt<true>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS_BYTES);
-    if (e != hipSuccess) return e;
-    return hipFuncSetAttribute(reinterpret_cast<const void*>(k_gemm_nt<false>),
-                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS_MAIN);
-  }();
-  if (attr != hipSuccess) return attr;
   if (M <= 0) return hipSuccess;
   if (ldb % BK != 0 || R < 8 || R > ldb) return hipErrorInvalidValue;
-  const int64_t tm = (M + BM - 1) / BM, tc = (Nc + BN - 1) / BN;
-  const int steps = (int)(ldb / BK);
-  if (r == LORA_R)
-    hipLaunchKernelGGL(k_gemm_nt<true>, dim3((unsigned)(tm * tc)), dim3(T), LDS_BYTES, st, A, lda,
-                       R, Bm, ldb, steps, M, Nc, V, L, r, s, C, (int)tm, (int)tc);
-  else
-    hipLaunchKernelGGL(k_gemm_nt<false>, dim3((unsigned)(tm * tc)), dim3(T), LDS_MAIN, st, A, lda,
-                       R, Bm, ldb, steps, M, Nc, V, L, r, s, C, (int)tm, (int)tc);
-  return hipGetLastError();
+  // 256 x 256 tiles once there are about as many as compute units; fewer
+  // would leave most of the chip idle, so 128 x 128 tiles then
+  if (gemm_nt_small_tiles(M, Nc))
+    return launch_wt<4>(A, lda, R, Bm, ldb, M, Nc, V, L, r, s, C, st);
+  return launch_wt<8>(A, lda, R, Bm, ldb, M, Nc, V, L, r, s, C, st);
 }
 
 }  // namespace qn
