@@ -730,6 +730,33 @@ def kernels_workload(torch, qn, wl, launches=5):
     print(f"[kernels] quantize {N}x{K} x {launches}", file=sys.stderr, flush=True)
 
 
+def layer_workload(torch, qn, wl, reps=3):
+    """The decoder layer's seven linears (M = 4096, r = 16), forward then
+    backward of each in turn, `reps` times after one untimed pass, with a
+    synchronization and a stderr line per linear so that a kernel trace can
+    be cut into linears."""
+    L = qn.load_library()
+    cfg = wl.DECODER_LAYER
+    M, r, alpha = cfg["M"], cfg["r"], cfg["alpha"]
+    layers = []
+    for idx, (name, N, K) in enumerate(wl.DECODER_LINEARS):
+        W, x, A, B, G = wl.linear_inputs(N, K, M, r, seed=cfg["seed"], index=idx)
+        st = qn.nf4_quantize_dq(torch.from_numpy(W).cuda())
+        layers.append(dict(name=name, st=st, x=_bf16(torch, x), A=_bf16(torch, A),
+                           B=_bf16(torch, B), G=_bf16(torch, G),
+                           fws=qn.linear_workspace(L.qlora_linear_workspace(M, N, K, r, 0)),
+                           bws=qn.linear_workspace(L.qlora_linear_workspace(M, N, K, r, 1)),
+                           y=torch.empty((M, N), dtype=torch.bfloat16, device="cuda")))
+    for rep in range(reps + 1):
+        for d in layers:
+            _, u = qn.qlora_linear_fwd(d["st"], d["x"], d["A"], d["B"], alpha, y=d["y"],
+                                       workspace=d["fws"])
+            qn.qlora_linear_bwd(d["st"], d["x"], d["G"], d["A"], d["B"], alpha, u,
+                                workspace=d["bws"])
+            torch.cuda.synchronize()
+            print(f"[layer] pass {rep} {d['name']}", file=sys.stderr, flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -739,6 +766,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--kernels", action="store_true",
                     help="only the fixed kernel launches used by the rocprofv3 summaries")
+    ap.add_argument("--layer", action="store_true",
+                    help="only the decoder layer's seven linears, forward and backward, "
+                         "three times (for a rocprofv3 kernel trace)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "bench.py runs on one GPU only: the hot path is measured "
@@ -754,6 +784,9 @@ def main():
     qn.load_library()
     if args.kernels:
         kernels_workload(torch, qn, wl)
+        return
+    if args.layer:
+        layer_workload(torch, qn, wl)
         return
     print(f"[bench] training step: {args.warmup} warmup + {args.steps} timed", file=sys.stderr,
           flush=True)
@@ -782,7 +815,7 @@ def main():
         without_dropout_ms=fwd_med + bwd_med)
     if not args.no_extras:
         print("[bench] extras", file=sys.stderr, flush=True)
-        extras = bench_extras(torch, qn, wl)
+        extras.update(bench_extras(torch, qn, wl))
     cpu = None
     if not args.no_cpu:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)

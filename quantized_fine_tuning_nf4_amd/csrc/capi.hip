@@ -393,7 +393,7 @@ qn_status nf4_dequantize(const qn_nf4dq* w, qn_dtype out_dtype, void* out, void*
   if (!aligned16(out)) return QN_EALIGN;
   return from_hip(launch_dequant(w->packed, w->qscale, w->scale2, w->offset, w->rows * w->cols,
                                  out_dtype == QN_BF16, out, static_cast<hipStream_t>(stream),
-                                 SliceSum{}, w->codebook, w->absmax));
+                                 SliceSum{}, w->codebook, w->absmax, /*nt=*/true));
 }
 
 size_t qlora_linear_workspace_ex(int64_t M, int64_t rows, int64_t cols, int r, int backward,

@@ -46,7 +46,8 @@ struct SliceSum {
 hipError_t launch_dequant(const uint8_t* packed, const uint8_t* qscale, const float* scale2,
                           const float* offset, int64_t n, bool bf16, void* out, hipStream_t st,
                           const SliceSum& ss = SliceSum{nullptr, 0, 0, nullptr},
-                          int codebook = kCodeNF4, const float* absmax = nullptr);
+                          int codebook = kCodeNF4, const float* absmax = nullptr,
+                          bool nt = false);
 
 // Small backward jobs, run by spare workgroups of another launch or alone:
 //   Bt [r, N] = B[N, r]^T and At [K, r] = A[r, K]^T (bf16);

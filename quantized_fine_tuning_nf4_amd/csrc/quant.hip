@@ -459,7 +459,7 @@ hipError_t launch_quantize(const float* W, int64_t n, uint8_t* packed, uint8_t* 
 // is used.  Whole workgroups (every chunk in range) take unconditional
 // loads; only the last workgroup checks bounds, and the kernel branches once
 // around the whole body, so no loaded value meets a branch join.
-template <bool BF16, bool FULL, bool ABS>
+template <bool BF16, bool FULL, bool ABS, bool NT>
 __device__ __forceinline__ void dequant_chunks(const uint8_t* __restrict__ packed,
                                                const uint8_t* __restrict__ qscale,
                                                const float* __restrict__ scale2,
@@ -505,10 +505,10 @@ __device__ __forceinline__ void dequant_chunks(const uint8_t* __restrict__ packe
       if (FULL || e + CH <= n) {
         u32x4 q = {pack_bf16x2(w[0], w[1]), pack_bf16x2(w[2], w[3]), pack_bf16x2(w[4], w[5]),
                    pack_bf16x2(w[6], w[7])};
-        // written once and not read back by this kernel: non-temporal
-        // stores (8.3 against 11.4 us at 4096x4096 bf16; 13.0 against 17.3
-        // fp32)
-        __builtin_nontemporal_store(q, reinterpret_cast<u32x4*>(o));
+        if (NT)
+          __builtin_nontemporal_store(q, reinterpret_cast<u32x4*>(o));
+        else
+          *reinterpret_cast<u32x4*>(o) = q;
       } else {
         for (int k = 0; k < CH && e + k < n; ++k)
           o[k] = (uint16_t)(pack_bf16x2(w[k], 0.f) & 0xffffu);
@@ -517,7 +517,10 @@ __device__ __forceinline__ void dequant_chunks(const uint8_t* __restrict__ packe
       float* o = reinterpret_cast<float*>(out) + e;
       if (FULL || e + CH <= n) {
         const f32x4 q = {w[0], w[1], w[2], w[3]};
-        __builtin_nontemporal_store(q, reinterpret_cast<f32x4*>(o));
+        if (NT)
+          __builtin_nontemporal_store(q, reinterpret_cast<f32x4*>(o));
+        else
+          *reinterpret_cast<f32x4*>(o) = q;
       } else {
         for (int k = 0; k < CH && e + k < n; ++k) o[k] = w[k];
       }
@@ -525,7 +528,12 @@ __device__ __forceinline__ void dequant_chunks(const uint8_t* __restrict__ packe
   }
 }
 
-template <bool BF16, int CB, bool ABS>
+// NT: non-temporal stores, for a copy that is written once and not read
+// back soon (the caller's nf4_dequantize: 8.3 against 11.4 us at 4096x4096
+// bf16, 13.0 against 17.3 fp32); the linear calls' own bf16 copy of W',
+// which the GEMM reads next, keeps ordinary stores so that it stays in the
+// memory-side cache.
+template <bool BF16, int CB, bool ABS, bool NT>
 __global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ packed,
                                                  const uint8_t* __restrict__ qscale,
                                                  const float* __restrict__ scale2,
@@ -550,21 +558,25 @@ __global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ pac
   }
   const int64_t last_elem = ((int64_t)blockIdx.x + 1) * 256 * UNROLL * CH;  // one past
   if (last_elem <= n)
-    dequant_chunks<BF16, true, ABS>(packed, qscale, scale2, offset, absmax, n, out, lut);
+    dequant_chunks<BF16, true, ABS, NT>(packed, qscale, scale2, offset, absmax, n, out, lut);
   else
-    dequant_chunks<BF16, false, ABS>(packed, qscale, scale2, offset, absmax, n, out, lut);
+    dequant_chunks<BF16, false, ABS, NT>(packed, qscale, scale2, offset, absmax, n, out, lut);
 }
 
 template <bool BF16, int CB, bool ABS>
 void launch_dq(dim3 grid, hipStream_t st, const uint8_t* packed, const ScaleSrc& sc,
-                      int64_t n, void* out, const SliceSum& ss, unsigned dq_blocks) {
-  hipLaunchKernelGGL((k_dequant<BF16, CB, ABS>), grid, dim3(256), 0, st, packed, sc.qscale,
-                     sc.scale2, sc.offset, sc.absmax, n, out, ss, dq_blocks);
+                      int64_t n, void* out, const SliceSum& ss, unsigned dq_blocks, bool nt) {
+  if (nt)
+    hipLaunchKernelGGL((k_dequant<BF16, CB, ABS, true>), grid, dim3(256), 0, st, packed,
+                       sc.qscale, sc.scale2, sc.offset, sc.absmax, n, out, ss, dq_blocks);
+  else
+    hipLaunchKernelGGL((k_dequant<BF16, CB, ABS, false>), grid, dim3(256), 0, st, packed,
+                       sc.qscale, sc.scale2, sc.offset, sc.absmax, n, out, ss, dq_blocks);
 }
 
 hipError_t launch_dequant(const uint8_t* packed, const uint8_t* qscale, const float* scale2,
                           const float* offset, int64_t n, bool bf16, void* out, hipStream_t st,
-                          const SliceSum& ss, int codebook, const float* absmax) {
+                          const SliceSum& ss, int codebook, const float* absmax, bool nt) {
   const int CH = bf16 ? 8 : 4;
   const int64_t nchunk = (n + CH - 1) / CH;
   const int64_t per_wg = 256 * 4;
@@ -575,18 +587,18 @@ hipError_t launch_dequant(const uint8_t* packed, const uint8_t* qscale, const fl
   const bool fp4 = codebook == kCodeFP4, abs = absmax != nullptr;
   if (bf16) {
     if (fp4)
-      abs ? launch_dq<true, kCodeFP4, true>(g, st, packed, sc, n, out, ss, grid)
-          : launch_dq<true, kCodeFP4, false>(g, st, packed, sc, n, out, ss, grid);
+      abs ? launch_dq<true, kCodeFP4, true>(g, st, packed, sc, n, out, ss, grid, nt)
+          : launch_dq<true, kCodeFP4, false>(g, st, packed, sc, n, out, ss, grid, nt);
     else
-      abs ? launch_dq<true, kCodeNF4, true>(g, st, packed, sc, n, out, ss, grid)
-          : launch_dq<true, kCodeNF4, false>(g, st, packed, sc, n, out, ss, grid);
+      abs ? launch_dq<true, kCodeNF4, true>(g, st, packed, sc, n, out, ss, grid, nt)
+          : launch_dq<true, kCodeNF4, false>(g, st, packed, sc, n, out, ss, grid, nt);
   } else {
     if (fp4)
-      abs ? launch_dq<false, kCodeFP4, true>(g, st, packed, sc, n, out, ss, grid)
-          : launch_dq<false, kCodeFP4, false>(g, st, packed, sc, n, out, ss, grid);
+      abs ? launch_dq<false, kCodeFP4, true>(g, st, packed, sc, n, out, ss, grid, nt)
+          : launch_dq<false, kCodeFP4, false>(g, st, packed, sc, n, out, ss, grid, nt);
     else
-      abs ? launch_dq<false, kCodeNF4, true>(g, st, packed, sc, n, out, ss, grid)
-          : launch_dq<false, kCodeNF4, false>(g, st, packed, sc, n, out, ss, grid);
+      abs ? launch_dq<false, kCodeNF4, true>(g, st, packed, sc, n, out, ss, grid, nt)
+          : launch_dq<false, kCodeNF4, false>(g, st, packed, sc, n, out, ss, grid, nt);
   }
   return hipGetLastError();
 }
@@ -670,7 +682,7 @@ __global__ __launch_bounds__(256) void k_dequant_t(const uint8_t* __restrict__ p
     const int k = 16 * h + (t >> 4);
     const u32x4 v = *reinterpret_cast<const u32x4*>(tile + k * DQT_PITCH + 16 * c);
     const int64_t kk = kq * DQT_K + k;
-    if (col < ldt && kk < cols) __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(out + kk * ldt + col));
+    if (col < ldt && kk < cols) *reinterpret_cast<u32x4*>(out + kk * ldt + col) = v;
   }
 }
 
