@@ -197,6 +197,25 @@ def _median_min(xs):
     return s[len(s) // 2], s[0]
 
 
+SETTLE_S = 0.05
+
+
+def settle(torch, fn, seconds):
+    """Run fn untimed until `seconds` of wall time have passed (at least
+    once), synchronizing at the end; returns how many calls ran."""
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        fn(n)
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
+            if time.perf_counter() - t0 >= seconds:
+                break
+    torch.cuda.synchronize()
+    return n
+
+
 def bench_train(torch, qn, wl, steps, warmup):
     cfg = wl.TRAIN
     N, K, M, r, alpha = cfg["rows"], cfg["cols"], cfg["M"], cfg["r"], cfg["alpha"]
@@ -220,6 +239,11 @@ def bench_train(torch, qn, wl, steps, warmup):
         _, u = qn.qlora_linear_fwd(st, xd, Ad, Bd, alpha, y=y, workspace=fws)
         return (u,) + qn.qlora_linear_bwd(st, xd, Gd, Ad, Bd, alpha, u, workspace=bws)
 
+    # clocks settle first: the chip reaches its sustained clock only after
+    # tens of milliseconds of this load (measured: 0.525-0.534 ms per step
+    # after 3 warm-up steps, 0.486-0.487 after 50, on one box), so the step
+    # runs untimed for at least SETTLE_S before the warm-up steps proper
+    settle_steps = settle(torch, step, SETTLE_S)
     # the step as issued from Python, call by call
     probe = DeviceProbe(torch)
     eager = time_window(step, range(warmup + steps), lambda _: 1, warmup, probe)
@@ -231,6 +255,9 @@ def bench_train(torch, qn, wl, steps, warmup):
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         outs = step(0)
+    # (building the graph leaves the chip idle long enough for its clocks to
+    # drop again: the replays settle the same way)
+    settle_steps += settle(torch, lambda _: graph.replay(), SETTLE_S)
     probe = DeviceProbe(torch)
     win = time_window(lambda _: graph.replay(), range(warmup + steps), lambda _: 1, warmup, probe)
     if int(flag.item()) != 0:
@@ -241,6 +268,7 @@ def bench_train(torch, qn, wl, steps, warmup):
     flops = fwd_flops(M, N, K, r) + bwd_flops(M, N, K, r)
     secs, nsteps = win.seconds, win.steps
     res = dict(seconds=secs, steps=nsteps, ms_per_step=1e3 * secs / nsteps,
+               settle_steps=settle_steps, settle_s=SETTLE_S,
                tflops=flops * nsteps / secs / 1e12, flops_per_step=flops,
                device_ms_per_step=1e3 * probe.device_seconds / nsteps,
                eager_ms_per_step=1e3 * eager.seconds / eager.steps,
@@ -280,7 +308,7 @@ def bench_train(torch, qn, wl, steps, warmup):
 
     for f in (fwd, bwd, gemm):
         f(0)
-    torch.cuda.synchronize()
+    settle(torch, lambda i: (fwd(i), bwd(i)), SETTLE_S)
     fwd_ms = [_event_time_ms(torch, fwd, 20) for _ in range(5)]
     bwd_ms = [_event_time_ms(torch, bwd, 20) for _ in range(5)]
     gemm_ms = [_event_time_ms(torch, gemm, 20) for _ in range(5)]
@@ -830,7 +858,10 @@ def main():
                    "step": "nf4_quantize_dq (device non-finite flag) + nf4_dequantize(bf16) + "
                            "qlora_linear_fwd + qlora_linear_bwd, captured once in a HIP graph "
                            "and replayed once per step", "flops_per_step": tr["flops_per_step"],
-                   "eager_ms_per_step": tr["eager_ms_per_step"]},
+                   "eager_ms_per_step": tr["eager_ms_per_step"],
+                   "settle": f"{tr['settle_steps']} untimed steps ({tr['settle_s']} s before "
+                             f"the eager and again before the graph-replay timing) ahead of "
+                             f"the {args.warmup} warm-up steps, for sustained clocks"},
         "roofline": roof,
         "cpu_baseline": cpu,
         "extras": extras,
