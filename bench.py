@@ -192,6 +192,13 @@ def _event_time_ms(torch, fn, iters):
     return e0.elapsed_time(e1) / iters
 
 
+def _settled_times(torch, fn, iters, reps):
+    """`reps` event timings of `iters` calls of fn each (ms per call), after
+    running fn untimed for SETTLE_S / 2 so that the clocks have settled."""
+    settle(torch, fn, SETTLE_S / 2)
+    return [_event_time_ms(torch, fn, iters) for _ in range(reps)]
+
+
 def _median_min(xs):
     s = sorted(xs)
     return s[len(s) // 2], s[0]
@@ -331,8 +338,7 @@ def bench_train(torch, qn, wl, steps, warmup):
 
     fwd_bwd_dropout(0)
     torch.cuda.synchronize()
-    res["fwd_bwd_dropout_ms"] = _median_min([_event_time_ms(torch, fwd_bwd_dropout, 10)
-                                             for _ in range(5)])
+    res["fwd_bwd_dropout_ms"] = _median_min(_settled_times(torch, fwd_bwd_dropout, 10, 5))
     res["fwd_flops"] = fwd_flops(M, N, K, r)
     res["bwd_flops"] = bwd_flops(M, N, K, r)
     res["gemm_flops"] = gemm_flops(M, N, K, r)
@@ -349,18 +355,16 @@ def bench_extras(torch, qn, wl):
     states = [qn.nf4_quantize_dq(W2) for _ in range(R)]
     outs = [torch.empty((4096, 4096), dtype=torch.bfloat16, device="cuda") for _ in range(R)]
     torch.cuda.synchronize()
-    ms = [_event_time_ms(torch, lambda i: qn.nf4_dequantize(states[i % R], torch.bfloat16,
-                                                             out=outs[i % R]), 48)
-          for _ in range(5)]
+    ms = _settled_times(torch, lambda i: qn.nf4_dequantize(states[i % R], torch.bfloat16,
+                                                             out=outs[i % R]), 48, 5)
     med, mn = _median_min(ms)
     nbytes = dequant_bytes(4096, 4096, 2)
     out["dequant_bf16_4096x4096"] = dict(ms=med, ms_min=mn, bytes=nbytes,
                                          GBs=nbytes / med / 1e6,
                                          hbm_frac=nbytes / med / 1e6 / HBM_PEAK_GBS)
     outs32 = [torch.empty((4096, 4096), dtype=torch.float32, device="cuda") for _ in range(6)]
-    ms = [_event_time_ms(torch, lambda i: qn.nf4_dequantize(states[i % 6], torch.float32,
-                                                             out=outs32[i % 6]), 24)
-          for _ in range(5)]
+    ms = _settled_times(torch, lambda i: qn.nf4_dequantize(states[i % 6], torch.float32,
+                                                             out=outs32[i % 6]), 24, 5)
     med, mn = _median_min(ms)
     nbytes = dequant_bytes(4096, 4096, 4)
     out["dequant_f32_4096x4096"] = dict(ms=med, ms_min=mn, bytes=nbytes,
@@ -377,9 +381,8 @@ def bench_extras(torch, qn, wl):
     for i in range(3):
         qn.nf4_quantize_dq(Ws[i % 6], out=states[i % R], workspace=qws, nonfinite=flag)
     torch.cuda.synchronize()
-    ms = [_event_time_ms(torch, lambda i: qn.nf4_quantize_dq(Ws[i % 6], out=states[i % R],
-                                                             workspace=qws, nonfinite=flag), 24)
-          for _ in range(5)]
+    ms = _settled_times(torch, lambda i: qn.nf4_quantize_dq(Ws[i % 6], out=states[i % R],
+                                                             workspace=qws, nonfinite=flag), 24, 5)
     med, mn = _median_min(ms)
     assert int(flag.item()) == 0
     t0 = time.perf_counter()
@@ -399,14 +402,12 @@ def bench_extras(torch, qn, wl):
         # as for the NF4 figures above
         sts = [qn.qn_quantize(Ws[i % 6], codebook=cb, double_quant=dq) for i in range(12)]
         torch.cuda.synchronize()
-        qms = [_event_time_ms(torch, lambda i: qn.qn_quantize(
-            Ws[i % 6], codebook=cb, double_quant=dq, workspace=qws, nonfinite=flag), 24)
-            for _ in range(5)]
+        qms = _settled_times(torch, lambda i: qn.qn_quantize(
+            Ws[i % 6], codebook=cb, double_quant=dq, workspace=qws, nonfinite=flag), 24, 5)
         outs_fmt = [torch.empty((4096, 4096), dtype=torch.bfloat16, device="cuda")
                     for _ in range(12)]
-        dms = [_event_time_ms(torch, lambda i: qn.nf4_dequantize(sts[i % 12], torch.bfloat16,
-                                                                  out=outs_fmt[i % 12]), 48)
-               for _ in range(5)]
+        dms = _settled_times(torch, lambda i: qn.nf4_dequantize(sts[i % 12], torch.bfloat16,
+                                                                  out=outs_fmt[i % 12]), 48, 5)
         sb = sts[0].nbytes()
         qb, db = 4 * 4096 * 4096 + sb, sb + 2 * 4096 * 4096
         qmed, dmed = _median_min(qms)[0], _median_min(dms)[0]
@@ -423,9 +424,8 @@ def bench_extras(torch, qn, wl):
     outs_m = [torch.empty((4096, 4096), dtype=torch.float32, device="cuda") for _ in range(6)]
     qn.nf4_merge_lora(states[0], Am, Bm, 32.0, out=outs_m[0])
     torch.cuda.synchronize()
-    ms = [_event_time_ms(torch, lambda i: qn.nf4_merge_lora(states[i % R], Am, Bm, 32.0,
-                                                             out=outs_m[i % 6]), 24)
-          for _ in range(5)]
+    ms = _settled_times(torch, lambda i: qn.nf4_merge_lora(states[i % R], Am, Bm, 32.0,
+                                                             out=outs_m[i % 6]), 24, 5)
     med, mn = _median_min(ms)
     nbytes = merge_bytes(4096, 4096, 16)
     out["merge_lora_4096x4096_r16"] = dict(ms=med, ms_min=mn, bytes=nbytes, GBs=nbytes / med / 1e6,
@@ -459,7 +459,7 @@ def bench_extras(torch, qn, wl):
                                us[i % R].data_ptr(), ws.data_ptr(), ws.numel(), stream)
         call(0)
         torch.cuda.synchronize()
-        ms = [_event_time_ms(torch, call, 100) for _ in range(5)]
+        ms = _settled_times(torch, call, 100, 5)
         med, mn = _median_min(ms)
         # the same R calls captured in one HIP graph: the GPU time of a decode
         # forward without the host's per-launch cost
@@ -472,7 +472,7 @@ def bench_extras(torch, qn, wl):
                                    torch.cuda.current_stream().cuda_stream)
         g.replay()
         torch.cuda.synchronize()
-        gms = [_event_time_ms(torch, lambda _: g.replay(), 10) / R for _ in range(5)]
+        gms = [t / R for t in _settled_times(torch, lambda _: g.replay(), 10, 5)]
         gmed, gmn = _median_min(gms)
         nbytes = decode_bytes(N, K, M, r)
         dec[f"M{M}"] = dict(ms=med, ms_min=mn, graph_ms=gmed, graph_ms_min=gmn, bytes=nbytes,
@@ -492,7 +492,7 @@ def bench_extras(torch, qn, wl):
     opt = qn.Adam8(pa, lr=2e-4)
     opt.step(ga, pab)
     torch.cuda.synchronize()
-    ms = [_event_time_ms(torch, lambda i: opt.step(ga, pab), 50) for _ in range(5)]
+    ms = _settled_times(torch, lambda i: opt.step(ga, pab), 50, 5)
     med, mn = _median_min(ms)
     nbytes = n_ad * (4 + 4 + 4 + 2 + 2 + 2) + 4 * 4 * ((n_ad + 255) // 256)
     out["adamw8_step_decoder_layer_adapters"] = dict(
@@ -521,7 +521,7 @@ def bench_extras(torch, qn, wl):
                                 workspace=d["bws"])
     layer_step(0)
     torch.cuda.synchronize()
-    ms = [_event_time_ms(torch, layer_step, 3) for _ in range(5)]
+    ms = _settled_times(torch, layer_step, 3, 5)
     med, mn = _median_min(ms)
     flops = sum(fwd_flops(M, d["N"], d["K"], r) + bwd_flops(M, d["N"], d["K"], r) for d in layers)
     # each linear's forward and backward on its own (same inputs, eager calls)
@@ -538,8 +538,8 @@ def bench_extras(torch, qn, wl):
                                 workspace=d["bws"])
         b_call(0)
         torch.cuda.synchronize()
-        fm, _ = _median_min([_event_time_ms(torch, f_call, 5) for _ in range(3)])
-        bm, _ = _median_min([_event_time_ms(torch, b_call, 5) for _ in range(3)])
+        fm, _ = _median_min(_settled_times(torch, f_call, 5, 3))
+        bm, _ = _median_min(_settled_times(torch, b_call, 5, 3))
         ff, bf = fwd_flops(M, N, K, r), bwd_flops(M, N, K, r)
         per[name] = dict(rows=N, cols=K, fwd_route=qn.route(M, N, K, r, False),
                          bwd_route=qn.route(M, N, K, r, True), fwd_ms=fm, bwd_ms=bm,
