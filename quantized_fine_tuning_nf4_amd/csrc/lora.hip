@@ -691,10 +691,14 @@ __global__ void k_sum_slices_tn(TnSum a, TnSum b, int r) {
 // fill the chip (about 512 per product), a multiple of 32 rows each, and
 // small enough that a slice of Z spans less than 2^31 bytes (the kernel
 // addresses one slice through a 32-bit buffer offset).
+// Rows per slice: about 512 workgroups per job, but at most 16 slices per
+// column tile: the tile's last workgroup adds the slices, and with 64 of them
+// (a 1024-column dB at M = 4096) that sum took longer than the products
+// (the k_proj backward's dA/dB launch: 24 us).
 int64_t thin_tn_slice_rows(int64_t M, int64_t P, int r) {
   (void)r;
   const int64_t pt = (P + TN_COLS - 1) / TN_COLS;
-  const int64_t S = (512 + pt - 1) / pt;
+  const int64_t S = std::min<int64_t>((512 + pt - 1) / pt, 16);
   int64_t slice = (M + S - 1) / S;
   slice = (slice + 31) / 32 * 32;
   const int64_t cap = ((((int64_t)1 << 31) - 1) / (2 * P)) / 32 * 32;
