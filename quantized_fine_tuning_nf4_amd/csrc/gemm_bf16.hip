@@ -39,33 +39,35 @@ namespace {
 constexpr int BK = 64, T = 256;
 constexpr int ROWB = BK * 2;  // bytes per tile row per stage (one cache line)
 constexpr int LORA_R = 16;
-// Tile geometry for a wave tile of WT x WT MFMA tiles (16 x 16 each): the
-// workgroup tile is BM x BM, BM = 32 WT.
-template <int WT>
+// Tile geometry for a wave tile of WTM x WTN MFMA tiles (16 x 16 each): the
+// workgroup tile is BM x BN, BM = 32 WTM rows of A, BN = 32 WTN rows of Bm
+// (output columns).
+template <int WTM, int WTN>
 struct Geo {
-  static constexpr int WR = 16 * WT;                 // rows (and columns) per wave
-  static constexpr int BM = 2 * WR;                  // workgroup tile rows and columns
-  static constexpr int OPB = BM * ROWB;              // bytes per operand per stage
-  static constexpr int STB = 2 * OPB;                // bytes per stage
-  static constexpr int OUTP = WR * 2 + 16;           // epilogue staging row pitch (bytes)
-  static constexpr int OUTW = WR * OUTP;             // staging bytes per wave
+  static constexpr int WRM = 16 * WTM, WRN = 16 * WTN;  // rows and columns per wave
+  static constexpr int BM = 2 * WRM, BN = 2 * WRN;      // workgroup tile
+  static constexpr int OPA = BM * ROWB, OPB = BN * ROWB;  // bytes per operand per stage
+  static constexpr int STB = OPA + OPB;                 // bytes per stage
+  static constexpr int OUTP = WRN * 2 + 16;             // epilogue staging row pitch (bytes)
+  static constexpr int OUTW = WRM * OUTP;               // staging bytes per wave
+  static constexpr int LPS = WTM + WTN;                 // loads per wave and step
   // LDS stages: a 128 x 128 tile's step is a quarter of a 256 x 256 one's
   // MFMA time, so its loads go out three steps ahead instead of one
-  static constexpr int NST = WT == 8 ? 2 : 4;
+  static constexpr int NST = WTM == 8 ? 2 : 4;
   static constexpr size_t LDS_MAIN = (size_t)NST * STB > (size_t)4 * OUTW ? (size_t)NST * STB
                                                                          : (size_t)4 * OUTW;
   // the LoRA operands of a tile for r == 16, above the stages and the
   // staging tiles: V rows m0 .. m0 + BM - 1 (fp32, 64 B each), then L rows
-  // c0 .. c0 + BM - 1 (bf16, 32 B each)
+  // c0 .. c0 + BN - 1 (bf16, 32 B each)
   static constexpr size_t LDS_V = LDS_MAIN, LDS_L = LDS_V + BM * LORA_R * 4;
-  static constexpr size_t LDS_BYTES = LDS_L + BM * LORA_R * 2;
+  static constexpr size_t LDS_BYTES = LDS_L + BN * LORA_R * 2;
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
   static_assert(NST == 2 || NST == 4, "stages");
-  // the loads of one operand and step: WT instructions per wave, each eight
-  // whole rows; the load slots of a step's second half where they go out
-  static constexpr int J1 = WT == 8 ? 3 : 1, J2 = WT == 8 ? 6 : 3;
-  // workgroups per compute unit the launch bounds ask for
-  static constexpr int OCC = 1;
+  static_assert(WTN <= WTM && WTN >= WTM / 2, "load slots");
+  // the loads of a step: WTM instructions of A rows and WTN of Bm rows per
+  // wave, each eight whole rows; two load slots per row of the second half's
+  // MFMAs, at these columns
+  static constexpr int J1 = WTM == 8 ? 3 : 1, J2 = WTM == 8 ? 6 : 3;
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -99,15 +101,15 @@ __device__ __forceinline__ void wait_all_loads() { asm volatile("s_waitcnt vmcnt
 // LORA16: r == 16, the LoRA operands prefetched into LDS; otherwise read in
 // the tail from global memory (one tail per instance keeps the registers of
 // the other out of the kernel).
-template <bool LORA16, int WT>
-__global__ __launch_bounds__(T, Geo<WT>::OCC) void k_gemm_nt(
+template <bool LORA16, int WTM, int WTN>
+__global__ __launch_bounds__(T, 1) void k_gemm_nt(
     const uint16_t* __restrict__ A, int64_t lda, int64_t R, const uint16_t* __restrict__ Bm,
     int64_t ldb, int steps, int64_t M, int64_t Nc, const float* __restrict__ V,
     const uint16_t* __restrict__ L, int r, float s, uint16_t* __restrict__ C, int tiles_m,
     int tiles_c) {
-  using G = Geo<WT>;
-  constexpr int BM = G::BM, BN = G::BM, WR = G::WR, OPB = G::OPB, STB = G::STB;
-  constexpr int OUTP = G::OUTP, OUTW = G::OUTW, NST = G::NST;
+  using G = Geo<WTM, WTN>;
+  constexpr int BM = G::BM, BN = G::BN, WRM = G::WRM, WRN = G::WRN, OPA = G::OPA, STB = G::STB;
+  constexpr int OUTP = G::OUTP, OUTW = G::OUTW, NST = G::NST, LPS = G::LPS;
   constexpr size_t LDS_V = G::LDS_V, LDS_L = G::LDS_L;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -136,21 +138,27 @@ __global__ __launch_bounds__(T, Geo<WT>::OCC) void k_gemm_nt(
   const int64_t mrows = min((int64_t)BM, M - m0), ncols = min((int64_t)BN, Nc - c0);
 
   // ---- loads: a stage holds 64 reduction elements (128-byte rows, one
-  // cache line per row and step).  Load instruction i (0..WT-1) of wave w
-  // covers rows 8 WT w + 8i + l/8 of an operand; lane l fills unit l%8 of its row with
+  // cache line per row and step).  Load instruction i (0..WTM-1 for A,
+  // 0..WTN-1 for Bm) of wave w covers rows 8 n w + 8i + l/8 of the operand
+  // (n its instruction count); lane l fills unit l%8 of its row with
   // source chunk (l%8) ^ ((row >> 1) & 7), so the 1 KB it writes is
   // contiguous and the sixteen rows a fragment read touches sit on distinct
   // banks.
   const rsrc_t rsA = make_rs(A + m0 * lda, (uint32_t)(mrows * lda * 2));
   const rsrc_t rsB = make_rs(Bm + c0 * ldb, (uint32_t)(ncols * ldb * 2));
-  uint32_t aoff[WT], boff[WT];
-  int achunk[WT];
+  uint32_t aoff[WTM], boff[WTN];
+  int achunk[WTM];
 #pragma unroll
-  for (int i = 0; i < WT; ++i) {
-    const int64_t row = 8 * WT * wave + 8 * i + (lane >> 3);
+  for (int i = 0; i < WTM; ++i) {
+    const int64_t row = 8 * WTM * wave + 8 * i + (lane >> 3);
     const int chunk = (lane & 7) ^ (int)((row >> 1) & 7);
     achunk[i] = chunk;
     aoff[i] = (uint32_t)((min(row, mrows - 1) * lda + 8 * chunk) * 2);
+  }
+#pragma unroll
+  for (int i = 0; i < WTN; ++i) {
+    const int64_t row = 8 * WTN * wave + 8 * i + (lane >> 3);
+    const int chunk = (lane & 7) ^ (int)((row >> 1) & 7);
     boff[i] = (uint32_t)((min(row, ncols - 1) * ldb + 8 * chunk) * 2);
   }
   // A's reduction tail: a chunk past R is moved back onto the row's last
@@ -159,38 +167,40 @@ __global__ __launch_bounds__(T, Geo<WT>::OCC) void k_gemm_nt(
     const int64_t k = (int64_t)st * BK + 8 * achunk[i];
     return (uint32_t)(2 * (k - min(k, R - 8)));
   };
-  // load q (0 .. 2 WT - 1) of step st: q < WT A rows, else B rows
+  // load q (0 .. LPS - 1) of step st: q < WTM A rows, else Bm rows
   auto load_one = [&](int q, int st, int stage) {
-    uint8_t* d = smem + stage * STB + (q >= WT ? OPB : 0) + wave * (1024 * WT) + 1024 * (q % WT);
     const uint32_t so = (uint32_t)st * (BK * 2);
-    if (q < WT)
-      dma16(rsA, aoff[q] - a_back(st, q), so, d);
-    else
-      dma16(rsB, boff[q - WT], so, d);
+    if (q < WTM) {
+      dma16(rsA, aoff[q] - a_back(st, q), so,
+            smem + stage * STB + wave * (1024 * WTM) + 1024 * q);
+    } else {
+      dma16(rsB, boff[q - WTM], so,
+            smem + stage * STB + OPA + wave * (1024 * WTN) + 1024 * (q - WTM));
+    }
   };
 
-  // ---- fragment reads (v_mfma_f32_16x16x32_bf16): tile t of the wave's WR
+  // ---- fragment reads (v_mfma_f32_16x16x32_bf16): tile t of the wave's
   // rows, half h of the stage: lane l reads row 16t + l%16 at chunk
   // 4h + l/16 (eight consecutive reduction elements)
   const int l16 = lane & 15, g4 = lane >> 4;
   int roff[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) roff[h] = l16 * ROWB + 16 * ((4 * h + g4) ^ ((l16 >> 1) & 7));
-  const int abase = wm * WR * ROWB, bbase = OPB + wn * WR * ROWB;
+  const int abase = wm * WRM * ROWB, bbase = OPA + wn * WRN * ROWB;
   auto frag = [&](int stage, int opbase, int t, int h) {
     return as_bf16x8(*reinterpret_cast<const u32x4*>(smem + stage * STB + opbase + t * 16 * ROWB +
                                                      roff[h]));
   };
 
-  f32x4 acc[WT][WT];
+  f32x4 acc[WTM][WTN];
 #pragma unroll
-  for (int i = 0; i < WT; ++i)
+  for (int i = 0; i < WTM; ++i)
 #pragma unroll
-    for (int j = 0; j < WT; ++j) acc[i][j] = f32x4{};
+    for (int j = 0; j < WTN; ++j) acc[i][j] = f32x4{};
 
   // A fragments are replaced in place once their row of MFMAs has issued;
   // B fragments come in two sets (first and second half of a stage)
-  bf16x8 fa[WT], fb[2][WT];
+  bf16x8 fa[WTM], fb[2][WTN];
 
   // ---- the LoRA operands (r == 16) go first, straight into LDS: they land
   // before step 0's loads (loads complete in order), long before the tail
@@ -199,38 +209,40 @@ __global__ __launch_bounds__(T, Geo<WT>::OCC) void k_gemm_nt(
   if constexpr (LORA16) {
     const rsrc_t rsV = make_rs(V + m0 * r, (uint32_t)(mrows * LORA_R * 4));
     const rsrc_t rsL = make_rs(L + c0 * r, (uint32_t)(ncols * LORA_R * 2));
-    // V: BM rows x 64 B = WT / 2 KB per wave; L: BM rows x 32 B = WT / 4 KB
-    constexpr int KV = WT / 2, KL = WT / 4;
+    // V: BM rows x 64 B = WTM / 2 KB per wave; L: BN rows x 32 B = WTN KB,
+    // instruction k from wave k % 4 (rows past Nc read zeros)
+    constexpr int KV = WTM / 2, KL = WTN;
 #pragma unroll
     for (int k = 0; k < KV; ++k)
       dma16(rsV, (uint32_t)(1024 * (KV * wave + k) + 16 * lane), 0,
             smem + LDS_V + 1024 * (KV * wave + k));
 #pragma unroll
-    for (int k = 0; k < KL; ++k)
-      dma16(rsL, (uint32_t)(1024 * (KL * wave + k) + 16 * lane), 0,
-            smem + LDS_L + 1024 * (KL * wave + k));
+    for (int k = 0; k < (KL + 3) / 4; ++k) {
+      const int q = 4 * k + wave;
+      if (q < KL)
+        dma16(rsL, (uint32_t)(1024 * q + 16 * lane), 0, smem + LDS_L + 1024 * q);
+    }
   }
 
   // ---- prologue: steps 0 .. NST-1 in flight, 0 landed (all but the later
-  // steps' 2 WT loads each)
+  // steps' LPS loads each)
 #pragma unroll
   for (int k = 0; k < NST; ++k)
 #pragma unroll
-    for (int q = 0; q < 2 * WT; ++q) load_one(q, min(k, steps - 1), k);
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * WT * (NST - 1)) : "memory");
+    for (int q = 0; q < LPS; ++q) load_one(q, min(k, steps - 1), k);
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LPS * (NST - 1)) : "memory");
   barrier_lds();
 #pragma unroll
-  for (int t = 0; t < WT; ++t) {
-    fa[t] = frag(0, abase, t, 0);
-    fb[0][t] = frag(0, bbase, t, 0);
-  }
+  for (int t = 0; t < WTM; ++t) fa[t] = frag(0, abase, t, 0);
+#pragma unroll
+  for (int t = 0; t < WTN; ++t) fb[0][t] = frag(0, bbase, t, 0);
 
-  // ---- half h of step st on stage P = st % NST: WT x WT MFMAs.  Half 0
+  // ---- half h of step st on stage P = st % NST: WTM x WTN MFMAs.  Half 0
   // reads half 1's fragments from the same stage, then waits for step st+1
   // (sent during half 1 of step st+1-NST; the later steps' loads stay in
   // flight) and meets the other waves: after that barrier no wave reads
   // stage P again.  Half 1 reads the next step's first half from the next
-  // stage and sends the 2 WT loads of step st+NST into stage P.  Half 1
+  // stage and sends the LPS loads of step st+NST into stage P.  Half 1
   // needs no barrier of its own: the next half 0 reads only data that every
   // wave waited for before the barrier above, and writes none.
   auto half = [&](auto p_t, auto h_t, int st) {
@@ -239,14 +251,15 @@ __global__ __launch_bounds__(T, Geo<WT>::OCC) void k_gemm_nt(
     constexpr int RH = H ^ 1;                       // their half
     const int lst = min(st + NST, steps - 1);
 #pragma unroll
-    for (int i = 0; i < WT; ++i) {
+    for (int i = 0; i < WTM; ++i) {
 #pragma unroll
-      for (int j = 0; j < WT; ++j) {
+      for (int j = 0; j < WTN; ++j) {
         mfma16_acc(fb[H][j], fa[i], acc[i][j]);
         // the next half's B fragments are all read during the first row of
         // MFMAs: its first row needs every one of them
         if (i == 0) fb[RH][j] = frag(RS, bbase, j, RH);
-        if (H == 1 && (j == G::J1 || j == G::J2)) load_one(2 * i + (j == G::J2), lst, P);
+        if (H == 1 && (j == G::J1 || j == G::J2) && 2 * i + (j == G::J2) < LPS)
+          load_one(2 * i + (j == G::J2), lst, P);
       }
       fa[i] = frag(RS, abase, i, RH);
       __builtin_amdgcn_sched_barrier(0);
@@ -255,7 +268,7 @@ __global__ __launch_bounds__(T, Geo<WT>::OCC) void k_gemm_nt(
       if constexpr (NST == 2)
         wait_all_loads();
       else
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * WT * (NST - 2)) : "memory");
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LPS * (NST - 2)) : "memory");
       barrier_lds();
     }
   };
@@ -267,20 +280,43 @@ __global__ __launch_bounds__(T, Geo<WT>::OCC) void k_gemm_nt(
     half(p_t, S0{}, st);
     half(p_t, S1{}, st);
   };
+  // Wherever control flow joins after MFMAs (the loop's exit, the end of a
+  // conditional step) the compiler may copy an accumulator to another AGPR
+  // for the join; 32 wait states first let the last products complete (it
+  // cannot know that the asm MFMAs write late: at the 256 x 224 tile's loop
+  // exit it copied the last accumulator 4 cycles after its MFMA issued).
+  // The exit test sits at the end of the body, so the back edge skips them.
+  auto drain = [&]() { asm volatile("s_nop 15\n\ts_nop 15" ::: "memory"); };
   int st = 0;
-  for (; st + NST <= steps; st += NST) {
-    step(S0{}, st);
-    step(S1{}, st + 1);
-    if constexpr (NST == 4) {
-      step(S2{}, st + 2);
-      step(S3{}, st + 3);
+  if (steps >= NST) {
+    for (;;) {
+      step(S0{}, st);
+      step(S1{}, st + 1);
+      if constexpr (NST == 4) {
+        step(S2{}, st + 2);
+        step(S3{}, st + 3);
+      }
+      st += NST;
+      if (st + NST > steps) {
+        drain();
+        break;
+      }
     }
   }
   // the last steps % NST steps, on stages 0, 1, 2 in turn
-  if (st < steps) step(S0{}, st++);
+  if (st < steps) {
+    step(S0{}, st++);
+    drain();
+  }
   if constexpr (NST == 4) {
-    if (st < steps) step(S1{}, st++);
-    if (st < steps) step(S2{}, st++);
+    if (st < steps) {
+      step(S1{}, st++);
+      drain();
+    }
+    if (st < steps) {
+      step(S2{}, st++);
+      drain();
+    }
   }
   // The compiler cannot see that the asm MFMAs write the accumulators some
   // cycles after they issue, so nothing it places may read one before the
@@ -292,9 +328,9 @@ __global__ __launch_bounds__(T, Geo<WT>::OCC) void k_gemm_nt(
   auto settle = [&]() {
     asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");
 #pragma unroll
-    for (int i = 0; i < WT; ++i)
+    for (int i = 0; i < WTM; ++i)
 #pragma unroll
-      for (int j = 0; j < WT; ++j) asm volatile("" : "+a"(acc[i][j]));
+      for (int j = 0; j < WTN; ++j) asm volatile("" : "+a"(acc[i][j]));
   };
   // every wave's loads have landed and all reads are done before the stages
   // are reused for the output staging below
@@ -308,17 +344,17 @@ __global__ __launch_bounds__(T, Geo<WT>::OCC) void k_gemm_nt(
   const bool vec = (r % 8) == 0;
   const bool lo_part = g4 >= 2;
   if constexpr (LORA16) {
-    // from LDS: L row (tile column) wn WR + 16 j + l16, ranks 8 (g4 & 1) ..;
-    // V row (tile row) wm WR + 16 i + l16, the same ranks
+    // from LDS: L row (tile column) wn WRN + 16 j + l16, ranks 8 (g4 & 1) ..;
+    // V row (tile row) wm WRM + 16 i + l16, the same ranks
     const int jb = 8 * (g4 & 1);
-    bf16x8 lh[WT];
+    bf16x8 lh[WTN];
 #pragma unroll
-    for (int j = 0; j < WT; ++j)
+    for (int j = 0; j < WTN; ++j)
       lh[j] = as_bf16x8(*reinterpret_cast<const u32x4*>(
-          smem + LDS_L + (wn * WR + 16 * j + l16) * (LORA_R * 2) + 2 * jb));
+          smem + LDS_L + (wn * WRN + 16 * j + l16) * (LORA_R * 2) + 2 * jb));
 #pragma unroll
-    for (int i = 0; i < WT; ++i) {
-      const uint8_t* vp = smem + LDS_V + (wm * WR + 16 * i + l16) * (LORA_R * 4) + 4 * jb;
+    for (int i = 0; i < WTM; ++i) {
+      const uint8_t* vp = smem + LDS_V + (wm * WRM + 16 * i + l16) * (LORA_R * 4) + 4 * jb;
       const f32x4 v0 = *reinterpret_cast<const f32x4*>(vp);
       const f32x4 v1 = *reinterpret_cast<const f32x4*>(vp + 16);
       const float vr[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
@@ -331,15 +367,15 @@ __global__ __launch_bounds__(T, Geo<WT>::OCC) void k_gemm_nt(
       }
       const bf16x8 av = as_bf16x8(u32x4{w[0], w[1], w[2], w[3]});
 #pragma unroll
-      for (int j = 0; j < WT; ++j) mfma16_acc(lh[j], av, acc[i][j]);
+      for (int j = 0; j < WTN; ++j) mfma16_acc(lh[j], av, acc[i][j]);
     }
   }
   for (int j0 = 0; j0 < (LORA16 ? 0 : r); j0 += 16) {
     const int jl = j0 + 8 * (g4 & 1);
-    bf16x8 lh[WT];
+    bf16x8 lh[WTN];
 #pragma unroll
-    for (int j = 0; j < WT; ++j) {
-      const int64_t col = min(c0 + wn * WR + 16 * j + l16, Nc - 1);
+    for (int j = 0; j < WTN; ++j) {
+      const int64_t col = min(c0 + wn * WRN + 16 * j + l16, Nc - 1);
       const uint16_t* lp = L + col * r;
       if (vec) {
         lh[j] = jl < r ? as_bf16x8(*reinterpret_cast<const u32x4*>(lp + jl)) : bf16x8{};
@@ -352,8 +388,8 @@ __global__ __launch_bounds__(T, Geo<WT>::OCC) void k_gemm_nt(
       }
     }
 #pragma unroll
-    for (int i = 0; i < WT; ++i) {
-      const int64_t m = min(m0 + wm * WR + 16 * i + l16, M - 1);
+    for (int i = 0; i < WTM; ++i) {
+      const int64_t m = min(m0 + wm * WRM + 16 * i + l16, M - 1);
       const float* vp = V + m * r;
       float vr[8];
       if (vec && jl < r) {
@@ -377,22 +413,23 @@ __global__ __launch_bounds__(T, Geo<WT>::OCC) void k_gemm_nt(
       }
       const bf16x8 av = as_bf16x8(u32x4{w[0], w[1], w[2], w[3]});
 #pragma unroll
-      for (int j = 0; j < WT; ++j) mfma16_acc(lh[j], av, acc[i][j]);
+      for (int j = 0; j < WTN; ++j) mfma16_acc(lh[j], av, acc[i][j]);
     }
+    drain();  // (a loop: its exit is a join)
   }
 
   // ---- store.  Tile (i, j) is held transposed: lane l has row 16i + l%16
   // and columns 16j + 4(l/16) .. +3 in its four registers; they go to the
   // wave's LDS staging tile as 8 bytes, and the tile then leaves as rows of
-  // 2 WR contiguous bytes (2 WT lanes of 16 bytes per row).  The staging
+  // 2 WRN contiguous bytes (2 WTN lanes of 16 bytes per row).  The staging
   // tiles overlap the stages, freed by the barrier above.
   uint8_t* stg = smem + wave * OUTW;
   // the last products' results are complete before they are read
   settle();
 #pragma unroll
-  for (int i = 0; i < WT; ++i) {
+  for (int i = 0; i < WTM; ++i) {
 #pragma unroll
-    for (int j = 0; j < WT; ++j) {
+    for (int j = 0; j < WTN; ++j) {
       const f32x4& c = acc[i][j];
       *reinterpret_cast<u32x2*>(stg + (16 * i + l16) * OUTP + 2 * (16 * j + 4 * g4)) =
           u32x2{pack_bf16x2(c[0], c[1]), pack_bf16x2(c[2], c[3])};
@@ -402,47 +439,63 @@ __global__ __launch_bounds__(T, Geo<WT>::OCC) void k_gemm_nt(
   // Streaming (non-temporal) stores: the output is written once and never
   // read here, while the caches still serve other tiles' re-reads of the A
   // and Bm rows; ordinary stores would displace those lines.
-  constexpr int LR = 2 * WT, RPS = 64 / LR;  // lanes per row, rows per store
+  // lanes per row, rows per store (with 14 lanes per row, lanes 56..63 idle)
+  constexpr int LR = 2 * WTN, RPS = 64 / LR;
+  static_assert(WRM % RPS == 0, "store rows");
   const int lc = lane % LR;
-  const int64_t col = c0 + wn * WR + 8 * lc;
+  const bool lane_on = lane < RPS * LR;
+  const int64_t col = c0 + wn * WRN + 8 * lc;
 #pragma unroll
-  for (int q = 0; q < WR / RPS; ++q) {
-    const int rl = RPS * q + lane / LR;
-    const int64_t row = m0 + wm * WR + rl;
+  for (int q = 0; q < WRM / RPS; ++q) {
+    const int rl = RPS * q + min(lane / LR, RPS - 1);
+    const int64_t row = m0 + wm * WRM + rl;
     const u32x4 v = *reinterpret_cast<const u32x4*>(stg + rl * OUTP + 16 * lc);
-    if (row < M && col < Nc)
+    if (lane_on && row < M && col < Nc)
       __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(C + row * Nc + col));
   }
 }
 
 }  // namespace
 
-size_t gemm_nt_lds_bytes() { return Geo<8>::LDS_BYTES; }
+size_t gemm_nt_lds_bytes() { return Geo<8, 8>::LDS_BYTES; }
 
 namespace {
-template <int WT>
+template <int WTM, int WTN>
 hipError_t launch_wt(const uint16_t* A, int64_t lda, int64_t R, const uint16_t* Bm, int64_t ldb,
                      int64_t M, int64_t Nc, const float* V, const uint16_t* L, int r, float s,
                      uint16_t* C, hipStream_t st) {
-  using G = Geo<WT>;
+  using G = Geo<WTM, WTN>;
   static hipError_t attr = [] {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_gemm_nt<true, WT>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_gemm_nt<true, WTM, WTN>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)G::LDS_BYTES);
     if (e != hipSuccess) return e;
-    return hipFuncSetAttribute(reinterpret_cast<const void*>(k_gemm_nt<false, WT>),
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(k_gemm_nt<false, WTM, WTN>),
                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)G::LDS_MAIN);
   }();
   if (attr != hipSuccess) return attr;
-  const int64_t tm = (M + G::BM - 1) / G::BM, tc = (Nc + G::BM - 1) / G::BM;
+  const int64_t tm = (M + G::BM - 1) / G::BM, tc = (Nc + G::BN - 1) / G::BN;
   const int steps = (int)(ldb / BK);
   if (r == LORA_R)
-    hipLaunchKernelGGL((k_gemm_nt<true, WT>), dim3((unsigned)(tm * tc)), dim3(T), G::LDS_BYTES, st,
-                       A, lda, R, Bm, ldb, steps, M, Nc, V, L, r, s, C, (int)tm, (int)tc);
+    hipLaunchKernelGGL((k_gemm_nt<true, WTM, WTN>), dim3((unsigned)(tm * tc)), dim3(T),
+                       G::LDS_BYTES, st, A, lda, R, Bm, ldb, steps, M, Nc, V, L, r, s, C, (int)tm,
+                       (int)tc);
   else
-    hipLaunchKernelGGL((k_gemm_nt<false, WT>), dim3((unsigned)(tm * tc)), dim3(T), G::LDS_MAIN,
-                       st, A, lda, R, Bm, ldb, steps, M, Nc, V, L, r, s, C, (int)tm, (int)tc);
+    hipLaunchKernelGGL((k_gemm_nt<false, WTM, WTN>), dim3((unsigned)(tm * tc)), dim3(T),
+                       G::LDS_MAIN, st, A, lda, R, Bm, ldb, steps, M, Nc, V, L, r, s, C, (int)tm,
+                       (int)tc);
   return hipGetLastError();
+}
+
+int compute_units() {
+  static int cus = [] {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 256;
+    return n > 0 ? n : 256;
+  }();
+  return cus;
 }
 }  // namespace
 
@@ -458,8 +511,17 @@ hipError_t launch_gemm_nt(const uint16_t* A, int64_t lda, int64_t R, const uint1
   // 256 x 256 tiles once there are about as many as compute units; fewer
   // would leave most of the chip idle, so 128 x 128 tiles then
   if (gemm_nt_small_tiles(M, Nc))
-    return launch_wt<4>(A, lda, R, Bm, ldb, M, Nc, V, L, r, s, C, st);
-  return launch_wt<8>(A, lda, R, Bm, ldb, M, Nc, V, L, r, s, C, st);
+    return launch_wt<4, 4>(A, lda, R, Bm, ldb, M, Nc, V, L, r, s, C, st);
+  // 256 x 224 tiles where they take fewer tile-widths of rounds: with 14336
+  // output columns at M = 4096, 896 tiles of 256 fill 3.5 rounds of the
+  // chip and the last round runs half empty, while 1024 tiles of 224 fill
+  // exactly 4 (4 x 224 < 4 x 256 column-widths of time)
+  const int64_t cu = compute_units(), tm = (M + 255) / 256;
+  const int64_t r256 = (tm * ((Nc + 255) / 256) + cu - 1) / cu;
+  const int64_t r224 = (tm * ((Nc + 223) / 224) + cu - 1) / cu;
+  if (r224 * 224 < r256 * 256)
+    return launch_wt<8, 7>(A, lda, R, Bm, ldb, M, Nc, V, L, r, s, C, st);
+  return launch_wt<8, 8>(A, lda, R, Bm, ldb, M, Nc, V, L, r, s, C, st);
 }
 
 }  // namespace qn

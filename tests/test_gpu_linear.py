@@ -146,6 +146,9 @@ def test_train_config_full_size(qn):
     (1000, 1088, 1960, 16),  # 128 x 128 tiles (too few 256 x 256 ones), ragged edges
     (1024, 4096, 4096, 16),  # the decoder layer's k_proj shape: 128 x 128 tiles
     (648, 320, 3000, 7),    # 128 x 128 tiles, scalar adapter loads
+    (7000, 1088, 4000, 16),  # 256 x 224 tiles (448 of 256 would need 2 rounds of 256 wide),
+                             # a 56-column last tile
+    (7168, 576, 4000, 7),   # 256 x 224 tiles, scalar adapter loads
 ])
 def test_dense_lora_linear_bf16(qn, rows, cols, M, r):
     """lora_linear_bf16 on nf4_dequantize's bf16 weight: against the oracle,
