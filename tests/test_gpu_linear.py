@@ -99,6 +99,8 @@ def test_tiny_config(qn):
     (3848, 3840, 4100, 5),  # dense forward and dX: ragged M, N % 32 == 8, rank 5
     (2056, 3904, 4100, 20), # dense dX: K % 256 == 64 (a partial column group in the
                             # transposed dequantization), rank 20 (B^T made first)
+    (4096, 4096, 32832, 16),  # a long batch: u and v in one column slice each (no slice
+                              # sums), 129 GEMM row tiles with a 64-row last one
 ])
 def test_ragged_shapes(qn, rows, cols, M, r):
     c = Case(rows, cols, M, r, 2.0 * r, seed=rows + cols + M)
