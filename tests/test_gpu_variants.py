@@ -79,6 +79,7 @@ def test_rslora_matches_oracle(qn, rows, cols, M, r):
     (520, 576, 300, 16, 0.3),    # 128 x 128 fused GEMM
     (3848, 3840, 4100, 16, 0.05),  # dense GEMM, masked dX add after it
     (1032, 320, 130, 64, 0.5),   # rank 64
+    (4096, 4096, 8192, 16, 0.05),  # the training shape with dropout (as the benchmark times it)
 ])
 def test_dropout_matches_oracle(qn, rows, cols, M, r, p):
     say(f"[variants] dropout rows={rows} cols={cols} M={M} r={r} p={p} "
