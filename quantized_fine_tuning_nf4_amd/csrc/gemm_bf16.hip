@@ -100,8 +100,11 @@ __device__ __forceinline__ void wait_all_loads() { asm volatile("s_waitcnt vmcnt
 
 // LORA16: r == 16, the LoRA operands prefetched into LDS; otherwise read in
 // the tail from global memory (one tail per instance keeps the registers of
-// the other out of the kernel).
-template <bool LORA16, int WTM, int WTN>
+// the other out of the kernel).  ATAIL: the reduction length R is shorter
+// than the steps cover (R < ldb), so A's chunks past R are moved back; with
+// R == ldb the A loads need no address arithmetic per step (the 64-bit
+// clamp in the loop cost 12% of the main loop's cycles at 8192x4096x4096).
+template <bool LORA16, int WTM, int WTN, bool ATAIL>
 __global__ __launch_bounds__(T, 1) void k_gemm_nt(
     const uint16_t* __restrict__ A, int64_t lda, int64_t R, const uint16_t* __restrict__ Bm,
     int64_t ldb, int steps, int64_t M, int64_t Nc, const float* __restrict__ V,
@@ -164,6 +167,7 @@ __global__ __launch_bounds__(T, 1) void k_gemm_nt(
   // A's reduction tail: a chunk past R is moved back onto the row's last
   // chunk (its Bm partner is zero)
   auto a_back = [&](int st, int i) {
+    if constexpr (!ATAIL) return 0u;
     const int64_t k = (int64_t)st * BK + 8 * achunk[i];
     return (uint32_t)(2 * (k - min(k, R - 8)));
   };
@@ -466,24 +470,35 @@ hipError_t launch_wt(const uint16_t* A, int64_t lda, int64_t R, const uint16_t* 
                      uint16_t* C, hipStream_t st) {
   using G = Geo<WTM, WTN>;
   static hipError_t attr = [] {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_gemm_nt<true, WTM, WTN>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)G::LDS_BYTES);
-    if (e != hipSuccess) return e;
-    return hipFuncSetAttribute(reinterpret_cast<const void*>(k_gemm_nt<false, WTM, WTN>),
-                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)G::LDS_MAIN);
+    const void* k16[2] = {reinterpret_cast<const void*>(k_gemm_nt<true, WTM, WTN, false>),
+                          reinterpret_cast<const void*>(k_gemm_nt<true, WTM, WTN, true>)};
+    const void* kr[2] = {reinterpret_cast<const void*>(k_gemm_nt<false, WTM, WTN, false>),
+                         reinterpret_cast<const void*>(k_gemm_nt<false, WTM, WTN, true>)};
+    for (int t = 0; t < 2; ++t) {
+      hipError_t e = hipFuncSetAttribute(k16[t], hipFuncAttributeMaxDynamicSharedMemorySize,
+                                         (int)G::LDS_BYTES);
+      if (e == hipSuccess)
+        e = hipFuncSetAttribute(kr[t], hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)G::LDS_MAIN);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
   }();
   if (attr != hipSuccess) return attr;
   const int64_t tm = (M + G::BM - 1) / G::BM, tc = (Nc + G::BN - 1) / G::BN;
   const int steps = (int)(ldb / BK);
-  if (r == LORA_R)
-    hipLaunchKernelGGL((k_gemm_nt<true, WTM, WTN>), dim3((unsigned)(tm * tc)), dim3(T),
-                       G::LDS_BYTES, st, A, lda, R, Bm, ldb, steps, M, Nc, V, L, r, s, C, (int)tm,
-                       (int)tc);
-  else
-    hipLaunchKernelGGL((k_gemm_nt<false, WTM, WTN>), dim3((unsigned)(tm * tc)), dim3(T),
-                       G::LDS_MAIN, st, A, lda, R, Bm, ldb, steps, M, Nc, V, L, r, s, C, (int)tm,
-                       (int)tc);
+  const dim3 grid((unsigned)(tm * tc)), block(T);
+#define QN_GEMM(L16, TAIL)                                                                     \
+  hipLaunchKernelGGL((k_gemm_nt<L16, WTM, WTN, TAIL>), grid, block,                           \
+                     L16 ? G::LDS_BYTES : G::LDS_MAIN, st, A, lda, R, Bm, ldb, steps, M, Nc, V, \
+                     L, r, s, C, (int)tm, (int)tc)
+  const bool tail = R != ldb;
+  if (r == LORA_R) {
+    if (tail) QN_GEMM(true, true); else QN_GEMM(true, false);
+  } else {
+    if (tail) QN_GEMM(false, true); else QN_GEMM(false, false);
+  }
+#undef QN_GEMM
   return hipGetLastError();
 }
 

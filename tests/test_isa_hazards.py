@@ -136,7 +136,8 @@ def test_gemm_reads_no_accumulator_early():
         asm = [f for f in os.listdir(d) if f.endswith("gfx950.s")]
         assert asm, os.listdir(d)
         kernels = _kernels(open(os.path.join(d, asm[0])).read())
-    assert len(kernels) >= 6, sorted(kernels)
+    # 3 tile shapes x (r == 16 or not) x (reduction tail or not)
+    assert len(kernels) >= 12, sorted(kernels)
     for name, lines in kernels.items():
         assert sum(t.startswith("v_mfma") for t in lines) > 0, name
         h = _hazards(lines)
