@@ -66,8 +66,10 @@ struct Geo {
   static_assert(WTN <= WTM && WTN >= WTM / 2, "load slots");
   // the loads of a step: WTM instructions of A rows and WTN of Bm rows per
   // wave, each eight whole rows; two load slots per row of the second half's
-  // MFMAs, at these columns
-  static constexpr int J1 = WTM == 8 ? 3 : 1, J2 = WTM == 8 ? 6 : 3;
+  // MFMAs, at these columns (with seven columns, off the row's last one: a
+  // load issued just before the row's fragment read cost ~45 cycles a step)
+  static constexpr int J1 = WTM == 8 ? (WTN == 7 ? 2 : 3) : 1;
+  static constexpr int J2 = WTM == 8 ? (WTN == 7 ? 5 : 6) : 3;
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
