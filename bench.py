@@ -514,14 +514,26 @@ def bench_extras(torch, qn, wl):
                            y=torch.empty((M, N), dtype=torch.bfloat16, device="cuda")))
 
     def layer_step(_):
+        outs = []
         for d in layers:
             _, u = qn.qlora_linear_fwd(d["st"], d["x"], d["A"], d["B"], alpha, y=d["y"],
                                        workspace=d["fws"])
-            qn.qlora_linear_bwd(d["st"], d["x"], d["G"], d["A"], d["B"], alpha, u,
-                                workspace=d["bws"])
-    layer_step(0)
+            outs += [u] + list(qn.qlora_linear_bwd(d["st"], d["x"], d["G"], d["A"], d["B"],
+                                                   alpha, u, workspace=d["bws"]))
+        return outs
+    ref = [t.clone() for t in layer_step(0)] + [d["y"].clone() for d in layers]
     torch.cuda.synchronize()
-    ms = _settled_times(torch, layer_step, 3, 5)
+    # as issued from Python, call by call
+    eager_med, eager_mn = _median_min(_settled_times(torch, layer_step, 3, 5))
+    # the fourteen calls captured once in a HIP graph and replayed (no host
+    # work between the kernels), as the training step is timed
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        gouts = layer_step(0)
+    ms = _settled_times(torch, lambda _: graph.replay(), 3, 5)
+    if not all(torch.equal(a, b) for a, b in zip(gouts + [d["y"] for d in layers], ref)):
+        raise RuntimeError("graph replay of the decoder layer differs from the eager calls")
+    del graph, gouts, ref
     med, mn = _median_min(ms)
     flops = sum(fwd_flops(M, d["N"], d["K"], r) + bwd_flops(M, d["N"], d["K"], r) for d in layers)
     # each linear's forward and backward on its own (same inputs, eager calls)
@@ -545,7 +557,8 @@ def bench_extras(torch, qn, wl):
                          bwd_route=qn.route(M, N, K, r, True), fwd_ms=fm, bwd_ms=bm,
                          fwd_mfma_frac=ff / fm / 1e9 / BF16_PEAK_TFLOPS,
                          bwd_mfma_frac=bf / bm / 1e9 / BF16_PEAK_TFLOPS)
-    out["decoder_layer_7_linears_M4096"] = dict(ms=med, ms_min=mn, flops=flops,
+    out["decoder_layer_7_linears_M4096"] = dict(ms=med, ms_min=mn, eager_ms=eager_med,
+                                                eager_ms_min=eager_mn, flops=flops,
                                                 TFLOPs=flops / med / 1e9,
                                                 mfma_frac=flops / med / 1e9 / BF16_PEAK_TFLOPS,
                                                 adapter_params=wl.adapter_params(r=r),
