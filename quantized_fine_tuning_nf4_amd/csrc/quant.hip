@@ -322,9 +322,11 @@ __global__ __launch_bounds__(1024) void k_quant_mean(double* __restrict__ part, 
 // same mu itself (the stride-halving tree over the group partials zero-padded
 // to len: levels of 256 entries and more inside each thread, then LDS, then
 // lane shuffles, with the same additions in the same order as
-// pass 2; up to 2048 groups), and workgroup 0 writes offset and the
-// non-finite flag.
-template <bool FUSED>
+// pass 2; up to 2048 groups, NQ partials per thread: 4 up to 1024 groups, 8
+// above), and workgroup 0 writes offset and the non-finite flag.  (Loading 8
+// per thread at 1024 groups, half of them the last partial again, cost 0.5 us
+// per call.)
+template <bool FUSED, int NQ>
 __global__ __launch_bounds__(256) void k_quant_dq(const float* __restrict__ absmax, int64_t nb,
                                                   float* __restrict__ offset,
                                                   uint8_t* __restrict__ qscale,
@@ -340,19 +342,19 @@ __global__ __launch_bounds__(256) void k_quant_dq(const float* __restrict__ absm
   // would otherwise keep the load behind it)
   const int64_t b = (int64_t)blockIdx.x * kGroup + tid;
   const float sb = b < nb ? absmax[b] : 0.f;
-  // workgroup 0 also reads the groups' non-finite flags up front (ng <= 2048
-  // when FUSED: at most eight per thread)
+  // workgroup 0 also reads the groups' non-finite flags up front (ng <= 256 NQ
+  // when FUSED: at most NQ per thread)
   // (every load below is unconditional, at an index clamped into range, and
   // the values past the end are dropped afterwards: a load under its own
   // condition gets its own branch and a wait of its own, which put eight
   // round trips in series)
   int any_bad = 0;
   if (FUSED && blockIdx.x == 0) {
-    int fl[8];
+    int fl[NQ];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) fl[q] = bad[min((int64_t)tid + 256 * q, ng - 1)];
+    for (int q = 0; q < NQ; ++q) fl[q] = bad[min((int64_t)tid + 256 * q, ng - 1)];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) any_bad |= fl[q];
+    for (int q = 0; q < NQ; ++q) any_bad |= fl[q];
   }
   float mu;
   if constexpr (FUSED) {
@@ -360,13 +362,13 @@ __global__ __launch_bounds__(256) void k_quant_dq(const float* __restrict__ absm
     // levels h >= 256 pair entries of one thread, h = 128 and 64 go through
     // LDS, h <= 32 through lane shuffles: t[j] + t[j + h] at every level,
     // as in pass 2
-    // len <= 2048 here: one partial per stage entry
+    // len <= 256 NQ here: one partial per stage entry
     const int64_t active = len;
-    double v[8];
+    double v[NQ];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) v[q] = part[min((int64_t)tid + 256 * q, ng - 1)];
+    for (int q = 0; q < NQ; ++q) v[q] = part[min((int64_t)tid + 256 * q, ng - 1)];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
+    for (int q = 0; q < NQ; ++q) {
       const int64_t j = tid + 256 * q;
       if (!(256 * q < active && j < ng)) v[q] = 0.0;
     }
@@ -374,7 +376,7 @@ __global__ __launch_bounds__(256) void k_quant_dq(const float* __restrict__ absm
     for (; h >= 256; h /= 2) {
       const int64_t qh = h / 256;
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
+      for (int q = 0; q < NQ / 2; ++q)
         if (q < qh) v[q] += v[q + qh];
     }
     double x = v[0];
@@ -437,14 +439,17 @@ hipError_t launch_quantize(const float* W, int64_t n, uint8_t* packed, uint8_t* 
                        ws_offset, ws_bad, flag);
     return hipGetLastError();
   }
-  if (part_len <= 2048) {
+  if (part_len <= 1024) {
     // the mean inside the scale pass: one launch fewer
-    hipLaunchKernelGGL(k_quant_dq<true>, dim3((unsigned)ng), dim3(256), 0, st, ws_absmax, nb,
+    hipLaunchKernelGGL((k_quant_dq<true, 4>), dim3((unsigned)ng), dim3(256), 0, st, ws_absmax, nb,
+                       offset, qscale, scale2, ws_part, ng, part_len, ws_bad, flag);
+  } else if (part_len <= 2048) {
+    hipLaunchKernelGGL((k_quant_dq<true, 8>), dim3((unsigned)ng), dim3(256), 0, st, ws_absmax, nb,
                        offset, qscale, scale2, ws_part, ng, part_len, ws_bad, flag);
   } else {
     hipLaunchKernelGGL(k_quant_mean, dim3(1), dim3(1024), 0, st, ws_part, ng, part_len, nb,
                        offset, ws_bad, flag);
-    hipLaunchKernelGGL(k_quant_dq<false>, dim3((unsigned)ng), dim3(256), 0, st, ws_absmax, nb,
+    hipLaunchKernelGGL((k_quant_dq<false, 1>), dim3((unsigned)ng), dim3(256), 0, st, ws_absmax, nb,
                        offset, qscale, scale2, ws_part, ng, part_len, ws_bad, flag);
   }
   return hipGetLastError();

@@ -62,6 +62,14 @@ def test_quant_parity_outlier_config(qn):
     assert np.all(Wd[2048, 33 * 64:34 * 64] == Wd[2048, 33 * 64]) and Wd[2048, 33 * 64] > 0
 
 
+@pytest.mark.parametrize("rows,cols", [(4104, 4096), (8192, 4096)])
+def test_quant_parity_mid_mean_tree(qn, rows, cols):
+    """1024 < ng <= 2048 groups: the scale pass forms the mean from eight
+    partials per thread (1026 and 2048 groups)."""
+    W = wl.weight(rows, cols, seed=rows + 3)
+    check_quant(qn, W, f"{rows}x{cols}")
+
+
 def test_quant_parity_long_mean_tree(qn):
     """ng > 4096 groups: the mean's tree runs two levels in global memory."""
     W = wl.weight(8192, 8320, seed=77)
