@@ -99,7 +99,8 @@ qn_status check_linear(const qn_nf4dq* w, int64_t M, int r) {
 }
 
 WState to_state(const qn_nf4dq* w) {
-  return WState{w->packed, w->qscale, w->scale2, w->offset, w->rows, w->cols};
+  return WState{w->packed, w->qscale, w->scale2, w->offset, w->rows, w->cols, w->absmax,
+                w->codebook};
 }
 
 // Large batches (enough 128 x 128 output tiles to fill the chip) take the
@@ -130,20 +131,23 @@ struct FwdWs {
 
 // dropout: the adapter branch reads a masked x, which the decode kernels
 // (one set of x fragments for both products) do not take; such forwards use
-// the GEMM routes.
+// the GEMM routes.  plain: a state other than NF4 with double quantization
+// (FP4 codes, or double quantization off), which the one-kernel decode
+// routes take and the other fused routes do not: past the decode routes it
+// goes through the bf16 copy and the dense GEMM.
 FwdWs carve_fwd(Carver& c, int64_t M, int64_t rows, int64_t cols, int r, bool need_u,
-                bool counters = true, bool dropout = false, bool dense_only = false) {
+                bool counters = true, bool dropout = false, bool plain = false) {
   FwdWs f;
   f.arrivals = counters ? c.take<unsigned>(kArrivalWords) : nullptr;
-  const bool dec = rows > 0 && !dropout && !dense_only;
+  const bool dec = rows > 0 && !dropout;
   f.dbr = dec ? decode_rows_band(M, rows, cols, r) : 0;
   f.dt = dec && f.dbr == 0 ? decode_tiles(M, rows, cols, r) : DecodeTiles{0, 0, 0};
-  f.dS = dec && f.dbr == 0 && f.dt.rgt == 0 ? decode_slices(M, rows, cols) : 0;
+  f.dS = dec && !plain && f.dbr == 0 && f.dt.rgt == 0 ? decode_slices(M, rows, cols) : 0;
   const bool decode = f.dbr > 0 || f.dt.rgt > 0 || f.dS > 0;  // u from the decode kernels
   f.S = thin_nt_slices(M, cols);
   f.u = need_u ? c.take<float>((size_t)M * r) : nullptr;
   f.upart = f.S > 1 && !decode ? c.take<float>((size_t)f.S * M * r) : nullptr;
-  f.wd = rows > 0 && M > 0 && (dense_only || dense_path(M, rows))
+  f.wd = rows > 0 && M > 0 && !decode && (plain || dense_path(M, rows))
              ? c.take<uint16_t>((size_t)rows * cols)
              : nullptr;
   f.dpart = f.dS > 0 ? c.take<float>((size_t)f.dS * M * rows) : nullptr;

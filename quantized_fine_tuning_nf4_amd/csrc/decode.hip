@@ -282,10 +282,15 @@ __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// CB: the codebook of the codes (NF4 or FP4); ABS: double quantization off,
+// the block scales read from absmax (fp32, into registers with the other
+// small loads) instead of decoded from qscale, scale2 and offset.
+template <int CB, bool ABS>
 __global__ __launch_bounds__(TT, 1) void k_decode_tile(
     const uint8_t* __restrict__ packed, const uint8_t* __restrict__ qscale,
     const float* __restrict__ scale2, const float* __restrict__ offset,
-    const uint16_t* __restrict__ X, int64_t M, int64_t N, int64_t K,
+    const float* __restrict__ absmax, const uint16_t* __restrict__ X, int64_t M, int64_t N,
+    int64_t K,
     const uint16_t* __restrict__ Aad, const uint16_t* __restrict__ Bad, int r, float s, int rgt,
     int S, unsigned* __restrict__ arrivals, float* __restrict__ part, float* __restrict__ upart,
     uint16_t* __restrict__ Y, float* __restrict__ u_out) {
@@ -302,7 +307,7 @@ __global__ __launch_bounds__(TT, 1) void k_decode_tile(
   const int64_t col0 = (int64_t)z * KSL + 128 * pr;  // first column of the wave's pair
 
   // ---- small loads first (their waits then never wait for the code stream)
-  const float lo_level = as_f32(kNF4Bits[(tid >> 5) & 15]);
+  const float lo_level = as_f32(level_bits(CB, (tid >> 5) & 15));
   const int koff1 = 32 * (g4 & 1) + ((g4 >> 1) ? 16 : 8);
   const int koff2 = 32 * (g4 & 1) + ((g4 >> 1) ? 24 : 0);
   // rows past M / r read the last valid row: finite values in outputs never stored
@@ -316,11 +321,24 @@ __global__ __launch_bounds__(TT, 1) void k_decode_tile(
     af[b][0] = as_bf16x8(*reinterpret_cast<const u32x4*>(arow + 64 * b + koff1));
     af[b][1] = as_bf16x8(*reinterpret_cast<const u32x4*>(arow + 64 * b + koff2));
   }
-  // the band's scales for this slice, straight into LDS (direct-to-LDS
-  // loads: nothing waits for them before the code stream is issued): the 16
-  // scale codes of each row (thread t: row t / 4, bytes 4 (t % 4) ..) and
-  // each row's second-level scale (rows past the band read its last row)
-  {
+  // the block scales of the wave's two blocks for row l16 of each of its
+  // row groups (double quantization off: two fp32 values per row group;
+  // rows past the band read its last row)
+  float sca[RPW], scb[RPW];
+  if constexpr (ABS) {
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+      const int row = min(16 * (par + 2 * i) + l16, nrows - 1);
+      const float2 ab = *reinterpret_cast<const float2*>(
+          absmax + (n0 + row) * kb + (int64_t)z * (KSL / 64) + 2 * pr);
+      sca[i] = ab.x;
+      scb[i] = ab.y;
+    }
+  } else {
+    // the band's scales for this slice, straight into LDS (direct-to-LDS
+    // loads: nothing waits for them before the code stream is issued): the
+    // 16 scale codes of each row (thread t: row t / 4, bytes 4 (t % 4) ..)
+    // and each row's second-level scale (rows past the band read its last row)
     const int row = min(tid >> 2, nrows - 1);
     const rsrc_t rq = make_rs(qscale + n0 * kb + (int64_t)z * (KSL / 64),
                               (uint32_t)((int64_t)(nrows - 1) * kb + KSL / 64));
@@ -365,25 +383,25 @@ __global__ __launch_bounds__(TT, 1) void k_decode_tile(
   uint32_t* trow = tab32 + ((tid >> 5) & 15) * 64 + (tid & 31);
 #pragma unroll
   for (int hi = 0; hi < 16; ++hi)
-    if ((hi & 1) == hi_par) trow[hi * 16 * 64] = pack_bf16x2(lo_level, as_f32(kNF4Bits[hi]));
+    if ((hi & 1) == hi_par) trow[hi * 16 * 64] = pack_bf16x2(lo_level, as_f32(level_bits(CB, hi)));
   // tables and scales ready (everything but the NST - 1 code units in
   // flight has landed); the code stream stays in flight across the barrier
   wait_vm<NST - 1>();
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   const uint8_t* tab = smem + L_TAB;
   const uint32_t tbase = 4u * (lane & 31);
-  const float mu = *offset;
   const int rd = 16 * (4 * l16 + (g4 ^ ((l16 >> 1) & 3)));  // this lane's chunk in a unit
-  // the block scales of the wave's two blocks for row l16 of each of its
-  // row groups, once: s'_b = fma(e4m3(q_b), s2, mu)
-  float sca[RPW], scb[RPW];
+  if constexpr (!ABS) {
+    // the block scales, once: s'_b = fma(e4m3(q_b), s2, mu)
+    const float mu = *offset;
 #pragma unroll
-  for (int i = 0; i < RPW; ++i) {
-    const int row = 16 * (par + 2 * i) + l16;
-    const uint32_t qs = *reinterpret_cast<const uint16_t*>(smem + L_QS + 16 * row + 2 * pr);
-    const float s2 = reinterpret_cast<const float*>(smem + L_S2)[row];
-    sca[i] = dq_scale(qs & 0xffu, s2, mu);
-    scb[i] = dq_scale((qs >> 8) & 0xffu, s2, mu);
+    for (int i = 0; i < RPW; ++i) {
+      const int row = 16 * (par + 2 * i) + l16;
+      const uint32_t qs = *reinterpret_cast<const uint16_t*>(smem + L_QS + 16 * row + 2 * pr);
+      const float s2 = reinterpret_cast<const float*>(smem + L_S2)[row];
+      sca[i] = dq_scale(qs & 0xffu, s2, mu);
+      scb[i] = dq_scale((qs >> 8) & 0xffu, s2, mu);
+    }
   }
 
   f32x4 acc[RPW];
@@ -571,7 +589,9 @@ constexpr int RW_RING_KB = 64;
 constexpr int RW_TAB = 0, RW_RING = 65536, RW_QS = RW_RING + RW_RING_KB * UB;
 constexpr int RW_S2 = RW_QS + RW_BR * 64, RW_B = RW_S2 + 64 * 4, RW_E4 = RW_B + RW_BR * 16 * 2;
 constexpr int RW_TOTAL = RW_E4 + 256 * 4;
-static_assert(RW_TOTAL <= 160 * 1024, "LDS");
+// double quantization off: the band's fp32 block scales, after the rest
+constexpr int RW_AB = RW_TOTAL, RW_TOTAL_ABS = RW_AB + RW_BR * 64 * 4;
+static_assert(RW_TOTAL_ABS <= 160 * 1024, "LDS");
 static_assert(16 * RW_RG * 4 * 64 * 4 <= RW_RING, "wave sums overlap the ring");
 
 // operations issued after unit q of NU when it is awaited: RS units go out
@@ -600,19 +620,22 @@ __device__ __forceinline__ void wait_vm_n(int n) {
   }
 }
 
-template <int PW, int NW>
+// CB: the codebook of the codes (NF4 or FP4); ABS: double quantization off,
+// the block scales read from absmax (fp32) instead of decoded from qscale,
+// scale2 and offset.
+template <int PW, int NW, int CB, bool ABS>
 __global__ __launch_bounds__(64 * NW, 1) void k_decode_rows(
     const uint8_t* __restrict__ packed, const uint8_t* __restrict__ qscale,
     const float* __restrict__ scale2, const float* __restrict__ offset,
-    const uint16_t* __restrict__ X, int64_t M, int64_t N, const uint16_t* __restrict__ Aad,
-    const uint16_t* __restrict__ Bad, int r, float s, int br, uint16_t* __restrict__ Y,
-    float* __restrict__ u_out) {
+    const float* __restrict__ absmax, const uint16_t* __restrict__ X, int64_t M, int64_t N,
+    const uint16_t* __restrict__ Aad, const uint16_t* __restrict__ Bad, int r, float s, int br,
+    uint16_t* __restrict__ Y, float* __restrict__ u_out) {
   constexpr int RW_T = 64 * NW, RW_W = NW;
   constexpr int64_t K = 128 * NW * PW, kb = K / 64;
   constexpr int NU = RW_RG * PW, RS = NU < RW_RING_KB / NW ? NU : RW_RING_KB / NW, NA = 0;
   constexpr int PT = (RW_BR * 16 + RW_T - 1) / RW_T;  // small-load elements per thread
   static_assert(rw_after<NU, RS, NA>(0) <= 39, "wait counts");
-  __shared__ __attribute__((aligned(16))) uint8_t smem[RW_TOTAL];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[ABS ? RW_TOTAL_ABS : RW_TOTAL];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g4 = lane >> 4;
@@ -620,26 +643,36 @@ __global__ __launch_bounds__(64 * NW, 1) void k_decode_rows(
   const int nrows = (int)min((int64_t)br, N - n0);
 
   // ---- the band's scale codes (nrows * kb bytes), second-level scales and
-  // B rows: PT dwords / PT elements per thread
+  // B rows: PT dwords / PT elements per thread (or, double quantization off,
+  // its fp32 block scales: PA per thread)
   constexpr int QW = RW_BR * (int)kb / 4;  // dwords of scale codes, at most
   static_assert(QW <= PT * RW_T && RW_BR * 16 <= PT * RW_T, "PT per thread");
+  constexpr int PA = (RW_BR * (int)kb + RW_T - 1) / RW_T;
   const int64_t g0 = n0 * kb / kGroup;
   const int ns2 = (int)(((n0 + nrows) * kb - 1) / kGroup - g0 + 1);
-  const int nq = nrows * (int)kb / 4, nb = nrows * r;
+  const int nq = nrows * (int)kb / 4, nb = nrows * r, na = nrows * (int)kb;
   uint32_t qv[PT];
   uint16_t bv[PT];
+  float av[ABS ? PA : 1];
 #pragma unroll
   for (int k = 0; k < PT; ++k) {
     const int e = tid + RW_T * k;
-    qv[k] = e < nq ? reinterpret_cast<const uint32_t*>(qscale + n0 * kb)[e] : 0u;
+    if constexpr (!ABS) qv[k] = e < nq ? reinterpret_cast<const uint32_t*>(qscale + n0 * kb)[e] : 0u;
     bv[k] = e < nb ? Bad[n0 * r + e] : (uint16_t)0;
   }
-  const float s2v = tid < ns2 ? scale2[g0 + tid] : 0.f;
+  if constexpr (ABS) {
+#pragma unroll
+    for (int k = 0; k < PA; ++k) {
+      const int e = tid + RW_T * k;
+      av[k] = e < na ? absmax[n0 * kb + e] : 0.f;
+    }
+  }
+  const float s2v = !ABS && tid < ns2 ? scale2[g0 + tid] : 0.f;
   // level of the low nibble tid / 32 % 16 = 2 (wave % 8) + bit 5 of the
   // lane: a wave-uniform index (scalar loads, never queued behind the code
   // stream) and a select
   const int lsel = 2 * (wave & 7);
-  const float lo_level = as_f32((lane & 32) ? kNF4Bits[lsel + 1] : kNF4Bits[lsel]);
+  const float lo_level = as_f32((lane & 32) ? level_bits(CB, lsel + 1) : level_bits(CB, lsel));
 
   // ---- X fragments of the wave's pairs (rows past M read the last row)
   const int koff1 = 32 * (g4 & 1) + ((g4 >> 1) ? 16 : 8);
@@ -684,22 +717,29 @@ __global__ __launch_bounds__(64 * NW, 1) void k_decode_rows(
     uint32_t* trow = reinterpret_cast<uint32_t*>(smem + RW_TAB) + ((tid >> 5) & 15) * 64 + (tid & 31);
 #pragma unroll
     for (int hi = 0; hi < 16; ++hi)
-      if (HS == 1 || hi % HS == hsel) trow[hi * 16 * 64] = pack_bf16x2(lo_level, as_f32(kNF4Bits[hi]));
+      if (HS == 1 || hi % HS == hsel)
+        trow[hi * 16 * 64] = pack_bf16x2(lo_level, as_f32(level_bits(CB, hi)));
   }
 #pragma unroll
   for (int k = 0; k < PT; ++k) {
-    reinterpret_cast<uint32_t*>(smem + RW_QS)[tid + RW_T * k] = qv[k];
+    if constexpr (!ABS) reinterpret_cast<uint32_t*>(smem + RW_QS)[tid + RW_T * k] = qv[k];
     reinterpret_cast<uint16_t*>(smem + RW_B)[tid + RW_T * k] = bv[k];
   }
-  if (tid < 64) reinterpret_cast<float*>(smem + RW_S2)[tid] = s2v;
-  // scale code -> value (a table keeps the main loop free of branches)
-  if (tid < 256) reinterpret_cast<float*>(smem + RW_E4)[tid] = e4m3_to_f32(tid);
+  if constexpr (ABS) {
+#pragma unroll
+    for (int k = 0; k < PA; ++k)
+      if (tid + RW_T * k < RW_BR * (int)kb) reinterpret_cast<float*>(smem + RW_AB)[tid + RW_T * k] = av[k];
+  } else {
+    if (tid < 64) reinterpret_cast<float*>(smem + RW_S2)[tid] = s2v;
+    // scale code -> value (a table keeps the main loop free of branches)
+    if (tid < 256) reinterpret_cast<float*>(smem + RW_E4)[tid] = e4m3_to_f32(tid);
+  }
   wait_vm_n(RS + NA);
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
   const uint8_t* tab = smem + RW_TAB;
   const uint32_t tbase = 4u * (lane & 31);
-  const float mu = *offset;
+  const float mu = ABS ? 0.f : *offset;
   const int rd = 16 * (4 * l16 + (g4 ^ ((l16 >> 1) & 3)));
   f32x4 acc[RW_RG];
 #pragma unroll
@@ -732,12 +772,19 @@ __global__ __launch_bounds__(64 * NW, 1) void k_decode_rows(
     // past the band use its last row: finite, never stored)
     const int row = min(16 * g + l16, nrows - 1);
     const int blk = 2 * (wave + NW * i);
-    const uint32_t qs = *reinterpret_cast<const uint16_t*>(smem + RW_QS + row * kb + blk);
-    const float s2 =
-        reinterpret_cast<const float*>(smem + RW_S2)[((n0 + row) * kb + blk) / kGroup - g0];
-    const float* e4 = reinterpret_cast<const float*>(smem + RW_E4);
-    const float sa = __builtin_fmaf(e4[qs & 0xffu], s2, mu);  // = dq_scale
-    const float sb = __builtin_fmaf(e4[(qs >> 8) & 0xffu], s2, mu);
+    float sa, sb;
+    if constexpr (ABS) {
+      const float2 ab = *reinterpret_cast<const float2*>(smem + RW_AB + 4 * (row * kb + blk));
+      sa = ab.x;
+      sb = ab.y;
+    } else {
+      const uint32_t qs = *reinterpret_cast<const uint16_t*>(smem + RW_QS + row * kb + blk);
+      const float s2 =
+          reinterpret_cast<const float*>(smem + RW_S2)[((n0 + row) * kb + blk) / kGroup - g0];
+      const float* e4 = reinterpret_cast<const float*>(smem + RW_E4);
+      sa = __builtin_fmaf(e4[qs & 0xffu], s2, mu);  // = dq_scale
+      sb = __builtin_fmaf(e4[(qs >> 8) & 0xffu], s2, mu);
+    }
     const auto h = __builtin_amdgcn_permlane32_swap(c[1], c[2], false, false);
     const auto l = __builtin_amdgcn_permlane32_swap(c[0], c[3], false, false);
     f32x4 t = mfma16(xf[i][0][0], tab_pairs4(tab, h[0], tbase), f32x4{0.f, 0.f, 0.f, 0.f});
@@ -849,9 +896,17 @@ hipError_t launch_decode_tile(const WState& w, const uint16_t* X, int64_t M, con
   if (t.rgt < 1 || t.rgt > RGM || t.S != K / KSL || t.bands < 1 || t.bands > kMaxBands ||
       (int64_t)t.bands * 16 * t.rgt < N || M < 1 || M > 16 || r < 1 || r > 16 || !arrivals)
     return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_decode_tile, dim3((unsigned)(t.bands * t.S)), dim3(TT), 0, st, w.packed,
-                     w.qscale, w.scale2, w.offset, X, M, N, K, A, B, r, s, t.rgt, t.S, arrivals,
-                     part, upart, Y, u_out);
+  if (w.codebook != kCodeNF4 && w.codebook != kCodeFP4) return hipErrorInvalidValue;
+#define QN_TILE(CB, ABS)                                                                       \
+  hipLaunchKernelGGL((k_decode_tile<CB, ABS>), dim3((unsigned)(t.bands * t.S)), dim3(TT), 0, st, \
+                     w.packed, w.qscale, w.scale2, w.offset, w.absmax, X, M, N, K, A, B, r, s,   \
+                     t.rgt, t.S, arrivals, part, upart, Y, u_out)
+  if (w.codebook == kCodeFP4) {
+    if (w.absmax) QN_TILE(kCodeFP4, true); else QN_TILE(kCodeFP4, false);
+  } else {
+    if (w.absmax) QN_TILE(kCodeNF4, true); else QN_TILE(kCodeNF4, false);
+  }
+#undef QN_TILE
   return hipGetLastError();
 }
 
@@ -882,20 +937,32 @@ hipError_t launch_decode_rows(const WState& w, const uint16_t* X, int64_t M, con
   if (br < 8 || br > RW_BR || br % 8 != 0 || M < 1 || M > 16 || r < 1 || r > 16 ||
       (K != 2048 && K != 4096))
     return hipErrorInvalidValue;
+  if (w.codebook != kCodeNF4 && w.codebook != kCodeFP4) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((N + br - 1) / br));
   constexpr int NW = kRowsWaves;
-  if (K == 4096)
-    hipLaunchKernelGGL((k_decode_rows<4096 / (128 * NW), NW>), grid, dim3(64 * NW), 0, st,
-                       w.packed, w.qscale, w.scale2, w.offset, X, M, N, A, B, r, s, br, Y, u_out);
-  else
-    hipLaunchKernelGGL((k_decode_rows<2048 / (128 * NW), NW>), grid, dim3(64 * NW), 0, st,
-                       w.packed, w.qscale, w.scale2, w.offset, X, M, N, A, B, r, s, br, Y, u_out);
+#define QN_ROWS(KC, CB, ABS)                                                                    \
+  hipLaunchKernelGGL((k_decode_rows<KC / (128 * NW), NW, CB, ABS>), grid, dim3(64 * NW), 0, st, \
+                     w.packed, w.qscale, w.scale2, w.offset, w.absmax, X, M, N, A, B, r, s, br,   \
+                     Y, u_out)
+#define QN_ROWS_K(CB, ABS)      \
+  if (K == 4096)                \
+    QN_ROWS(4096, CB, ABS);     \
+  else                          \
+    QN_ROWS(2048, CB, ABS)
+  if (w.codebook == kCodeFP4) {
+    if (w.absmax) { QN_ROWS_K(kCodeFP4, true); } else { QN_ROWS_K(kCodeFP4, false); }
+  } else {
+    if (w.absmax) { QN_ROWS_K(kCodeNF4, true); } else { QN_ROWS_K(kCodeNF4, false); }
+  }
+#undef QN_ROWS_K
+#undef QN_ROWS
   return hipGetLastError();
 }
 
 hipError_t launch_decode_fwd(const WState& w, const uint16_t* X, int64_t M, const uint16_t* A,
                              const uint16_t* B, int r, float s, uint16_t* Y, float* u_out,
                              float* part, float* upart, int S, hipStream_t st) {
+  if (w.absmax || w.codebook != kCodeNF4) return hipErrorInvalidValue;  // NF4 with DQ only
   const int64_t N = w.rows, K = w.cols;
   const int nbs = (int)(K / 64 / S);
   const size_t lds = (size_t)M * (nbs * 128 + 16);

@@ -442,12 +442,14 @@ int pick(int64_t M) { return M <= 32 ? 0 : 1; }
 
 hipError_t launch_qgemm_fwd(const WState& w, const uint16_t* X, int64_t M, const float* u,
                             const uint16_t* B, int r, float s, uint16_t* Y, hipStream_t st) {
+  if (w.absmax || w.codebook != kCodeNF4) return hipErrorInvalidValue;  // NF4 with DQ only
   if (pick(M) == 0) return run_fwd<1, 4, 1, 1>(w, X, M, u, B, r, s, Y, st);
   return run_fwd<2, 2, 2, 2>(w, X, M, u, B, r, s, Y, st);
 }
 
 hipError_t launch_qgemm_dx(const WState& w, const uint16_t* G, int64_t M, const float* v,
                            const uint16_t* A, int r, float s, uint16_t* dX, hipStream_t st) {
+  if (w.absmax || w.codebook != kCodeNF4) return hipErrorInvalidValue;  // NF4 with DQ only
   if (pick(M) == 0) return run_dx<1, 4, 1, 1>(w, G, M, v, A, r, s, dX, st);
   return run_dx<2, 2, 2, 2>(w, G, M, v, A, r, s, dX, st);
 }

@@ -216,6 +216,8 @@ struct WState {
   const float* scale2;
   const float* offset;
   int64_t rows, cols;
+  const float* absmax = nullptr;  // fp32 block scales (double quantization off), or null
+  int codebook = kCodeNF4;        // kCodeNF4 or kCodeFP4
 };
 
 // out[M, r] (fp32) = sum over S slices of Z[M, P] * T[r, P]^T.  When S > 1

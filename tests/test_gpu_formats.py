@@ -2,8 +2,9 @@
 FT-02: "Guided example 3: double quantization" on/off and "Exercise 3: NF4
 vs FP4 at equal memory"): quantize and dequantize bit-exact for NF4 and FP4
 codes with and without double quantization; merge bit-exact; the linear
-calls (which route these states through the large-batch route) within
-5e-3 of fp64."""
+calls within 5e-3 of fp64, at decode sizes through the decode kernels
+(which take every format) and otherwise through the large-batch route; an
+exact one-hot pin through the decode kernels for every format."""
 import numpy as np
 import pytest
 import torch
@@ -142,6 +143,67 @@ def test_linear_formats(qn, codebook, dq, rows, cols, M, r):
                 dA=rel_err(dA.cpu().numpy(), dA_ref), dB=rel_err(dB.cpu().numpy(), dB_ref))
     say("  rel err", {k: f"{v:.2e}" for k, v in errs.items()})
     assert all(e <= REL_TOL for e in errs.values()), errs
+
+
+@pytest.mark.parametrize("codebook,dq", FORMATS)
+@pytest.mark.parametrize("rows,cols,M,r,route", [
+    (14336, 4096, 1, 16, "decode_rows"), (14336, 4096, 16, 16, "decode_rows"),
+    (14336, 2048, 5, 16, "decode_rows"), (4096, 4096, 4, 16, "decode_tiles"),
+    (4104, 3072, 3, 8, "decode_tiles"), (2048, 2048, 2, 32, "decode_split"),
+])
+def test_decode_formats(qn, codebook, dq, rows, cols, M, r, route):
+    """Decode-sized forwards of every format: y and u against the fp64
+    oracle on every row (the split route, NF4 with double quantization only,
+    sends the other formats through the large-batch route)."""
+    assert qn.route(M, rows, cols, r) == route
+    say(f"[formats] decode {codebook} dq={dq} rows={rows} cols={cols} M={M} r={r}")
+    W, x, A, B = (wl.weight(rows, cols, 1400 + rows + M), wl.normal_bf16((M, cols), 1401, 1.0),
+                  wl.normal_bf16((r, cols), 1402, 0.05), wl.normal_bf16((rows, r), 1403, 0.05))
+    alpha = 2.0 * r
+    st = qn.qn_quantize(f32_dev(W), codebook=codebook, double_quant=dq)
+    y, u = qn.qlora_linear_fwd(st, bf16_dev(x), bf16_dev(A), bf16_dev(B), alpha)
+    torch.cuda.synchronize()
+    s = float(np.float32(alpha) / np.float32(r))
+    Wd, _ = oracle.dequantize(oracle.quantize(W, double_quant=dq, codebook=codebook),
+                              want_bf16=False)
+    Y_ref, U_ref = oracle.qlora_fwd(Wd, x, A, B, s)
+    errs = dict(y=rel_err(bf16_host_f64(y), Y_ref), u=rel_err(u.cpu().numpy(), U_ref))
+    say("  rel err", {k: f"{v:.2e}" for k, v in errs.items()})
+    assert errs["y"] <= REL_TOL and errs["u"] <= 1e-5, errs
+
+
+@pytest.mark.parametrize("codebook,dq", FORMATS)
+@pytest.mark.parametrize("rows,cols,r,route", [
+    (14336, 4096, 16, "decode_rows"),
+    (4096, 4096, 16, "decode_tiles"),
+])
+def test_decode_formats_one_hot_exact(qn, codebook, dq, rows, cols, r, route):
+    """x rows = e_k (16 per call, every column k over the calls), B = 0:
+    y[m, :] = bf16(W'[:, k]) exactly through the decode kernels for every
+    format (the block scale 0.25 is a power of two)."""
+    assert qn.route(16, rows, cols, r) == route
+    say(f"[formats] decode one-hot {codebook} dq={dq} route={route}")
+    W = wl.equal_absmax_weight(rows, cols, seed=rows + cols + 7)
+    ref = oracle.quantize(W, double_quant=dq, codebook=codebook)
+    if dq:
+        assert ref.offset == np.float32(0.25) and not ref.scale2.any()
+    else:
+        assert np.all(ref.absmax == np.float32(0.25))
+    _, Wb = oracle.dequantize(ref, want_f32=False)
+    st = qn.qn_quantize(f32_dev(W), codebook=codebook, double_quant=dq)
+    A = bf16_dev(wl.normal_bf16((r, cols), 7, 0.01))
+    B = torch.zeros((rows, r), dtype=torch.bfloat16, device="cuda")
+    eye = torch.zeros((cols, cols), dtype=torch.bfloat16, device="cuda")
+    eye.fill_diagonal_(1.0)
+    got = torch.empty((cols, rows), dtype=torch.bfloat16, device="cuda")
+    L = qn.load_library()
+    ws = qn.linear_workspace(L.qlora_linear_workspace_state(qn.ctypes.byref(st.c_struct()), 16,
+                                                            r, 0, None))
+    for k0 in range(0, cols, 16):
+        qn.qlora_linear_fwd(st, eye[k0:k0 + 16], A, B, 2.0 * r, y=got[k0:k0 + 16], workspace=ws)
+    torch.cuda.synchronize()
+    want = wl.bf16_bits_to_f32(np.ascontiguousarray(Wb.T))
+    assert np.array_equal(got.float().cpu().numpy(), want)
 
 
 @pytest.mark.parametrize("codebook,dq", FORMATS)

@@ -131,20 +131,6 @@ def test_adapter_b_zero_leaves_base_exact(qn, route):
     assert int(torch.count_nonzero(dA)) == 0 and float(dB.abs().sum()) > 0
 
 
-def _equal_absmax_weight(rows, cols, seed):
-    """Every 64-block holds one element of +-0.25 and the rest inside
-    (-0.2, 0.2): all block scales are 0.25, so their mean is 0.25, every
-    group's spread C2 is 0 and the dequantization scale s' is exactly 0.25
-    for every block (a power of two: L[c] s' and bf16(L[c]) s' are exact)."""
-    rng = np.random.default_rng(seed)
-    W = rng.uniform(-0.2, 0.2, (rows, cols)).astype(np.float32)
-    pos = rng.integers(0, 64, size=(rows, cols // 64))
-    sign = np.where(rng.integers(0, 2, size=pos.shape) == 1, 1.0, -1.0).astype(np.float32)
-    W.reshape(rows, cols // 64, 64)[np.arange(rows)[:, None], np.arange(cols // 64)[None, :],
-                                    pos] = 0.25 * sign
-    return W
-
-
 @pytest.mark.parametrize("rows,cols,r,route", [
     (14336, 4096, 16, "decode_rows"),
     (4096, 4096, 16, "decode_tiles"),
@@ -156,7 +142,7 @@ def test_decode_one_hot_reads_every_column_exactly(qn, rows, cols, r, route):
     each block's fp32 partial by s' (exact here: s' = 0.25)."""
     assert qn.route(16, rows, cols, r) == route
     say(f"[paths] decode one-hot route={route} rows={rows} cols={cols}")
-    W = _equal_absmax_weight(rows, cols, seed=rows + cols)
+    W = wl.equal_absmax_weight(rows, cols, seed=rows + cols)
     ref = oracle.quantize(W)
     assert ref.offset == np.float32(0.25) and not ref.scale2.any() and not ref.qscale.any()
     _, Wb = oracle.dequantize(ref, want_f32=False)

@@ -67,6 +67,20 @@ def weight(rows: int, cols: int, seed: int, std: float = 0.02) -> np.ndarray:
     return normal_f32((rows, cols), seed, std)
 
 
+
+def equal_absmax_weight(rows: int, cols: int, seed: int) -> np.ndarray:
+    """Every 64-block holds one element of +-0.25 and the rest inside
+    (-0.2, 0.2), so every block's largest magnitude is 0.25, a power of two
+    (with double quantization the scales' mean is 0.25 and every group's
+    spread is 0; without it the stored scale is 0.25)."""
+    rng = np.random.default_rng(seed)
+    W = rng.uniform(-0.2, 0.2, (rows, cols)).astype(np.float32)
+    pos = rng.integers(0, 64, size=(rows, cols // 64))
+    sign = np.where(rng.integers(0, 2, size=pos.shape) == 1, 1.0, -1.0).astype(np.float32)
+    W.reshape(rows, cols // 64, 64)[np.arange(rows)[:, None], np.arange(cols // 64)[None, :],
+                                    pos] = 0.25 * sign
+    return W
+
 def outlier_weight(rows: int = 4096, cols: int = 4096, seed: int = SEED_W + 2) -> np.ndarray:
     """The quantize/dequantize round-trip weight: N(0, 0.02), 1% of the
     columns scaled x20, plus four all-zero and four constant 64-blocks."""
