@@ -112,12 +112,9 @@ typedef enum { QN_F32 = 0, QN_BF16 = 1 } qn_dtype;
  * FT-02, "Guided example 3: double quantization"): absmax [nb] holds the
  * fp32 block scales and qscale, scale2, offset are ignored (4.5 bits per
  * weight against 4.127).  codebook: QN_CODE_NF4 (zero-initialised structs
- * are NF4) or QN_CODE_FP4.  Quantize, dequantize, merge, the linear calls'
- * one-kernel decode routes (QN_ROUTE_DECODE_ROWS / _TILES) and their
- * large-batch route take every state; where qlora_linear_route names another
- * route (QN_ROUTE_DECODE_SPLIT or a fused one, which take NF4 with double
- * quantization only), the linear calls send other states through the
- * large-batch route (a bf16 copy of the weight in the workspace). */
+ * are NF4) or QN_CODE_FP4.  Every call and every route of the linear calls
+ * takes every state (only the level table and the source of the block
+ * scales differ). */
 typedef struct {
   const uint8_t* packed; /* [32*nb] */
   const uint8_t* qscale; /* [nb]    */
@@ -301,10 +298,8 @@ enum {
 
 /* Which route qlora_linear_fwd (backward == 0) or the dX product of
  * qlora_linear_bwd (backward != 0) takes for these sizes on the current
- * device, for NF4 states with double quantization; -1 for sizes the calls
- * reject.  Other states take the same decode-rows / decode-tiles routes and
- * QN_ROUTE_DENSE in place of the others.  For tests and profiling: every
- * route computes the same function. */
+ * device (the same for every state format); -1 for sizes the calls reject.
+ * For tests and profiling: every route computes the same function. */
 int qlora_linear_route(int64_t M, int64_t rows, int64_t cols, int r, int backward);
 
 /* qlora_linear_bwd with adapter options (opts nullable; the same options as

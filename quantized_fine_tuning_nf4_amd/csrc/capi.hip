@@ -77,10 +77,6 @@ qn_status check_state(const qn_nf4dq* w) {
   return QN_OK;
 }
 
-// NF4 codes with double-quantized scales: the format every route takes;
-// other states go through the large-batch route (dequantization kernels
-// that take every format, then the dense GEMM).
-bool default_format(const qn_nf4dq* w) { return !w->absmax && w->codebook == QN_CODE_NF4; }
 
 // Largest M and weight dimension the linear calls take: the kernels address
 // buffers through 32-bit offsets from a row or slice base, which these
@@ -131,23 +127,20 @@ struct FwdWs {
 
 // dropout: the adapter branch reads a masked x, which the decode kernels
 // (one set of x fragments for both products) do not take; such forwards use
-// the GEMM routes.  plain: a state other than NF4 with double quantization
-// (FP4 codes, or double quantization off), which the one-kernel decode
-// routes take and the other fused routes do not: past the decode routes it
-// goes through the bf16 copy and the dense GEMM.
+// the GEMM routes.  Every route takes every state format.
 FwdWs carve_fwd(Carver& c, int64_t M, int64_t rows, int64_t cols, int r, bool need_u,
-                bool counters = true, bool dropout = false, bool plain = false) {
+                bool counters = true, bool dropout = false) {
   FwdWs f;
   f.arrivals = counters ? c.take<unsigned>(kArrivalWords) : nullptr;
   const bool dec = rows > 0 && !dropout;
   f.dbr = dec ? decode_rows_band(M, rows, cols, r) : 0;
   f.dt = dec && f.dbr == 0 ? decode_tiles(M, rows, cols, r) : DecodeTiles{0, 0, 0};
-  f.dS = dec && !plain && f.dbr == 0 && f.dt.rgt == 0 ? decode_slices(M, rows, cols) : 0;
+  f.dS = dec && f.dbr == 0 && f.dt.rgt == 0 ? decode_slices(M, rows, cols) : 0;
   const bool decode = f.dbr > 0 || f.dt.rgt > 0 || f.dS > 0;  // u from the decode kernels
   f.S = thin_nt_slices(M, cols);
   f.u = need_u ? c.take<float>((size_t)M * r) : nullptr;
   f.upart = f.S > 1 && !decode ? c.take<float>((size_t)f.S * M * r) : nullptr;
-  f.wd = rows > 0 && M > 0 && !decode && (plain || dense_path(M, rows))
+  f.wd = rows > 0 && M > 0 && !decode && dense_path(M, rows)
              ? c.take<uint16_t>((size_t)rows * cols)
              : nullptr;
   f.dpart = f.dS > 0 ? c.take<float>((size_t)f.dS * M * rows) : nullptr;
@@ -177,7 +170,7 @@ struct BwdWs {
 };
 
 BwdWs carve_bwd(Carver& c, int64_t M, int64_t rows, int64_t cols, int r, bool need_u,
-                bool dropout = false, bool dense_only = false) {
+                bool dropout = false) {
   BwdWs b;
   b.arrivals = c.take<unsigned>(kArrivalWords);
   if (need_u) {
@@ -198,7 +191,7 @@ BwdWs carve_bwd(Carver& c, int64_t M, int64_t rows, int64_t cols, int r, bool ne
   b.dApart = c.take<float>((size_t)b.Sa * cols * r);
   b.sv = c.take<uint16_t>((size_t)2 * rp * thin_tn_rows_padded(M, cols, r));
   b.ldt = round_up(rows, 64);
-  const bool dense = M > 0 && (dense_only || dense_path(M, cols));
+  const bool dense = M > 0 && dense_path(M, cols);
   b.wt = dense ? c.take<uint16_t>((size_t)cols * b.ldt) : nullptr;
   b.At = dense ? c.take<uint16_t>((size_t)cols * r) : nullptr;
   b.xd = dropout ? c.take<uint16_t>((size_t)M * cols) : nullptr;
@@ -242,15 +235,15 @@ qn_status forward(const qn_nf4dq* w, const uint16_t* x, int64_t M, const uint16_
       (u_out && !aligned16(u_out)))
     return QN_EALIGN;
   Carver probe(nullptr);
-  const bool drop = lo.mask != nullptr, plain = !default_format(w);
-  carve_fwd(probe, M, w->rows, w->cols, r, u_out == nullptr, true, drop, plain);
+  const bool drop = lo.mask != nullptr;
+  carve_fwd(probe, M, w->rows, w->cols, r, u_out == nullptr, true, drop);
   if (probe.used > 0) {
     if (!workspace) return QN_EINVAL;
     if (reinterpret_cast<uintptr_t>(workspace) & 255u) return QN_EALIGN;
     if (workspace_bytes < probe.used) return QN_EWORKSPACE;
   }
   Carver c(workspace);
-  FwdWs f = carve_fwd(c, M, w->rows, w->cols, r, u_out == nullptr, true, drop, plain);
+  FwdWs f = carve_fwd(c, M, w->rows, w->cols, r, u_out == nullptr, true, drop);
   float* u = u_out ? u_out : f.u;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const float scale = lo.s;
@@ -419,12 +412,12 @@ size_t qlora_linear_workspace(int64_t M, int64_t rows, int64_t cols, int r, int 
 size_t qlora_linear_workspace_state(const qn_nf4dq* w, int64_t M, int r, int backward,
                                     const qn_lora_opts* opts) {
   if (!w || M < 0 || w->rows < 1 || w->cols < 1 || r < 1 || r > 64) return 0;
-  const bool drop = opts && opts->dropout_mask, plain = !default_format(w);
+  const bool drop = opts && opts->dropout_mask;
   Carver c(nullptr);
   if (backward)
-    carve_bwd(c, M, w->rows, w->cols, r, true, drop, plain);
+    carve_bwd(c, M, w->rows, w->cols, r, true, drop);
   else
-    carve_fwd(c, M, w->rows, w->cols, r, true, true, drop, plain);
+    carve_fwd(c, M, w->rows, w->cols, r, true, true, drop);
   return c.used;
 }
 
@@ -498,14 +491,13 @@ qn_status qlora_linear_bwd_ex(const qn_nf4dq* w, const uint16_t* x, const uint16
     if (e == hipSuccess) e = launch_fill_zero(dB, N * (int64_t)r, st);
     return from_hip(e);
   }
-  const bool plain = !default_format(w);
   Carver probe(nullptr);
-  carve_bwd(probe, M, N, K, r, u_saved == nullptr, drop, plain);
+  carve_bwd(probe, M, N, K, r, u_saved == nullptr, drop);
   if (!workspace) return QN_EINVAL;
   if (reinterpret_cast<uintptr_t>(workspace) & 255u) return QN_EALIGN;
   if (workspace_bytes < probe.used) return QN_EWORKSPACE;
   Carver c(workspace);
-  BwdWs b = carve_bwd(c, M, N, K, r, u_saved == nullptr, drop, plain);
+  BwdWs b = carve_bwd(c, M, N, K, r, u_saved == nullptr, drop);
   const float scale = lo.s;
   hipError_t e = hipSuccess;
   // dropout: the adapter branch's masked input, for dA (u takes the mask on

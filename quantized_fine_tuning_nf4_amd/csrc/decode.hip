@@ -62,10 +62,13 @@ __device__ __forceinline__ u32x4 pairs4(const uint8_t* tab, uint32_t w) {
 // MFMA rows past M read zeros from registers.
 // Workgroups with blockIdx.x == groups compute u's partial over the slice
 // instead: upart[z][m][j] = sum_k X[m][k] A[j][k] (wave w: ranks 16w ..).
+// CBK: the codebook (NF4 or FP4); ABS: double quantization off (the block
+// scales read from absmax instead of decoded from qscale, scale2, offset).
+template <int CBK, bool ABS>
 __global__ __launch_bounds__(T, 4) void k_decode_partial(
     const uint8_t* __restrict__ packed, const uint8_t* __restrict__ qscale,
     const float* __restrict__ scale2, const float* __restrict__ offset,
-    const uint16_t* __restrict__ X, const uint16_t* __restrict__ Aad, int r, int64_t M,
+    const float* __restrict__ absmax, const uint16_t* __restrict__ X, const uint16_t* __restrict__ Aad, int r, int64_t M,
     int64_t N, int64_t K, int nbs, float* __restrict__ part, float* __restrict__ upart) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ uint32_t s_tab[256];
@@ -73,7 +76,7 @@ __global__ __launch_bounds__(T, 4) void k_decode_partial(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g4 = lane >> 4;
   {  // pair table: entry b = bf16(L[b & 15]) | bf16(L[b >> 4]) << 16
-    const float lo = as_f32(kNF4Bits[tid & 15]), hi = as_f32(kNF4Bits[tid >> 4]);
+    const float lo = as_f32(level_bits(CBK, tid & 15)), hi = as_f32(level_bits(CBK, tid >> 4));
     s_tab[tid] = pack_bf16x2(lo, hi);
     s_e4m3[tid] = e4m3_to_f32(tid);  // scale code -> value
   }
@@ -91,12 +94,19 @@ __global__ __launch_bounds__(T, 4) void k_decode_partial(
   uint2 code[CB];
   u32x4 q4 = {0u, 0u, 0u, 0u};
   float s2 = 0.f;
+  f32x4 a4[ABS ? CB / 4 : 1];  // double quantization off: the pass's block scales
   auto load_pass = [&](int jb) {
     const int64_t bb = b0 + jb;
 #pragma unroll
     for (int j = 0; j < CB; ++j) code[j] = *reinterpret_cast<const uint2*>(crow + (bb + j) * 32);
-    q4 = *reinterpret_cast<const u32x4*>(qscale + n * kblocks + bb);
-    s2 = scale2[(n * kblocks + bb) / kGroup];
+    if constexpr (ABS) {
+#pragma unroll
+      for (int q = 0; q < CB / 4; ++q)
+        a4[q] = *reinterpret_cast<const f32x4*>(absmax + n * kblocks + bb + 4 * q);
+    } else {
+      q4 = *reinterpret_cast<const u32x4*>(qscale + n * kblocks + bb);
+      s2 = scale2[(n * kblocks + bb) / kGroup];
+    }
   };
   // ---- stage X[0:M, slice] (nbs == 16: at most 8 16-byte chunks per
   // thread) before the weight loads go out, so that waiting for X does not
@@ -149,14 +159,14 @@ __global__ __launch_bounds__(T, 4) void k_decode_partial(
     return;
   }
 
-  const float mu = *offset;
+  const float mu = ABS ? 0.f : *offset;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int jb = 0; jb < nbs; jb += CB) {
     if (jb > 0) load_pass(jb);
 #pragma unroll
     for (int j = 0; j < CB; ++j) {
       const uint32_t qb = (q4[j >> 2] >> (8 * (j & 3))) & 0xffu;
-      const float sc = __builtin_fmaf(s_e4m3[qb], s2, mu);
+      const float sc = ABS ? a4[j >> 2][j & 3] : __builtin_fmaf(s_e4m3[qb], s2, mu);
       const bf16x8 a0 = xfrag((jb + j) * 128);
       const bf16x8 a1 = xfrag((jb + j) * 128 + 16);
       const bf16x8 w0 = as_bf16x8(pairs4(tab, code[j].x));
@@ -282,10 +292,10 @@ __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// CB: the codebook of the codes (NF4 or FP4); ABS: double quantization off,
+// CBK: the codebook of the codes (NF4 or FP4); ABS: double quantization off,
 // the block scales read from absmax (fp32, into registers with the other
 // small loads) instead of decoded from qscale, scale2 and offset.
-template <int CB, bool ABS>
+template <int CBK, bool ABS>
 __global__ __launch_bounds__(TT, 1) void k_decode_tile(
     const uint8_t* __restrict__ packed, const uint8_t* __restrict__ qscale,
     const float* __restrict__ scale2, const float* __restrict__ offset,
@@ -307,7 +317,7 @@ __global__ __launch_bounds__(TT, 1) void k_decode_tile(
   const int64_t col0 = (int64_t)z * KSL + 128 * pr;  // first column of the wave's pair
 
   // ---- small loads first (their waits then never wait for the code stream)
-  const float lo_level = as_f32(level_bits(CB, (tid >> 5) & 15));
+  const float lo_level = as_f32(level_bits(CBK, (tid >> 5) & 15));
   const int koff1 = 32 * (g4 & 1) + ((g4 >> 1) ? 16 : 8);
   const int koff2 = 32 * (g4 & 1) + ((g4 >> 1) ? 24 : 0);
   // rows past M / r read the last valid row: finite values in outputs never stored
@@ -383,7 +393,7 @@ __global__ __launch_bounds__(TT, 1) void k_decode_tile(
   uint32_t* trow = tab32 + ((tid >> 5) & 15) * 64 + (tid & 31);
 #pragma unroll
   for (int hi = 0; hi < 16; ++hi)
-    if ((hi & 1) == hi_par) trow[hi * 16 * 64] = pack_bf16x2(lo_level, as_f32(level_bits(CB, hi)));
+    if ((hi & 1) == hi_par) trow[hi * 16 * 64] = pack_bf16x2(lo_level, as_f32(level_bits(CBK, hi)));
   // tables and scales ready (everything but the NST - 1 code units in
   // flight has landed); the code stream stays in flight across the barrier
   wait_vm<NST - 1>();
@@ -620,10 +630,10 @@ __device__ __forceinline__ void wait_vm_n(int n) {
   }
 }
 
-// CB: the codebook of the codes (NF4 or FP4); ABS: double quantization off,
+// CBK: the codebook of the codes (NF4 or FP4); ABS: double quantization off,
 // the block scales read from absmax (fp32) instead of decoded from qscale,
 // scale2 and offset.
-template <int PW, int NW, int CB, bool ABS>
+template <int PW, int NW, int CBK, bool ABS>
 __global__ __launch_bounds__(64 * NW, 1) void k_decode_rows(
     const uint8_t* __restrict__ packed, const uint8_t* __restrict__ qscale,
     const float* __restrict__ scale2, const float* __restrict__ offset,
@@ -672,7 +682,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_decode_rows(
   // lane: a wave-uniform index (scalar loads, never queued behind the code
   // stream) and a select
   const int lsel = 2 * (wave & 7);
-  const float lo_level = as_f32((lane & 32) ? level_bits(CB, lsel + 1) : level_bits(CB, lsel));
+  const float lo_level = as_f32((lane & 32) ? level_bits(CBK, lsel + 1) : level_bits(CBK, lsel));
 
   // ---- X fragments of the wave's pairs (rows past M read the last row)
   const int koff1 = 32 * (g4 & 1) + ((g4 >> 1) ? 16 : 8);
@@ -718,7 +728,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_decode_rows(
 #pragma unroll
     for (int hi = 0; hi < 16; ++hi)
       if (HS == 1 || hi % HS == hsel)
-        trow[hi * 16 * 64] = pack_bf16x2(lo_level, as_f32(level_bits(CB, hi)));
+        trow[hi * 16 * 64] = pack_bf16x2(lo_level, as_f32(level_bits(CBK, hi)));
   }
 #pragma unroll
   for (int k = 0; k < PT; ++k) {
@@ -897,8 +907,8 @@ hipError_t launch_decode_tile(const WState& w, const uint16_t* X, int64_t M, con
       (int64_t)t.bands * 16 * t.rgt < N || M < 1 || M > 16 || r < 1 || r > 16 || !arrivals)
     return hipErrorInvalidValue;
   if (w.codebook != kCodeNF4 && w.codebook != kCodeFP4) return hipErrorInvalidValue;
-#define QN_TILE(CB, ABS)                                                                       \
-  hipLaunchKernelGGL((k_decode_tile<CB, ABS>), dim3((unsigned)(t.bands * t.S)), dim3(TT), 0, st, \
+#define QN_TILE(CBK, ABS)                                                                       \
+  hipLaunchKernelGGL((k_decode_tile<CBK, ABS>), dim3((unsigned)(t.bands * t.S)), dim3(TT), 0, st, \
                      w.packed, w.qscale, w.scale2, w.offset, w.absmax, X, M, N, K, A, B, r, s,   \
                      t.rgt, t.S, arrivals, part, upart, Y, u_out)
   if (w.codebook == kCodeFP4) {
@@ -940,15 +950,15 @@ hipError_t launch_decode_rows(const WState& w, const uint16_t* X, int64_t M, con
   if (w.codebook != kCodeNF4 && w.codebook != kCodeFP4) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((N + br - 1) / br));
   constexpr int NW = kRowsWaves;
-#define QN_ROWS(KC, CB, ABS)                                                                    \
-  hipLaunchKernelGGL((k_decode_rows<KC / (128 * NW), NW, CB, ABS>), grid, dim3(64 * NW), 0, st, \
+#define QN_ROWS(KC, CBK, ABS)                                                                    \
+  hipLaunchKernelGGL((k_decode_rows<KC / (128 * NW), NW, CBK, ABS>), grid, dim3(64 * NW), 0, st, \
                      w.packed, w.qscale, w.scale2, w.offset, w.absmax, X, M, N, A, B, r, s, br,   \
                      Y, u_out)
-#define QN_ROWS_K(CB, ABS)      \
+#define QN_ROWS_K(CBK, ABS)      \
   if (K == 4096)                \
-    QN_ROWS(4096, CB, ABS);     \
+    QN_ROWS(4096, CBK, ABS);     \
   else                          \
-    QN_ROWS(2048, CB, ABS)
+    QN_ROWS(2048, CBK, ABS)
   if (w.codebook == kCodeFP4) {
     if (w.absmax) { QN_ROWS_K(kCodeFP4, true); } else { QN_ROWS_K(kCodeFP4, false); }
   } else {
@@ -962,20 +972,36 @@ hipError_t launch_decode_rows(const WState& w, const uint16_t* X, int64_t M, con
 hipError_t launch_decode_fwd(const WState& w, const uint16_t* X, int64_t M, const uint16_t* A,
                              const uint16_t* B, int r, float s, uint16_t* Y, float* u_out,
                              float* part, float* upart, int S, hipStream_t st) {
-  if (w.absmax || w.codebook != kCodeNF4) return hipErrorInvalidValue;  // NF4 with DQ only
+  if (w.codebook != kCodeNF4 && w.codebook != kCodeFP4) return hipErrorInvalidValue;
   const int64_t N = w.rows, K = w.cols;
   const int nbs = (int)(K / 64 / S);
   const size_t lds = (size_t)M * (nbs * 128 + 16);
   constexpr size_t kMaxLds = 64 * 1024;  // X slice: at most 16 rows of 16 blocks
-  static hipError_t attr =
-      hipFuncSetAttribute(reinterpret_cast<const void*>(k_decode_partial),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds);
+  static hipError_t attr = [] {
+    const void* k[4] = {reinterpret_cast<const void*>(k_decode_partial<kCodeNF4, false>),
+                        reinterpret_cast<const void*>(k_decode_partial<kCodeNF4, true>),
+                        reinterpret_cast<const void*>(k_decode_partial<kCodeFP4, false>),
+                        reinterpret_cast<const void*>(k_decode_partial<kCodeFP4, true>)};
+    for (const void* f : k) {
+      const hipError_t e =
+          hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }();
   if (attr != hipSuccess) return attr;
   if (nbs != 16 || lds > kMaxLds) return hipErrorInvalidValue;
   const int64_t groups = (N + 63) / 64;
   const dim3 grid((unsigned)(groups + 1), (unsigned)S);
-  hipLaunchKernelGGL(k_decode_partial, grid, dim3(T), lds, st, w.packed, w.qscale, w.scale2,
-                     w.offset, X, A, r, M, N, K, nbs, part, upart);
+#define QN_PART(CBK, ABS)                                                                      \
+  hipLaunchKernelGGL((k_decode_partial<CBK, ABS>), grid, dim3(T), lds, st, w.packed, w.qscale, \
+                     w.scale2, w.offset, w.absmax, X, A, r, M, N, K, nbs, part, upart)
+  if (w.codebook == kCodeFP4) {
+    if (w.absmax) QN_PART(kCodeFP4, true); else QN_PART(kCodeFP4, false);
+  } else {
+    if (w.absmax) QN_PART(kCodeNF4, true); else QN_PART(kCodeNF4, false);
+  }
+#undef QN_PART
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_decode_finish, dim3((unsigned)((N + T - 1) / T), (unsigned)M), dim3(T), 0,

@@ -141,11 +141,13 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[TM][TN], uint16_t
 // Forward.  Weight tile: BN rows n0.. of W, columns k0..k0+63 = one NF4 block
 // per row.  Thread t dequantizes SPT consecutive 16-weight segments of one
 // row (8 packed bytes each) and writes them as bf16 to sB[row][...].
-template <int WM, int WN, int TM, int TN>
+// CB: the codebook (NF4 or FP4); ABS: double quantization off (the block
+// scales read from absmax instead of decoded from qscale, scale2, offset).
+template <int WM, int WN, int TM, int TN, int CB, bool ABS>
 __global__ __launch_bounds__(64 * WM * WN) void k_qgemm_fwd(
     const uint8_t* __restrict__ packed, const uint8_t* __restrict__ qscale,
     const float* __restrict__ scale2, const float* __restrict__ offset,
-    const uint16_t* __restrict__ X, const float* __restrict__ U, const uint16_t* __restrict__ Bl,
+    const float* __restrict__ absmax, const uint16_t* __restrict__ X, const float* __restrict__ U, const uint16_t* __restrict__ Bl,
     int64_t M, int64_t N, int64_t K, int r, float s, uint16_t* __restrict__ Y, int tiles_n) {
   using Cfg = Tile<WM, WN, TM, TN>;
   constexpr int BM = Cfg::BM, BN = Cfg::BN, T = Cfg::T;
@@ -156,11 +158,11 @@ __global__ __launch_bounds__(64 * WM * WN) void k_qgemm_fwd(
   uint16_t* sB = sA + 2 * BM * LDK;
   float* lut = reinterpret_cast<float*>(sB + 2 * BN * LDK);
   const int tid = threadIdx.x;
-  if (tid < 16) lut[tid] = as_f32(kNF4Bits[tid]);
+  if (tid < 16) lut[tid] = as_f32(level_bits(CB, tid));
 
   const int64_t m0 = (int64_t)(blockIdx.x / tiles_n) * BM;
   const int64_t n0 = (int64_t)(blockIdx.x % tiles_n) * BN;
-  const float mu = *offset;
+  const float mu = ABS ? 0.f : *offset;
   const int64_t kblocks = K / BK;
 
   // this thread's weight segments: row wr of the tile, segments ws0..ws0+SPT-1
@@ -186,7 +188,7 @@ __global__ __launch_bounds__(64 * WM * WN) void k_qgemm_fwd(
       wreg[0] = a[0]; wreg[1] = a[1];
     }
     const int64_t b = wn_row * kblocks + kb;
-    wscale = dq_scale(qscale[b], scale2[b / kGroup], mu);
+    wscale = ABS ? absmax[b] : dq_scale(qscale[b], scale2[b / kGroup], mu);
   };
   auto store_w = [&](uint16_t* sBs) {
     uint16_t* dst = sBs + wr * LDK + ws0 * 16;
@@ -277,11 +279,11 @@ __global__ __launch_bounds__(64 * WM * WN) void k_qgemm_fwd(
 // transposed (sB[k][n]).  A thread unit is 8 rows x 8 columns: eight u32 of
 // codes (one per row, one scale per row), written as eight 16-byte LDS rows
 // of eight n-values.  Rows past N are zero.
-template <int WM, int WN, int TM, int TN>
+template <int WM, int WN, int TM, int TN, int CB, bool ABS>
 __global__ __launch_bounds__(64 * WM * WN) void k_qgemm_dx(
     const uint8_t* __restrict__ packed, const uint8_t* __restrict__ qscale,
     const float* __restrict__ scale2, const float* __restrict__ offset,
-    const uint16_t* __restrict__ G, const float* __restrict__ Vv, const uint16_t* __restrict__ Al,
+    const float* __restrict__ absmax, const uint16_t* __restrict__ G, const float* __restrict__ Vv, const uint16_t* __restrict__ Al,
     int64_t M, int64_t N, int64_t K, int r, float s, uint16_t* __restrict__ dX, int tiles_k) {
   using Cfg = Tile<WM, WN, TM, TN>;
   constexpr int BM = Cfg::BM, BN = Cfg::BN, T = Cfg::T;
@@ -291,11 +293,11 @@ __global__ __launch_bounds__(64 * WM * WN) void k_qgemm_dx(
   uint16_t* sB = sA + 2 * BM * LDK;
   float* lut = reinterpret_cast<float*>(sB + 2 * BN * LDK);
   const int tid = threadIdx.x;
-  if (tid < 16) lut[tid] = as_f32(kNF4Bits[tid]);
+  if (tid < 16) lut[tid] = as_f32(level_bits(CB, tid));
 
   const int64_t m0 = (int64_t)(blockIdx.x / tiles_k) * BM;
   const int64_t k0 = (int64_t)(blockIdx.x % tiles_k) * BN;
-  const float mu = *offset;
+  const float mu = ABS ? 0.f : *offset;
   const int64_t kblocks = K / BK;
   const int64_t nsteps = (N + BK - 1) / BK;
 
@@ -315,7 +317,7 @@ __global__ __launch_bounds__(64 * WM * WN) void k_qgemm_dx(
         const int64_t nc = min(n, N - 1);
         wreg[u][i] = *reinterpret_cast<const uint32_t*>(packed + (nc * K + k) / 2);
         const int64_t b = nc * kblocks + k / BK;
-        wsc[u][i] = ok ? dq_scale(qscale[b], scale2[b / kGroup], mu) : 0.f;
+        wsc[u][i] = ok ? (ABS ? absmax[b] : dq_scale(qscale[b], scale2[b / kGroup], mu)) : 0.f;
       }
     }
   };
@@ -408,30 +410,53 @@ hipError_t set_lds(Kern k, size_t bytes) {
                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
 }
 
-template <int WM, int WN, int TM, int TN>
-hipError_t run_fwd(const WState& w, const uint16_t* X, int64_t M, const float* u,
-                   const uint16_t* B, int r, float s, uint16_t* Y, hipStream_t st) {
+template <int WM, int WN, int TM, int TN, int CB, bool ABS>
+hipError_t run_fwd_f(const WState& w, const uint16_t* X, int64_t M, const float* u,
+                     const uint16_t* B, int r, float s, uint16_t* Y, hipStream_t st) {
   using Cfg = Tile<WM, WN, TM, TN>;
-  auto kern = k_qgemm_fwd<WM, WN, TM, TN>;
+  auto kern = k_qgemm_fwd<WM, WN, TM, TN, CB, ABS>;
   static hipError_t attr = set_lds(kern, Cfg::LDS);
   if (attr != hipSuccess) return attr;
   const int64_t tm = (M + Cfg::BM - 1) / Cfg::BM, tn = (w.rows + Cfg::BN - 1) / Cfg::BN;
   hipLaunchKernelGGL(kern, dim3((unsigned)(tm * tn)), dim3(Cfg::T), Cfg::LDS, st, w.packed,
-                     w.qscale, w.scale2, w.offset, X, u, B, M, w.rows, w.cols, r, s, Y, (int)tn);
+                     w.qscale, w.scale2, w.offset, w.absmax, X, u, B, M, w.rows, w.cols, r, s, Y,
+                     (int)tn);
   return hipGetLastError();
+}
+
+template <int WM, int WN, int TM, int TN, int CB, bool ABS>
+hipError_t run_dx_f(const WState& w, const uint16_t* G, int64_t M, const float* v,
+                    const uint16_t* A, int r, float s, uint16_t* dX, hipStream_t st) {
+  using Cfg = Tile<WM, WN, TM, TN>;
+  auto kern = k_qgemm_dx<WM, WN, TM, TN, CB, ABS>;
+  static hipError_t attr = set_lds(kern, Cfg::LDS);
+  if (attr != hipSuccess) return attr;
+  const int64_t tm = (M + Cfg::BM - 1) / Cfg::BM, tk = (w.cols + Cfg::BN - 1) / Cfg::BN;
+  hipLaunchKernelGGL(kern, dim3((unsigned)(tm * tk)), dim3(Cfg::T), Cfg::LDS, st, w.packed,
+                     w.qscale, w.scale2, w.offset, w.absmax, G, v, A, M, w.rows, w.cols, r, s, dX,
+                     (int)tk);
+  return hipGetLastError();
+}
+
+// the state's format picks the instance
+template <int WM, int WN, int TM, int TN>
+hipError_t run_fwd(const WState& w, const uint16_t* X, int64_t M, const float* u,
+                   const uint16_t* B, int r, float s, uint16_t* Y, hipStream_t st) {
+  if (w.codebook == kCodeFP4)
+    return w.absmax ? run_fwd_f<WM, WN, TM, TN, kCodeFP4, true>(w, X, M, u, B, r, s, Y, st)
+                    : run_fwd_f<WM, WN, TM, TN, kCodeFP4, false>(w, X, M, u, B, r, s, Y, st);
+  return w.absmax ? run_fwd_f<WM, WN, TM, TN, kCodeNF4, true>(w, X, M, u, B, r, s, Y, st)
+                  : run_fwd_f<WM, WN, TM, TN, kCodeNF4, false>(w, X, M, u, B, r, s, Y, st);
 }
 
 template <int WM, int WN, int TM, int TN>
 hipError_t run_dx(const WState& w, const uint16_t* G, int64_t M, const float* v,
                   const uint16_t* A, int r, float s, uint16_t* dX, hipStream_t st) {
-  using Cfg = Tile<WM, WN, TM, TN>;
-  auto kern = k_qgemm_dx<WM, WN, TM, TN>;
-  static hipError_t attr = set_lds(kern, Cfg::LDS);
-  if (attr != hipSuccess) return attr;
-  const int64_t tm = (M + Cfg::BM - 1) / Cfg::BM, tk = (w.cols + Cfg::BN - 1) / Cfg::BN;
-  hipLaunchKernelGGL(kern, dim3((unsigned)(tm * tk)), dim3(Cfg::T), Cfg::LDS, st, w.packed,
-                     w.qscale, w.scale2, w.offset, G, v, A, M, w.rows, w.cols, r, s, dX, (int)tk);
-  return hipGetLastError();
+  if (w.codebook == kCodeFP4)
+    return w.absmax ? run_dx_f<WM, WN, TM, TN, kCodeFP4, true>(w, G, M, v, A, r, s, dX, st)
+                    : run_dx_f<WM, WN, TM, TN, kCodeFP4, false>(w, G, M, v, A, r, s, dX, st);
+  return w.absmax ? run_dx_f<WM, WN, TM, TN, kCodeNF4, true>(w, G, M, v, A, r, s, dX, st)
+                  : run_dx_f<WM, WN, TM, TN, kCodeNF4, false>(w, G, M, v, A, r, s, dX, st);
 }
 
 // Tile choice: a 32-row tile for decode-sized batches, else 128x128 (larger
@@ -442,14 +467,14 @@ int pick(int64_t M) { return M <= 32 ? 0 : 1; }
 
 hipError_t launch_qgemm_fwd(const WState& w, const uint16_t* X, int64_t M, const float* u,
                             const uint16_t* B, int r, float s, uint16_t* Y, hipStream_t st) {
-  if (w.absmax || w.codebook != kCodeNF4) return hipErrorInvalidValue;  // NF4 with DQ only
+  if (w.codebook != kCodeNF4 && w.codebook != kCodeFP4) return hipErrorInvalidValue;
   if (pick(M) == 0) return run_fwd<1, 4, 1, 1>(w, X, M, u, B, r, s, Y, st);
   return run_fwd<2, 2, 2, 2>(w, X, M, u, B, r, s, Y, st);
 }
 
 hipError_t launch_qgemm_dx(const WState& w, const uint16_t* G, int64_t M, const float* v,
                            const uint16_t* A, int r, float s, uint16_t* dX, hipStream_t st) {
-  if (w.absmax || w.codebook != kCodeNF4) return hipErrorInvalidValue;  // NF4 with DQ only
+  if (w.codebook != kCodeNF4 && w.codebook != kCodeFP4) return hipErrorInvalidValue;
   if (pick(M) == 0) return run_dx<1, 4, 1, 1>(w, G, M, v, A, r, s, dX, st);
   return run_dx<2, 2, 2, 2>(w, G, M, v, A, r, s, dX, st);
 }

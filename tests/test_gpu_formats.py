@@ -2,8 +2,7 @@
 FT-02: "Guided example 3: double quantization" on/off and "Exercise 3: NF4
 vs FP4 at equal memory"): quantize and dequantize bit-exact for NF4 and FP4
 codes with and without double quantization; merge bit-exact; the linear
-calls within 5e-3 of fp64, at decode sizes through the decode kernels
-(which take every format) and otherwise through the large-batch route; an
+calls within 5e-3 of fp64 on every route (each takes every format); an
 exact one-hot pin through the decode kernels for every format."""
 import numpy as np
 import pytest
@@ -152,9 +151,8 @@ def test_linear_formats(qn, codebook, dq, rows, cols, M, r):
     (4104, 3072, 3, 8, "decode_tiles"), (2048, 2048, 2, 32, "decode_split"),
 ])
 def test_decode_formats(qn, codebook, dq, rows, cols, M, r, route):
-    """Decode-sized forwards of every format: y and u against the fp64
-    oracle on every row (the split route, NF4 with double quantization only,
-    sends the other formats through the large-batch route)."""
+    """Decode-sized forwards of every format on each decode route: y and u
+    against the fp64 oracle on every row."""
     assert qn.route(M, rows, cols, r) == route
     say(f"[formats] decode {codebook} dq={dq} rows={rows} cols={cols} M={M} r={r}")
     W, x, A, B = (wl.weight(rows, cols, 1400 + rows + M), wl.normal_bf16((M, cols), 1401, 1.0),
@@ -176,6 +174,7 @@ def test_decode_formats(qn, codebook, dq, rows, cols, M, r, route):
 @pytest.mark.parametrize("rows,cols,r,route", [
     (14336, 4096, 16, "decode_rows"),
     (4096, 4096, 16, "decode_tiles"),
+    (2048, 2048, 32, "decode_split"),
 ])
 def test_decode_formats_one_hot_exact(qn, codebook, dq, rows, cols, r, route):
     """x rows = e_k (16 per call, every column k over the calls), B = 0:
