@@ -17,6 +17,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras] [--no-c
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import math
 import os
@@ -441,6 +442,9 @@ def bench_extras(torch, qn, wl):
     R = 20
     copies = [qn.NF4State(base.packed.clone(), base.qscale.clone(), base.scale2.clone(),
                           base.offset.clone(), N, K) for _ in range(R)]
+    # the same weight in the other formats (FP4 codes, double quantization off)
+    fmt_states = {f"{cb}_{'dq' if dq else 'nodq'}": qn.qn_quantize(Wq, codebook=cb, double_quant=dq)
+                  for cb, dq in (("fp4", True), ("nf4", False), ("fp4", False))}
     del Wq
     A = _bf16(torch, wl.normal_bf16((r, K), wl.SEED_A + 3, 0.01))
     B = _bf16(torch, wl.normal_bf16((N, r), wl.SEED_B + 3, 0.01))
@@ -479,8 +483,37 @@ def bench_extras(torch, qn, wl):
                             GBs=nbytes / gmed / 1e6, hbm_frac=nbytes / gmed / 1e6 / HBM_PEAK_GBS,
                             eager_GBs=nbytes / med / 1e6)
         del g
+    # M = 1 in the other formats: the same kernels with their level table and
+    # block-scale source (graph of R rotated copies)
+    M = 1
+    x = _bf16(torch, wl.normal_bf16((M, K), wl.SEED_X + 3, 1.0))
+    for name, st0 in fmt_states.items():
+        fc = [dataclasses.replace(st0, **{f: (None if getattr(st0, f) is None
+                                              else getattr(st0, f).clone())
+                                          for f in ("packed", "qscale", "scale2", "offset",
+                                                    "absmax")}) for _ in range(R)]
+        fs = [c.c_struct() for c in fc]
+        ws = qn.linear_workspace(L.qlora_linear_workspace_state(qn.ctypes.byref(fs[0]), M, r, 0,
+                                                                None))
+        ys = [torch.empty((M, N), dtype=torch.bfloat16, device="cuda") for _ in range(R)]
+        us = [torch.empty((M, r), dtype=torch.float32, device="cuda") for _ in range(R)]
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(R):
+                L.qlora_linear_fwd(qn.ctypes.byref(fs[i]), x.data_ptr(), M, A.data_ptr(),
+                                   B.data_ptr(), r, float(alpha), ys[i].data_ptr(),
+                                   us[i].data_ptr(), ws.data_ptr(), ws.numel(),
+                                   torch.cuda.current_stream().cuda_stream)
+        g.replay()
+        torch.cuda.synchronize()
+        gmed, gmn = _median_min([t / R for t in _settled_times(torch, lambda _: g.replay(), 10, 5)])
+        nbytes = decode_bytes(N, K, M, r) - state_bytes(N, K) + st0.nbytes()
+        dec[f"M1_{name}"] = dict(graph_ms=gmed, graph_ms_min=gmn, bytes=nbytes,
+                                 GBs=nbytes / gmed / 1e6,
+                                 hbm_frac=nbytes / gmed / 1e6 / HBM_PEAK_GBS)
+        del g, fc, fs
     out["decode_fwd_14336x4096"] = dec
-    del copies, base
+    del copies, base, fmt_states
     torch.cuda.empty_cache()
 
     # 8-bit AdamW step over the decoder layer's adapters (1,310,720
