@@ -27,12 +27,20 @@ __global__ __launch_bounds__(256) void k_dropout_apply(const uint16_t* __restric
   reinterpret_cast<u32x4*>(Xd)[c] = v;
 }
 
-// Thread = 8 consecutive columns k of one row band: A[j][k .. k+7] for the
-// ranks of a chunk of 16 stay in registers (bf16 pairs), the rows of the
-// band go one after another with their v[m][j] read from LDS as broadcasts.
-// Per element: t = sum_j v[m][j] A[j][k] in fp32 in rank order, then
-// dX = bf16(dX + s t) where the mask bit is set.
-constexpr int LB = 8;   // rows per workgroup
+// Thread = 4 consecutive columns k (one mask nibble, 8 bytes of dX) of a
+// band of LB rows.  With r <= 16 (ONE) the thread's A[j][k .. k+3] are held
+// in fp32 registers for the whole band, loaded before the first barrier;
+// above 16 ranks they are reloaded in chunks of 16 for every row.  The rows go
+// one after another, each row's v[m][j] read from LDS as broadcasts; they
+// move in groups of RG, the next group's dX and mask loaded while the current
+// one is computed (at 8192 x 4096, r = 16: 55 us with groups of 8 rows, 59
+// with 4, 66 with one row ahead, 73 for a first design that converted A for
+// every row).  Per
+// element: t = sum_j v[m][j] A[j][k] in fp32 in rank order, then
+// dX = bf16(dX + s t) where the mask bit is set (dX unchanged elsewhere).
+constexpr int LB = 32;  // rows per workgroup
+constexpr int RG = 8;   // rows per group (the next group's loads go out before this one's products)
+template <bool ONE>
 __global__ __launch_bounds__(256) void k_lora_masked_add(uint16_t* __restrict__ dX,
                                                          const float* __restrict__ v,
                                                          const uint16_t* __restrict__ A,
@@ -45,51 +53,73 @@ __global__ __launch_bounds__(256) void k_lora_masked_add(uint16_t* __restrict__ 
     const int i = e / r, j = e - i * r;
     sv[i][j] = v[min(m0 + i, M - 1) * r + j];
   }
-  const int64_t k = 8 * ((int64_t)blockIdx.x * 256 + tid);
-  const int64_t kc = min(k, K - 8);
-  float t[LB][8];
+  const int64_t k = 4 * ((int64_t)blockIdx.x * 256 + tid);
+  const int64_t kc = min(k, K - 4);  // K % 64 == 0: four columns never straddle a row
+  float a[16][4];
+  auto load_a = [&](int j0) {
 #pragma unroll
-  for (int i = 0; i < LB; ++i)
+    for (int j = 0; j < 16; ++j) {
+      const uint2 q = *reinterpret_cast<const uint2*>(A + (int64_t)min(j0 + j, r - 1) * K + kc);
+      a[j][0] = bf16_lo(q.x);
+      a[j][1] = bf16_hi(q.x);
+      a[j][2] = bf16_lo(q.y);
+      a[j][3] = bf16_hi(q.y);
+    }
+  };
+  if (ONE) load_a(0);
+  const int nrow = (int)min((int64_t)LB, M - m0);
+  // a group's dX and mask nibbles (rows past the band repeat its last row and
+  // are not stored; a thread past K loads at the clamped column, never stores)
+  uint2 d[RG];
+  uint32_t mb[RG];
+  auto load_rows = [&](int i0, uint2* dd, uint32_t* mm) {
 #pragma unroll
-    for (int q = 0; q < 8; ++q) t[i][q] = 0.f;
+    for (int g = 0; g < RG; ++g) {
+      const int64_t e = (m0 + min(i0 + g, nrow - 1)) * K + kc;
+      dd[g] = *reinterpret_cast<const uint2*>(dX + e);
+      mm[g] = mask[e >> 3] >> (kc & 4);
+    }
+  };
+  load_rows(0, d, mb);
   __syncthreads();
-  for (int j0 = 0; j0 < r; j0 += 16) {
-    const int jn = min(16, r - j0);
-    u32x4 a[16];
+  for (int i0 = 0; i0 < nrow; i0 += RG) {
+    uint2 dn[RG];
+    uint32_t mn[RG];
+    if (i0 + RG < nrow) load_rows(i0 + RG, dn, mn);  // the next group, ahead of this one
 #pragma unroll
-    for (int j = 0; j < 16; ++j)
-      a[j] = *reinterpret_cast<const u32x4*>(A + (int64_t)min(j0 + j, r - 1) * K + kc);
+    for (int g = 0; g < RG; ++g) {
+      const int i = i0 + g;
+      if (i >= nrow) break;
+      float t[4] = {0.f, 0.f, 0.f, 0.f};
+      for (int j0 = 0; j0 < r; j0 += 16) {
+        if (!ONE) load_a(j0);
+        const int jn = min(16, r - j0);
 #pragma unroll
-    for (int i = 0; i < LB; ++i)
+        for (int j = 0; j < 16; ++j) {
+          if (j < jn) {
+            const float vj = sv[i][j0 + j];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        if (j < jn) {
-          const float vj = sv[i][j0 + j];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            t[i][2 * q] = __builtin_fmaf(vj, bf16_lo(a[j][q]), t[i][2 * q]);
-            t[i][2 * q + 1] = __builtin_fmaf(vj, bf16_hi(a[j][q]), t[i][2 * q + 1]);
+            for (int c = 0; c < 4; ++c) t[c] = __builtin_fmaf(vj, a[j][c], t[c]);
           }
         }
       }
-  }
-  if (k >= K) return;
-#pragma unroll
-  for (int i = 0; i < LB; ++i) {
-    const int64_t m = m0 + i;
-    if (m >= M) break;
-    const uint32_t mb = mask[(m * K + k) >> 3];
-    u32x4* p = reinterpret_cast<u32x4*>(dX + m * K + k);
-    const u32x4 d = *p;
-    uint32_t o[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      float lo = bf16_lo(d[q]), hi = bf16_hi(d[q]);
-      if ((mb >> (2 * q)) & 1u) lo += s * t[i][2 * q];
-      if ((mb >> (2 * q + 1)) & 1u) hi += s * t[i][2 * q + 1];
-      o[q] = pack_bf16x2(lo, hi);
+      if (k < K) {
+        const uint2 x = d[g];
+        const uint32_t q = mb[g];
+        float lo0 = bf16_lo(x.x), hi0 = bf16_hi(x.x), lo1 = bf16_lo(x.y), hi1 = bf16_hi(x.y);
+        if (q & 1u) lo0 += s * t[0];
+        if (q & 2u) hi0 += s * t[1];
+        if (q & 4u) lo1 += s * t[2];
+        if (q & 8u) hi1 += s * t[3];
+        *reinterpret_cast<uint2*>(dX + (m0 + i) * K + k) =
+            uint2{pack_bf16x2(lo0, hi0), pack_bf16x2(lo1, hi1)};
+      }
     }
-    *p = u32x4{o[0], o[1], o[2], o[3]};
+#pragma unroll
+    for (int g = 0; g < RG; ++g) {
+      d[g] = dn[g];
+      mb[g] = mn[g];
+    }
   }
 }
 
@@ -108,8 +138,13 @@ hipError_t launch_lora_masked_add(uint16_t* dX, const float* v, const uint16_t* 
                                   const uint8_t* mask, int64_t M, int64_t K, int r, float s,
                                   hipStream_t st) {
   if (M <= 0) return hipSuccess;
-  const dim3 grid((unsigned)((K / 8 + 255) / 256), (unsigned)((M + LB - 1) / LB));
-  hipLaunchKernelGGL(k_lora_masked_add, grid, dim3(256), 0, st, dX, v, A, mask, M, K, r, s);
+  const dim3 grid((unsigned)((K / 4 + 255) / 256), (unsigned)((M + LB - 1) / LB));
+  if (r <= 16)
+    hipLaunchKernelGGL(k_lora_masked_add<true>, grid, dim3(256), 0, st, dX, v, A, mask, M, K, r,
+                       s);
+  else
+    hipLaunchKernelGGL(k_lora_masked_add<false>, grid, dim3(256), 0, st, dX, v, A, mask, M, K, r,
+                       s);
   return hipGetLastError();
 }
 
