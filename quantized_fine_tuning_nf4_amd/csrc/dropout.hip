@@ -33,13 +33,14 @@ __global__ __launch_bounds__(256) void k_dropout_apply(const uint16_t* __restric
 // above 16 ranks they are reloaded in chunks of 16 for every row.  The rows go
 // one after another, each row's v[m][j] read from LDS as broadcasts; they
 // move in groups of RG, the next group's dX and mask loaded while the current
-// one is computed (at 8192 x 4096, r = 16: 55 us with groups of 8 rows, 59
-// with 4, 66 with one row ahead, 73 for a first design that converted A for
-// every row).  Per
+// one is computed.  At 8192 x 4096, r = 16: 39 us (groups of 8: 46 us at 3
+// waves per SIMD; with a branch per rank, which kept every rank's LDS read
+// waiting on its own, 55-59 us; one row ahead 66 us; a first design that
+// converted A for every row 73 us).  Per
 // element: t = sum_j v[m][j] A[j][k] in fp32 in rank order, then
 // dX = bf16(dX + s t) where the mask bit is set (dX unchanged elsewhere).
 constexpr int LB = 32;  // rows per workgroup
-constexpr int RG = 8;   // rows per group (the next group's loads go out before this one's products)
+constexpr int RG = 4;   // rows per group (the next group's loads go out before this one's products)
 template <bool ONE>
 __global__ __launch_bounds__(256) void k_lora_masked_add(uint16_t* __restrict__ dX,
                                                          const float* __restrict__ v,
@@ -49,9 +50,13 @@ __global__ __launch_bounds__(256) void k_lora_masked_add(uint16_t* __restrict__ 
   __shared__ float sv[LB][64];
   const int tid = threadIdx.x;
   const int64_t m0 = (int64_t)blockIdx.y * LB;
-  for (int e = tid; e < LB * r; e += 256) {
-    const int i = e / r, j = e - i * r;
-    sv[i][j] = v[min(m0 + i, M - 1) * r + j];
+  // ONE: ranks r..15 are zero in both operands, so the products run without a
+  // branch per rank; t starts at +0 and a sum of nonzero terms is never -0,
+  // so adding +0 leaves every t as the sum over the r ranks alone
+  const int rw = ONE ? 16 : r;
+  for (int e = tid; e < LB * rw; e += 256) {
+    const int i = e / rw, j = e - i * rw;
+    sv[i][j] = j < r ? v[min(m0 + i, M - 1) * r + j] : 0.f;
   }
   const int64_t k = 4 * ((int64_t)blockIdx.x * 256 + tid);
   const int64_t kc = min(k, K - 4);  // K % 64 == 0: four columns never straddle a row
@@ -60,10 +65,11 @@ __global__ __launch_bounds__(256) void k_lora_masked_add(uint16_t* __restrict__ 
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const uint2 q = *reinterpret_cast<const uint2*>(A + (int64_t)min(j0 + j, r - 1) * K + kc);
-      a[j][0] = bf16_lo(q.x);
-      a[j][1] = bf16_hi(q.x);
-      a[j][2] = bf16_lo(q.y);
-      a[j][3] = bf16_hi(q.y);
+      const bool live = !ONE || j < r;
+      a[j][0] = live ? bf16_lo(q.x) : 0.f;
+      a[j][1] = live ? bf16_hi(q.x) : 0.f;
+      a[j][2] = live ? bf16_lo(q.y) : 0.f;
+      a[j][3] = live ? bf16_hi(q.y) : 0.f;
     }
   };
   if (ONE) load_a(0);
@@ -91,15 +97,24 @@ __global__ __launch_bounds__(256) void k_lora_masked_add(uint16_t* __restrict__ 
       const int i = i0 + g;
       if (i >= nrow) break;
       float t[4] = {0.f, 0.f, 0.f, 0.f};
-      for (int j0 = 0; j0 < r; j0 += 16) {
-        if (!ONE) load_a(j0);
-        const int jn = min(16, r - j0);
+      if (ONE) {
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-          if (j < jn) {
-            const float vj = sv[i][j0 + j];
+          const float vj = sv[i][j];
 #pragma unroll
-            for (int c = 0; c < 4; ++c) t[c] = __builtin_fmaf(vj, a[j][c], t[c]);
+          for (int c = 0; c < 4; ++c) t[c] = __builtin_fmaf(vj, a[j][c], t[c]);
+        }
+      } else {
+        for (int j0 = 0; j0 < r; j0 += 16) {
+          load_a(j0);
+          const int jn = min(16, r - j0);
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            if (j < jn) {
+              const float vj = sv[i][j0 + j];
+#pragma unroll
+              for (int c = 0; c < 4; ++c) t[c] = __builtin_fmaf(vj, a[j][c], t[c]);
+            }
           }
         }
       }
