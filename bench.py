@@ -325,7 +325,8 @@ def bench_train(torch, qn, wl, steps, warmup):
     res["gemm_ms"] = _median_min(gemm_ms)
     # the adapter-branch variants on the same workload: rsLoRA's scale (no
     # extra work) and dropout p = 0.05 on the branch's input (a keep mask in,
-    # the masked x for dA, the branch's dX share added after the base product)
+    # the u and dA products mask x as they load it, the branch's dX share is
+    # added after the base product)
     mask = qn.dropout_mask(M, K, 0.05, generator=torch.Generator(device="cuda").manual_seed(7))
     dws = qn.linear_workspace(max(L.qlora_linear_workspace_ex(M, N, K, r, 1, None),
                                   L.qlora_linear_workspace_ex(

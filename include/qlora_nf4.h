@@ -211,8 +211,8 @@ qn_status qlora_linear_fwd_noalloc(const qn_nf4dq* w, const uint16_t* x, int64_t
  *     bit-packed row-major (element e kept when bit e % 8 of byte e / 8 is
  *     set), device memory; the caller draws it.  Kept elements pass
  *     unchanged and the branch's scale becomes s / (1 - dropout_p); the
- *     backward takes the same mask (dA reads the masked x, the branch's
- *     share of dX is masked).  Forwards with dropout take the GEMM routes,
+ *     backward takes the same mask (the dA product masks x where it loads
+ *     it, the branch's share of dX is masked).  Forwards with dropout take the GEMM routes,
  *     never the decode kernels.
  *   dropout_p: in [0, 1) with a mask; 0 without one. */
 typedef struct {
@@ -226,9 +226,9 @@ typedef struct {
 size_t qlora_linear_workspace_state(const qn_nf4dq* w, int64_t M, int r, int backward,
                                     const qn_lora_opts* opts);
 
-/* Workspace bytes for the _ex calls with these options (dropout needs room
- * for the masked x in the backward), for an NF4 state with double
- * quantization. */
+/* Workspace bytes for the _ex calls with these options (with dropout the
+ * forward of a small batch takes a GEMM route instead of a decode kernel),
+ * for an NF4 state with double quantization. */
 size_t qlora_linear_workspace_ex(int64_t M, int64_t rows, int64_t cols, int r, int backward,
                                  const qn_lora_opts* opts);
 

@@ -166,11 +166,9 @@ struct BwdWs {
   uint16_t* wt;   // [cols, ldt] bf16 Qhat(W)^T (dense path)
   int64_t ldt;
   uint16_t* At;   // [cols, r] A^T (dense path)
-  uint16_t* xd;   // [M, cols] the adapter branch's masked input (dropout)
 };
 
-BwdWs carve_bwd(Carver& c, int64_t M, int64_t rows, int64_t cols, int r, bool need_u,
-                bool dropout = false) {
+BwdWs carve_bwd(Carver& c, int64_t M, int64_t rows, int64_t cols, int r, bool need_u) {
   BwdWs b;
   b.arrivals = c.take<unsigned>(kArrivalWords);
   if (need_u) {
@@ -194,7 +192,6 @@ BwdWs carve_bwd(Carver& c, int64_t M, int64_t rows, int64_t cols, int r, bool ne
   const bool dense = M > 0 && dense_path(M, cols);
   b.wt = dense ? c.take<uint16_t>((size_t)cols * b.ldt) : nullptr;
   b.At = dense ? c.take<uint16_t>((size_t)cols * r) : nullptr;
-  b.xd = dropout ? c.take<uint16_t>((size_t)M * cols) : nullptr;
   return b;
 }
 
@@ -399,7 +396,7 @@ size_t qlora_linear_workspace_ex(int64_t M, int64_t rows, int64_t cols, int r, i
   const bool drop = opts && opts->dropout_mask;
   Carver c(nullptr);
   if (backward)
-    carve_bwd(c, M, rows, cols, r, true, drop);
+    carve_bwd(c, M, rows, cols, r, true);
   else
     carve_fwd(c, M, rows, cols, r, true, true, drop);
   return c.used;
@@ -415,7 +412,7 @@ size_t qlora_linear_workspace_state(const qn_nf4dq* w, int64_t M, int r, int bac
   const bool drop = opts && opts->dropout_mask;
   Carver c(nullptr);
   if (backward)
-    carve_bwd(c, M, w->rows, w->cols, r, true, drop);
+    carve_bwd(c, M, w->rows, w->cols, r, true);
   else
     carve_fwd(c, M, w->rows, w->cols, r, true, true, drop);
   return c.used;
@@ -492,17 +489,14 @@ qn_status qlora_linear_bwd_ex(const qn_nf4dq* w, const uint16_t* x, const uint16
     return from_hip(e);
   }
   Carver probe(nullptr);
-  carve_bwd(probe, M, N, K, r, u_saved == nullptr, drop);
+  carve_bwd(probe, M, N, K, r, u_saved == nullptr);
   if (!workspace) return QN_EINVAL;
   if (reinterpret_cast<uintptr_t>(workspace) & 255u) return QN_EALIGN;
   if (workspace_bytes < probe.used) return QN_EWORKSPACE;
   Carver c(workspace);
-  BwdWs b = carve_bwd(c, M, N, K, r, u_saved == nullptr, drop);
+  BwdWs b = carve_bwd(c, M, N, K, r, u_saved == nullptr);
   const float scale = lo.s;
   hipError_t e = hipSuccess;
-  // dropout: the adapter branch's masked input, for dA (u takes the mask on
-  // the fly)
-  if (drop) e = launch_dropout_apply(x, lo.mask, M, K, b.xd, st);
   const float* u = u_saved;
   // an early launch of the call zeroes the arrival counters the adapter
   // gradients' launch counts on, so the backward never depends on what the
@@ -569,7 +563,7 @@ qn_status qlora_linear_bwd_ex(const qn_nf4dq* w, const uint16_t* x, const uint16
   // dB = s G^T u and dA = s v^T X in one launch (and their slice sums in one)
   if (e == hipSuccess)
     e = launch_thin_tn2(ThinTn{dY, b.su, N, dB, false, b.dBpart},
-                        ThinTn{drop ? b.xd : x, b.sv, K, dA, true, b.dApart}, M, r, b.arrivals,
+                        ThinTn{x, b.sv, K, dA, true, b.dApart, lo.mask}, M, r, b.arrivals,
                         st);
   return from_hip(e);
 }

@@ -2,30 +2,15 @@
 // the QLoRA setup: lora_dropout).  The keep mask is an input, bit-packed
 // over the row-major elements of x [M, K] (bit e % 8 of byte e / 8 set:
 // kept); kept elements pass unchanged and 1/(1-p) is folded into the
-// branch's scale by the caller.  Two streaming kernels:
-//   - k_dropout_apply writes the branch's input mask (.) x (the backward's
-//     dA product reads it);
-//   - k_lora_masked_add adds the branch's share of the input gradient,
-//     s ((G B) A) (.) mask, to the base product's dX.
+// branch's scale by the caller.  The products that read x apply the mask
+// where they load it (u in the forward, dA in the backward); this file's
+// streaming kernel, k_lora_masked_add, adds the branch's share of the input
+// gradient, s ((G B) A) (.) mask, to the base product's dX.
 #include "qn_device.h"
 #include "qn_internal.h"
 
 namespace qn {
 namespace {
-
-// Thread = 8 consecutive elements (one mask byte, 16 bytes of x).
-__global__ __launch_bounds__(256) void k_dropout_apply(const uint16_t* __restrict__ X,
-                                                       const uint8_t* __restrict__ mask,
-                                                       int64_t n8, uint16_t* __restrict__ Xd) {
-  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (c >= n8) return;
-  u32x4 v = reinterpret_cast<const u32x4*>(X)[c];
-  const uint32_t mb = mask[c];
-#pragma unroll
-  for (int q = 0; q < 4; ++q)
-    v[q] &= (((mb >> (2 * q)) & 1u) * 0xffffu) | (((mb >> (2 * q + 1)) & 1u) * 0xffff0000u);
-  reinterpret_cast<u32x4*>(Xd)[c] = v;
-}
 
 // Thread = 4 consecutive columns k (one mask nibble, 8 bytes of dX) of a
 // band of LB rows.  With r <= 16 (ONE) the thread's A[j][k .. k+3] are held
@@ -139,15 +124,6 @@ __global__ __launch_bounds__(256) void k_lora_masked_add(uint16_t* __restrict__ 
 }
 
 }  // namespace
-
-hipError_t launch_dropout_apply(const uint16_t* X, const uint8_t* mask, int64_t M, int64_t K,
-                                uint16_t* Xd, hipStream_t st) {
-  const int64_t n8 = M * K / 8;
-  if (n8 <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_dropout_apply, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st, X,
-                     mask, n8, Xd);
-  return hipGetLastError();
-}
 
 hipError_t launch_lora_masked_add(uint16_t* dX, const float* v, const uint16_t* A,
                                   const uint8_t* mask, int64_t M, int64_t K, int r, float s,

@@ -405,6 +405,7 @@ struct TnJob {
   float* part;         // [S, P, r]
   float* out;          // [P, r], or [r, P] when transposed
   int transposed;
+  const uint8_t* zmask;  // keep bits of Z (dropout on x), or null
 };
 
 // Arrival counters of the column tiles of one launch (both jobs' tiles in
@@ -418,12 +419,32 @@ constexpr int kDeviceScope = 16;  // sc1: the level every XCD shares
 // tile's S workgroups to arrive (an arrival counter per tile) adds the S
 // slices of the tile in slice order with device-coherent loads and writes
 // the output.
-template <int NJ>
+// vmcnt wait for the given count (an immediate of the instruction).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 4 && N <= 11, "counts of k_thin_tn's steps");
+  if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+  else if constexpr (N == 5) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+  else if constexpr (N == 6) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+  else if constexpr (N == 7) asm volatile("s_waitcnt vmcnt(7)" ::: "memory");
+  else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  else if constexpr (N == 9) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+  else if constexpr (N == 10) asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(11)" ::: "memory");
+}
+
+// MASK: a job may carry keep bits of Z (dropout on the adapter branch's
+// input, for dA): the step's 32 rows x 16 bytes of bits go global -> LDS
+// beside Z (one 4-byte-per-lane load in waves 0 and 1: rows 16w .. 16w+15;
+// the direct-to-LDS path writes one dword per lane), and the dropped values
+// are zeroed in the A operand after the transposed reads.
+template <int NJ, bool MASK>
 __global__ __launch_bounds__(kThreads) void k_thin_tn(TnJob j0, TnJob j1, int64_t M, int r,
                                                       unsigned* __restrict__ arrivals) {
   constexpr int ZB = 32 * TN_ROWB;             // Z bytes per stage
   constexpr int VB = 2 * 16 * NJ * 64;         // (sV)^T bytes per stage
-  constexpr int SB = ZB + VB;
+  constexpr int KB = MASK ? 32 * 16 : 0;       // keep bits per stage
+  constexpr int SB = ZB + VB + KB;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const bool second = (int)blockIdx.x >= j0.tiles;
@@ -434,6 +455,8 @@ __global__ __launch_bounds__(kThreads) void k_thin_tn(TnJob j0, TnJob j1, int64_
   const int64_t slice = second ? j1.slice : j0.slice;
   const int S = second ? j1.S : j0.S;
   float* part = second ? j1.part : j0.part;
+  const uint8_t* zmask = MASK ? (second ? j1.zmask : j0.zmask) : nullptr;
+  const bool hm = MASK && zmask != nullptr;  // workgroup-uniform
   if ((int)blockIdx.y >= S) return;
   const int64_t p0 = (int64_t)((int)blockIdx.x - (second ? j0.tiles : 0)) * TN_COLS;
   const int64_t mb = (int64_t)blockIdx.y * slice;
@@ -451,6 +474,10 @@ __global__ __launch_bounds__(kThreads) void k_thin_tn(TnJob j0, TnJob j1, int64_
   // bytes (below 2^31, thin_tn_slice_rows) are ever addressed by an offset
   const rsrc_t rz = make_rs(Z + mb * P, (uint32_t)((me - mb) * P * 2));
   const rsrc_t rv = make_rs(vt + mb, (uint32_t)((2 * 16 * NJ * Mp - mb) * 2));
+  // keep bits from the slice's first row (P % 64 == 0: rows start on a byte);
+  // bytes past the slice read as zero (columns past P are not stored)
+  const rsrc_t rk = make_rs(hm ? zmask + mb * P / 8 : reinterpret_cast<const uint8_t*>(Z),
+                            hm ? (uint32_t)((me - mb) * P / 8) : 0u);
   uint32_t zoff[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
@@ -477,14 +504,24 @@ __global__ __launch_bounds__(kThreads) void k_thin_tn(TnJob j0, TnJob j1, int64_
     for (int k = 0; k < 2 * NJ; ++k)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(base + ZB + 256 * (2 * NJ * wave + k)),
                                                4, voff[k] + (uint32_t)(64 * st), 0, 0, 0);
+    if constexpr (MASK) {
+      if (hm && wave < 2) {  // lane l: row 16w + l/4, bytes 4(l%4) .. +3 of the tile's 16
+        const int row = 16 * wave + (lane >> 2);
+        const int64_t mm = min(mb + 32 * (int64_t)st + row, M - 1);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rk, (lds_void*)(base + ZB + VB + 256 * wave), 4,
+            (uint32_t)((((mm - mb) * P + p0) >> 3) + 4 * (lane & 3)), 0, 0, 0);
+      }
+    }
   };
   // all but the newest step's loads (2 + 2 NJ per wave) have landed
+  // (one more in waves 0 and 1 when the keep bits come along)
   auto wait_step = [&]() {
     static_assert(TN_NST == 3, "one step in flight beyond the next");
-    if constexpr (NJ == 1) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-    else if constexpr (NJ == 2) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
-    else if constexpr (NJ == 3) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+    if (MASK && hm && wave < 2)
+      wait_vm<2 + 2 * NJ + (MASK ? 1 : 0)>();
+    else
+      wait_vm<2 + 2 * NJ>();
   };
   for (int k = 0; k < TN_NST - 1; ++k) load_step(min(k, steps - 1), k);
   wait_step();
@@ -525,9 +562,30 @@ __global__ __launch_bounds__(kThreads) void k_thin_tn(TnJob j0, TnJob j1, int64_
         : "=&v"(x00), "=&v"(x01), "=&v"(x10), "=&v"(x11)
         : "v"(zb + aoff[0][0]), "v"(zb + aoff[0][1]), "v"(zb + aoff[1][0]), "v"(zb + aoff[1][1])
         : "memory");
+    u32x4 za[2] = {u32x4{x00[0], x00[1], x01[0], x01[1]}, u32x4{x10[0], x10[1], x11[0], x11[1]}};
+    if constexpr (MASK) {
+      if (hm) {
+        // word i of za[pt] holds rows 8g + 2i, 8g + 2i + 1 of column
+        // 32w + 16pt + t, whose keep bits are bit 16pt + t of the word at
+        // byte 4w of each row's 16 bytes
+        const uint8_t* ks = zs + ZB + VB + 4 * wave;
+        uint32_t kw[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          kw[q] = *reinterpret_cast<const uint32_t*>(ks + 16 * (8 * g + q));
+#pragma unroll
+        for (int pt = 0; pt < 2; ++pt) {
+          const int sh = 16 * pt + t;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            za[pt][i] &= (((kw[2 * i] >> sh) & 1u) * 0xffffu) |
+                         (((kw[2 * i + 1] >> sh) & 1u) * 0xffff0000u);
+        }
+      }
+    }
     bf16x8 a[2];
-    a[0] = as_bf16x8(u32x4{x00[0], x00[1], x01[0], x01[1]});
-    a[1] = as_bf16x8(u32x4{x10[0], x10[1], x11[0], x11[1]});
+    a[0] = as_bf16x8(za[0]);
+    a[1] = as_bf16x8(za[1]);
 #pragma unroll
     for (int jt = 0; jt < NJ; ++jt) {
       // B operand: column j = 16jt + l%16, rows 8g..8g+7 of the step
@@ -736,6 +794,7 @@ hipError_t launch_thin_tn2(const ThinTn& a, const ThinTn& b, int64_t M, int r,
     j.part = x.part;
     j.out = x.out;
     j.transposed = x.transposed ? 1 : 0;
+    j.zmask = x.zmask;
     if (j.tiles > 0) s_max = std::max(s_max, j.S);
   }
   const int tiles = job[0].tiles + job[1].tiles;
@@ -743,14 +802,23 @@ hipError_t launch_thin_tn2(const ThinTn& a, const ThinTn& b, int64_t M, int r,
   // slices added by the last workgroup of each tile (one arrival counter per
   // tile), else by a second launch
   unsigned* ctr = tiles <= kTnMaxTiles ? arrivals : nullptr;
-  const size_t lds = (size_t)TN_NST * (32 * TN_ROWB + 2 * 16 * nj * 64);
+  const bool mask = (job[0].tiles > 0 && job[0].zmask) || (job[1].tiles > 0 && job[1].zmask);
+  const size_t lds = (size_t)TN_NST * (32 * TN_ROWB + 2 * 16 * nj * 64 + (mask ? 32 * 16 : 0));
   const dim3 grid((unsigned)tiles, (unsigned)s_max);
+#define QN_TN(NJ)                                                                              \
+  if (mask)                                                                                    \
+    hipLaunchKernelGGL((k_thin_tn<NJ, true>), grid, dim3(kThreads), lds, st, job[0], job[1], M, \
+                       r, ctr);                                                                \
+  else                                                                                         \
+    hipLaunchKernelGGL((k_thin_tn<NJ, false>), grid, dim3(kThreads), lds, st, job[0], job[1], M, \
+                       r, ctr)
   switch (nj) {
-    case 1: hipLaunchKernelGGL(k_thin_tn<1>, grid, dim3(kThreads), lds, st, job[0], job[1], M, r, ctr); break;
-    case 2: hipLaunchKernelGGL(k_thin_tn<2>, grid, dim3(kThreads), lds, st, job[0], job[1], M, r, ctr); break;
-    case 3: hipLaunchKernelGGL(k_thin_tn<3>, grid, dim3(kThreads), lds, st, job[0], job[1], M, r, ctr); break;
-    default: hipLaunchKernelGGL(k_thin_tn<4>, grid, dim3(kThreads), lds, st, job[0], job[1], M, r, ctr); break;
+    case 1: QN_TN(1); break;
+    case 2: QN_TN(2); break;
+    case 3: QN_TN(3); break;
+    default: QN_TN(4); break;
   }
+#undef QN_TN
   if (ctr) return hipGetLastError();
   TnSum sum[2];
   int64_t count = 0;

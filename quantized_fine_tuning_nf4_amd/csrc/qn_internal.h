@@ -244,10 +244,6 @@ struct AdamScalars {
 hipError_t launch_adamw8(float* p, const float* g, int64_t n, uint8_t* mq, float* ms, uint8_t* vq,
                          float* vs, uint16_t* pb, const AdamScalars& h, hipStream_t st);
 
-// Xd [M, K] = X with the elements whose mask bit is clear zeroed (K % 8 == 0).
-hipError_t launch_dropout_apply(const uint16_t* X, const uint8_t* mask, int64_t M, int64_t K,
-                                uint16_t* Xd, hipStream_t st);
-
 // dX[m][k] (bf16) += s (v A)[m][k] where mask bit (m, k) is set: the
 // adapter branch's input gradient under dropout.  v fp32 [M, r], A bf16
 // [r, K], K % 8 == 0, 1 <= r <= 64.
@@ -273,6 +269,7 @@ struct ThinTn {
   float* out;
   bool transposed;
   float* part;
+  const uint8_t* zmask = nullptr;  // keep bits of Z [M, P] (dropout), or null
 };
 // Two such products (same M and r) in one launch; the slices are added by
 // the last workgroup of each column tile to finish (arrivals: kArrivalWords
