@@ -832,6 +832,46 @@ def layer_workload(torch, qn, wl, reps=3):
             print(f"[layer] pass {rep} {d['name']}", file=sys.stderr, flush=True)
 
 
+def adapter_workload(torch, qn, wl, reps=5):
+    """The adapter rows' kernels for a kernel trace: the merge W' + s B A of a
+    4096x4096 weight (r = 16) `reps` times, then the training shape's forward
+    and backward (8192x4096x4096, r = 16) with dropout p = 0.05 on the
+    adapter branch `reps` times, then once more without dropout; a
+    synchronization and a stderr line after each call so that the trace can be
+    cut into calls."""
+    L = qn.load_library()
+    cfg = wl.TRAIN
+    N, K, M, r, alpha = cfg["rows"], cfg["cols"], cfg["M"], cfg["r"], cfg["alpha"]
+    st = qn.nf4_quantize_dq(torch.from_numpy(wl.weight(N, K, wl.SEED_W)).cuda())
+    Am = _bf16(torch, wl.normal_bf16((16, K), wl.SEED_A + 2, 0.01))
+    Bm = _bf16(torch, wl.normal_bf16((N, 16), wl.SEED_B + 2, 0.01))
+    merged = torch.empty((N, K), dtype=torch.float32, device="cuda")
+    for rep in range(reps):
+        qn.nf4_merge_lora(st, Am, Bm, 32.0, out=merged)
+        torch.cuda.synchronize()
+        print(f"[adapter] merge {rep}", file=sys.stderr, flush=True)
+    xd = _bf16(torch, wl.normal_bf16((M, K), wl.SEED_X, 1.0))
+    Gd = _bf16(torch, wl.normal_bf16((M, N), wl.SEED_DY, 1.0))
+    Ad = _bf16(torch, wl.normal_bf16((r, K), wl.SEED_A, 0.01))
+    Bd = _bf16(torch, wl.normal_bf16((N, r), wl.SEED_B, 0.01))
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    mask = qn.dropout_mask(M, K, 0.05, generator=torch.Generator(device="cuda").manual_seed(7))
+    dws = qn.linear_workspace(max(L.qlora_linear_workspace_ex(M, N, K, r, 1, None),
+                                  L.qlora_linear_workspace_ex(
+                                      M, N, K, r, 1, qn.ctypes.byref(qn._LoraOpts(0, 1, 0.05)))))
+    for rep in range(reps + 1):
+        drop = rep < reps
+        kw = dict(dropout_mask=mask, dropout_p=0.05) if drop else {}
+        _, u = qn.qlora_linear_fwd(st, xd, Ad, Bd, alpha, y=y, workspace=dws, **kw)
+        torch.cuda.synchronize()
+        print(f"[adapter] forward {'dropout' if drop else 'plain'} {rep}", file=sys.stderr,
+              flush=True)
+        qn.qlora_linear_bwd(st, xd, Gd, Ad, Bd, alpha, u, workspace=dws, **kw)
+        torch.cuda.synchronize()
+        print(f"[adapter] backward {'dropout' if drop else 'plain'} {rep}", file=sys.stderr,
+              flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -844,6 +884,9 @@ def main():
     ap.add_argument("--layer", action="store_true",
                     help="only the decoder layer's seven linears, forward and backward, "
                          "three times (for a rocprofv3 kernel trace)")
+    ap.add_argument("--adapter", action="store_true",
+                    help="only the adapter merge and the dropout training step, five times "
+                         "each (for a rocprofv3 kernel trace)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "bench.py runs on one GPU only: the hot path is measured "
@@ -862,6 +905,9 @@ def main():
         return
     if args.layer:
         layer_workload(torch, qn, wl)
+        return
+    if args.adapter:
+        adapter_workload(torch, qn, wl)
         return
     print(f"[bench] training step: {args.warmup} warmup + {args.steps} timed", file=sys.stderr,
           flush=True)
