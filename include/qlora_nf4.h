@@ -209,7 +209,8 @@ qn_status qlora_linear_fwd_noalloc(const qn_nf4dq* w, const uint16_t* x, int64_t
  *   dropout_mask (nullable): dropout on the adapter branch's input (FT-02,
  *     the LoraConfig's lora_dropout): a keep mask over x [M, cols],
  *     bit-packed row-major (element e kept when bit e % 8 of byte e / 8 is
- *     set), device memory; the caller draws it.  Kept elements pass
+ *     set), device memory, 16-byte aligned (QN_EALIGN otherwise); the
+ *     caller draws it.  Kept elements pass
  *     unchanged and the branch's scale becomes s / (1 - dropout_p); the
  *     backward takes the same mask (the dA product masks x where it loads
  *     it, the branch's share of dX is masked).  Forwards with dropout take the GEMM routes,

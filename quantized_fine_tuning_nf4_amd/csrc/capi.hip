@@ -211,6 +211,7 @@ qn_status lora_options(const qn_lora_opts* o, float alpha, int r, Lora* out) {
   if (o->dropout_mask) {
     const float p = o->dropout_p;
     if (!(p >= 0.f && p < 1.f)) return QN_EINVAL;
+    if (!aligned16(o->dropout_mask)) return QN_EALIGN;  // read in 8- and 16-byte pieces
     out->mask = o->dropout_mask;
     out->s = out->s / (1.f - p);  // inverted dropout, folded into the scale
   } else if (o->dropout_p != 0.f) {

@@ -146,13 +146,25 @@ __global__ __launch_bounds__(kThreads) void k_thin_nt1(const uint16_t* __restric
   const uint16_t* zp = Z + m * P + pb + 8 * g;
   const int64_t lim = width - 8 * g;  // in-slice columns left for this lane's chunk
   u32x4 za[2][TN1_U];
-  uint32_t zm[2][TN1_U];  // their mask bytes (dropout on Z), loaded beside them
+  // the batch's mask bytes (dropout on Z), loaded beside it: row m's 16
+  // bytes for the batch's 128 columns as two 8-byte halves (two steps each;
+  // P % 64 == 0 and the slice starts on 128 columns, so each half is aligned
+  // and lies in the row when its first column is in the slice; a half past
+  // the slice reads the slice's first one instead, for steps zeroed at use)
+  static_assert(TN1_U == 4, "two steps per 8-byte half of a batch's mask bytes");
+  uint2 zk[2][2];
   auto load_batch = [&](int buf, int b) {
 #pragma unroll
     for (int u = 0; u < TN1_U; ++u) {
       const int64_t off = 32 * (int64_t)(TN1_U * b + u);
       za[buf][u] = *reinterpret_cast<const u32x4*>(zp + (off < lim ? off : 0));
-      if (zmask) zm[buf][u] = zmask[(m * P + pb + 8 * g + (off < lim ? off : 0)) >> 3];
+    }
+    if (zmask) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int64_t c = 128 * (int64_t)b + 64 * h;
+        zk[buf][h] = *reinterpret_cast<const uint2*>(zmask + ((m * P + pb + (c < width ? c : 0)) >> 3));
+      }
     }
   };
   if constexpr (TMODE == 0) {
@@ -238,7 +250,10 @@ __global__ __launch_bounds__(kThreads) void k_thin_nt1(const uint16_t* __restric
       const int st = TN1_U * b + u;
       if (st < steps) {
         u32x4 z = 32 * (int64_t)st < lim ? za[buf][u] : u32x4{0u, 0u, 0u, 0u};
-        if (zmask) z = keep8(z, zm[buf][u]);
+        if (zmask) {  // byte g of the step's four: this lane's eight columns
+          const uint32_t w = (u & 1) ? zk[buf][u >> 1].y : zk[buf][u >> 1].x;
+          z = keep8(z, (w >> (8 * g)) & 0xffu);
+        }
         const u32x4 t = *reinterpret_cast<const u32x4*>(trow + 64 * st);
         acc = mfma16(as_bf16x8(z), as_bf16x8(t), acc);
       }

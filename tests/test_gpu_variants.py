@@ -146,3 +146,10 @@ def test_options_are_checked_on_the_host(qn):
                                    Bd.data_ptr(), 4, 8.0, ctypes.byref(opts), y.data_ptr(), None,
                                    ws.data_ptr(), ws.numel(), None)
         assert rc == qn.QN_EINVAL
+    # the mask is read in 8- and 16-byte pieces: a misaligned one is refused
+    # before anything is launched
+    bad = qn._LoraOpts(0, md.data_ptr() + 1, 0.05)
+    rc = L.qlora_linear_fwd_ex(ctypes.byref(s), xd.data_ptr(), 8, Ad.data_ptr(), Bd.data_ptr(), 4,
+                               8.0, ctypes.byref(bad), y.data_ptr(), None, ws.data_ptr(),
+                               ws.numel(), None)
+    assert rc == qn.QN_EALIGN
